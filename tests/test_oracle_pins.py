@@ -1,0 +1,490 @@
+"""Pins for the CPU oracle: facts fixed by the pages and by mathematics.
+
+Each test ties an oracle function to something other than itself -- numbers
+the pages print, closed forms, invariants, or special cases that reduce to a
+textbook library routine (numpy complex rotation, torch's scaled dot-product
+attention in float64, numpy SVD).  Each is chosen so that a plausible slip in
+the oracle (a dropped mu, a wrong RoPE sign or pair layout, a transposed W_up,
+the wrong loop slice, the wrong page-table index) fails at least one of them.
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fixtures import (BF16, F32, PER_HEAD, TWO_D, dims, f64, param_shapes, pool_shape,
+                      random_codec, random_pools, rank8_activations, store, svd_codec_one)
+from looped_transformer_latent_amd import gen
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- references
+
+def rope_complex(x: np.ndarray, pos, base: float = 10000.0) -> np.ndarray:
+    """RoPE written as complex multiplication: pair (i, i + d/2) is the complex
+    number x_i + 1j*x_{i+d/2}, rotated by exp(1j * pos * base**(-2i/d))."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    h = d // 2
+    pos = np.asarray(pos, dtype=np.float64)[..., None]
+    theta = pos * np.power(base, -2.0 * np.arange(h) / d)
+    z = (x[..., :h] + 1j * x[..., h:]) * np.exp(1j * theta)
+    return np.concatenate([z.real, z.imag], axis=-1)
+
+
+def sdpa(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
+    """torch's scaled_dot_product_attention (float64, CPU) for one query."""
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64))
+    o = torch.nn.functional.scaled_dot_product_attention(
+        t(q)[None, None, None, :], t(K)[None, None], t(V)[None, None], scale=scale)
+    return o[0, 0, 0].numpy()
+
+
+def gather_latents(pool: np.ndarray, page_table: np.ndarray, b: int, L: int, P: int, h=None):
+    """Latent rows of logical tokens 0..L-1 of sequence b (float64), read with
+    numpy fancy indexing (independent of the oracle's slot arithmetic)."""
+    j = np.arange(L)
+    pages = page_table[b, j // P]
+    if h is None:
+        rows = pool[:, pages, j % P, :]
+    else:
+        rows = pool[:, pages, h, j % P, :]
+    return f64(rows)  # [D][L][r]
+
+
+# ---------------------------------------------------------------- P1: eq. (4), Table 5
+
+def _golden_rows():
+    rows = []
+    with open(os.path.join(GOLDEN, "cache_scalars.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+@pytest.mark.parametrize("row", _golden_rows(), ids=lambda r: r[0])
+def test_p1_cache_scalars_match_pages(row):
+    (_, T, H, D, d, rk, rv, bps, t_sc, l_sc, t_kib, l_kib, rn, rd, t_gib, l_gib) = row
+    T, H, D, d, rk, rv, bps = map(int, (T, H, D, d, rk, rv, bps))
+    teacher, latent = oracle.cache_scalars(T, H, d, rk, rv, PER_HEAD)
+    assert teacher == int(t_sc) and latent == int(l_sc)
+    # ratio rho = 2 T d / (r_k + r_v), exact rational
+    assert teacher * int(rd) == latent * int(rn)
+    assert 2 * T * d * int(rd) == (rk + rv) * int(rn)
+    # bytes per token over all D layers, in KiB (bf16)
+    assert teacher * D * bps == int(t_kib) * 1024
+    assert latent * D * bps == int(l_kib) * 1024
+    # 1M context on the 2**20-token reading, in GiB
+    assert teacher * D * bps * 2 ** 20 == int(t_gib) * 2 ** 30
+    assert latent * D * bps * 2 ** 20 == int(l_gib) * 2 ** 30
+
+
+def test_p1_two_d_is_h_times_smaller():
+    # LLA-2D stores r_k + r_v per token and layer: H times fewer than per-head at fixed ranks.
+    for H in (1, 16, 32):
+        _, ph = oracle.cache_scalars(8, H, 128, 256, 256, PER_HEAD)
+        _, td = oracle.cache_scalars(8, H, 128, 256, 256, TWO_D)
+        assert ph == H * td == H * 512
+
+
+# ---------------------------------------------------------------- bf16 rounding
+
+@pytest.mark.parametrize("x,bits", [
+    (1.0, 0x3F80), (-2.0, 0xC000), (0.0, 0x0000), (-0.0, 0x8000),
+    (1.0 + 2 ** -8, 0x3F80),             # exact midpoint, tie to even (down)
+    (1.0 + 3 * 2 ** -8, 0x3F82),         # exact midpoint, tie to even (up)
+    (1.0 + 2 ** -8 + 2 ** -40, 0x3F81),  # just above the midpoint (no double rounding via fp32)
+    (1.0 + 2 ** -8 - 2 ** -40, 0x3F80),
+    (3.0e38, 0x7F62), (3.4e38, 0x7F80),  # rounds up past the largest bf16 -> inf
+    (2.0 ** -133, 0x0001), (2.0 ** -134, 0x0000), (3 * 2.0 ** -135, 0x0001),
+    (float("inf"), 0x7F80), (float("-inf"), 0xFF80),
+])
+def test_bf16_rne_closed_form(x, bits):
+    assert oracle.bf16_rne(x) == bits
+
+
+def test_bf16_rne_matches_torch_on_fp32_values():
+    # For values exactly representable in fp32, RNE from double equals torch's fp32->bf16 RNE.
+    v = gen.normal_f32(7, 1, 20000, scale=3.0)
+    v = np.concatenate([v, v * 1e-30, v * 1e30]).astype(np.float32)
+    want = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([oracle.bf16_rne(float(x)) for x in v], dtype=np.uint16)
+    assert np.array_equal(got, want)
+
+
+# ---------------------------------------------------------------- RoPE
+
+@pytest.mark.parametrize("d", [4, 64, 128])
+def test_rope_matches_complex_rotation(d):
+    x = gen.normal_f32(3, d, d).astype(np.float64)
+    for pos in (0, 1, 7, 255, 4095, 16383):
+        # the angle pos * base**(-2i/d) itself carries ~pos ulps from pow(); allow that
+        atol = 1e-13 + 8 * pos * np.finfo(np.float64).eps * np.abs(x).max()
+        np.testing.assert_allclose(oracle.rope(x, pos), rope_complex(x, pos), rtol=0, atol=atol)
+
+
+def test_rope_invariants():
+    d = 128
+    x = gen.normal_f32(4, 1, d).astype(np.float64)
+    y = gen.normal_f32(4, 2, d).astype(np.float64)
+    assert np.array_equal(oracle.rope(x, 0), x)                                  # R(0) = I
+    for p in (1, 100, 4095):
+        assert abs(np.linalg.norm(oracle.rope(x, p)) - np.linalg.norm(x)) < 1e-12  # orthogonal
+        np.testing.assert_allclose(oracle.rope(oracle.rope(x, p), 17), oracle.rope(x, p + 17),
+                                   atol=1e-11)                                   # R(a)R(b)=R(a+b)
+    # scores depend on the position difference only (shift invariance)
+    s0 = oracle.rope(x, 300) @ oracle.rope(y, 12)
+    for delta in (1, 64, 3000):
+        assert abs(oracle.rope(x, 300 + delta) @ oracle.rope(y, 12 + delta) - s0) < 1e-10
+
+
+# ---------------------------------------------------------------- paging
+
+def test_slot_matches_direct_page_lookup():
+    P, B, maxp, npages = 16, 3, 5, 40
+    pt = gen.shuffled_page_table(11, B, maxp, npages)
+    for b in range(B):
+        for j in range(maxp * P):
+            assert oracle.slot(pt, npages, P, b, j) == int(pt[b, j // P]) * P + j % P
+        assert oracle.slot(pt, npages, P, b, maxp * P) == -1   # beyond the table
+    bad = pt.copy()
+    bad[1, 2] = npages                                          # page index out of range
+    assert oracle.slot(bad, npages, P, 1, 2 * P + 3) == -1
+
+
+# ---------------------------------------------------------------- P2: lossless SVD round trip
+
+def _svd_problem(T, H, d, L, r, seed, dtype=F32, r_v=None):
+    """Per-head codec from the SVD of centred calibration draws (one per head and K/V),
+    plus L fresh tokens of loop-concatenated K/V from the same distribution."""
+    r_v = r if r_v is None else r_v
+    m = dims(T, 1, H, d, r, r_v, PER_HEAD, dtype)
+    sh = param_shapes(m)
+    codec = {k: np.zeros(v, dtype=np.float64) for k, v in sh.items()}
+    fresh = {}
+    for h in range(H):
+        for kv, rr in (("k", r), ("v", r_v)):
+            stream = 1000 + 10 * h + (0 if kv == "k" else 5)
+            calib = rank8_activations(seed, stream, 4096, T * d)
+            mu, wd, wu = svd_codec_one(calib, rr, T, d)
+            codec["mu_" + kv][0, h] = mu.reshape(T, d)
+            codec["w_down_" + kv][0, h] = wd
+            codec["w_up_" + kv][0, h] = wu
+            x = rank8_activations(seed, stream, L, T * d, draw=1)  # fresh tokens, same signal
+            fresh[kv + str(h)] = x
+    codec = {k: store(v, dtype) for k, v in codec.items()}
+    return m, codec, fresh
+
+
+def test_p2_lossless_full_rank_svd_reduces_to_plain_attention():
+    T, H, d, L = 4, 2, 16, 37
+    m, codec, fresh = _svd_problem(T, H, d, L, r=T * d, seed=5)
+    P = m["page_size"]
+    npages = (L + P - 1) // P
+    pt = gen.shuffled_page_table(3, 1, npages)
+    kp = np.full(pool_shape(m, npages, "k"), np.nan, dtype=np.float32)
+    vp = np.full(pool_shape(m, npages, "v"), np.nan, dtype=np.float32)
+    # x [n_layers][B][n_new][H][T][d]
+    xk = np.stack([fresh["k%d" % h] for h in range(H)], axis=1).reshape(1, 1, L, H, T, d)
+    xv = np.stack([fresh["v%d" % h] for h in range(H)], axis=1).reshape(1, 1, L, H, T, d)
+    xk_s, xv_s = store(xk, F32), store(xv, F32)
+    assert oracle.encode(m, codec, kp, vp, pt, xk_s, xv_s, np.array([0]), L, 0, 1) == 0
+    q = store(gen.normal_f32(9, 1, H * d).reshape(1, H, d), F32)
+    qpos = L - 1
+    for t in range(T):
+        out, rc = oracle.decode(m, codec, kp, vp, pt, 0, t, q, np.array([qpos]), np.array([L]))
+        assert rc == 0
+        for h in range(H):
+            K = f64(xk_s)[0, 0, :, h, t]          # the original loop-t vectors
+            V = f64(xv_s)[0, 0, :, h, t]
+            want = sdpa(rope_complex(f64(q)[0, h], qpos), rope_complex(K, np.arange(L)), V,
+                        1 / math.sqrt(d))
+            np.testing.assert_allclose(out[0, h], want, rtol=0, atol=2e-5 * np.abs(want).max())
+
+
+def test_p9_svd_fixture_sanity():
+    T, d, r = 4, 64, 16
+    calib = rank8_activations(1001, 50, 4096, T * d)
+    mu, wd, wu = svd_codec_one(calib, r, T, d)
+    np.testing.assert_allclose(wd.T @ wd, np.eye(r), atol=1e-10)          # orthonormal columns
+    resid = (calib - mu) - (calib - mu) @ wd @ wd.T
+    assert np.abs(resid @ wd).max() < 1e-9                                 # residual orthogonal
+    _, _, vt = np.linalg.svd(calib - mu, full_matrices=False)              # library SVD, up to sign
+    assert np.allclose(np.abs(np.sum(vt[:r].T * wd, axis=0)), 1.0, atol=1e-9)
+    fresh = rank8_activations(1001, 50, 2048, T * d, draw=1)
+    rec = (fresh - mu) @ wd @ wd.T + mu
+    err = np.linalg.norm(rec - fresh) / np.linalg.norm(fresh - mu)
+    assert 0.0 < err < 0.2                                                 # rank-8 signal kept
+
+
+# ---------------------------------------------------------------- P3: identity reductions
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("shuffle", [False, True])
+def test_p3_identity_decoder_is_plain_rope_attention(dtype, shuffle):
+    T, D, H, d, L = 3, 2, 2, 8, 35
+    m = dims(T, D, H, d, d, d, PER_HEAD, dtype)
+    P = 16
+    npages = 4
+    sh = param_shapes(m)
+    eye = np.broadcast_to(np.eye(d), sh["w_up_k"]).copy()
+    codec = dict(mu_k=np.zeros(sh["mu_k"]), mu_v=np.zeros(sh["mu_v"]), w_up_k=eye, w_up_v=eye,
+                 w_down_k=np.zeros(sh["w_down_k"]), w_down_v=np.zeros(sh["w_down_v"]))
+    codec = {k: store(v, dtype) for k, v in codec.items()}
+    kp, vp = random_pools(m, npages, seed=21)
+    pt = gen.shuffled_page_table(2, 1, npages) if shuffle else gen.identity_page_table(1, npages)
+    q = store(gen.normal_f32(22, 1, H * d).reshape(1, H, d), dtype)
+    qpos = 50
+    for layer in range(D):
+        for t in range(T):
+            out, rc = oracle.decode(m, codec, kp, vp, pt, layer, t, q, np.array([qpos]), np.array([L]))
+            assert rc == 0
+            for h in range(H):
+                K = gather_latents(kp, pt, 0, L, P, h)[layer]
+                V = gather_latents(vp, pt, 0, L, P, h)[layer]
+                want = sdpa(rope_complex(f64(q)[0, h], qpos), rope_complex(K, np.arange(L)), V,
+                            1 / math.sqrt(d))
+                np.testing.assert_allclose(out[0, h], want, rtol=0, atol=1e-12)
+
+
+def test_p3_identity_encoder_and_slice_decoder():
+    # W_down = I_{T d}, r = T d, mu = 0, W_up,t = identity slice t: the latents are the raw
+    # concatenated vectors (bit-exact in bf16) and loop t attends over the loop-t slice.
+    T, H, d, L = 3, 2, 8, 21
+    m = dims(T, 1, H, d, T * d, T * d, PER_HEAD, BF16)
+    sh = param_shapes(m)
+    wd = np.broadcast_to(np.eye(T * d), sh["w_down_k"]).copy()
+    wu = np.broadcast_to(np.eye(T * d).reshape(T, d, T * d), sh["w_up_k"]).copy()
+    codec = dict(mu_k=np.zeros(sh["mu_k"]), mu_v=np.zeros(sh["mu_v"]), w_down_k=wd, w_down_v=wd,
+                 w_up_k=wu, w_up_v=wu)
+    codec = {k: store(v, BF16) for k, v in codec.items()}
+    npages = 2
+    pt = gen.shuffled_page_table(8, 1, npages)
+    kp = np.full(pool_shape(m, npages, "k"), 0x7FC1, dtype=np.uint16)
+    vp = np.full(pool_shape(m, npages, "v"), 0x7FC1, dtype=np.uint16)
+    xk = gen.normal(31, 1, (1, 1, L, H, T, d))
+    xv = gen.normal(31, 2, (1, 1, L, H, T, d))
+    assert oracle.encode(m, codec, kp, vp, pt, xk, xv, np.array([0]), L, 0, 1) == 0
+    for h in range(H):
+        j = np.arange(L)
+        got_k = kp[0, pt[0, j // 16], h, j % 16]
+        assert np.array_equal(got_k, xk[0, 0, :, h].reshape(L, T * d))   # bit-exact latents
+    q = gen.normal(31, 3, (1, H, d))
+    for t in range(T):
+        out, rc = oracle.decode(m, codec, kp, vp, pt, 0, t, q, np.array([L - 1]), np.array([L]))
+        assert rc == 0
+        for h in range(H):
+            K, V = f64(xk)[0, 0, :, h, t], f64(xv)[0, 0, :, h, t]
+            want = sdpa(rope_complex(f64(q)[0, h], L - 1), rope_complex(K, np.arange(L)), V,
+                        1 / math.sqrt(d))
+            np.testing.assert_allclose(out[0, h], want, rtol=0, atol=1e-12)
+
+
+def test_encoder_subtracts_mean_and_permutes():
+    # W_down a permutation matrix: c = permuted (x - mu), one rounding.
+    T, H, d, L = 2, 1, 4, 5
+    m = dims(T, 1, H, d, T * d, T * d, PER_HEAD, F32)
+    sh = param_shapes(m)
+    perm = gen.shuffled_page_table(4, 1, T * d)[0]
+    pm = np.zeros((T * d, T * d))
+    pm[perm, np.arange(T * d)] = 1.0                         # c[k] = (x - mu)[perm[k]]
+    mu = gen.normal_f32(40, 1, T * d).reshape(sh["mu_k"])
+    codec = dict(mu_k=mu, mu_v=mu, w_down_k=pm.reshape(sh["w_down_k"]),
+                 w_down_v=pm.reshape(sh["w_down_v"]), w_up_k=np.zeros(sh["w_up_k"]),
+                 w_up_v=np.zeros(sh["w_up_v"]))
+    codec = {k: store(v, F32) for k, v in codec.items()}
+    kp = np.zeros(pool_shape(m, 1, "k"), dtype=np.float32)
+    vp = np.zeros(pool_shape(m, 1, "v"), dtype=np.float32)
+    x = gen.normal(40, 2, (1, 1, L, H, T, d), dtype="f32")
+    assert oracle.encode(m, codec, kp, vp, gen.identity_page_table(1, 1), x, x, np.array([3]), L,
+                         0, 1) == 0
+    diff = f64(x).reshape(L, T * d) - f64(codec["mu_k"]).reshape(T * d)
+    np.testing.assert_array_equal(kp[0, 0, 0, 3:3 + L], diff[:, perm].astype(np.float32))
+    assert np.all(kp[0, 0, 0, :3] == 0) and np.all(kp[0, 0, 0, 3 + L:] == 0)   # untouched
+
+
+# ---------------------------------------------------------------- P4: brute force, tiny shapes
+
+def brute_force_decode(m, codec, kp, vp, pt, layer, t, q, qpos, L, scale):
+    """Materialise the teacher-style per-loop cache with numpy einsum, rotate with
+    complex numbers, softmax with numpy; V summed in the absorbed (latent) form."""
+    H, d, P = m["H"], m["d_head"], m["page_size"]
+    out = np.zeros((H, d))
+    for h in range(H):
+        ck = gather_latents(kp, pt, 0, L, P, h)[layer]
+        cv = gather_latents(vp, pt, 0, L, P, h)[layer]
+        wk, wv = f64(codec["w_up_k"])[layer, h, t], f64(codec["w_up_v"])[layer, h, t]
+        muk, muv = f64(codec["mu_k"])[layer, h, t], f64(codec["mu_v"])[layer, h, t]
+        K = np.einsum("er,jr->je", wk, ck) + muk
+        s = scale * rope_complex(K, np.arange(L)) @ rope_complex(f64(q)[0, h], qpos)
+        p = np.exp(s - s.max())
+        out[h] = muv + wv @ (p @ cv) / p.sum()       # absorbed V: exact by linearity
+    return out
+
+
+@pytest.mark.parametrize("L", [1, 2, 3, 17])
+@pytest.mark.parametrize("r", [1, 2, 3])
+def test_p4_brute_force_tiny(L, r):
+    T, D, H, d = 2, 2, 2, 4
+    m = dims(T, D, H, d, r, r + 1, PER_HEAD, F32)
+    codec = random_codec(m, seed=50 + r, ortho_down=False)
+    npages = 2
+    kp, vp = random_pools(m, npages, seed=60 + L)
+    pt = gen.shuffled_page_table(L, 1, npages)
+    q = gen.normal(70, 1, (1, H, d), dtype="f32")
+    for layer in range(D):
+        for t in range(T):
+            out, rc = oracle.decode(m, codec, kp, vp, pt, layer, t, q, np.array([L + 3]),
+                                    np.array([L]), scale=0.7)
+            assert rc == 0
+            want = brute_force_decode(m, codec, kp, vp, pt, layer, t, q, L + 3, L, 0.7)
+            np.testing.assert_allclose(out[0], want, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- P5: LLA-2D reductions
+
+def test_p5_two_d_with_one_head_is_per_head_bitwise():
+    T, D, d, L = 2, 2, 8, 19
+    for dt in (F32, BF16):
+        mp = dims(T, D, 1, d, 5, 6, PER_HEAD, dt)
+        m2 = dict(mp, variant=TWO_D)
+        codec = random_codec(mp, seed=80)  # same memory layout for H = 1
+        npages = 2
+        pt = gen.shuffled_page_table(81, 1, npages)
+        kp1, vp1 = random_pools(mp, npages, seed=82)
+        kp2, vp2 = kp1.reshape(pool_shape(m2, npages, "k")).copy(), vp1.reshape(pool_shape(m2, npages, "v")).copy()
+        x = gen.normal(83, 1, (1, 1, 4, 1, T, d), dtype="bf16" if dt else "f32")
+        pos0 = np.array([L - 4])
+        assert oracle.encode(mp, codec, kp1, vp1, pt, x, x, pos0, 4, 1, 1) == 0
+        assert oracle.encode(m2, codec, kp2, vp2, pt, x.reshape(1, 1, 4, T, 1, d), x.reshape(1, 1, 4, T, 1, d), pos0, 4, 1, 1) == 0
+        assert np.array_equal(kp1.reshape(-1).view(np.uint8), kp2.reshape(-1).view(np.uint8))
+        q = gen.normal(84, 1, (1, 1, d), dtype="bf16" if dt else "f32")
+        for t in range(T):
+            o1, _ = oracle.decode(mp, codec, kp1, vp1, pt, 1, t, q, np.array([L - 1]), np.array([L]))
+            o2, _ = oracle.decode(m2, codec, kp2, vp2, pt, 1, t, q, np.array([L - 1]), np.array([L]))
+            assert np.array_equal(o1, o2)
+
+
+def test_p5_block_diagonal_two_d_equals_per_head():
+    # LLA-2D whose head-h decoder reads only latent block h (and whose encoder writes
+    # block h from head h's slice of the [t][h][d] input) is per-head LLA with rank r/H.
+    T, D, H, d, r1, L, P = 2, 1, 3, 4, 2, 23, 16
+    mp = dims(T, D, H, d, r1, r1, PER_HEAD, F32)
+    m2 = dims(T, D, H, d, H * r1, H * r1, TWO_D, F32)
+    cp = {k: f64(v) for k, v in random_codec(mp, seed=90, ortho_down=False).items()}
+    s2 = param_shapes(m2)
+    c2 = {k: np.zeros(s2[k]) for k in s2}
+    for kv in "kv":
+        for h in range(H):
+            blk = slice(h * r1, (h + 1) * r1)
+            for t in range(T):
+                c2["mu_" + kv][0, t, h] = cp["mu_" + kv][0, h, t]
+                c2["w_up_" + kv][0, t, h][:, blk] = cp["w_up_" + kv][0, h, t]
+                rows = t * H * d + h * d + np.arange(d)              # [t][h][d] order
+                c2["w_down_" + kv][0][rows, blk] = cp["w_down_" + kv][0, h][t * d:(t + 1) * d]
+    cp = {k: store(v, F32) for k, v in cp.items()}
+    c2 = {k: store(v, F32) for k, v in c2.items()}
+    npages = 2
+    pt = gen.shuffled_page_table(91, 1, npages)
+    kp1 = np.zeros(pool_shape(mp, npages, "k"), np.float32); vp1 = np.zeros_like(kp1)
+    kp2 = np.zeros(pool_shape(m2, npages, "k"), np.float32); vp2 = np.zeros_like(kp2)
+    xk = gen.normal(92, 1, (1, 1, L, H, T, d), dtype="f32")
+    xv = gen.normal(92, 2, (1, 1, L, H, T, d), dtype="f32")
+    assert oracle.encode(mp, cp, kp1, vp1, pt, xk, xv, np.array([0]), L, 0, 1) == 0
+    x2k = np.ascontiguousarray(xk.transpose(0, 1, 2, 4, 3, 5))           # -> [t][h][d]
+    x2v = np.ascontiguousarray(xv.transpose(0, 1, 2, 4, 3, 5))
+    assert oracle.encode(m2, c2, kp2, vp2, pt, x2k, x2v, np.array([0]), L, 0, 1) == 0
+    for h in range(H):
+        np.testing.assert_allclose(kp2[..., h * r1:(h + 1) * r1], kp1[:, :, h], rtol=1e-6, atol=1e-6)
+    q = gen.normal(93, 1, (1, H, d), dtype="f32")
+    for t in range(T):
+        o1, _ = oracle.decode(mp, cp, kp1, vp1, pt, 0, t, q, np.array([L - 1]), np.array([L]))
+        o2, _ = oracle.decode(m2, c2, kp2, vp2, pt, 0, t, q, np.array([L - 1]), np.array([L]))
+        np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-5)
+
+
+# ---------------------------------------------------------------- P7: softmax / V special cases
+
+def test_p7_zero_query_gives_mean_value_and_single_token_gives_that_value():
+    T, D, H, d, r_k, r_v, L, P = 2, 1, 2, 8, 3, 5, 29, 16
+    m = dims(T, D, H, d, r_k, r_v, PER_HEAD, F32)
+    codec = random_codec(m, seed=100, ortho_down=False)
+    kp, vp = random_pools(m, 2, seed=101)
+    pt = gen.shuffled_page_table(102, 1, 2)
+    q0 = np.zeros((1, H, d), np.float32)
+    for t in range(T):
+        out, _ = oracle.decode(m, codec, kp, vp, pt, 0, t, q0, np.array([5]), np.array([L]))
+        out1, _ = oracle.decode(m, codec, kp, vp, pt, 0, t, gen.normal(103, 1, (1, H, d), dtype="f32"),
+                                np.array([0]), np.array([1]))
+        for h in range(H):
+            cv = gather_latents(vp, pt, 0, L, P, h)[0]
+            wv, muv = f64(codec["w_up_v"])[0, h, t], f64(codec["mu_v"])[0, h, t]
+            np.testing.assert_allclose(out[0, h], muv + wv @ cv.mean(axis=0), atol=1e-12)
+            np.testing.assert_allclose(out1[0, h], muv + wv @ cv[0], atol=1e-12)
+
+
+# ---------------------------------------------------------------- P8: paging invariance
+
+def test_p8_shuffled_and_contiguous_page_tables_agree_bitwise():
+    T, D, H, d, L = 2, 2, 2, 8, 45
+    m = dims(T, D, H, d, 4, 6, PER_HEAD, BF16)
+    codec = random_codec(m, seed=110)
+    npages = 3
+    kp, vp = random_pools(m, npages, seed=111)
+    pt_id = gen.identity_page_table(1, npages)
+    pt_sh = gen.shuffled_page_table(112, 1, npages)
+    kp_sh, vp_sh = np.empty_like(kp), np.empty_like(vp)
+    kp_sh[:, pt_sh[0]] = kp[:, pt_id[0]]                          # move each page to its new home
+    vp_sh[:, pt_sh[0]] = vp[:, pt_id[0]]
+    q = gen.normal(113, 1, (1, H, d))
+    for t in range(T):
+        a, _ = oracle.decode(m, codec, kp, vp, pt_id, 1, t, q, np.array([L - 1]), np.array([L]))
+        b, _ = oracle.decode(m, codec, kp_sh, vp_sh, pt_sh, 1, t, q, np.array([L - 1]), np.array([L]))
+        assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------- prefill = per-query decode
+
+def test_prefill_query_i_equals_decode_at_its_position():
+    T, D, H, d, n_q, p0 = 2, 1, 2, 8, 5, 11
+    m = dims(T, D, H, d, 3, 4, PER_HEAD, F32)
+    codec = random_codec(m, seed=120)
+    kp, vp = random_pools(m, 2, seed=121)
+    pt = gen.shuffled_page_table(122, 1, 2)
+    q = gen.normal(123, 1, (1, n_q, H, d), dtype="f32")
+    out, rc = oracle.prefill(m, codec, kp, vp, pt, 0, 1, n_q, q, np.array([p0]))
+    assert rc == 0
+    for i in range(n_q):
+        o1, _ = oracle.decode(m, codec, kp, vp, pt, 0, 1, np.ascontiguousarray(q[:, i]),
+                              np.array([p0 + i]), np.array([p0 + i + 1]))
+        assert np.array_equal(out[:, i], o1)
+    # the first query (p0 = 0) sees only token 0: it returns that token's v_hat
+    out0, _ = oracle.prefill(m, codec, kp, vp, pt, 0, 1, 1, q[:, :1].copy(), np.array([0]))
+    for h in range(H):
+        want = f64(codec["mu_v"])[0, h, 1] + f64(codec["w_up_v"])[0, h, 1] @ f64(vp)[0, pt[0, 0], h, 0]
+        np.testing.assert_allclose(out0[0, 0, h], want, atol=1e-12)
+
+
+# ---------------------------------------------------------------- error behaviour
+
+def test_oracle_reports_bad_indices():
+    m = dims(2, 1, 1, 4, 2, 2, PER_HEAD, F32)
+    codec = random_codec(m, seed=130, ortho_down=False)
+    kp, vp = random_pools(m, 2, seed=131)
+    pt = np.array([[0, 5]], dtype=np.int32)                            # page 5 does not exist
+    q = gen.normal(132, 1, (1, 1, 4), dtype="f32")
+    out, rc = oracle.decode(m, codec, kp, vp, pt, 0, 0, q, np.array([20]), np.array([20]))
+    assert rc != 0 and np.isnan(out).all()
+    out, rc = oracle.decode(m, codec, kp, vp, pt, 0, 0, q, np.array([3]), np.array([33]))
+    assert rc != 0                                                      # beyond the page table
+    out, rc = oracle.decode(m, codec, kp, vp, pt, 0, 0, q, np.array([3]), np.array([0]))
+    assert rc != 0                                                      # empty context
+    out, rc = oracle.decode(m, codec, kp, vp, pt, 0, 0, q, np.array([3]), np.array([16]))
+    assert rc == 0 and np.isfinite(out).all()
