@@ -1,0 +1,186 @@
+"""Benchmark: latent-cache decode attention on one MI355X.
+
+One step = one decode step of a looped model at the high-capacity point
+(Ouro-1.4B shapes: T=4 loops x D=24 layers, H=16, d_head=128, r_k=16, r_v=32,
+batch 768, context 4096, shuffled 16-token pages): append the new token's
+latents for every layer (lla_encode_append), then run lla_decode_attn for every
+(loop, layer) pair -- T*D = 96 calls, loop-major as the looped model issues
+them, so consecutive calls read different layers' pools and the working set
+(116 GB) never stays in the 256 MB last-level cache.
+
+value = cached-token reads / s over the timed steps (one read = one token's
+latents for one layer during one call: all 16 heads' c_k and c_v).  Inputs are
+resident in HBM before timing starts.  The roofline object describes the decode
+kernel, timed with HIP events on the stream it is launched on.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--workload", default="ouro1.4b-21x-b768-paged")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle sample time")
+    return p.parse_args()
+
+
+def cpu_baseline(w, codec_h, pt_h, layer, loop, target_s):
+    """Time the fp64 oracle on a bounded sample of the same call: whole
+    sequences (all heads, full context) of one (layer, loop)."""
+    import oracle
+    from looped_transformer_latent_amd import workloads as wl
+
+    # the oracle sees one layer: that layer's codec slice and pool pages
+    one = dict(w.dims, D=1)
+    codec1 = {k: np.ascontiguousarray(v[layer:layer + 1]) for k, v in codec_h.items()}
+
+    # latent pages of the first (up to) 4 sequences, regenerated on the host; longer
+    # samples cycle through them (the oracle's cost does not depend on the values)
+    n_data = min(4, w.batch)
+    pages = pt_h[:n_data].reshape(-1)
+    kp = wl.pool_pages_host(w, "k", layer, pages)[None]
+    vp = wl.pool_pages_host(w, "v", layer, pages)[None]
+    local = np.arange(len(pages), dtype=np.int32).reshape(n_data, -1)
+
+    def run(n_seq):
+        pt_local = np.ascontiguousarray(local[np.arange(n_seq) % n_data])
+        q = wl.q_host(w, n_seq)
+        ctx = np.full(n_seq, w.ctx, np.int32)
+        t0 = time.perf_counter()
+        _, rc = oracle.decode(one, codec1, kp, vp, pt_local, 0, loop, q, ctx - 1, ctx)
+        dt = time.perf_counter() - t0
+        assert rc == 0
+        return dt
+
+    threads = oracle.max_threads(0)
+    t1 = run(1)
+    n = int(max(1, min(w.batch, round(target_s / max(t1, 1e-3)))))
+    dt = run(n) if n > 1 else t1
+    reads = n * w.ctx
+    return {"value": reads / dt, "unit": "cached-token reads/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {w.batch} sequences x full context {w.ctx} x all {w.H} heads, "
+                      f"one (layer, loop) call (latent data of {n_data} sequences, reused); "
+                      f"fp64 C oracle, OpenMP over (sequence, head); {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
+        sys.exit(2)
+    import torch
+
+    from looped_transformer_latent_amd import lla
+    from looped_transformer_latent_amd import workloads as wl
+
+    w = wl.WORKLOADS[args.workload]
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    D = lla.dims_from_dict(w.dims)
+    dt_t = torch.bfloat16 if w.dtype == wl.BF16 else torch.float32
+
+    codec_h = wl.codec_host(w)
+    codec_d = {k: wl.to_device(v, dev) for k, v in codec_h.items()}
+    codec = lla.make_codec(codec_d["mu_k"], codec_d["mu_v"], codec_d["w_down_k"],
+                           codec_d["w_down_v"], codec_d["w_up_k"], codec_d["w_up_v"])
+    pt_h = wl.page_table_host(w)
+    pt = wl.to_device(pt_h, dev)
+    k_pool = wl.device_pool(w, "k", dev)
+    v_pool = wl.device_pool(w, "v", dev)
+    cache = lla.make_cache(k_pool, v_pool, pt, w.num_pages)
+    rope = lla.rope_table(D, w.ctx)
+
+    calls = [(t, l) for t in range(w.T) for l in range(w.D)]
+    q = torch.empty((len(calls), w.batch, w.H, w.d_head), dtype=dt_t, device=dev)
+    lla.gen_normal_(q, w.seed, wl.STREAMS["q"])
+    out = torch.empty_like(q)
+    ctx = torch.full((w.batch,), w.ctx, dtype=torch.int32, device=dev)
+    q_pos = ctx - 1
+    ws_dec = lla.workspace(D, lla.OP_DECODE, w.batch, w.ctx)
+    # the step's new token: its per-loop K/V for every layer, appended at ctx - 1
+    n_new = max(1, w.n_new if w.n_new <= 1 else 1)
+    xs = (w.D, w.batch, n_new) + ((w.H, w.T, w.d_head) if w.variant == wl.PER_HEAD else (w.T, w.H, w.d_head))
+    x_k = torch.empty(xs, dtype=dt_t, device=dev)
+    x_v = torch.empty(xs, dtype=dt_t, device=dev)
+    lla.gen_normal_(x_k, w.seed, wl.STREAMS["x_k"])
+    lla.gen_normal_(x_v, w.seed, wl.STREAMS["x_v"])
+    pos0 = ctx - n_new
+    ws_enc = lla.workspace(D, lla.OP_ENCODE, w.batch, 0, w.D)
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in calls]
+
+    def step(record):
+        lla.encode_append(D, codec, cache, x_k, x_v, pos0, n_new, 0, w.D, ws_enc)
+        for i, (t, l) in enumerate(calls):
+            if record:
+                ev[i][0].record(stream)
+            lla.decode_attn(D, codec, cache, rope, l, t, q[i], q_pos, ctx, w.ctx, out[i], ws_dec)
+            if record:
+                ev[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    kern_ms = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+        torch.cuda.synchronize()
+        kern_ms += [a.elapsed_time(b) for a, b in ev]
+    elapsed = time.perf_counter() - t0
+    assert lla.device_error_word(ws_dec) == 0 and lla.device_error_word(ws_enc) == 0
+    assert torch.isfinite(out.float()).all().item()
+
+    ms_step = 1e3 * elapsed / args.steps
+    reads_per_step = len(calls) * w.batch * w.ctx
+    value = reads_per_step / (ms_step / 1e3)
+    kern_avg_ms = float(np.mean(kern_ms))
+    bytes_per_launch = w.batch * w.ctx * w.read_bytes()
+    achieved = bytes_per_launch / (kern_avg_ms / 1e3) / 1e9
+    result = {
+        "metric": "latent-cache decode attention: cached-token reads/s and achieved HBM GB/s",
+        "value": value,
+        "unit": "cached-token reads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == wl.BF16 else "f32",
+        "data": "synthetic (seeded generator; random codec parameters, N(0,1) latents)",
+        "config": {"workload": w.name, "batch": w.batch, "ctx": w.ctx, "T": w.T, "D": w.D,
+                   "H": w.H, "d_head": w.d_head, "r_k": w.r_k, "r_v": w.r_v, "page_size": 16,
+                   "page_table": "shuffled" if w.shuffled else "identity",
+                   "step": f"encode_append(1 token x {w.D} layers) + {len(calls)} lla_decode_attn calls"},
+        "roofline": {"kernel": "decode_ph_kernel", "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None, "algorithmic_bytes_per_launch": bytes_per_launch,
+                     "avg_launch_ms": kern_avg_ms},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, codec_h, pt_h, layer=w.D - 1, loop=w.T - 1,
+                                              target_s=args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,192 @@
+/*
+ * lla.h -- C ABI of the MI355X (gfx950) Looped Latent Attention (LLA) library.
+ *
+ * LLA is a post-training cache codec for looped, weight-tied Transformers: for
+ * every cached token, layer and head it stores a K latent c_k (width r_k) and a
+ * V latent c_v (width r_v) instead of T per-loop K/V vectors, and rebuilds the
+ * loop-t K/V only when attention reads them.  Sources, cited by page title and
+ * section:
+ *   [CR] "Looped Latent Attention: 跨循环 KV 压缩精读" (cc.laoqi.cc close reading of
+ *        arXiv 2607.15456v2), section 二:方法 items 1-3 and 6, section 四:结果 item 9
+ *        (Table 5).
+ *   [GS] gist.science summary of arXiv 2607.15456, "Technisches Resümee" /
+ *        "Kernmechanismus" (text form of eq. (2)-(4)).
+ *   encoder  eq. (2): c = (x - mu) W_down, x = [x_1; ...; x_T] (loop-major).
+ *   decoder  eq. (3): x_hat_t = c W_up,t^T + mu_t.
+ *   ratio    eq. (4): 2 T H d_head scalars per token and layer become
+ *            (r_k + r_v) H (per-head) or r_k + r_v (LLA-2D).
+ *   RoPE is applied to the rebuilt K at the token's position ([CR] 方法 item 3).
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor arguments are DEVICE pointers owned by the caller, row-major,
+ *     dense, in the layouts given below.  The library never allocates, frees or
+ *     synchronises; each call enqueues its kernels on `stream` and returns.
+ *   - Floating-point storage is `dims->dtype`: LLA_F32 (IEEE fp32) or LLA_BF16
+ *     (bfloat16 bit patterns).  It applies to latents, codec parameters, q, x
+ *     and out.  Accumulation is fp32; bf16 results are rounded to nearest-even.
+ *   - Indices: `layer` in [0, D); `loop` in [0, T) (loop t = loop + 1 in the
+ *     pages' 1-based notation).  A cached token's RoPE position is its logical
+ *     index j in its sequence; logical token j of sequence b lives in physical
+ *     page page_table[b][j / page_size] at row j % page_size.
+ *   - RoPE: pairs (i, i + d_head/2), angle p * rope_base^(-2i/d_head), rotation
+ *     (a, b) -> (a cos - b sin, a sin + b cos).  The angles come from a caller-
+ *     owned table filled once by lla_rope_table().
+ *   - Return value: LLA_OK or a negative LLA_ERR_* code for errors the host can
+ *     see (null pointers, bad sizes or indices, unsupported shapes, workspace
+ *     too small, launch failure); lla_last_error() gives a thread-local message.
+ *   - Errors only the device can see (a ctx_len, q_pos, p0 or pos0 out of range,
+ *     a page-table entry outside [0, num_pages)) never cause out-of-bounds
+ *     accesses: the affected output rows are written as NaN (decode, prefill) or
+ *     the affected latents are not written (encode), and a bit is OR-ed into the
+ *     int32 error word at byte 0 of the workspace (LLA_DEVERR_*).  That word is
+ *     sticky: the library never clears it.
+ *   - Workspace: size it with lla_workspace_bytes() and ZERO it once after
+ *     allocation (the split-merge counters must start at zero; every call
+ *     leaves them at zero again).  One workspace must not be used by two calls
+ *     that may run concurrently.
+ */
+#ifndef LLA_H
+#define LLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  LLA_OK = 0,
+  LLA_ERR_INVALID_ARG = -1, /* null pointer, bad size, index out of range */
+  LLA_ERR_UNSUPPORTED = -2, /* valid but not built: see lla_supported() */
+  LLA_ERR_WORKSPACE = -3,   /* workspace null or smaller than lla_workspace_bytes() */
+  LLA_ERR_LAUNCH = -4       /* the HIP runtime refused a launch */
+};
+
+enum { LLA_PER_HEAD = 0, LLA_2D = 1 }; /* [CR] 方法 item 6: LLA-2D folds heads into one latent */
+enum { LLA_F32 = 0, LLA_BF16 = 1 };
+enum { LLA_OP_ENCODE = 0, LLA_OP_DECODE = 1, LLA_OP_PREFILL = 2 };
+
+/* Device-side error bits (workspace byte 0). */
+enum {
+  LLA_DEVERR_CTX = 1,   /* ctx_len < 1 or > max_ctx, or q_pos / p0 outside the RoPE table */
+  LLA_DEVERR_PAGE = 2,  /* page-table entry outside [0, num_pages) */
+  LLA_DEVERR_APPEND = 4 /* pos0[b] + n_new beyond the sequence's page-table row */
+};
+
+/* Shapes, in the pages' notation ([CR] 方法 item 1 symbol table). */
+typedef struct lla_dims {
+  int32_t T;         /* loops (recurrence steps) */
+  int32_t D;         /* shared layers */
+  int32_t H;         /* attention heads */
+  int32_t d_head;    /* head width */
+  int32_t r_k, r_v;  /* K and V latent widths */
+  int32_t variant;   /* LLA_PER_HEAD or LLA_2D */
+  int32_t dtype;     /* LLA_F32 or LLA_BF16 */
+  int32_t page_size; /* tokens per cache page; must be 16 */
+  float rope_base;   /* RoPE base, e.g. 10000 */
+} lla_dims;
+
+/* Codec parameters, fixed and shared across tokens ([CR] 方法 item 1).
+ * Per-head: an independent codec per (layer, head); mu_t and W_up,t per loop.
+ *   mu_k, mu_v           [D][H][T][d_head]          (mu_t = mu[..][t][:])
+ *   w_down_k / w_down_v  [D][H][T*d_head][r_k|r_v]
+ *   w_up_k / w_up_v      [D][H][T][d_head][r_k|r_v] (W_up,t is d_head x r)
+ * LLA-2D: one codec per layer over x ordered [t][h][d]:
+ *   mu_k, mu_v           [D][T][H][d_head]
+ *   w_down_k / w_down_v  [D][T*H*d_head][r_k|r_v]
+ *   w_up_k / w_up_v      [D][T][H][d_head][r_k|r_v] (head h of loop t decodes with
+ *                        its own d_head x r slice) */
+typedef struct lla_codec {
+  const void *mu_k, *mu_v;
+  const void *w_down_k, *w_down_v;
+  const void *w_up_k, *w_up_v;
+} lla_codec;
+
+/* Paged latent cache.  One page table serves every layer.
+ *   per-head: k_pool [D][num_pages][H][page_size][r_k], v_pool [..][r_v]
+ *   LLA-2D:   k_pool [D][num_pages][page_size][r_k],    v_pool [..][r_v]
+ *   page_table [batch][max_pages_per_seq] int32 physical page indices. */
+typedef struct lla_cache {
+  void *k_pool, *v_pool;
+  const int32_t *page_table;
+  int32_t batch;
+  int32_t max_pages_per_seq;
+  int32_t num_pages;
+} lla_cache;
+
+/* Fill table[n_pos][d_head/2][2] (fp32 cos, sin of p * base^(-2i/d_head),
+ * evaluated in fp64) for positions 0..n_pos-1.  The decode and prefill calls
+ * read angles only from this table. */
+int32_t lla_rope_table(const lla_dims *dims, int32_t n_pos, float *table, hipStream_t stream);
+
+/* Bytes of workspace that `op` needs.  batch = sequences; max_ctx = the
+ * host-known upper bound on every context the call may read (decode: on
+ * ctx_len; prefill: on p0[b] + n); n = n_q for prefill, n_layers for encode,
+ * ignored for decode.  Returns 0 for invalid arguments. */
+size_t lla_workspace_bytes(const lla_dims *dims, int32_t op, int32_t batch, int32_t max_ctx,
+                           int32_t n);
+
+/* Encode + append, eq. (2) ([CR] 方法 item 1; [GS] Kernmechanismus).
+ * For layers layer0 .. layer0+n_layers-1, sequences b and new tokens n < n_new:
+ *   c_k = (x_k - mu_k) W_down,k   and   c_v = (x_v - mu_v) W_down,v,
+ * computed as x W_down - mu W_down with fp32 accumulation, rounded once to the
+ * storage dtype, and written to the slot of logical token pos0[b] + n.  No
+ * other slot is touched.
+ *   x_k, x_v  per-head [n_layers][batch][n_new][H][T][d_head]
+ *             LLA-2D   [n_layers][batch][n_new][T][H][d_head]   (pre-RoPE)
+ *   pos0      device int32 [batch]: first logical position written per sequence.
+ * The caller owns ctx_len and must append a token before attending to it. */
+int32_t lla_encode_append(const lla_dims *dims, const lla_codec *codec, const lla_cache *cache,
+                          const void *x_k, const void *x_v, const int32_t *pos0, int32_t n_new,
+                          int32_t layer0, int32_t n_layers, void *workspace, size_t ws_bytes,
+                          hipStream_t stream);
+
+/* Decode attention of one query per sequence over its latent cache, for one
+ * (layer, loop) ([CR] 方法 items 1-3; 四:结果 item 9 latent-store path):
+ *   k_hat_j = mu_k,t + c_k,j W_up,k,t^T,  v_hat_j = mu_v,t + c_v,j W_up,v,t^T  (eq. (3))
+ *   out = sum_j softmax_j(scale <R(q_pos) q, R(j) k_hat_j>) v_hat_j,  j in [0, ctx_len[b]).
+ * The V side is summed in latent space and up-projected once (exact by the
+ * linearity of eq. (3)); K is rebuilt per token.
+ *   q         [batch][H][d_head] pre-RoPE;  out [batch][H][d_head]
+ *   q_pos     device int32 [batch], in [0, rope_len)
+ *   ctx_len   device int32 [batch], in [1, max_ctx]; max_ctx <= rope_len and
+ *             max_ctx <= max_pages_per_seq * page_size
+ *   scale     softmax scale; 0 selects 1/sqrt(d_head). */
+int32_t lla_decode_attn(const lla_dims *dims, const lla_codec *codec, const lla_cache *cache,
+                        const float *rope_table, int32_t rope_len, int32_t layer, int32_t loop,
+                        const void *q, const int32_t *q_pos, const int32_t *ctx_len,
+                        int32_t max_ctx, float scale, void *out, void *workspace,
+                        size_t ws_bytes, hipStream_t stream);
+
+/* Causal prefill attention over the latent cache ([CR] 方法 item 6: long
+ * prefill reconstructs per layer).  Query i of sequence b sits at position
+ * p0[b] + i and attends over logical tokens [0, p0[b] + i]; those tokens must
+ * already be appended.
+ *   q, out   [batch][n_q][H][d_head];  p0 device int32 [batch];
+ *   max_ctx  >= p0[b] + n_q for every b (bounds the split grid);
+ *   other arguments as for lla_decode_attn. */
+int32_t lla_prefill_attn(const lla_dims *dims, const lla_codec *codec, const lla_cache *cache,
+                         const float *rope_table, int32_t rope_len, int32_t layer, int32_t loop,
+                         int32_t n_q, const void *q, const int32_t *p0, int32_t max_ctx,
+                         float scale, void *out, void *workspace, size_t ws_bytes,
+                         hipStream_t stream);
+
+/* Eq. (4): persistent cache scalars per token and layer, for the teacher
+ * (2 T H d_head) and for the latent cache ((r_k + r_v) H, or r_k + r_v for
+ * LLA-2D).  Host only.  ([CR] 方法 item 2; Table 5.) */
+int32_t lla_cache_scalars(const lla_dims *dims, int64_t *teacher, int64_t *latent);
+
+/* 1 if this build has kernels for (dims, op), else 0 (host only). */
+int32_t lla_supported(const lla_dims *dims, int32_t op);
+
+const char *lla_status_string(int32_t status);
+const char *lla_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LLA_H */

@@ -1,0 +1,302 @@
+// C ABI of the LLA library: argument validation, workspace planning and
+// kernel dispatch.  See include/lla.h for the contract of every entry point.
+#include <math.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "lla_internal.h"
+
+namespace lla {
+namespace {
+
+thread_local std::string g_last_error;
+
+int32_t fail(int32_t code, const char *msg) {
+  g_last_error = msg;
+  return code;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool dims_valid(const lla_dims *d) {
+  return d && d->T > 0 && d->D > 0 && d->H > 0 && d->d_head > 0 && d->d_head % 2 == 0 &&
+         d->r_k > 0 && d->r_v > 0 && (d->variant == LLA_PER_HEAD || d->variant == LLA_2D) &&
+         (d->dtype == LLA_F32 || d->dtype == LLA_BF16) && d->page_size == kPage &&
+         d->rope_base > 0.f;
+}
+
+size_t esize(const lla_dims *d) { return d->dtype == LLA_BF16 ? 2 : 4; }
+
+// How an attention call is cut into workgroups.
+struct AttnPlan {
+  int hpw, waves, head_groups, splits, pages_per_split;
+  size_t counters_off, partials_off, bytes;
+};
+
+bool plan_attn(const lla_dims *d, long long rows, int max_ctx, AttnPlan *p) {
+  const int H = d->H;
+  int hpw = 1;
+  if (H % 2 == 0 && H >= 4 && decode_supported(d->dtype, d->d_head, d->r_k, d->r_v, 2)) hpw = 2;
+  if (!decode_supported(d->dtype, d->d_head, d->r_k, d->r_v, hpw)) return false;
+  const int wave_heads = H / hpw;
+  int waves = 1;
+  for (int w = 8; w >= 1; --w)
+    if (wave_heads % w == 0) { waves = w; break; }
+  p->hpw = hpw;
+  p->waves = waves;
+  p->head_groups = wave_heads / waves;
+  const int pages = (max_ctx + kPage - 1) / kPage;
+  const long long base = rows * p->head_groups;
+  long long s = (1024 + base - 1) / base;
+  const long long smax = pages / 4 > 1 ? pages / 4 : 1;
+  if (s > smax) s = smax;
+  if (s < 1) s = 1;
+  int pps = (int)((pages + s - 1) / s);
+  if (pps < 1) pps = 1;
+  p->pages_per_split = pps;
+  p->splits = (pages + pps - 1) / pps;
+  if (p->splits < 1) p->splits = 1;
+  p->counters_off = kHeaderBytes;
+  p->partials_off = align256(p->counters_off + sizeof(int) * (size_t)rows * p->head_groups);
+  p->bytes = p->splits > 1
+                 ? align256(p->partials_off + sizeof(float) * (size_t)rows * H * p->splits * (d->r_v + 2))
+                 : kHeaderBytes;
+  return true;
+}
+
+size_t encode_ws_bytes(const lla_dims *d, int n_layers) {
+  const int groups = d->variant == LLA_PER_HEAD ? d->H : 1;
+  return align256(kHeaderBytes + sizeof(float) * (size_t)n_layers * groups * (d->r_k + d->r_v));
+}
+
+int32_t check_launch(hipError_t e) {
+  if (e == hipSuccess) return LLA_OK;
+  if (e == hipErrorInvalidConfiguration) return fail(LLA_ERR_UNSUPPORTED, "no kernel for this shape");
+  g_last_error = std::string("HIP launch failed: ") + hipGetErrorString(e);
+  return LLA_ERR_LAUNCH;
+}
+
+// Common validation + argument filling for decode and prefill.
+int32_t attn_call(const lla_dims *d, const lla_codec *c, const lla_cache *k, const float *rope,
+                  int32_t rope_len, int32_t layer, int32_t loop, const void *q,
+                  const int32_t *q_pos, const int32_t *ctx_len, const int32_t *p0, int32_t n_q,
+                  int32_t prefill, int32_t max_ctx, float scale, void *out, void *ws,
+                  size_t ws_bytes, hipStream_t stream) {
+  if (!dims_valid(d)) return fail(LLA_ERR_INVALID_ARG, "invalid lla_dims");
+  if (!c || !k) return fail(LLA_ERR_INVALID_ARG, "null codec or cache");
+  if (!c->mu_k || !c->mu_v || !c->w_up_k || !c->w_up_v)
+    return fail(LLA_ERR_INVALID_ARG, "null decoder parameter (mu or W_up)");
+  if (!k->k_pool || !k->v_pool || !k->page_table) return fail(LLA_ERR_INVALID_ARG, "null pool or page table");
+  if (k->batch < 0 || k->max_pages_per_seq < 1 || k->num_pages < 1)
+    return fail(LLA_ERR_INVALID_ARG, "invalid cache sizes");
+  if (layer < 0 || layer >= d->D) return fail(LLA_ERR_INVALID_ARG, "layer out of range");
+  if (loop < 0 || loop >= d->T) return fail(LLA_ERR_INVALID_ARG, "loop out of range");
+  if (!rope || rope_len < 1) return fail(LLA_ERR_INVALID_ARG, "null RoPE table");
+  if (max_ctx < 1) return fail(LLA_ERR_INVALID_ARG, "max_ctx must be >= 1");
+  if (max_ctx > rope_len) return fail(LLA_ERR_INVALID_ARG, "max_ctx exceeds the RoPE table");
+  if ((long long)max_ctx > (long long)k->max_pages_per_seq * kPage)
+    return fail(LLA_ERR_INVALID_ARG, "max_ctx exceeds the page table row");
+  if (prefill ? (n_q < 0 || !p0) : (!q_pos || !ctx_len))
+    return fail(LLA_ERR_INVALID_ARG, "null position array or bad n_q");
+  if (!q || !out) return fail(LLA_ERR_INVALID_ARG, "null q or out");
+  if (!(scale >= 0.f) || isinf(scale)) return fail(LLA_ERR_INVALID_ARG, "invalid scale");
+  const long long rows = (long long)k->batch * (prefill ? n_q : 1);
+  if (rows > (1LL << 30)) return fail(LLA_ERR_INVALID_ARG, "too many query rows");
+  AttnPlan p;
+  if (!plan_attn(d, rows > 0 ? rows : 1, max_ctx, &p))
+    return fail(LLA_ERR_UNSUPPORTED, "no decode kernel built for this (dtype, d_head, r_k, r_v)");
+  if (!ws || ws_bytes < p.bytes) return fail(LLA_ERR_WORKSPACE, "workspace missing or too small");
+  if (rows == 0) return LLA_OK;
+
+  const size_t es = esize(d);
+  const long long T = d->T, H = d->H, dh = d->d_head, rk = d->r_k, rv = d->r_v;
+  const long long np = k->num_pages;
+  AttnArgs a = {};
+  a.q = q;
+  a.out = out;
+  if (d->variant == LLA_PER_HEAD) {
+    a.k_pool = (const char *)k->k_pool + (size_t)layer * np * H * kPage * rk * es;
+    a.v_pool = (const char *)k->v_pool + (size_t)layer * np * H * kPage * rv * es;
+    a.pool_page_stride_k = H * kPage * rk;
+    a.pool_page_stride_v = H * kPage * rv;
+    a.pool_head_stride_k = kPage * rk;
+    a.pool_head_stride_v = kPage * rv;
+    const long long mu0 = ((long long)layer * H * T + loop) * dh;  // [D][H][T][d]
+    a.mu_k = (const char *)c->mu_k + mu0 * es;
+    a.mu_v = (const char *)c->mu_v + mu0 * es;
+    a.wup_k = (const char *)c->w_up_k + mu0 * rk * es;              // [D][H][T][d][r]
+    a.wup_v = (const char *)c->w_up_v + mu0 * rv * es;
+    a.mu_head_stride = T * dh;
+    a.wup_head_stride_k = T * dh * rk;
+    a.wup_head_stride_v = T * dh * rv;
+  } else {
+    a.k_pool = (const char *)k->k_pool + (size_t)layer * np * kPage * rk * es;
+    a.v_pool = (const char *)k->v_pool + (size_t)layer * np * kPage * rv * es;
+    a.pool_page_stride_k = kPage * rk;
+    a.pool_page_stride_v = kPage * rv;
+    a.pool_head_stride_k = 0;
+    a.pool_head_stride_v = 0;
+    const long long mu0 = ((long long)layer * T + loop) * H * dh;   // [D][T][H][d]
+    a.mu_k = (const char *)c->mu_k + mu0 * es;
+    a.mu_v = (const char *)c->mu_v + mu0 * es;
+    a.wup_k = (const char *)c->w_up_k + mu0 * rk * es;              // [D][T][H][d][r]
+    a.wup_v = (const char *)c->w_up_v + mu0 * rv * es;
+    a.mu_head_stride = dh;
+    a.wup_head_stride_k = dh * rk;
+    a.wup_head_stride_v = dh * rv;
+  }
+  a.page_table = k->page_table;
+  a.max_pages = k->max_pages_per_seq;
+  a.num_pages = k->num_pages;
+  a.rope = rope;
+  a.rope_len = rope_len;
+  a.q_pos = q_pos;
+  a.ctx_len = ctx_len;
+  a.p0 = p0;
+  a.n_q = prefill ? n_q : 1;
+  a.prefill = prefill;
+  a.rows = (int)rows;
+  a.H = d->H;
+  a.max_ctx = max_ctx;
+  a.splits = p.splits;
+  a.pages_per_split = p.pages_per_split;
+  a.head_groups = p.head_groups;
+  a.heads_per_wave = p.hpw;
+  a.waves = p.waves;
+  const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)d->d_head);
+  a.qscale = sc * 1.4426950408889634f;
+  a.err = (int *)ws;
+  a.counters = (int *)((char *)ws + p.counters_off);
+  a.partials = (float *)((char *)ws + p.partials_off);
+  return check_launch(launch_decode(d->dtype, d->d_head, d->r_k, d->r_v, a, stream));
+}
+
+}  // namespace
+}  // namespace lla
+
+using namespace lla;
+
+extern "C" {
+
+int32_t lla_rope_table(const lla_dims *d, int32_t n_pos, float *table, hipStream_t stream) {
+  if (!dims_valid(d)) return fail(LLA_ERR_INVALID_ARG, "invalid lla_dims");
+  if (n_pos < 0 || (n_pos > 0 && !table)) return fail(LLA_ERR_INVALID_ARG, "bad RoPE table arguments");
+  return check_launch(launch_rope_table(n_pos, d->d_head, (double)d->rope_base, table, stream));
+}
+
+size_t lla_workspace_bytes(const lla_dims *d, int32_t op, int32_t batch, int32_t max_ctx, int32_t n) {
+  if (!dims_valid(d) || batch < 0) return 0;
+  if (op == LLA_OP_ENCODE) return n >= 0 ? encode_ws_bytes(d, n) : 0;
+  if (op != LLA_OP_DECODE && op != LLA_OP_PREFILL) return 0;
+  if (max_ctx < 1 || (op == LLA_OP_PREFILL && n < 0)) return 0;
+  const long long rows = (long long)batch * (op == LLA_OP_PREFILL ? n : 1);
+  AttnPlan p;
+  if (!plan_attn(d, rows > 0 ? rows : 1, max_ctx, &p)) return 0;
+  return p.bytes;
+}
+
+int32_t lla_encode_append(const lla_dims *d, const lla_codec *c, const lla_cache *k,
+                          const void *x_k, const void *x_v, const int32_t *pos0, int32_t n_new,
+                          int32_t layer0, int32_t n_layers, void *ws, size_t ws_bytes,
+                          hipStream_t stream) {
+  if (!dims_valid(d)) return fail(LLA_ERR_INVALID_ARG, "invalid lla_dims");
+  if (!c || !k) return fail(LLA_ERR_INVALID_ARG, "null codec or cache");
+  if (!c->mu_k || !c->mu_v || !c->w_down_k || !c->w_down_v)
+    return fail(LLA_ERR_INVALID_ARG, "null encoder parameter (mu or W_down)");
+  if (!k->k_pool || !k->v_pool || !k->page_table) return fail(LLA_ERR_INVALID_ARG, "null pool or page table");
+  if (k->batch < 0 || k->max_pages_per_seq < 1 || k->num_pages < 1)
+    return fail(LLA_ERR_INVALID_ARG, "invalid cache sizes");
+  if (n_new < 0 || n_layers < 0 || layer0 < 0 || layer0 + n_layers > d->D)
+    return fail(LLA_ERR_INVALID_ARG, "layer range or n_new out of range");
+  if ((!x_k || !x_v || !pos0) && n_new > 0 && n_layers > 0 && k->batch > 0)
+    return fail(LLA_ERR_INVALID_ARG, "null x or pos0");
+  const int groups = d->variant == LLA_PER_HEAD ? d->H : 1;
+  const int width = d->variant == LLA_PER_HEAD ? d->T * d->d_head : d->T * d->H * d->d_head;
+  if (!encode_supported(d->dtype, width, d->r_k, d->r_v))
+    return fail(LLA_ERR_UNSUPPORTED, "no encode kernel for this shape");
+  if (!ws || ws_bytes < encode_ws_bytes(d, n_layers)) return fail(LLA_ERR_WORKSPACE, "workspace missing or too small");
+  if ((long long)k->batch * n_new == 0 || n_layers == 0) return LLA_OK;
+  const size_t es = esize(d);
+  const long long np = k->num_pages, rk = d->r_k, rv = d->r_v;
+  EncodeArgs a = {};
+  a.x_k = (const char *)x_k;
+  a.x_v = (const char *)x_v;
+  a.mu_k = (const char *)c->mu_k + (size_t)layer0 * groups * width * es;
+  a.mu_v = (const char *)c->mu_v + (size_t)layer0 * groups * width * es;
+  a.wd_k = (const char *)c->w_down_k + (size_t)layer0 * groups * width * rk * es;
+  a.wd_v = (const char *)c->w_down_v + (size_t)layer0 * groups * width * rv * es;
+  const long long hk = d->variant == LLA_PER_HEAD ? d->H : 1;
+  a.pool_page_stride_k = hk * kPage * rk;
+  a.pool_page_stride_v = hk * kPage * rv;
+  a.pool_head_stride_k = d->variant == LLA_PER_HEAD ? kPage * rk : 0;
+  a.pool_head_stride_v = d->variant == LLA_PER_HEAD ? kPage * rv : 0;
+  a.pool_layer_stride_k = np * a.pool_page_stride_k;
+  a.pool_layer_stride_v = np * a.pool_page_stride_v;
+  a.k_pool = (char *)k->k_pool + (size_t)layer0 * a.pool_layer_stride_k * es;
+  a.v_pool = (char *)k->v_pool + (size_t)layer0 * a.pool_layer_stride_v * es;
+  a.page_table = k->page_table;
+  a.pos0 = pos0;
+  a.max_pages = k->max_pages_per_seq;
+  a.num_pages = k->num_pages;
+  a.batch = k->batch;
+  a.n_new = n_new;
+  a.n_layers = n_layers;
+  a.groups = groups;
+  a.width = width;
+  a.err = (int *)ws;
+  a.muw = (float *)((char *)ws + kHeaderBytes);
+  return check_launch(launch_encode(d->dtype, d->r_k, d->r_v, a, stream));
+}
+
+int32_t lla_decode_attn(const lla_dims *d, const lla_codec *c, const lla_cache *k,
+                        const float *rope, int32_t rope_len, int32_t layer, int32_t loop,
+                        const void *q, const int32_t *q_pos, const int32_t *ctx_len,
+                        int32_t max_ctx, float scale, void *out, void *ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  return attn_call(d, c, k, rope, rope_len, layer, loop, q, q_pos, ctx_len, nullptr, 1, 0,
+                   max_ctx, scale, out, ws, ws_bytes, stream);
+}
+
+int32_t lla_prefill_attn(const lla_dims *d, const lla_codec *c, const lla_cache *k,
+                         const float *rope, int32_t rope_len, int32_t layer, int32_t loop,
+                         int32_t n_q, const void *q, const int32_t *p0, int32_t max_ctx,
+                         float scale, void *out, void *ws, size_t ws_bytes, hipStream_t stream) {
+  return attn_call(d, c, k, rope, rope_len, layer, loop, q, nullptr, nullptr, p0, n_q, 1,
+                   max_ctx, scale, out, ws, ws_bytes, stream);
+}
+
+int32_t lla_cache_scalars(const lla_dims *d, int64_t *teacher, int64_t *latent) {
+  if (!dims_valid(d) || !teacher || !latent) return fail(LLA_ERR_INVALID_ARG, "invalid arguments");
+  *teacher = 2LL * d->T * d->H * d->d_head;
+  *latent = d->variant == LLA_2D ? (int64_t)(d->r_k + d->r_v) : (int64_t)(d->r_k + d->r_v) * d->H;
+  return LLA_OK;
+}
+
+int32_t lla_supported(const lla_dims *d, int32_t op) {
+  if (!dims_valid(d)) return 0;
+  if (op == LLA_OP_ENCODE) {
+    const int width = d->variant == LLA_PER_HEAD ? d->T * d->d_head : d->T * d->H * d->d_head;
+    return encode_supported(d->dtype, width, d->r_k, d->r_v) ? 1 : 0;
+  }
+  if (op == LLA_OP_DECODE || op == LLA_OP_PREFILL) {
+    AttnPlan p;
+    return plan_attn(d, 1, kPage, &p) ? 1 : 0;
+  }
+  return 0;
+}
+
+const char *lla_status_string(int32_t s) {
+  switch (s) {
+    case LLA_OK: return "ok";
+    case LLA_ERR_INVALID_ARG: return "invalid argument";
+    case LLA_ERR_UNSUPPORTED: return "unsupported shape or variant";
+    case LLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case LLA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char *lla_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

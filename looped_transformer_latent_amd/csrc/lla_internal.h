@@ -1,0 +1,64 @@
+// Host-side interfaces between the C ABI layer (lla_api.hip) and the kernel
+// launchers.  Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lla.h"
+
+namespace lla {
+
+constexpr int kPage = 16;          // tokens per cache page
+constexpr int kHeaderBytes = 256;  // workspace header: int32 error word at byte 0
+
+// Arguments of one attention launch (decode or prefill).  All pointers are
+// device pointers; codec and pool pointers are already offset to (layer, loop).
+struct AttnArgs {
+  const void *q;
+  void *out;
+  const char *k_pool, *v_pool;          // pool base of the layer
+  long long pool_page_stride_k;         // elements between physical pages
+  long long pool_page_stride_v;
+  long long pool_head_stride_k;         // elements between heads within a page (0 for LLA-2D)
+  long long pool_head_stride_v;
+  const char *mu_k, *mu_v;              // mu_t of head 0
+  const char *wup_k, *wup_v;            // W_up,t of head 0
+  long long mu_head_stride;             // elements between heads
+  long long wup_head_stride_k, wup_head_stride_v;
+  const int32_t *page_table;
+  int max_pages, num_pages;
+  const float *rope;                    // [rope_len][d/2][2]
+  int rope_len;
+  const int32_t *q_pos, *ctx_len, *p0;  // decode uses q_pos/ctx_len; prefill uses p0
+  int n_q, prefill, rows, H, max_ctx;
+  int splits, pages_per_split, head_groups, heads_per_wave, waves;
+  float qscale;                          // softmax scale * log2(e)
+  int *err;
+  int *counters;                         // [rows][head_groups], zero between calls
+  float *partials;                       // [rows][H][splits][r_v + 2]
+};
+
+struct EncodeArgs {
+  const char *x_k, *x_v;       // [n_layers][B][n_new][groups][width]
+  const char *mu_k, *mu_v;     // layer0 base, [D][groups][width]
+  const char *wd_k, *wd_v;     // layer0 base, [D][groups][width][r]
+  char *k_pool, *v_pool;       // layer0 base
+  long long pool_layer_stride_k, pool_layer_stride_v;  // elements
+  long long pool_page_stride_k, pool_page_stride_v;
+  long long pool_head_stride_k, pool_head_stride_v;
+  const int32_t *page_table, *pos0;
+  int max_pages, num_pages, batch, n_new, n_layers, groups, width;
+  float *muw;                  // workspace [n_layers][groups][r_k + r_v]
+  int *err;
+};
+
+// Kernel dispatch: return hipSuccess, or hipErrorInvalidConfiguration when the
+// shape has no instantiated kernel.
+bool decode_supported(int dtype, int d_head, int r_k, int r_v, int heads_per_wave);
+hipError_t launch_decode(int dtype, int d_head, int r_k, int r_v, const AttnArgs &a,
+                         hipStream_t stream);
+bool encode_supported(int dtype, int width, int r_k, int r_v);
+hipError_t launch_encode(int dtype, int r_k, int r_v, const EncodeArgs &a, hipStream_t stream);
+hipError_t launch_rope_table(int n_pos, int d_head, double base, float *table, hipStream_t s);
+
+}  // namespace lla

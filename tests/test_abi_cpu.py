@@ -1,0 +1,126 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and
+its host-side logic (validation, workspace planning, eq. (4)) behaves.  No call
+here reaches a kernel launch."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from looped_transformer_latent_amd import lla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+NULL = ctypes.c_void_p(0)
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    names = set()
+    for hdr in os.listdir(os.path.join(ROOT, "include")):
+        if hdr.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", hdr)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(lla_\w+)\s*\(", text))
+    return sorted(names)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = lla.load()
+    names = declared_functions()
+    assert len(names) >= 9
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(lla.EXPORTS) <= set(names)
+
+
+def _dims(**kw):
+    base = dict(T=4, D=24, H=16, d_head=128, r_k=16, r_v=32)
+    base.update(kw)
+    return lla.make_dims(**base)
+
+
+@pytest.mark.parametrize("rk,rv,teacher_kib,latent_kib", [(96, 160, 768, 192), (16, 32, 768, 36)])
+def test_cache_scalars_table5(rk, rv, teacher_kib, latent_kib):
+    # Table 5 (cc.laoqi.cc close reading, 四:结果 item 9): KV bytes per token of Ouro-1.4B in bf16
+    t, l = lla.cache_scalars(_dims(r_k=rk, r_v=rv))
+    assert t * 24 * 2 == teacher_kib * 1024 and l * 24 * 2 == latent_kib * 1024
+    t2, l2 = lla.cache_scalars(_dims(r_k=rk, r_v=rv, variant=lla.TWO_D))
+    assert t2 == t and l2 * 16 == l
+
+
+def test_supported_shapes():
+    assert lla.supported(_dims(), lla.OP_DECODE)
+    assert lla.supported(_dims(dtype=lla.F32, T=4, D=1, H=2, d_head=64), lla.OP_DECODE)
+    assert lla.supported(_dims(r_k=96, r_v=160), lla.OP_DECODE)
+    assert not lla.supported(_dims(d_head=96), lla.OP_DECODE)
+    assert not lla.supported(_dims(r_k=24), lla.OP_DECODE)
+    assert lla.supported(_dims(), lla.OP_ENCODE)
+    assert not lla.supported(_dims(page_size=32), lla.OP_DECODE)
+
+
+def test_workspace_bytes_planning():
+    d = _dims()
+    small = lla.workspace_bytes(d, lla.OP_DECODE, 32, 4096)
+    big = lla.workspace_bytes(d, lla.OP_DECODE, 768, 4096)
+    assert small >= 256 and big >= 256
+    assert lla.workspace_bytes(d, lla.OP_DECODE, 1, 16) == 256          # one split: header only
+    assert lla.workspace_bytes(d, lla.OP_DECODE, 32, 0) == 0            # invalid max_ctx
+    assert lla.workspace_bytes(_dims(d_head=96), lla.OP_DECODE, 32, 4096) == 0
+    pre = lla.workspace_bytes(d, lla.OP_PREFILL, 4, 4096, 8)
+    assert pre == lla.workspace_bytes(d, lla.OP_DECODE, 32, 4096)      # 4 x 8 query rows
+    enc = lla.workspace_bytes(d, lla.OP_ENCODE, 64, 0, 24)
+    assert enc >= 256 + 4 * 24 * 16 * 48
+
+
+def _decode(d, cache=None, codec=None, rope=FAKE, rope_len=4096, layer=0, loop=0, q=FAKE,
+            q_pos=FAKE, ctx=FAKE, max_ctx=4096, scale=0.0, out=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    lib = lla.load()
+    codec = codec or lla.Codec(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
+    cache = cache or lla.Cache(0x1000, 0x1000, 0x1000, 32, 256, 8192)
+    return lib.lla_decode_attn(ctypes.byref(d) if d is not None else None, ctypes.byref(codec),
+                               ctypes.byref(cache), rope, rope_len, layer, loop, q, q_pos, ctx,
+                               max_ctx, scale, out, ws, ws_bytes, NULL)
+
+
+def test_decode_validation_errors():
+    d = _dims()
+    E = lla.ERR_INVALID_ARG
+    assert _decode(None) == E
+    assert _decode(d, layer=24) == E and _decode(d, layer=-1) == E
+    assert _decode(d, loop=4) == E
+    assert _decode(d, rope=NULL) == E
+    assert _decode(d, max_ctx=4097) == E                                 # beyond the RoPE table
+    assert _decode(d, max_ctx=0) == E
+    assert _decode(d, rope_len=1 << 20, max_ctx=256 * 16 + 1) == E       # beyond the page table
+    assert _decode(d, q=NULL) == E and _decode(d, out=NULL) == E and _decode(d, ctx=NULL) == E
+    assert _decode(d, scale=-1.0) == E or _decode(d, scale=float("nan")) == E
+    assert _decode(d, codec=lla.Codec(0x1000, 0, 0x1000, 0x1000, 0x1000, 0x1000)) == E
+    assert _decode(d, cache=lla.Cache(0x1000, 0x1000, 0, 32, 256, 8192)) == E
+    assert _decode(_dims(d_head=96)) == lla.ERR_UNSUPPORTED
+    assert _decode(_dims(page_size=8)) == E
+    assert _decode(d, ws_bytes=16) == lla.ERR_WORKSPACE
+    assert _decode(d, ws=NULL) == lla.ERR_WORKSPACE
+    assert b"workspace" in lla.load().lla_last_error()
+
+
+def test_encode_and_prefill_validation_errors():
+    lib = lla.load()
+    d = _dims()
+    codec = lla.Codec(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
+    cache = lla.Cache(0x1000, 0x1000, 0x1000, 64, 512, 32768)
+    enc = lambda **kw: lib.lla_encode_append(
+        ctypes.byref(d), ctypes.byref(kw.get("codec", codec)), ctypes.byref(cache), FAKE, FAKE,
+        kw.get("pos0", FAKE), kw.get("n_new", 512), kw.get("layer0", 0), kw.get("n_layers", 24),
+        kw.get("ws", FAKE), kw.get("ws_bytes", 16), NULL)
+    assert enc(layer0=1) == lla.ERR_INVALID_ARG                         # 1 + 24 > D
+    assert enc(n_new=-1) == lla.ERR_INVALID_ARG
+    assert enc(pos0=NULL) == lla.ERR_INVALID_ARG
+    assert enc(codec=lla.Codec(0x1000, 0x1000, 0, 0x1000, 0x1000, 0x1000)) == lla.ERR_INVALID_ARG
+    assert enc() == lla.ERR_WORKSPACE
+    pre = lib.lla_prefill_attn(ctypes.byref(d), ctypes.byref(codec), ctypes.byref(cache), FAKE,
+                               8192, 0, 0, -1, FAKE, FAKE, 8192, 0.0, FAKE, FAKE, 1 << 30, NULL)
+    assert pre == lla.ERR_INVALID_ARG
+    assert lib.lla_rope_table(ctypes.byref(d), -1, FAKE, NULL) == lla.ERR_INVALID_ARG
+    assert lla.load().lla_status_string(lla.ERR_WORKSPACE) == b"workspace missing or too small"
