@@ -37,7 +37,23 @@ def parse():
     p.add_argument("--workload", default="ouro1.4b-21x-b768-paged")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle sample time")
+    p.add_argument("--calibrate-copy", type=float, default=0.0, metavar="GIB",
+                   help="only run a plain device copy of GIB gibibytes, three times (a known "
+                        "byte count for scaling the HBM traffic counters)")
     return p.parse_args()
+
+
+def calibrate_copy(gib: float) -> None:
+    import torch
+    n = int(gib * 2 ** 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read_per_launch": 4 * n,
+                      "bytes_written_per_launch": 4 * n, "launches": 3}), flush=True)
 
 
 def cpu_baseline(w, codec_h, pt_h, layer, loop, target_s):
@@ -84,6 +100,9 @@ def main():
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
         sys.exit(2)
+    if args.calibrate_copy > 0:
+        calibrate_copy(args.calibrate_copy)
+        return
     import torch
 
     from looped_transformer_latent_amd import lla

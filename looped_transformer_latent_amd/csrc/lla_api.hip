@@ -19,6 +19,8 @@ int32_t fail(int32_t code, const char *msg) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+constexpr int kMaxPagesPerSplit = 2048;  // page-table entries a workgroup stages in LDS
+
 bool dims_valid(const lla_dims *d) {
   return d && d->T > 0 && d->D > 0 && d->H > 0 && d->d_head > 0 && d->d_head % 2 == 0 &&
          d->r_k > 0 && d->r_v > 0 && (d->variant == LLA_PER_HEAD || d->variant == LLA_2D) &&
@@ -30,7 +32,7 @@ size_t esize(const lla_dims *d) { return d->dtype == LLA_BF16 ? 2 : 4; }
 
 // How an attention call is cut into workgroups.
 struct AttnPlan {
-  int hpw, waves, head_groups, splits, pages_per_split;
+  int hpw, waves, head_groups, splits, pages_per_split, chunk_pages;
   size_t counters_off, partials_off, bytes;
 };
 
@@ -46,11 +48,18 @@ bool plan_attn(const lla_dims *d, long long rows, int max_ctx, AttnPlan *p) {
   p->hpw = hpw;
   p->waves = waves;
   p->head_groups = wave_heads / waves;
+  // RoPE rows are staged in LDS in chunks of pages, at most 4 16-byte slots per
+  // thread per pass: d_head/4 slots per position, 16 positions per page.
+  const int slots_per_page = kPage * (d->d_head / 4);
+  int ch = (4 * 64 * waves) / slots_per_page;
+  p->chunk_pages = ch < 1 ? 1 : (ch > 8 ? 8 : ch);
   const int pages = (max_ctx + kPage - 1) / kPage;
   const long long base = rows * p->head_groups;
   long long s = (1024 + base - 1) / base;
   const long long smax = pages / 4 > 1 ? pages / 4 : 1;
   if (s > smax) s = smax;
+  const long long smin = (pages + kMaxPagesPerSplit - 1) / kMaxPagesPerSplit;  // LDS staging bound
+  if (s < smin) s = smin;
   if (s < 1) s = 1;
   int pps = (int)((pages + s - 1) / s);
   if (pps < 1) pps = 1;
@@ -164,6 +173,7 @@ int32_t attn_call(const lla_dims *d, const lla_codec *c, const lla_cache *k, con
   a.head_groups = p.head_groups;
   a.heads_per_wave = p.hpw;
   a.waves = p.waves;
+  a.chunk_pages = p.chunk_pages;
   const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)d->d_head);
   a.qscale = sc * 1.4426950408889634f;
   a.err = (int *)ws;

@@ -173,77 +173,141 @@ __global__ __launch_bounds__(512) void decode_ph_kernel(AttnArgs a) {
     for (int k = 0; k < CV; ++k) acc[hh][k] = 0.f;
   }
 
-  // ---- main loop over this split's pages ----
-  for (int lp = lp0; lp < lp1; ++lp) {
-    const int pp = a.page_table[(long long)b * a.max_pages + lp];
-    if (pp < 0 || pp >= a.num_pages) {
-      errbits |= LLA_DEVERR_PAGE;
-      continue;
-    }
-    const int pos = lp * kPage + n;
-    const bool valid = pos < ctx;
-    const int tpos = valid ? pos : ctx - 1;  // keep table reads in range on a ragged page
-    float cs[NT][8];
-    {
-      const float *rt = a.rope + (long long)tpos * DH + 8 * g;
+  // ---- main loop over this split's pages, software-pipelined by one page ----
+  // Per page, lane (g, n) loads: cos/sin of its 16 pair indices at its token's
+  // position (2*NT x 16 B), and per head its K B-operand (KS x 16 B) and its
+  // r_v/4-wide V chunk.  Tokens past ctx_len (only on the last page) read the
+  // last valid row instead, so every loaded value is real data; their scores
+  // are forced to -inf and their weights are exactly zero.
+  constexpr int KV = BF ? CV / 8 : CV / 4;  // 16-byte V loads per lane per head
+  constexpr int KK = BF ? KS : RK / 16;     // 16-byte K loads per lane per head
+  struct Page {
+    u32x4 k[HPW][KK];
+    u32x4 v[HPW][KV];
+    int ok;
+    int last;  // last valid row of this page (15 unless the page is the last one)
+  };
+  // LDS: [trig: 2 chunk buffers][page-table entries of the split][epilogue floats]
+  constexpr int SPR = DH / 4;           // 16-byte slots per RoPE table row (d/2 pairs x cos, sin)
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int CH = a.chunk_pages;         // pages per trig chunk
+  const int TS = CH * kPage * SPR;      // 16-byte slots per chunk buffer
+  char *s_trig = smem;
+  int *s_pt = (int *)(smem + 2 * TS * 16);
+  {
+    const int *pt_row = a.page_table + (long long)b * a.max_pages;
+    for (int i = threadIdx.x; i < lp1 - lp0; i += blockDim.x) s_pt[i] = pt_row[lp0 + i];
+    __syncthreads();
+  }
+  auto page_at = [&](int lp) -> int { return __builtin_amdgcn_readfirstlane(s_pt[lp - lp0]); };
+
+  // Trig staging.  Chunk c covers pages [lp0 + c*CH, lp0 + (c+1)*CH).  Its rows
+  // (one per token position) hold the table row of that position; within a row
+  // the 16-byte slot `ls` is stored at ls ^ (position % 16), so the 16 lanes of a
+  // row-group, which read the same logical slot of 16 consecutive positions, hit
+  // 16 different bank groups.  Each thread moves at most 4 slots per chunk.
+  const int nthreads = blockDim.x;
+  const char *rope_b = (const char *)a.rope;
+  const int npass = (TS + 4 * nthreads - 1) / (4 * nthreads);
+  f32x4 stg[4];
+  auto stage_load = [&](int c, int pass) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const f32x4 u = *(const f32x4 *)(rt + 32 * t);
-        const f32x4 v = *(const f32x4 *)(rt + 32 * t + 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          cs[t][e] = u[e];
-          cs[t][4 + e] = v[e];
-        }
+    for (int j = 0; j < 4; ++j) {
+      const int q = threadIdx.x + (4 * pass + j) * nthreads;
+      if (q < TS) {
+        const int R = q / SPR, ps = q % SPR, rn = R % kPage;
+        int pos = (lp0 + c * CH + R / kPage) * kPage + rn;
+        pos = min(pos, ctx - 1);
+        stg[j] = *(const f32x4 *)(rope_b + ((long long)pos * SPR + (ps ^ rn)) * 16);
       }
     }
+  };
+  auto stage_store = [&](int c, int pass) {
+    char *dst = s_trig + (c & 1) * TS * 16;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int q = threadIdx.x + (4 * pass + j) * nthreads;
+      if (q < TS) *(f32x4 *)(dst + q * 16) = stg[j];
+    }
+  };
+
+  auto load_page = [&](int lp, int pp_raw, Page &pg) {
+    pg.ok = (pp_raw >= 0 && pp_raw < a.num_pages);
+    const long long pp = pg.ok ? pp_raw : 0;
+    pg.last = min(kPage - 1, ctx - 1 - lp * kPage);
+    const int row_n = min(n, pg.last);
+    // uniform page bases (scalar registers) + 32-bit per-lane offsets
+    const char *kpage = a.k_pool + pp * a.pool_page_stride_k * S::esz;
+    const char *vpage = a.v_pool + pp * a.pool_page_stride_v * S::esz;
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
       const int h = h0 + hh;
-      const char *kp = a.k_pool + ((long long)pp * a.pool_page_stride_k +
-                                   (long long)h * a.pool_head_stride_k + (long long)n * RK) * S::esz;
-      const char *vp = a.v_pool + ((long long)pp * a.pool_page_stride_v +
-                                   (long long)h * a.pool_head_stride_v + (long long)n * RV + CV * g) * S::esz;
+      const uint32_t koff = (uint32_t)((h * a.pool_head_stride_k + row_n * RK) * S::esz);
+      const uint32_t voff = (uint32_t)((h * a.pool_head_stride_v + row_n * RV + CV * g) * S::esz);
+      if constexpr (BF) {
+#pragma unroll
+        for (int ks = 0; ks < KK; ++ks) {
+          const int r0 = 32 * ks + 8 * g;
+          if (r0 + 8 <= RK) {
+            pg.k[hh][ks] = *(const u32x4 *)(kpage + koff + r0 * 2);
+          } else {  // constant column: bf16 (1, 1) picks up alpha hi + lo
+            const u32x4 c = {r0 == RK ? 0x3F803F80u : 0u, 0u, 0u, 0u};
+            pg.k[hh][ks] = c;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int k4 = 0; k4 < KK; ++k4)
+          pg.k[hh][k4] = *(const u32x4 *)(kpage + koff + ((RK / 4) * g + 4 * k4) * 4);
+      }
+#pragma unroll
+      for (int kv = 0; kv < KV; ++kv) pg.v[hh][kv] = *(const u32x4 *)(vpage + voff + kv * 16);
+    }
+  };
+
+  // An invalid page-table entry was replaced by page 0 at load time; its
+  // tokens are masked out here (no branch, so every path waits the same way)
+  // and the row is poisoned through the error bits.
+  auto compute_page = [&](const Page &cur, int lp) {
+    errbits |= cur.ok ? 0 : LLA_DEVERR_PAGE;
+    const bool valid = cur.ok && n <= cur.last;
+    const int row_n = min(n, cur.last);
+    const char *tb = s_trig + (((lp - lp0) / CH) & 1) * TS * 16 +
+                     (((lp - lp0) % CH) * kPage + row_n) * SPR * 16;
+    f32x4 trig[2 * NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int ls = 8 * t + 2 * g;
+      trig[2 * t] = *(const f32x4 *)(tb + ((ls ^ row_n) * 16));
+      trig[2 * t + 1] = *(const f32x4 *)(tb + (((ls + 1) ^ row_n) * 16));
+    }
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
       Op bk[KS];
       float cv[CV];
       if constexpr (BF) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int r0 = 32 * ks + 8 * g;
-          u32x4 v = {0, 0, 0, 0};
-          if (r0 + 8 <= RK) v = *(const u32x4 *)(kp + r0 * 2);
-          else if (r0 == RK) v[0] = 0x3F803F80u;  // bf16 (1, 1) multiplies alpha hi, lo
-          bk[ks] = as_bf16x8(v);
-        }
+        for (int ks = 0; ks < KS; ++ks) bk[ks] = as_bf16x8(cur.k[hh][ks]);
 #pragma unroll
-        for (int k8 = 0; k8 < CV / 8; ++k8) {
-          const u32x4 v = *(const u32x4 *)(vp + k8 * 16);
+        for (int kv = 0; kv < KV; ++kv) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            cv[8 * k8 + 2 * e] = bf16_lo(v[e]);
-            cv[8 * k8 + 2 * e + 1] = bf16_hi(v[e]);
+            cv[8 * kv + 2 * e] = bf16_lo(cur.v[hh][kv][e]);
+            cv[8 * kv + 2 * e + 1] = bf16_hi(cur.v[hh][kv][e]);
           }
         }
       } else {
-        float kr[RK / 4];
 #pragma unroll
-        for (int k4 = 0; k4 < RK / 16; ++k4) {
-          const f32x4 v = *(const f32x4 *)(kp + ((RK / 4) * g + 4 * k4) * 4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) kr[4 * k4 + e] = v[e];
-        }
-#pragma unroll
-        for (int ks = 0; ks < RK / 4; ++ks) bk[ks] = kr[ks];
+        for (int ks = 0; ks < RK / 4; ++ks) bk[ks] = __uint_as_float(cur.k[hh][ks / 4][ks % 4]);
         bk[RK / 4] = (g == 0) ? 1.f : 0.f;
 #pragma unroll
-        for (int k4 = 0; k4 < CV / 4; ++k4) {
-          const f32x4 v = *(const f32x4 *)(vp + k4 * 16);
+        for (int kv = 0; kv < KV; ++kv) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) cv[4 * k4 + e] = v[e];
+          for (int e = 0; e < 4; ++e) cv[4 * kv + e] = __uint_as_float(cur.v[hh][kv][e]);
         }
       }
       // X / Y tiles: rows = pair indices 16t + 4g + e, column = token n
-      float sc = 0.f;
+      float sc0 = 0.f, sc1 = 0.f;
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         f32x4 X = {0.f, 0.f, 0.f, 0.f}, Y = {0.f, 0.f, 0.f, 0.f};
@@ -252,26 +316,64 @@ __global__ __launch_bounds__(512) void decode_ph_kernel(AttnArgs a) {
           X = S::mma(A[hh][t][0][ks], bk[ks], X);
           Y = S::mma(A[hh][t][1][ks], bk[ks], Y);
         }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          sc = fmaf(cs[t][2 * e], X[e], sc);
-          sc = fmaf(cs[t][2 * e + 1], Y[e], sc);
-        }
+        const f32x4 c0 = trig[2 * t], c1 = trig[2 * t + 1];  // (cos, sin) x 4
+        sc0 = fmaf(c0[0], X[0], sc0);
+        sc1 = fmaf(c0[1], Y[0], sc1);
+        sc0 = fmaf(c0[2], X[1], sc0);
+        sc1 = fmaf(c0[3], Y[1], sc1);
+        sc0 = fmaf(c1[0], X[2], sc0);
+        sc1 = fmaf(c1[1], Y[2], sc1);
+        sc0 = fmaf(c1[2], X[3], sc0);
+        sc1 = fmaf(c1[3], Y[3], sc1);
       }
-      sc = sum_across_rows(sc);
+      float sc = sum_across_rows(sc0 + sc1);
       sc = valid ? sc : -INFINITY;
       const float mt = max_in_row(sc);
       if (mt > m_run[hh]) {  // wave-uniform
-        const float corr = exp2f(m_run[hh] - mt);
+        const float corr = fast_exp2(m_run[hh] - mt);
         z[hh] *= corr;
 #pragma unroll
         for (int k = 0; k < CV; ++k) acc[hh][k] *= corr;
         m_run[hh] = mt;
       }
-      const float p = exp2f(sc - m_run[hh]);
+      const float p = fast_exp2(sc - m_run[hh]);
       z[hh] += p;
 #pragma unroll
-      for (int k = 0; k < CV; ++k) acc[hh][k] = fmaf(p, valid ? cv[k] : 0.f, acc[hh][k]);
+      for (int k = 0; k < CV; ++k) acc[hh][k] = fmaf(p, cv[k], acc[hh][k]);
+    }
+  };
+
+  // Ping-pong over two page buffers.  Every half-iteration issues exactly one
+  // page of latent loads (past the end it re-reads the split's last page, which
+  // is never computed), so each compute has the next page's loads in flight.
+  // At a chunk boundary all waves drain, store the staged trig chunk to LDS,
+  // synchronise, and start staging the chunk after it.
+  auto chunk_boundary = [&](int lp) {
+    const int c = (lp - lp0) / CH;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    stage_store(c, 0);
+    for (int pass = 1; pass < npass; ++pass) {  // small workgroups only: synchronous
+      stage_load(c, pass);
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      stage_store(c, pass);
+    }
+    __syncthreads();
+    if (lp0 + (c + 1) * CH < lp1) stage_load(c + 1, 0);
+  };
+  if (lp0 < lp1) {
+    Page pa, pb;
+    stage_load(0, 0);
+    load_page(lp0, page_at(lp0), pa);
+    for (int lp = lp0; lp < lp1; lp += 2) {
+      if ((lp - lp0) % CH == 0) chunk_boundary(lp);
+      const int l1 = min(lp + 1, lp1 - 1);
+      load_page(l1, page_at(l1), pb);
+      compute_page(pa, lp);
+      if (lp + 1 >= lp1) break;
+      if ((lp + 1 - lp0) % CH == 0) chunk_boundary(lp + 1);
+      const int l2 = min(lp + 2, lp1 - 1);
+      load_page(l2, page_at(l2), pa);
+      compute_page(pb, lp + 1);
     }
   }
 
@@ -285,8 +387,8 @@ __global__ __launch_bounds__(512) void decode_ph_kernel(AttnArgs a) {
   if (errbits && threadIdx.x == 0) atomicOr(a.err, errbits);
   const bool bad = errbits != 0;
 
-  extern __shared__ float sh[];  // [waves][HPW][RV + 2]
   __shared__ int s_last;
+  float *sh = (float *)(s_pt + a.pages_per_split);  // [waves][HPW][RV + 2]
   float *mine = sh + (wave * HPW) * (RV + 2);
 
   if (a.splits > 1) {
@@ -384,9 +486,17 @@ struct Shape {
 };
 template <bool BF, int DH, int RK, int RV, int HPW>
 hipError_t go(const AttnArgs &a, hipStream_t stream) {
+  static bool lds_raised = false;  // allow more than the default 64 KiB of LDS once per kernel
+  if (!lds_raised) {
+    const hipError_t e = hipFuncSetAttribute((const void *)decode_ph_kernel<BF, DH, RK, RV, HPW>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 256);
+    if (e != hipSuccess) return e;
+    lds_raised = true;
+  }
   const dim3 grid((unsigned)(a.rows * a.head_groups * a.splits));
   const dim3 block((unsigned)(64 * a.waves));
-  const size_t shmem = sizeof(float) * a.waves * HPW * (RV + 2);
+  const size_t shmem = 2 * (size_t)a.chunk_pages * kPage * (DH / 4) * 16 + sizeof(int) * a.pages_per_split +
+                       sizeof(float) * a.waves * HPW * (RV + 2);
   hipLaunchKernelGGL((decode_ph_kernel<BF, DH, RK, RV, HPW>), grid, block, shmem, stream, a);
   return hipGetLastError();
 }
@@ -396,7 +506,6 @@ hipError_t go(const AttnArgs &a, hipStream_t stream) {
   X(false, 64, 16, 32, 1)      \
   X(false, 64, 16, 32, 2)      \
   X(false, 128, 16, 32, 1)     \
-  X(false, 128, 16, 32, 2)     \
   X(true, 64, 16, 32, 1)       \
   X(true, 64, 16, 32, 2)       \
   X(true, 128, 16, 32, 1)      \

@@ -24,27 +24,50 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 }
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// Sum over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48).
-__device__ __forceinline__ float sum_across_rows(float x) {
-  x += __shfl_xor(x, 32);
-  x += __shfl_xor(x, 16);
-  return x;
+// 2^x on the hardware exp unit.  Used for softmax weights, whose arguments are
+// <= 0; results below the fp32 normal range may flush to zero, which only drops
+// weights smaller than 2^-126 of the largest one.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// DPP lane permutations within 16-lane rows.
+constexpr int kDppQuadSwap1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kDppQuadSwap2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // row_half_mirror (lane i <-> 7 - i within 8)
+constexpr int kDppMirror = 0x140;     // row_mirror (lane i <-> 15 - i within 16)
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
-// Max / sum within each 16-lane row.
+
+// Max / sum over the 16 lanes of each row; every lane of the row gets the result.
 __device__ __forceinline__ float max_in_row(float x) {
-  x = fmaxf(x, __shfl_xor(x, 1));
-  x = fmaxf(x, __shfl_xor(x, 2));
-  x = fmaxf(x, __shfl_xor(x, 4));
-  x = fmaxf(x, __shfl_xor(x, 8));
+  x = fmaxf(x, dpp<kDppQuadSwap1>(x));
+  x = fmaxf(x, dpp<kDppQuadSwap2>(x));
+  x = fmaxf(x, dpp<kDppHalfMirror>(x));
+  x = fmaxf(x, dpp<kDppMirror>(x));
   return x;
 }
 __device__ __forceinline__ float sum_in_row(float x) {
-  x += __shfl_xor(x, 1);
-  x += __shfl_xor(x, 2);
-  x += __shfl_xor(x, 4);
-  x += __shfl_xor(x, 8);
+  x += dpp<kDppQuadSwap1>(x);
+  x += dpp<kDppQuadSwap2>(x);
+  x += dpp<kDppHalfMirror>(x);
+  x += dpp<kDppMirror>(x);
   return x;
 }
+
+// Sum over the four 16-lane rows (lanes l, l^16, l^32, l^48) with the gfx950
+// row-swap permutes: after the 32-lane swap each lane holds rows {0+2, 1+3},
+// after the 16-lane swap all four.
+__device__ __forceinline__ float sum_across_rows(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const float y = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  const uint32_t v = __float_as_uint(y);
+  const auto q = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
 __device__ __forceinline__ float max_in_wave(float x) {
   for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
   return x;

@@ -32,6 +32,7 @@ struct AttnArgs {
   const int32_t *q_pos, *ctx_len, *p0;  // decode uses q_pos/ctx_len; prefill uses p0
   int n_q, prefill, rows, H, max_ctx;
   int splits, pages_per_split, head_groups, heads_per_wave, waves;
+  int chunk_pages;                       // pages per LDS-staged RoPE chunk
   float qscale;                          // softmax scale * log2(e)
   int *err;
   int *counters;                         // [rows][head_groups], zero between calls

@@ -99,6 +99,9 @@ WORKLOADS = {
     # the high-capacity point: batch 768, 4k context, shuffled 16-token pages
     "ouro1.4b-21x-b768-paged": Workload("ouro1.4b-21x-b768-paged", 4, 24, 16, 128, 16, 32,
                                         PER_HEAD, BF16, 768, 4096, True, 1, 1003),
+    # the same with an identity page table (isolates the cost of scattered pages)
+    "ouro1.4b-21x-b768-contig": Workload("ouro1.4b-21x-b768-contig", 4, 24, 16, 128, 16, 32,
+                                         PER_HEAD, BF16, 768, 4096, False, 1, 1003),
     # 4x compression plus encode/append of 512 tokens per sequence, 8k context
     "ouro1.4b-4x-b64-encode": Workload("ouro1.4b-4x-b64-encode", 4, 24, 16, 128, 96, 160,
                                        PER_HEAD, BF16, 64, 8192, False, 512, 1004),
