@@ -37,22 +37,23 @@ struct AttnPlan {
 };
 
 bool plan_attn(const lla_dims *d, long long rows, int max_ctx, AttnPlan *p) {
+  // Workgroup shape: 8 waves of 2 heads (16 heads) where possible; otherwise
+  // 8 waves of 1 head, or 2 waves for small head counts.
   const int H = d->H;
-  int hpw = 1;
-  if (H % 2 == 0 && H >= 4 && decode_supported(d->dtype, d->d_head, d->r_k, d->r_v, 2)) hpw = 2;
-  if (!decode_supported(d->dtype, d->d_head, d->r_k, d->r_v, hpw)) return false;
-  const int wave_heads = H / hpw;
-  int waves = 1;
-  for (int w = 8; w >= 1; --w)
-    if (wave_heads % w == 0) { waves = w; break; }
+  int hpw = 0, waves = 0;
+  const int cand[4][2] = {{2, 8}, {1, 8}, {2, 2}, {1, 2}};
+  for (const auto &c : cand) {
+    if (H % (c[0] * c[1]) == 0 && decode_supported(d->dtype, d->d_head, d->r_k, d->r_v, c[0], c[1])) {
+      hpw = c[0];
+      waves = c[1];
+      break;
+    }
+  }
+  if (!hpw) return false;
   p->hpw = hpw;
   p->waves = waves;
-  p->head_groups = wave_heads / waves;
-  // RoPE rows are staged in LDS in chunks of pages, at most 4 16-byte slots per
-  // thread per pass: d_head/4 slots per position, 16 positions per page.
-  const int slots_per_page = kPage * (d->d_head / 4);
-  int ch = (4 * 64 * waves) / slots_per_page;
-  p->chunk_pages = ch < 1 ? 1 : (ch > 8 ? 8 : ch);
+  p->head_groups = H / (hpw * waves);
+  p->chunk_pages = kDecodeRing;
   const int pages = (max_ctx + kPage - 1) / kPage;
   const long long base = rows * p->head_groups;
   long long s = (1024 + base - 1) / base;
@@ -62,7 +63,8 @@ bool plan_attn(const lla_dims *d, long long rows, int max_ctx, AttnPlan *p) {
   if (s < smin) s = smin;
   if (s < 1) s = 1;
   int pps = (int)((pages + s - 1) / s);
-  if (pps < 1) pps = 1;
+  pps = (pps + kDecodeRing - 1) / kDecodeRing * kDecodeRing;  // whole trips of the page ring
+  if (pps < kDecodeRing) pps = kDecodeRing;
   p->pages_per_split = pps;
   p->splits = (pages + pps - 1) / pps;
   if (p->splits < 1) p->splits = 1;

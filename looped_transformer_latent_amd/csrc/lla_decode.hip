@@ -61,8 +61,8 @@ constexpr int ksteps() {
   return BF ? (RK + 2 + 31) / 32 : RK / 4 + 1;
 }
 
-template <bool BF, int DH, int RK, int RV, int HPW>
-__global__ __launch_bounds__(512) void decode_ph_kernel(AttnArgs a) {
+template <bool BF, int DH, int RK, int RV, int HPW, int NW>
+__global__ __launch_bounds__(64 * NW) void decode_ph_kernel(AttnArgs a) {
   using S = St<BF>;
   using Op = typename S::Opnd;
   constexpr int NT = DH / 32;         // tile pairs: pair indices [16t, 16t + 16)
@@ -72,6 +72,7 @@ __global__ __launch_bounds__(512) void decode_ph_kernel(AttnArgs a) {
   static_assert(DH % 32 == 0 && RK % 16 == 0 && RV % 32 == 0, "shape");
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int NTH = 64 * NW;
   const int g = lane >> 4, n = lane & 15;
 
   int bid = blockIdx.x;
@@ -181,19 +182,35 @@ __global__ __launch_bounds__(512) void decode_ph_kernel(AttnArgs a) {
   // are forced to -inf and their weights are exactly zero.
   constexpr int KV = BF ? CV / 8 : CV / 4;  // 16-byte V loads per lane per head
   constexpr int KK = BF ? KS : RK / 16;     // 16-byte K loads per lane per head
+  // Two heads with r_k = 16 (bf16): one 64-lane load fetches both heads' K rows
+  // (lanes 0-31 head h0, lanes 32-63 head h0+1, each lane one 16-byte chunk of
+  // its token's row); a permlane32 swap later splits them into the two MFMA
+  // B-operands, bringing in the constant column from the other half.
+  constexpr bool KPAIR = BF && HPW == 2 && RK == 16;
   struct Page {
-    u32x4 k[HPW][KK];
+    u32x4 k[KPAIR ? 1 : HPW][KK];
     u32x4 v[HPW][KV];
     int ok;
     int last;  // last valid row of this page (15 unless the page is the last one)
   };
   // LDS: [trig: 2 chunk buffers][page-table entries of the split][epilogue floats]
-  constexpr int SPR = DH / 4;           // 16-byte slots per RoPE table row (d/2 pairs x cos, sin)
+  // RoPE rows in LDS: fp32 (cos, sin) pairs for fp32 storage; for bf16 storage
+  // fp16 pairs (4 bytes), read straight into mixed-precision FMAs.  fp16 keeps
+  // cos/sin to 2^-12 absolute, adding ~3e-4 relative error to the scores -- far
+  // inside what bf16 latents already carry -- and halves registers and LDS.
+  constexpr bool T16 = BF;
+  constexpr int SPR = T16 ? DH / 8 : DH / 4;  // 16-byte LDS slots per position row
+  constexpr int SWZ = SPR < 16 ? SPR - 1 : 15; // XOR swizzle mask (row index low bits)
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const int CH = a.chunk_pages;         // pages per trig chunk
-  const int TS = CH * kPage * SPR;      // 16-byte slots per chunk buffer
+  constexpr int LOOK = LLA_DECODE_LOOK;  // pages in flight beyond the one computed
+  constexpr int NBUF = LOOK + 2;        // page ring slots (see the main loop)
+  constexpr int CH = NBUF;              // pages per trig chunk: one trip round the ring
+  constexpr int TS = CH * kPage * SPR;  // 16-byte slots of one chunk
+  constexpr int GL = T16 ? 2 : 1;       // global 16-byte loads per LDS slot
+  constexpr int SLOTS = (TS + NTH - 1) / NTH;  // slots staged per thread
+  constexpr int TSB = SLOTS * NTH;      // slots per chunk buffer (surplus = padding)
   char *s_trig = smem;
-  int *s_pt = (int *)(smem + 2 * TS * 16);
+  int *s_pt = (int *)(smem + 2 * TSB * 16);
   {
     const int *pt_row = a.page_table + (long long)b * a.max_pages;
     for (int i = threadIdx.x; i < lp1 - lp0; i += blockDim.x) s_pt[i] = pt_row[lp0 + i];
@@ -201,33 +218,46 @@ __global__ __launch_bounds__(512) void decode_ph_kernel(AttnArgs a) {
   }
   auto page_at = [&](int lp) -> int { return __builtin_amdgcn_readfirstlane(s_pt[lp - lp0]); };
 
-  // Trig staging.  Chunk c covers pages [lp0 + c*CH, lp0 + (c+1)*CH).  Its rows
-  // (one per token position) hold the table row of that position; within a row
-  // the 16-byte slot `ls` is stored at ls ^ (position % 16), so the 16 lanes of a
-  // row-group, which read the same logical slot of 16 consecutive positions, hit
-  // 16 different bank groups.  Each thread moves at most 4 slots per chunk.
-  const int nthreads = blockDim.x;
+  // Trig staging.  Chunk c covers pages [lp0 + c*CH, lp0 + (c+1)*CH); row R of a
+  // chunk buffer holds the table row of token position 16*(lp0 + c*CH) + R.
+  // Within a row, logical 16-byte slot `ls` is stored at ls ^ (R % 16 & SWZ), so
+  // the 16 lanes of a row-group -- which read the same logical slot of 16
+  // consecutive positions -- hit different bank groups.  A logical slot holds 4
+  // pairs; in fp32 that is 2 slots of the global table, so each staged slot
+  // takes two 16-byte global loads.  Loads are unconditional (clamped slot) so
+  // the number in flight is the same on every path.
   const char *rope_b = (const char *)a.rope;
-  const int npass = (TS + 4 * nthreads - 1) / (4 * nthreads);
-  f32x4 stg[4];
-  auto stage_load = [&](int c, int pass) {
+  f32x4 stg[SLOTS][GL];
+  auto stage_load = [&](int c) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int q = threadIdx.x + (4 * pass + j) * nthreads;
-      if (q < TS) {
-        const int R = q / SPR, ps = q % SPR, rn = R % kPage;
-        int pos = (lp0 + c * CH + R / kPage) * kPage + rn;
-        pos = min(pos, ctx - 1);
-        stg[j] = *(const f32x4 *)(rope_b + ((long long)pos * SPR + (ps ^ rn)) * 16);
-      }
+    for (int j = 0; j < SLOTS; ++j) {
+      const int q = min((int)threadIdx.x + j * NTH, TS - 1);
+      const int R = q / SPR, ps = q % SPR, rn = R % kPage;
+      const int pos = min((lp0 + c * CH + R / kPage) * kPage + rn, ctx - 1);
+      const char *src = rope_b + (long long)pos * (DH * 4) + (ps ^ (rn & SWZ)) * 16 * GL;
+#pragma unroll
+      for (int u = 0; u < GL; ++u) stg[j][u] = *(const f32x4 *)(src + 16 * u);
     }
   };
-  auto stage_store = [&](int c, int pass) {
-    char *dst = s_trig + (c & 1) * TS * 16;
+  auto stage_store = [&](int c) {
+    char *dst = s_trig + (c & 1) * TSB * 16;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int q = threadIdx.x + (4 * pass + j) * nthreads;
-      if (q < TS) *(f32x4 *)(dst + q * 16) = stg[j];
+    for (int j = 0; j < SLOTS; ++j) {
+      const int q = threadIdx.x + j * NTH;  // q >= TS lands in the buffer's padding
+      {
+        if constexpr (T16) {
+          u32x4 h;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float cval = stg[j][e >> 1][(e & 1) * 2], sval = stg[j][e >> 1][(e & 1) * 2 + 1];
+            const _Float16 ch = (_Float16)cval, sh = (_Float16)sval;  // round to nearest even
+            h[e] = (uint32_t)__builtin_bit_cast(uint16_t, ch) | ((uint32_t)__builtin_bit_cast(uint16_t, sh) << 16);
+          }
+          *(u32x4 *)(dst + q * 16) = h;
+        } else {
+          *(f32x4 *)(dst + q * 16) = stg[j][0];
+        }
+      }
     }
   };
 
@@ -236,20 +266,27 @@ __global__ __launch_bounds__(512) void decode_ph_kernel(AttnArgs a) {
     const long long pp = pg.ok ? pp_raw : 0;
     pg.last = min(kPage - 1, ctx - 1 - lp * kPage);
     const int row_n = min(n, pg.last);
-    // uniform page bases (scalar registers) + 32-bit per-lane offsets
+    // uniform page bases (scalar registers) + 32-bit per-lane offsets; latents
+    // are read exactly once per call, so they are loaded non-temporally
     const char *kpage = a.k_pool + pp * a.pool_page_stride_k * S::esz;
     const char *vpage = a.v_pool + pp * a.pool_page_stride_v * S::esz;
+    if constexpr (KPAIR) {
+      const uint32_t koff =
+          (uint32_t)(((h0 + (g >> 1)) * a.pool_head_stride_k + row_n * RK + 8 * (g & 1)) * 2);
+      pg.k[0][0] = *(const u32x4 *)(kpage + koff);
+    }
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
       const int h = h0 + hh;
       const uint32_t koff = (uint32_t)((h * a.pool_head_stride_k + row_n * RK) * S::esz);
       const uint32_t voff = (uint32_t)((h * a.pool_head_stride_v + row_n * RV + CV * g) * S::esz);
-      if constexpr (BF) {
+      if constexpr (KPAIR) {
+      } else if constexpr (BF) {
 #pragma unroll
         for (int ks = 0; ks < KK; ++ks) {
           const int r0 = 32 * ks + 8 * g;
           if (r0 + 8 <= RK) {
-            pg.k[hh][ks] = *(const u32x4 *)(kpage + koff + r0 * 2);
+            pg.k[hh][ks] = __builtin_nontemporal_load((const u32x4 *)(kpage + koff + r0 * 2));
           } else {  // constant column: bf16 (1, 1) picks up alpha hi + lo
             const u32x4 c = {r0 == RK ? 0x3F803F80u : 0u, 0u, 0u, 0u};
             pg.k[hh][ks] = c;
@@ -258,10 +295,11 @@ __global__ __launch_bounds__(512) void decode_ph_kernel(AttnArgs a) {
       } else {
 #pragma unroll
         for (int k4 = 0; k4 < KK; ++k4)
-          pg.k[hh][k4] = *(const u32x4 *)(kpage + koff + ((RK / 4) * g + 4 * k4) * 4);
+          pg.k[hh][k4] = __builtin_nontemporal_load((const u32x4 *)(kpage + koff + ((RK / 4) * g + 4 * k4) * 4));
       }
 #pragma unroll
-      for (int kv = 0; kv < KV; ++kv) pg.v[hh][kv] = *(const u32x4 *)(vpage + voff + kv * 16);
+      for (int kv = 0; kv < KV; ++kv)
+        pg.v[hh][kv] = __builtin_nontemporal_load((const u32x4 *)(vpage + voff + kv * 16));
     }
   };
 
@@ -270,41 +308,51 @@ __global__ __launch_bounds__(512) void decode_ph_kernel(AttnArgs a) {
   // and the row is poisoned through the error bits.
   auto compute_page = [&](const Page &cur, int lp) {
     errbits |= cur.ok ? 0 : LLA_DEVERR_PAGE;
-    const bool valid = cur.ok && n <= cur.last;
+    const bool valid = cur.ok && n <= cur.last && lp < lp1;  // lp >= lp1: ring padding
     const int row_n = min(n, cur.last);
-    const char *tb = s_trig + (((lp - lp0) / CH) & 1) * TS * 16 +
+    const char *tb = s_trig + (((lp - lp0) / CH) & 1) * TSB * 16 +
                      (((lp - lp0) % CH) * kPage + row_n) * SPR * 16;
-    f32x4 trig[2 * NT];
+    Op bpair[2][KS];
+    if constexpr (KPAIR) {
+      // lanes 0-15 / 32-47 of the constant hold bf16 (1, 1): after the swap they
+      // sit in the g = 2 lanes of both operands; g = 3 lanes get zeros.
+      const uint32_t one = ((lane >> 4) & 1) ? 0u : 0x3F803F80u;
+      u32x4 b0, b1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(cur.k[0][0][e], e == 0 ? one : 0u, false, false);
+        b0[e] = sw[0];
+        b1[e] = sw[1];
+      }
+      bpair[0][0] = as_bf16x8(b0);
+      bpair[1][0] = as_bf16x8(b1);
+    }
+    // cos/sin of this lane's 16 pair indices at its token's position: fp16
+    // pairs (bf16 storage) feed mixed-precision FMAs directly; fp32 otherwise.
+    u32x4 th[NT];
+    float tc[NT][4], ts[NT][4];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const int ls = 8 * t + 2 * g;
-      trig[2 * t] = *(const f32x4 *)(tb + ((ls ^ row_n) * 16));
-      trig[2 * t + 1] = *(const f32x4 *)(tb + (((ls + 1) ^ row_n) * 16));
+      if constexpr (T16) {
+        th[t] = *(const u32x4 *)(tb + (((4 * t + g) ^ (row_n & SWZ)) * 16));
+      } else {
+        const int ls = 8 * t + 2 * g;
+        const f32x4 c0 = *(const f32x4 *)(tb + ((ls ^ (row_n & SWZ)) * 16));
+        const f32x4 c1 = *(const f32x4 *)(tb + (((ls + 1) ^ (row_n & SWZ)) * 16));
+        tc[t][0] = c0[0]; ts[t][0] = c0[1]; tc[t][1] = c0[2]; ts[t][1] = c0[3];
+        tc[t][2] = c1[0]; ts[t][2] = c1[1]; tc[t][3] = c1[2]; ts[t][3] = c1[3];
+      }
     }
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
       Op bk[KS];
-      float cv[CV];
       if constexpr (BF) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) bk[ks] = as_bf16x8(cur.k[hh][ks]);
-#pragma unroll
-        for (int kv = 0; kv < KV; ++kv) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            cv[8 * kv + 2 * e] = bf16_lo(cur.v[hh][kv][e]);
-            cv[8 * kv + 2 * e + 1] = bf16_hi(cur.v[hh][kv][e]);
-          }
-        }
+        for (int ks = 0; ks < KS; ++ks) bk[ks] = KPAIR ? bpair[hh][ks] : as_bf16x8(cur.k[hh][ks]);
       } else {
 #pragma unroll
         for (int ks = 0; ks < RK / 4; ++ks) bk[ks] = __uint_as_float(cur.k[hh][ks / 4][ks % 4]);
         bk[RK / 4] = (g == 0) ? 1.f : 0.f;
-#pragma unroll
-        for (int kv = 0; kv < KV; ++kv) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) cv[4 * kv + e] = __uint_as_float(cur.v[hh][kv][e]);
-        }
       }
       // X / Y tiles: rows = pair indices 16t + 4g + e, column = token n
       float sc0 = 0.f, sc1 = 0.f;
@@ -316,15 +364,16 @@ __global__ __launch_bounds__(512) void decode_ph_kernel(AttnArgs a) {
           X = S::mma(A[hh][t][0][ks], bk[ks], X);
           Y = S::mma(A[hh][t][1][ks], bk[ks], Y);
         }
-        const f32x4 c0 = trig[2 * t], c1 = trig[2 * t + 1];  // (cos, sin) x 4
-        sc0 = fmaf(c0[0], X[0], sc0);
-        sc1 = fmaf(c0[1], Y[0], sc1);
-        sc0 = fmaf(c0[2], X[1], sc0);
-        sc1 = fmaf(c0[3], Y[1], sc1);
-        sc0 = fmaf(c1[0], X[2], sc0);
-        sc1 = fmaf(c1[1], Y[2], sc1);
-        sc0 = fmaf(c1[2], X[3], sc0);
-        sc1 = fmaf(c1[3], Y[3], sc1);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if constexpr (T16) {  // the compiler emits v_fma_mix_f32 (no conversion)
+            sc0 = fmaf((float)__builtin_bit_cast(_Float16, (uint16_t)(th[t][e] & 0xFFFFu)), X[e], sc0);
+            sc1 = fmaf((float)__builtin_bit_cast(_Float16, (uint16_t)(th[t][e] >> 16)), Y[e], sc1);
+          } else {
+            sc0 = fmaf(tc[t][e], X[e], sc0);
+            sc1 = fmaf(ts[t][e], Y[e], sc1);
+          }
+        }
       }
       float sc = sum_across_rows(sc0 + sc1);
       sc = valid ? sc : -INFINITY;
@@ -338,8 +387,23 @@ __global__ __launch_bounds__(512) void decode_ph_kernel(AttnArgs a) {
       }
       const float p = fast_exp2(sc - m_run[hh]);
       z[hh] += p;
+      if constexpr (BF) {
 #pragma unroll
-      for (int k = 0; k < CV; ++k) acc[hh][k] = fmaf(p, cv[k], acc[hh][k]);
+        for (int kv = 0; kv < KV; ++kv) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[hh][8 * kv + 2 * e] = fmaf(p, bf16_lo(cur.v[hh][kv][e]), acc[hh][8 * kv + 2 * e]);
+            acc[hh][8 * kv + 2 * e + 1] = fmaf(p, bf16_hi(cur.v[hh][kv][e]), acc[hh][8 * kv + 2 * e + 1]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int kv = 0; kv < KV; ++kv) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[hh][4 * kv + e] = fmaf(p, __uint_as_float(cur.v[hh][kv][e]), acc[hh][4 * kv + e]);
+        }
+      }
     }
   };
 
@@ -348,32 +412,38 @@ __global__ __launch_bounds__(512) void decode_ph_kernel(AttnArgs a) {
   // is never computed), so each compute has the next page's loads in flight.
   // At a chunk boundary all waves drain, store the staged trig chunk to LDS,
   // synchronise, and start staging the chunk after it.
-  auto chunk_boundary = [&](int lp) {
-    const int c = (lp - lp0) / CH;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    stage_store(c, 0);
-    for (int pass = 1; pass < npass; ++pass) {  // small workgroups only: synchronous
-      stage_load(c, pass);
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-      stage_store(c, pass);
-    }
-    __syncthreads();
-    if (lp0 + (c + 1) * CH < lp1) stage_load(c + 1, 0);
-  };
+  // Ring of NBUF page slots: while page p is computed, pages p+1 .. p+LOOK are
+  // in flight.  A slot is refilled LOOK steps after it was computed (NBUF =
+  // LOOK + 2), so the old and new contents of a slot never overlap and no
+  // register copies (which would wait for the loads in flight) are needed.
+  // Every trip computes exactly NBUF pages (pages past the split's end are
+  // masked) and every load is issued unconditionally (clamped to the split's
+  // last page); the next RoPE chunk is published at the end of the trip.  Both
+  // ways into the loop head thus leave the same loads outstanding, so the
+  // compiler's waits keep the ring's loads in flight.
   if (lp0 < lp1) {
-    Page pa, pb;
-    stage_load(0, 0);
-    load_page(lp0, page_at(lp0), pa);
-    for (int lp = lp0; lp < lp1; lp += 2) {
-      if ((lp - lp0) % CH == 0) chunk_boundary(lp);
-      const int l1 = min(lp + 1, lp1 - 1);
-      load_page(l1, page_at(l1), pb);
-      compute_page(pa, lp);
-      if (lp + 1 >= lp1) break;
-      if ((lp + 1 - lp0) % CH == 0) chunk_boundary(lp + 1);
-      const int l2 = min(lp + 2, lp1 - 1);
-      load_page(l2, page_at(l2), pa);
-      compute_page(pb, lp + 1);
+    const int lp_end = lp0 + (lp1 - lp0 + NBUF - 1) / NBUF * NBUF;
+    Page ring[NBUF];
+    stage_load(0);
+#pragma unroll
+    for (int u = 0; u < LOOK; ++u) {
+      const int l = min(lp0 + u, lp1 - 1);
+      load_page(l, page_at(l), ring[u]);
+    }
+    stage_store(0);
+    __syncthreads();
+    stage_load(1);
+    for (int lp = lp0; lp < lp_end; lp += NBUF) {
+#pragma unroll
+      for (int u = 0; u < NBUF; ++u) {
+        const int l = min(lp + u + LOOK, lp1 - 1);
+        load_page(l, page_at(l), ring[(u + LOOK) % NBUF]);
+        compute_page(ring[u], lp + u);
+      }
+      const int c = (lp - lp0) / CH;  // chunk just computed
+      stage_store(c + 1);             // buffer of chunk c-1: every wave is past it
+      __syncthreads();
+      stage_load(c + 2);              // past the split's end: clamped rows, unused
     }
   }
 
@@ -484,40 +554,47 @@ namespace {
 struct Shape {
   int bf, dh, rk, rv, hpw;
 };
-template <bool BF, int DH, int RK, int RV, int HPW>
+template <bool BF, int DH, int RK, int RV, int HPW, int NW>
 hipError_t go(const AttnArgs &a, hipStream_t stream) {
+  if (a.waves != NW) return hipErrorInvalidConfiguration;
   static bool lds_raised = false;  // allow more than the default 64 KiB of LDS once per kernel
   if (!lds_raised) {
-    const hipError_t e = hipFuncSetAttribute((const void *)decode_ph_kernel<BF, DH, RK, RV, HPW>,
+    const hipError_t e = hipFuncSetAttribute((const void *)decode_ph_kernel<BF, DH, RK, RV, HPW, NW>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 256);
     if (e != hipSuccess) return e;
     lds_raised = true;
   }
   const dim3 grid((unsigned)(a.rows * a.head_groups * a.splits));
   const dim3 block((unsigned)(64 * a.waves));
-  const size_t shmem = 2 * (size_t)a.chunk_pages * kPage * (DH / 4) * 16 + sizeof(int) * a.pages_per_split +
+  constexpr int TS = (LLA_DECODE_LOOK + 2) * kPage * (BF ? DH / 8 : DH / 4);  // one chunk = ring
+  constexpr int TSB = (TS + 64 * NW - 1) / (64 * NW) * (64 * NW);
+  const size_t shmem = 2 * (size_t)TSB * 16 + sizeof(int) * a.pages_per_split +
                        sizeof(float) * a.waves * HPW * (RV + 2);
-  hipLaunchKernelGGL((decode_ph_kernel<BF, DH, RK, RV, HPW>), grid, block, shmem, stream, a);
+  hipLaunchKernelGGL((decode_ph_kernel<BF, DH, RK, RV, HPW, NW>), grid, block, shmem, stream, a);
   return hipGetLastError();
 }
 }  // namespace
 
+// (bf16?, d_head, r_k, r_v, heads per wave, waves per workgroup)
 #define LLA_DECODE_SHAPES(X)   \
-  X(false, 64, 16, 32, 1)      \
-  X(false, 64, 16, 32, 2)      \
-  X(false, 128, 16, 32, 1)     \
-  X(true, 64, 16, 32, 1)       \
-  X(true, 64, 16, 32, 2)       \
-  X(true, 128, 16, 32, 1)      \
-  X(true, 128, 16, 32, 2)      \
-  X(true, 128, 32, 64, 1)      \
-  X(true, 128, 96, 160, 1)     \
-  X(false, 128, 96, 160, 1)
+  X(false, 64, 16, 32, 1, 2)   \
+  X(false, 64, 16, 32, 1, 8)   \
+  X(false, 128, 16, 32, 1, 2)  \
+  X(false, 128, 16, 32, 1, 8)  \
+  X(true, 64, 16, 32, 1, 2)    \
+  X(true, 64, 16, 32, 2, 8)    \
+  X(true, 128, 16, 32, 1, 2)   \
+  X(true, 128, 16, 32, 2, 2)   \
+  X(true, 128, 16, 32, 1, 8)   \
+  X(true, 128, 16, 32, 2, 8)   \
+  X(true, 128, 32, 64, 1, 8)   \
+  X(true, 128, 96, 160, 1, 8)  \
+  X(false, 128, 96, 160, 1, 8)
 
-bool decode_supported(int dtype, int d_head, int r_k, int r_v, int hpw) {
+bool decode_supported(int dtype, int d_head, int r_k, int r_v, int hpw, int waves) {
   const bool bf = dtype == LLA_BF16;
-#define X(BF, DH, RK, RV, HPW) \
-  if (bf == BF && d_head == DH && r_k == RK && r_v == RV && hpw == HPW) return true;
+#define X(BF, DH, RK, RV, HPW, NW) \
+  if (bf == BF && d_head == DH && r_k == RK && r_v == RV && hpw == HPW && waves == NW) return true;
   LLA_DECODE_SHAPES(X)
 #undef X
   return false;
@@ -526,9 +603,10 @@ bool decode_supported(int dtype, int d_head, int r_k, int r_v, int hpw) {
 hipError_t launch_decode(int dtype, int d_head, int r_k, int r_v, const AttnArgs &a,
                          hipStream_t stream) {
   const bool bf = dtype == LLA_BF16;
-#define X(BF, DH, RK, RV, HPW)                                                  \
-  if (bf == BF && d_head == DH && r_k == RK && r_v == RV && a.heads_per_wave == HPW) \
-    return go<BF, DH, RK, RV, HPW>(a, stream);
+#define X(BF, DH, RK, RV, HPW, NW)                                                  \
+  if (bf == BF && d_head == DH && r_k == RK && r_v == RV && a.heads_per_wave == HPW && \
+      a.waves == NW)                                                                   \
+    return go<BF, DH, RK, RV, HPW, NW>(a, stream);
   LLA_DECODE_SHAPES(X)
 #undef X
   return hipErrorInvalidConfiguration;

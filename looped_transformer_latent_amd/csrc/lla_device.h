@@ -40,12 +40,21 @@ __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
-// Max / sum over the 16 lanes of each row; every lane of the row gets the result.
+// Max over the 16 lanes of each row; every lane of the row gets the result.
+// One fused DPP max per step (the compiler's fmaxf would add a move and a NaN
+// canonicalisation per step).  Each step first waits the 2 wait states a DPP
+// read of a just-written VGPR requires.  Inputs are finite or -inf.
 __device__ __forceinline__ float max_in_row(float x) {
-  x = fmaxf(x, dpp<kDppQuadSwap1>(x));
-  x = fmaxf(x, dpp<kDppQuadSwap2>(x));
-  x = fmaxf(x, dpp<kDppHalfMirror>(x));
-  x = fmaxf(x, dpp<kDppMirror>(x));
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %0, %0, %0 row_mirror row_mask:0xf bank_mask:0xf"
+      : "+v"(x));
   return x;
 }
 __device__ __forceinline__ float sum_in_row(float x) {

@@ -9,6 +9,10 @@
 namespace lla {
 
 constexpr int kPage = 16;          // tokens per cache page
+#ifndef LLA_DECODE_LOOK
+#define LLA_DECODE_LOOK 4          // decode: latent pages in flight per wave beyond the one computed
+#endif
+constexpr int kDecodeRing = LLA_DECODE_LOOK + 2;  // decode page-ring slots = pages per trip
 constexpr int kHeaderBytes = 256;  // workspace header: int32 error word at byte 0
 
 // Arguments of one attention launch (decode or prefill).  All pointers are
@@ -55,7 +59,7 @@ struct EncodeArgs {
 
 // Kernel dispatch: return hipSuccess, or hipErrorInvalidConfiguration when the
 // shape has no instantiated kernel.
-bool decode_supported(int dtype, int d_head, int r_k, int r_v, int heads_per_wave);
+bool decode_supported(int dtype, int d_head, int r_k, int r_v, int heads_per_wave, int waves);
 hipError_t launch_decode(int dtype, int d_head, int r_k, int r_v, const AttnArgs &a,
                          hipStream_t stream);
 bool encode_supported(int dtype, int width, int r_k, int r_v);
