@@ -127,15 +127,19 @@ def _stream(stream=None):
 
 
 def make_codec(mu_k, mu_v, w_down_k, w_down_v, w_up_k, w_up_v) -> Codec:
-    return Codec(*[(t.data_ptr() if t is not None else None)
-                   for t in (mu_k, mu_v, w_down_k, w_down_v, w_up_k, w_up_v)])
+    ts = (mu_k, mu_v, w_down_k, w_down_v, w_up_k, w_up_v)
+    c = Codec(*[(t.data_ptr() if t is not None else None) for t in ts])
+    c._tensors = ts  # the struct holds raw pointers: keep the storage alive with it
+    return c
 
 
 def make_cache(k_pool: torch.Tensor, v_pool: torch.Tensor, page_table: torch.Tensor,
                num_pages: int) -> Cache:
     assert page_table.dtype == torch.int32 and page_table.dim() == 2
-    return Cache(k_pool.data_ptr(), v_pool.data_ptr(), page_table.data_ptr(),
-                 page_table.shape[0], page_table.shape[1], num_pages)
+    c = Cache(k_pool.data_ptr(), v_pool.data_ptr(), page_table.data_ptr(),
+              page_table.shape[0], page_table.shape[1], num_pages)
+    c._tensors = (k_pool, v_pool, page_table)  # keep the storage alive with the pointers
+    return c
 
 
 def cache_scalars(dims: Dims) -> tuple[int, int]:

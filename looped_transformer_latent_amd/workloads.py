@@ -40,6 +40,7 @@ class Workload:
     shuffled: bool      # page table: seeded permutation (True) or identity
     n_new: int          # tokens appended per sequence by one encode call
     seed: int
+    ortho_down: bool = False  # W_down orthonormal (QR) and W_up,t its loop-t row slice
 
     @property
     def dims(self) -> dict:
@@ -104,7 +105,7 @@ WORKLOADS = {
                                          PER_HEAD, BF16, 768, 4096, False, 1, 1003),
     # 4x compression plus encode/append of 512 tokens per sequence, 8k context
     "ouro1.4b-4x-b64-encode": Workload("ouro1.4b-4x-b64-encode", 4, 24, 16, 128, 96, 160,
-                                       PER_HEAD, BF16, 64, 8192, False, 512, 1004),
+                                       PER_HEAD, BF16, 64, 8192, False, 512, 1004, True),
     # LLA-2D: heads folded into one latent per token and layer
     "lla2d-t8-h32-b128": Workload("lla2d-t8-h32-b128", 8, 4, 32, 128, 256, 256, TWO_D, BF16,
                                   128, 16384, True, 0, 1005),
@@ -115,8 +116,11 @@ def _gdt(w: Workload) -> str:
     return "bf16" if w.dtype == BF16 else "f32"
 
 
-def codec_host(w: Workload, ortho_down: bool = False) -> dict:
-    """Codec parameters as host storage arrays (uint16 bf16 bits or fp32)."""
+def codec_host(w: Workload, ortho_down: bool | None = None) -> dict:
+    """Codec parameters as host storage arrays (uint16 bf16 bits or fp32).
+    With orthonormal W_down, W_up,t is W_down's loop-t row slice (the SVD-style
+    initialisation the close reading describes, 方法 item 3), not a separate draw."""
+    ortho_down = w.ortho_down if ortho_down is None else ortho_down
     sh = w.param_shapes()
     out = {}
     for name in ("mu_k", "mu_v", "w_up_k", "w_up_v"):
@@ -133,6 +137,9 @@ def codec_host(w: Workload, ortho_down: bool = False) -> dict:
         else:
             out[name] = gen.normal(w.seed, STREAMS[name], shape, scale=1.0 / np.sqrt(shape[-2]),
                                    dtype=_gdt(w))
+    if ortho_down:
+        for kv in ("k", "v"):
+            out["w_up_" + kv] = np.ascontiguousarray(out["w_down_" + kv].reshape(sh["w_up_" + kv]))
     return out
 
 

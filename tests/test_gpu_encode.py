@@ -1,0 +1,157 @@
+"""GPU parity: lla_encode_append (HIP) against the CPU oracle.
+
+Encode is eq. (2) of the LLA pages (c = (x - mu) W_down over the loop-concatenated
+pre-RoPE vector), appended at slot(b, pos0[b] + n) of the paged pool.  Checks:
+  * placement is bit-exact: every slot the oracle writes is written, every
+    other slot keeps its sentinel bits;
+  * values: bf16 storage within 2e-2 per latent row (||.||_inf relative) and at
+    most one bf16 ulp apart elementwise for nearly all elements (the GPU sums
+    x W_down - mu W_down in fp32; the oracle sums (x - mu) W_down in fp64, and
+    both round once to bf16); fp32 storage within 1e-4 per row.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fixtures import BF16, F32, PER_HEAD, TWO_D, dims, pool_shape, random_codec, store
+from gpu_util import device_codec, row_rel_err, to_device, to_host
+from looped_transformer_latent_amd import gen, lla
+
+pytestmark = pytest.mark.gpu
+SENT = {BF16: np.uint16(0x7FC1), F32: np.float32(np.nan)}
+
+
+def x_shape(m, n_layers, B, n_new):
+    if m["variant"] == PER_HEAD:
+        return (n_layers, B, n_new, m["H"], m["T"], m["d_head"])
+    return (n_layers, B, n_new, m["T"], m["H"], m["d_head"])
+
+
+def run_both(m, codec, pt, num_pages, pos0, n_new, layer0, n_layers, seed):
+    B = pt.shape[0]
+    dt = "bf16" if m["dtype"] == BF16 else "f32"
+    xk = gen.normal(seed, 401, x_shape(m, n_layers, B, n_new), dtype=dt)
+    xv = gen.normal(seed, 402, x_shape(m, n_layers, B, n_new), dtype=dt)
+    sent = SENT[m["dtype"]]
+    kp = np.full(pool_shape(m, num_pages, "k"), sent)
+    vp = np.full(pool_shape(m, num_pages, "v"), sent)
+    kp_ref, vp_ref = kp.copy(), vp.copy()
+    assert oracle.encode(m, codec, kp_ref, vp_ref, pt, xk, xv, pos0, n_new, layer0, n_layers) == 0
+
+    D = lla.dims_from_dict(m)
+    c, keep = device_codec(codec)
+    kp_d, vp_d = to_device(kp), to_device(vp)
+    cache = lla.make_cache(kp_d, vp_d, to_device(np.ascontiguousarray(pt, np.int32)), num_pages)
+    ws = lla.workspace(D, lla.OP_ENCODE, B, 0, n_layers)
+    lla.encode_append(D, c, cache, to_device(xk), to_device(xv), to_device(np.int32(pos0)),
+                      n_new, layer0, n_layers, ws)
+    torch.cuda.synchronize()
+    assert lla.device_error_word(ws) == 0
+    return (to_host(kp_d), to_host(vp_d)), (kp_ref, vp_ref), (kp, vp)
+
+
+def placement_report(g_written, r_written):
+    """Readable summary of where the written-slot masks differ."""
+    diff = np.argwhere(g_written != r_written)
+    return (f"written: gpu {int(g_written.sum())}, oracle {int(r_written.sum())}; "
+            f"{len(diff)} elements differ, first (layer, page, [head,] row, r): "
+            f"{[tuple(int(v) for v in x) for x in diff[:6]]}")
+
+
+def compare(m, got, ref, init, label):
+    for g, r, i in zip(got, ref, init):
+        if m["dtype"] == BF16:
+            written = r != i
+            # placement: bit-exact (a written latent is never the sentinel NaN pattern)
+            assert np.array_equal(g != i, written), f"{label}: " + placement_report(g != i, written)
+            assert np.array_equal(g[~written], i[~written])
+            gv = gen.storage_to_f64(g[written]).reshape(-1, g.shape[-1])
+            rv = gen.storage_to_f64(r[written]).reshape(-1, r.shape[-1])
+            err = row_rel_err(gv, rv)
+            # ulp distance on the bf16 lattice (same-sign values)
+            ud = np.abs(g[written].astype(np.int64) - r[written].astype(np.int64))
+            same_sign = (g[written] >> 15) == (r[written] >> 15)
+            frac_1ulp = np.mean((ud <= 1) & same_sign | (np.abs(gv.reshape(-1) - rv.reshape(-1)) == 0))
+            print(f"{label}: rows {gv.shape[0]}, max row rel err {err.max():.3e}, "
+                  f"elements within 1 ulp {frac_1ulp:.5f}", flush=True)
+            assert err.max() <= 2e-2
+            assert frac_1ulp >= 0.995
+        else:
+            written = ~np.isnan(r)
+            assert np.array_equal(~np.isnan(g), written), f"{label}: " + placement_report(~np.isnan(g), written)
+            gv = g[written].astype(np.float64).reshape(-1, g.shape[-1])
+            rv = r[written].astype(np.float64).reshape(-1, r.shape[-1])
+            err = row_rel_err(gv, rv)
+            print(f"{label}: rows {gv.shape[0]}, max row rel err {err.max():.3e}", flush=True)
+            assert err.max() <= 1e-4
+
+
+@pytest.mark.parametrize("dtype", [BF16, F32])
+def test_encode_per_head_ragged_positions(dtype):
+    """4x-compression shapes (r_k=96, r_v=160), 3 sequences appending 37 tokens each
+    at positions that start mid-page, cross page boundaries and end mid-page; a
+    shuffled page table with pages that no sequence owns; two of three layers."""
+    m = dims(4, 3, 16, 128, 96, 160, PER_HEAD, dtype)
+    B, pps = 3, 6
+    num_pages = B * pps + 5
+    pt = gen.shuffled_page_table(3001, B, pps, num_pages)
+    codec = random_codec(m, seed=3002, ortho_down=True)
+    pos0 = np.array([0, 13, 55])
+    got, ref, init = run_both(m, codec, pt, num_pages, pos0, 37, 1, 2, seed=3003)
+    compare(m, got, ref, init, f"encode per-head dt={dtype}")
+
+
+def test_encode_21x_single_token_all_layers():
+    """The decode-step append: one token per sequence into every layer (r_k=16, r_v=32)."""
+    m = dims(4, 24, 16, 128, 16, 32, PER_HEAD, BF16)
+    B, pps = 5, 2
+    pt = gen.shuffled_page_table(3101, B, pps)
+    codec = random_codec(m, seed=3102, ortho_down=True)
+    pos0 = np.array([0, 15, 16, 31, 7])
+    got, ref, init = run_both(m, codec, pt, B * pps, pos0, 1, 0, 24, seed=3103)
+    compare(m, got, ref, init, "encode 21x n_new=1")
+
+
+@pytest.mark.parametrize("dtype", [BF16, F32])
+def test_encode_lla2d(dtype):
+    """LLA-2D: one latent per token and layer from the [t][h][d] concatenation."""
+    m = dims(2, 2, 4, 64, 32, 48, TWO_D, dtype)
+    B, pps = 2, 3
+    pt = gen.shuffled_page_table(3201, B, pps)
+    codec = random_codec(m, seed=3202, ortho_down=True)
+    pos0 = np.array([3, 20])
+    got, ref, init = run_both(m, codec, pt, B * pps, pos0, 21, 0, 2, seed=3203)
+    compare(m, got, ref, init, f"encode 2D dt={dtype}")
+
+
+def test_encode_device_errors():
+    """A position past the page-table row, or a page entry out of range, is
+    flagged in the workspace error word and the slot is not written."""
+    m = dims(2, 1, 2, 64, 16, 16, PER_HEAD, BF16)
+    B, pps = 2, 2
+    pt = gen.identity_page_table(B, pps)
+    pt[1, 1] = 999
+    codec = random_codec(m, seed=3302, ortho_down=True)
+    D = lla.dims_from_dict(m)
+    c, keep = device_codec(codec)
+    kp = np.full(pool_shape(m, B * pps, "k"), SENT[BF16])
+    vp = np.full(pool_shape(m, B * pps, "v"), SENT[BF16])
+    kp_d, vp_d = to_device(kp), to_device(vp)
+    cache = lla.make_cache(kp_d, vp_d, to_device(pt), B * pps)
+    xk = to_device(gen.normal(3303, 401, x_shape(m, 1, B, 4)))
+    xv = to_device(gen.normal(3303, 402, x_shape(m, 1, B, 4)))
+    ws = lla.workspace(D, lla.OP_ENCODE, B, 0, 1)
+    lla.encode_append(D, c, cache, xk, xv, to_device(np.int32([30, 14])), 4, 0, 1, ws)
+    torch.cuda.synchronize()
+    word = lla.device_error_word(ws)
+    assert word & lla.DEVERR_APPEND and word & lla.DEVERR_PAGE
+    k_after = to_host(kp_d)
+    # sequence 0: positions 30, 31 land in its page 1; 32, 33 are past its row
+    assert (k_after[0, 1, :, 14:16] != SENT[BF16]).all()
+    # sequence 1: positions 14, 15 in page 2; 16, 17 hit the bad entry and are dropped
+    assert (k_after[0, 2, :, 14:16] != SENT[BF16]).all()
+    assert (k_after[0, 3] == SENT[BF16]).all()
+    assert (k_after[0, 0] == SENT[BF16]).all()
