@@ -27,6 +27,35 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+DECODE_SOURCES = ("lla_decode.hip", "lla_device.h", "lla_internal.h")
+
+
+def kernel_source_digest(names=DECODE_SOURCES) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "looped_transformer_latent_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def profiled_traffic(workload: str):
+    """HBM bytes per decode launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary of this workload, or None when the kernel sources have
+    changed since those counters were taken (or no summary exists)."""
+    path = os.path.join(ROOT, "profiles", f"decode_ph_kernel_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and line.split(":", 1)[0] in ("kernel_source_sha256", "traffic_bytes_per_launch"):
+                k, v = line.split(":", 1)
+                fields[k] = v.strip()
+    if fields.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    v = fields.get("traffic_bytes_per_launch")
+    return int(v) if v else None
 
 
 def parse():
@@ -192,7 +221,8 @@ def main():
                    "step": f"encode_append(1 token x {w.D} layers) + {len(calls)} lla_decode_attn calls"},
         "roofline": {"kernel": "decode_ph_kernel", "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None, "algorithmic_bytes_per_launch": bytes_per_launch,
+                     "traffic": profiled_traffic(w.name), "traffic_unit": "HBM bytes per launch (rocprofv3)",
+                     "algorithmic_bytes_per_launch": bytes_per_launch,
                      "avg_launch_ms": kern_avg_ms},
     }
     if not args.no_cpu_baseline:
