@@ -27,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 DECODE_SOURCES = ("lla_decode.hip", "lla_device.h", "lla_internal.h")
 
 
@@ -63,7 +64,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=5)
     p.add_argument("--warmup", type=int, default=2)
-    p.add_argument("--workload", default="ouro1.4b-21x-b768-paged")
+    p.add_argument("--workload", default="ouro1.4b-21x-b768-paged",
+                   help="decode workload: ouro1.4b-21x-b768-paged (default), ouro1.4b-21x-b32, "
+                        "ouro1.4b-21x-b768-contig, lla2d-t8-h32-b128")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle sample time")
     p.add_argument("--calibrate-copy", type=float, default=0.0, metavar="GIB",
@@ -201,7 +204,22 @@ def main():
     value = reads_per_step / (ms_step / 1e3)
     kern_avg_ms = float(np.mean(kern_ms))
     bytes_per_launch = w.batch * w.ctx * w.read_bytes()
-    achieved = bytes_per_launch / (kern_avg_ms / 1e3) / 1e9
+    if w.variant == wl.PER_HEAD:
+        achieved = bytes_per_launch / (kern_avg_ms / 1e3) / 1e9
+        roof = {"kernel": "decode_ph_kernel", "bound": "hbm", "achieved": achieved,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                "traffic": profiled_traffic(w.name), "traffic_unit": "HBM bytes per launch (rocprofv3)",
+                "algorithmic_bytes_per_launch": bytes_per_launch, "avg_launch_ms": kern_avg_ms}
+    else:
+        # LLA-2D is bound by the matrix cores: per token and head, rebuilding K is
+        # 2 d r_k FLOP and the latent-space value sum 2 r_v FLOP
+        flops = w.batch * w.ctx * w.H * (2 * w.d_head * w.r_k + 2 * w.r_v)
+        achieved = flops / (kern_avg_ms / 1e3) / 1e12
+        roof = {"kernel": "decode_2d_kernel", "bound": "mfma", "achieved": achieved,
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                "traffic": None, "algorithmic_flops_per_launch": flops,
+                "algorithmic_bytes_per_launch": bytes_per_launch,
+                "hbm_gbs": bytes_per_launch / (kern_avg_ms / 1e3) / 1e9, "avg_launch_ms": kern_avg_ms}
     result = {
         "metric": "latent-cache decode attention: cached-token reads/s and achieved HBM GB/s",
         "value": value,
@@ -219,11 +237,7 @@ def main():
                    "H": w.H, "d_head": w.d_head, "r_k": w.r_k, "r_v": w.r_v, "page_size": 16,
                    "page_table": "shuffled" if w.shuffled else "identity",
                    "step": f"encode_append(1 token x {w.D} layers) + {len(calls)} lla_decode_attn calls"},
-        "roofline": {"kernel": "decode_ph_kernel", "bound": "hbm", "achieved": achieved,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": profiled_traffic(w.name), "traffic_unit": "HBM bytes per launch (rocprofv3)",
-                     "algorithmic_bytes_per_launch": bytes_per_launch,
-                     "avg_launch_ms": kern_avg_ms},
+        "roofline": roof,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, codec_h, pt_h, layer=w.D - 1, loop=w.T - 1,

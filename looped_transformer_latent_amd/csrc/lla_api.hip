@@ -32,11 +32,50 @@ size_t esize(const lla_dims *d) { return d->dtype == LLA_BF16 ? 2 : 4; }
 
 // How an attention call is cut into workgroups.
 struct AttnPlan {
+  bool two_d;  // LLA-2D kernel (shared latent, 4 heads x 2 waves per workgroup)
   int hpw, waves, head_groups, splits, pages_per_split, chunk_pages;
   size_t counters_off, partials_off, bytes;
 };
 
+void plan_workspace(const lla_dims *d, long long rows, AttnPlan *p) {
+  p->counters_off = kHeaderBytes;
+  p->partials_off = align256(p->counters_off + sizeof(int) * (size_t)rows * p->head_groups);
+  p->bytes = p->splits > 1
+                 ? align256(p->partials_off + sizeof(float) * (size_t)rows * d->H * p->splits * (d->r_v + 2))
+                 : kHeaderBytes;
+}
+
+// LLA-2D: one workgroup per (row, 4 heads, split), 32-token blocks.  The
+// kernel is bound by the matrix cores, so splits only need to fill the chip:
+// about 4 workgroups per CU in total, none shorter than 8 pages.
+bool plan_attn_2d(const lla_dims *d, long long rows, int max_ctx, AttnPlan *p) {
+  if (d->variant != LLA_2D || d->H % 4 || !decode2d_supported(d->dtype, d->d_head, d->r_k, d->r_v))
+    return false;
+  p->two_d = true;
+  p->hpw = 1;
+  p->waves = 8;
+  p->head_groups = d->H / 4;
+  p->chunk_pages = 2;
+  const int pages = (max_ctx + kPage - 1) / kPage;
+  const long long base = rows * p->head_groups;
+  long long s = (1024 + base - 1) / base;
+  const long long smax = (pages + 7) / 8;
+  if (s > smax) s = smax;
+  const long long smin = (pages + kMaxPagesPerSplit - 1) / kMaxPagesPerSplit;
+  if (s < smin) s = smin;
+  if (s < 1) s = 1;
+  int pps = (int)((pages + s - 1) / s);
+  pps += pps & 1;  // whole 32-token blocks
+  p->pages_per_split = pps;
+  p->splits = (pages + pps - 1) / pps;
+  if (p->splits < 1) p->splits = 1;
+  plan_workspace(d, rows, p);
+  return true;
+}
+
 bool plan_attn(const lla_dims *d, long long rows, int max_ctx, AttnPlan *p) {
+  if (plan_attn_2d(d, rows, max_ctx, p)) return true;
+  p->two_d = false;
   // Workgroup shape: 8 waves of 2 heads (16 heads) where possible; otherwise
   // 8 waves of 1 head, or 2 waves for small head counts.
   const int H = d->H;
@@ -68,11 +107,7 @@ bool plan_attn(const lla_dims *d, long long rows, int max_ctx, AttnPlan *p) {
   p->pages_per_split = pps;
   p->splits = (pages + pps - 1) / pps;
   if (p->splits < 1) p->splits = 1;
-  p->counters_off = kHeaderBytes;
-  p->partials_off = align256(p->counters_off + sizeof(int) * (size_t)rows * p->head_groups);
-  p->bytes = p->splits > 1
-                 ? align256(p->partials_off + sizeof(float) * (size_t)rows * H * p->splits * (d->r_v + 2))
-                 : kHeaderBytes;
+  plan_workspace(d, rows, p);
   return true;
 }
 
@@ -181,6 +216,7 @@ int32_t attn_call(const lla_dims *d, const lla_codec *c, const lla_cache *k, con
   a.err = (int *)ws;
   a.counters = (int *)((char *)ws + p.counters_off);
   a.partials = (float *)((char *)ws + p.partials_off);
+  if (p.two_d) return check_launch(launch_decode2d(d->d_head, d->r_k, d->r_v, a, stream));
   return check_launch(launch_decode(d->dtype, d->d_head, d->r_k, d->r_v, a, stream));
 }
 

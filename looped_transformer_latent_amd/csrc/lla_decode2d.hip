@@ -1,0 +1,424 @@
+// LLA-2D decode attention (gfx950, wave64): heads folded into one latent.
+//
+// What it computes (cc.laoqi.cc close reading, 方法 item 6; gist.science
+// "LLA-2D-Variante"): every cached token keeps ONE K latent c_k (r_k wide) and
+// ONE V latent c_v (r_v wide) per layer, shared by all H heads; loop t and head
+// h decode it with their own mu_t,h and W_up,t,h (d x r):
+//   k_hat_j,h = mu_k,t,h + c_k,j W_up,k,t,h^T, RoPE at position j,
+//   s_j,h     = scale <R(q_pos) q_h, R(j) k_hat_j,h>,
+//   out_h     = mu_v,t,h + (sum_j e^{s_j,h - m} c_v,j) W_up,v,t,h^T / sum_j e^{s_j,h - m}.
+//
+// Per token this is d*r_k multiply-adds per head for the K side (2 MFLOP per
+// token at H=32, d=128, r_k=256), so unlike per-head LLA the path is bound by
+// the matrix cores, not by HBM.  Layout of the work:
+//  * A workgroup = 4 waves = 4 heads of one query row and one split of the
+//    context.  Wave w folds the rotated query of its head into the K decoder
+//    (the same exact algebra as the per-head kernel: for RoPE pair i,
+//    X_i = alpha_i + A_i . c, Y_i = beta_i + B_i . c and
+//    s * log2(e) = sum_i cos_i(j) X_i + sin_i(j) Y_i) and keeps the d x (r_k+1)
+//    result in registers as the A-operands of v_mfma_f32_32x32x16_bf16
+//    (alpha / beta as hi + lo bf16 in one extra K-step).
+//  * Tokens go in blocks of 32 (two 16-token pages).  The block's c_k, c_v and
+//    RoPE rows are copied global -> LDS with direct-to-LDS loads (no register
+//    staging), double-buffered: block b+1 is in flight while block b computes.
+//    The tile is shared by the 4 waves, so each latent is fetched from L2 once
+//    per workgroup.  Workgroups of the same (row, split) but different head
+//    groups are dispatched to the same XCD so that they share its L2.
+//  * K side: 4 x 17 MFMAs per wave per block give X / Y for the 64 pairs x 32
+//    tokens; each lane weights its 32 values by cos / sin (fp32) and one
+//    permlane32 swap completes the score.  Online softmax in base 2.
+//  * V side, exact by linearity: sum_j p_j,h c_v,j for the 4 heads is one more
+//    MFMA product, P[tokens x 4 heads] (bf16 weights via LDS) times the c_v
+//    tile; wave w owns r_v/4 of the columns for all 4 heads.
+//  * Splits write (m, Z, acc) partials; the last workgroup of (row, head group)
+//    merges them in fixed order and up-projects once per head.
+#include "lla_device.h"
+#include "lla_internal.h"
+
+namespace lla {
+
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+typedef uint32_t u32x2 __attribute__((__vector_size__(2 * sizeof(uint32_t))));
+
+#define LLA_LDS(p) ((__attribute__((address_space(3))) void *)(p))
+
+template <int DH, int RK, int RV>
+struct Tile2d {
+  u32x4 ck[RK / 8 * 32];    // [r chunk of 8][token 32]: 16-byte MFMA B-operand pieces
+  u32x4 cv[32 * RV / 8];    // [token 32][r_v]: row-major latent rows
+  f32x4 trig[DH / 4 * 32];  // [pair chunk of 2][token 32]: (cos, sin) x 2, fp32
+};
+
+template <int DH, int RK, int RV>
+__global__ __launch_bounds__(512) void decode_2d_kernel(AttnArgs a) {
+  constexpr int NW = 8;          // waves per workgroup: 4 heads x 2 halves of the RoPE pairs
+  constexpr int NH = 4;          // heads per workgroup
+  constexpr int HALF = DH / 2;   // RoPE pairs of a head
+  constexpr int PW = HALF / 2;   // pairs per wave
+  constexpr int RTW = PW / 16;   // 32-row tiles per wave (X and Y rows of 16 pairs each)
+  constexpr int KS = RK / 16;    // K-steps of 16 (8 per lane half)
+  constexpr int CKQ = RK / 16;   // 1 KiB direct loads per tile: c_k
+  constexpr int CVQ = RV / 16;   //                               c_v
+  constexpr int TRQ = DH / 8;    //                               RoPE rows
+  constexpr int VR = RV / NW;    // V columns per wave (all 4 heads)
+  constexpr int VT = VR / 16;    // V MFMA tiles per wave (16x16x32)
+  static_assert(PW % 16 == 0 && RK % 128 == 0 && VR == 32 && VT == 2, "shape");
+  static_assert(CKQ % NW == 0 && CVQ % NW == 0 && TRQ % NW == 0, "tile split");
+
+  __shared__ Tile2d<DH, RK, RV> tile0, tile1;
+  __shared__ __attribute__((aligned(16))) uint16_t s_p[16][32];  // bf16 weights; rows >= 4 stay 0
+  __shared__ float s_alpha[16];                                   // rescale per head; >= 4 stay 1
+  __shared__ float s_part[NH][2][32];                             // half-scores per head
+  __shared__ int s_pt[2048 + 2];
+  __shared__ float s_red[NH][RV + 2];  // epilogue: normalised latent sums per head
+  __shared__ float s_z[NH];
+  __shared__ int s_last;
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int hl = w >> 1, rh = w & 1;         // head within the group, half of the pairs
+  const int t = lane & 31, kh = lane >> 5;   // 32x32 operand column (token) and K half
+  const int g16 = lane >> 4, n16 = lane & 15;  // 16x16 operand layout
+
+  // ---- XCD-aware placement: the head groups of one (row, split) share an XCD ----
+  const int units = a.rows * a.splits;
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, u = bid >> 3;
+  const int hg = u % a.head_groups;
+  const int unit = (u / a.head_groups) * 8 + xcd;
+  if (unit >= units) return;  // grid padding, uniform over the workgroup
+  const int row = unit / a.splits, split = unit - row * a.splits;
+  const int b = row / a.n_q, qi = row - b * a.n_q;
+  const int h = hg * NH + hl;
+
+  int qp, ctx;
+  if (a.prefill) {
+    qp = a.p0[b] + qi;
+    ctx = qp + 1;
+  } else {
+    qp = a.q_pos[b];
+    ctx = a.ctx_len[b];
+  }
+  int errbits = 0;
+  if (ctx < 1 || ctx > a.max_ctx || qp < 0 || qp >= a.rope_len) {
+    errbits |= LLA_DEVERR_CTX;
+    ctx = 0;
+    qp = 0;
+  }
+  const int npages = (ctx + kPage - 1) / kPage;
+  const int lp0 = split * a.pages_per_split;
+  const int lp1 = min(lp0 + a.pages_per_split, npages);
+  const int j_lo = lp0 * kPage, j_hi = min(lp1 * kPage, ctx);
+  const int nblk = j_hi > j_lo ? (j_hi - j_lo + 31) / 32 : 0;
+
+  for (int i = threadIdx.x; i < 16 * 32; i += blockDim.x) (&s_p[0][0])[i] = 0;
+  if (threadIdx.x < 16) s_alpha[threadIdx.x] = 1.f;
+  {
+    const int *pt_row = a.page_table + (long long)b * a.max_pages;
+    for (int i = threadIdx.x; i < lp1 - lp0; i += blockDim.x) {
+      const int p = pt_row[lp0 + i];
+      const bool ok = p >= 0 && p < a.num_pages;
+      if (!ok) errbits |= LLA_DEVERR_PAGE;
+      s_pt[i] = ok ? p : 0;
+    }
+  }
+
+  // ---- prologue: the rotated query folded into W_up,k,t,h as MFMA A-operands ----
+  // Row m of this wave's row tile rt (global tile gt = RTW rh + rt) is RoPE pair
+  //   i = 16 gt + 8 ((m / 4) % 2) + 2 (m / 8) + (m % 4) / 2, an X row if m is even,
+  // which makes lane (t, kh)'s accumulator element j of tile rt the X (j even)
+  // or Y (j odd) value of pair 16 gt + 8 kh + 2 (j / 4) + (j % 4) / 2 at token t.
+  // K-slot e of K-step s in lane half kh is latent column 8 (kh KS + s) + e.
+  bf16x8 A[RTW][KS];
+  uint32_t A1[RTW];  // extra K-step, slot pair (0, 1): alpha or beta as bf16 hi + lo
+  {
+    const float *rq = a.rope + (long long)qp * DH;
+    const uint16_t *qrow = (const uint16_t *)a.q + ((long long)row * a.H + h) * DH;
+    const char *wk = a.wup_k + (long long)h * a.wup_head_stride_k * 2;
+    const uint16_t *mu = (const uint16_t *)a.mu_k + (long long)h * a.mu_head_stride;
+    const int m = t;
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+      const int gt = RTW * rh + rt;
+      const int i = 16 * gt + 8 * ((m >> 2) & 1) + 2 * (m >> 3) + ((m & 3) >> 1);
+      const float c = rq[2 * i], s = rq[2 * i + 1];
+      const float qa = bf16_to_f32(qrow[i]), qb = bf16_to_f32(qrow[i + HALF]);
+      const float pa = a.qscale * (qa * c - qb * s);
+      const float pb = a.qscale * (qa * s + qb * c);
+      // X = pa k_a + pb k_b ; Y = pb k_a - pa k_b
+      const float ca = (m & 1) ? pb : pa, cb = (m & 1) ? -pa : pb;
+#pragma unroll
+      for (int s8 = 0; s8 < KS; ++s8) {
+        const int r0 = 8 * (kh * KS + s8);
+        const u32x4 wa = *(const u32x4 *)(wk + ((long long)i * RK + r0) * 2);
+        const u32x4 wb = *(const u32x4 *)(wk + ((long long)(i + HALF) * RK + r0) * 2);
+        u32x4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          x[e] = pack_bf16(ca * bf16_lo(wa[e]) + cb * bf16_lo(wb[e]),
+                           ca * bf16_hi(wa[e]) + cb * bf16_hi(wb[e]));
+        // materialise now (otherwise the packing sinks to the loop and the raw
+        // W_up rows stay live, twice the registers of the result)
+        asm volatile("" : "+v"(x));
+        A[rt][s8] = as_bf16x8(x);
+      }
+      const float v = ca * bf16_to_f32(mu[i]) + cb * bf16_to_f32(mu[i + HALF]);
+      const uint32_t hi = f32_to_bf16(v);
+      const uint32_t lo = f32_to_bf16(v - bf16_to_f32(hi));
+      A1[rt] = kh == 0 ? (hi | (lo << 16)) : 0u;
+    }
+  }
+  // constant B-operand of the extra K-step: bf16 (1, 1) in slots 0, 1 of half 0
+  const bf16x8 bone = as_bf16x8(u32x4{kh == 0 ? 0x3F803F80u : 0u, 0u, 0u, 0u});
+  __syncthreads();  // s_pt, s_p, s_alpha
+
+  // ---- direct-to-LDS loads of one 32-token block ----
+  const char *rope_b = (const char *)a.rope;
+  auto issue = [&](int blk, Tile2d<DH, RK, RV> &T) {
+    const int j0 = j_lo + 32 * blk;
+    const int lpa = min(j0 / kPage, lp1 - 1) - lp0, lpb = min(j0 / kPage + 1, lp1 - 1) - lp0;
+    const long long pa = s_pt[lpa], pb = s_pt[lpb];
+    const char *kb = a.k_pool + (t < 16 ? pa : pb) * a.pool_page_stride_k * 2;
+#pragma unroll
+    for (int i = 0; i < CKQ / NW; ++i) {
+      const int q = w * (CKQ / NW) + i;
+      const int c = 2 * q + kh;  // lane (kh, t) -> chunk c, token t
+      __builtin_amdgcn_global_load_lds((const void *)(kb + ((t & 15) * RK + 8 * c) * 2),
+                                       LLA_LDS(&T.ck[q * 64]), 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < CVQ / NW; ++i) {
+      const int q = w * (CVQ / NW) + i;
+      const int tok = (q * 64 + lane) / (RV / 8), c = (q * 64 + lane) % (RV / 8);
+      const char *vb = a.v_pool + (tok < 16 ? pa : pb) * a.pool_page_stride_v * 2;
+      __builtin_amdgcn_global_load_lds((const void *)(vb + ((tok & 15) * RV + 8 * c) * 2),
+                                       LLA_LDS(&T.cv[q * 64]), 16, 0, 0);
+    }
+    const int pos = min(j0 + t, a.rope_len - 1);
+#pragma unroll
+    for (int i = 0; i < TRQ / NW; ++i) {
+      const int q = w * (TRQ / NW) + i;
+      const int c = 2 * q + kh;
+      __builtin_amdgcn_global_load_lds((const void *)(rope_b + (long long)pos * (DH * 4) + c * 16),
+                                       LLA_LDS(&T.trig[q * 64]), 16, 0, 0);
+    }
+  };
+
+  float m_run = -INFINITY, z_run = 0.f;
+  f32x4 accv[VT];
+#pragma unroll
+  for (int v = 0; v < VT; ++v) accv[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto run_block = [&](int blk, Tile2d<DH, RK, RV> &T, Tile2d<DH, RK, RV> &N) {
+    if (blk + 1 < nblk) issue(blk + 1, N);
+    __builtin_amdgcn_sched_barrier(0);
+    const int j0 = j_lo + 32 * blk;
+    const int nvalid = min(32, j_hi - j0);
+
+    // K side: X / Y of this wave's 32 pairs x 32 tokens
+    f32x16 acc[RTW];
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) acc[rt] = f32x16{};
+    // B-operands two K-steps ahead of their MFMAs
+    u32x4 bk[3];
+    bk[0] = T.ck[(kh * KS + 0) * 32 + t];
+    bk[1] = T.ck[(kh * KS + 1) * 32 + t];
+#pragma unroll
+    for (int s8 = 0; s8 < KS; ++s8) {
+      if (s8 + 2 < KS) bk[(s8 + 2) % 3] = T.ck[(kh * KS + s8 + 2) * 32 + t];
+#pragma unroll
+      for (int rt = 0; rt < RTW; ++rt)
+        acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[rt][s8], as_bf16x8(bk[s8 % 3]), acc[rt], 0, 0, 0);
+    }
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt)
+      acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(u32x4{A1[rt], 0u, 0u, 0u}), bone,
+                                                         acc[rt], 0, 0, 0);
+
+    float sp = 0.f;
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+      const int gt = RTW * rh + rt;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 tr = T.trig[(8 * gt + 4 * kh + q) * 32 + t];
+        sp = fmaf(tr[0], acc[rt][4 * q + 0], sp);
+        sp = fmaf(tr[1], acc[rt][4 * q + 1], sp);
+        sp = fmaf(tr[2], acc[rt][4 * q + 2], sp);
+        sp = fmaf(tr[3], acc[rt][4 * q + 3], sp);
+      }
+    }
+    {
+      const uint32_t us = __float_as_uint(sp);
+      const auto sw = __builtin_amdgcn_permlane32_swap(us, us, false, false);
+      sp = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+    if (kh == 0) s_part[hl][rh][t] = sp;
+    __syncthreads();
+    // both halves of a head add the two half-scores in the same order
+    const float sfull = s_part[hl][0][t] + s_part[hl][1][t];
+    const float s = t < nvalid ? sfull : -INFINITY;
+    float bm = max_in_row(s);
+    {
+      const uint32_t ub = __float_as_uint(bm);
+      const auto sw = __builtin_amdgcn_permlane16_swap(ub, ub, false, false);
+      bm = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    const float m_new = fmaxf(m_run, bm);  // finite: block has >= 1 valid token
+    const float alpha = fast_exp2(m_run - m_new);
+    const uint32_t pbits = f32_to_bf16(fast_exp2(s - m_new));
+    float ps = sum_in_row(bf16_to_f32(pbits));
+    {
+      const uint32_t up = __float_as_uint(ps);
+      const auto sw = __builtin_amdgcn_permlane16_swap(up, up, false, false);
+      ps = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+    z_run = fmaf(z_run, alpha, ps);
+    m_run = m_new;
+    if (rh == 0 && kh == 0) s_p[hl][t] = (uint16_t)pbits;
+    if (rh == 0 && lane == 0) s_alpha[hl] = alpha;
+    __syncthreads();
+
+    // V side: accv[head n][r] = accv * alpha_n + sum_t p[n][t] c_v[t][r]
+    const float al = s_alpha[n16];
+    const u32x4 pv = *(const u32x4 *)&s_p[n16][8 * g16];
+    const int rb = w * VR + 2 * n16;  // lane's 2 columns: rb, rb + 1 (one per tile)
+    uint32_t cvr[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int tok = 8 * g16 + e;
+      cvr[e] = *(const uint32_t *)((const char *)T.cv + (tok * RV + rb) * 2);
+      if (nvalid < 32 && tok >= nvalid) cvr[e] = 0u;
+    }
+#pragma unroll
+    for (int v = 0; v < VT; ++v) {
+      // tile v holds column rb + v for tokens 8 g16 + e: select bf16 half v of each dword
+      u32x4 av;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        av[d] = v ? __builtin_amdgcn_perm(cvr[2 * d + 1], cvr[2 * d], 0x07060302u)
+                  : __builtin_amdgcn_perm(cvr[2 * d + 1], cvr[2 * d], 0x05040100u);
+      accv[v] = accv[v] * al;
+      accv[v] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(pv), accv[v], 0, 0, 0);
+    }
+    __syncthreads();  // tile T, s_part and s_p free; block blk+1 landed in N
+  };
+
+  if (nblk > 0) issue(0, tile0);
+  __syncthreads();
+  for (int blk = 0; blk < nblk; blk += 2) {
+    run_block(blk, tile0, tile1);
+    if (blk + 1 < nblk) run_block(blk + 1, tile1, tile0);
+  }
+
+  // ---- epilogue ----
+  if (errbits) atomicOr(a.err, errbits);
+  const bool bad = __syncthreads_or(errbits != 0);
+  // accv[v][e] = latent sum of head n16 at column w VR + 2 (4 g16 + e) + v
+  auto col = [&](int v, int e) { return w * VR + 2 * (4 * g16 + e) + v; };
+
+  if (a.splits > 1) {
+    if (n16 < NH) {
+      float *part = a.partials + (((long long)row * a.H + hg * NH + n16) * a.splits + split) * (RV + 2);
+#pragma unroll
+      for (int v = 0; v < VT; ++v)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) part[col(v, e)] = accv[v][e];
+    }
+    if (rh == 0 && lane == 0) {
+      float *part = a.partials + (((long long)row * a.H + h) * a.splits + split) * (RV + 2);
+      part[RV] = m_run;
+      part[RV + 1] = bad ? __builtin_nanf("") : z_run;
+    }
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const int prev = atomicAdd(&a.counters[row * a.head_groups + hg], 1);
+      s_last = (prev == a.splits - 1);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    if (threadIdx.x == 0) a.counters[row * a.head_groups + hg] = 0;
+    {  // waves (hl, rh) merge head h in fixed split order, columns rh * RV/2 ...
+      const float *pb = a.partials + ((long long)row * a.H + h) * a.splits * (RV + 2);
+      float M = -INFINITY;
+      for (int s = 0; s < a.splits; ++s) M = fmaxf(M, pb[s * (RV + 2) + RV]);
+      float Z = 0.f;
+      for (int s = 0; s < a.splits; ++s)
+        Z = fmaf(exp2f(pb[s * (RV + 2) + RV] - M), pb[s * (RV + 2) + RV + 1], Z);
+      for (int r = rh * (RV / 2) + lane; r < (rh + 1) * (RV / 2); r += 64) {
+        float acc_r = 0.f;
+        for (int s = 0; s < a.splits; ++s)
+          acc_r = fmaf(exp2f(pb[s * (RV + 2) + RV] - M), pb[s * (RV + 2) + r], acc_r);
+        s_red[hl][r] = acc_r / Z;
+      }
+    }
+  } else {
+    if (rh == 0 && lane == 0) s_z[hl] = bad ? __builtin_nanf("") : z_run;
+    __syncthreads();
+    if (n16 < NH) {
+      const float zz = s_z[n16];
+#pragma unroll
+      for (int v = 0; v < VT; ++v)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s_red[n16][col(v, e)] = accv[v][e] / zz;
+    }
+  }
+  __syncthreads();
+
+  // ---- V up-projection of head h, outputs rh * d/2 ... : out = mu_v + accn W_up,v^T ----
+  {
+    const char *wv = a.wup_v + (long long)h * a.wup_head_stride_v * 2;
+    const uint16_t *mu = (const uint16_t *)a.mu_v + (long long)h * a.mu_head_stride;
+    const float *an = s_red[hl];
+    for (int e = rh * HALF + lane; e < (rh + 1) * HALF; e += 64) {
+      float o = bf16_to_f32(mu[e]);
+      const char *we = wv + (long long)e * RV * 2;
+#pragma unroll 4
+      for (int r8 = 0; r8 < RV / 8; ++r8) {
+        const u32x4 v = *(const u32x4 *)(we + r8 * 16);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          o = fmaf(bf16_lo(v[k]), an[8 * r8 + 2 * k], o);
+          o = fmaf(bf16_hi(v[k]), an[8 * r8 + 2 * k + 1], o);
+        }
+      }
+      ((uint16_t *)a.out)[((long long)row * a.H + h) * DH + e] = (uint16_t)f32_to_bf16(o);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- dispatch
+
+// (d_head, r_k, r_v); r_v = 256 gives each lane 2 adjacent V columns (one per tile)
+#define LLA_DECODE2D_SHAPES(X) \
+  X(128, 256, 256)             \
+  X(64, 128, 256)
+
+bool decode2d_supported(int dtype, int d_head, int r_k, int r_v) {
+  if (dtype != LLA_BF16) return false;
+#define X(DH, RK, RV) \
+  if (d_head == DH && r_k == RK && r_v == RV) return true;
+  LLA_DECODE2D_SHAPES(X)
+#undef X
+  return false;
+}
+
+hipError_t launch_decode2d(int d_head, int r_k, int r_v, const AttnArgs &a, hipStream_t stream) {
+  if (a.waves != 8 || a.heads_per_wave != 1) return hipErrorInvalidConfiguration;
+  if (a.pages_per_split > 2048 || a.pages_per_split % 2) return hipErrorInvalidConfiguration;
+  const long long units = (long long)a.rows * a.splits;
+  const long long grid = (units + 7) / 8 * 8 * a.head_groups;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+#define X(DH, RK, RV)                                                                        \
+  if (d_head == DH && r_k == RK && r_v == RV) {                                              \
+    hipLaunchKernelGGL((decode_2d_kernel<DH, RK, RV>), dim3((unsigned)grid), dim3(512), 0,   \
+                       stream, a);                                                           \
+    return hipGetLastError();                                                                \
+  }
+  LLA_DECODE2D_SHAPES(X)
+#undef X
+  return hipErrorInvalidConfiguration;
+}
+
+}  // namespace lla
