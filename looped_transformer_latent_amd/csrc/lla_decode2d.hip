@@ -74,7 +74,7 @@ __global__ __launch_bounds__(512) void decode_2d_kernel(AttnArgs a) {
   __shared__ float s_z[NH];
   __shared__ int s_last;
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hl = w >> 1, rh = w & 1;         // head within the group, half of the pairs
   const int t = lane & 31, kh = lane >> 5;   // 32x32 operand column (token) and K half
   const int g16 = lane >> 4, n16 = lane & 15;  // 16x16 operand layout

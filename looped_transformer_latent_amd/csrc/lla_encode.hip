@@ -74,6 +74,179 @@ __global__ __launch_bounds__(256) void encode_append_kernel(EncodeArgs a, int RK
   }
 }
 
+// ---------------------------------------------------------------- MFMA path (bf16)
+//
+// Per (layer, latent group, K|V) the encoder is a plain GEMM,
+//   C[tokens x r] = X[tokens x width] W_down[width x r] - 1 (mu W_down),
+// run on v_mfma_f32_16x16x32_bf16.  A workgroup (4 waves) takes 128 tokens;
+// wave w owns 32 of them (two 16-row tiles) and all r columns.  W_down is
+// streamed in chunks of 128 rows, transposed into LDS ([r][k], rows padded so
+// the 16-byte B-operand reads of 16 consecutive r hit distinct banks) and
+// shared by the 4 waves.  Each lane reads its tokens' x as 64 contiguous bytes
+// per chunk: K-slot e of K-step s in lane group g is chunk column
+// 32 g + 8 s + e, on both operands.  mu W_down is one more MFMA row tile
+// (mu in row 0, zeros below) per column tile, spread over the waves, so it is
+// computed with the same fp32 accumulation as the tokens.  The result (minus
+// mu W_down, rounded once to bf16) goes through LDS and leaves as 16-byte
+// stores into the paged pool.
+template <int R>
+__global__ __launch_bounds__(256) void encode_mfma_kernel(EncodeArgs a, int kv) {
+  constexpr int TOK = 128;        // tokens per workgroup
+  constexpr int KC = 128;         // W_down rows per chunk
+  constexpr int LROW = KC + 8;    // padded LDS row (elements) of the transposed chunk
+  constexpr int CT = R / 16;      // column tiles
+  constexpr int MT = (CT + 3) / 4;  // mu column tiles per wave
+  static_assert(R % 16 == 0 && R <= 256, "r");
+  static_assert(R * LROW >= TOK * R, "output staging reuses the chunk buffer");
+  __shared__ __attribute__((aligned(16))) uint16_t s_w[R * LROW];
+  __shared__ __attribute__((aligned(16))) uint16_t s_mu[KC];
+  __shared__ float s_muw[R];
+  __shared__ long long s_off[TOK];  // element offset of each token's latent row, -1 = dropped
+
+  // wave index as a scalar: branches on it must be uniform scalar branches,
+  // never EXEC-masked MFMAs
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, n = lane & 15;
+  const int grp = blockIdx.y, li = blockIdx.z;
+  const long long tokens = (long long)a.batch * a.n_new;
+  const long long tok0 = (long long)blockIdx.x * TOK;
+  const long long gl = (long long)li * a.groups + grp;
+  const char *x = kv ? a.x_v : a.x_k;
+  const uint16_t *mu = (const uint16_t *)(kv ? a.mu_v : a.mu_k) + gl * a.width;
+  const uint16_t *wd = (const uint16_t *)(kv ? a.wd_v : a.wd_k) + gl * a.width * (long long)R;
+  uint16_t *pool = (uint16_t *)(kv ? a.v_pool : a.k_pool) +
+                   (long long)li * (kv ? a.pool_layer_stride_v : a.pool_layer_stride_k);
+  const long long pstride = kv ? a.pool_page_stride_v : a.pool_page_stride_k;
+  const long long hstride = kv ? a.pool_head_stride_v : a.pool_head_stride_k;
+
+  // destination slot of each token (placement is integer work, checked here)
+  if (threadIdx.x < TOK) {
+    const long long tok = tok0 + threadIdx.x;
+    long long off = -1;
+    if (tok < tokens) {
+      const int b = (int)(tok / a.n_new), nn = (int)(tok % a.n_new);
+      const long long pos = (long long)a.pos0[b] + nn;
+      if (pos < 0 || pos >= (long long)a.max_pages * kPage) {
+        atomicOr(a.err, LLA_DEVERR_APPEND);
+      } else {
+        const int page = a.page_table[(long long)b * a.max_pages + pos / kPage];
+        if (page < 0 || page >= a.num_pages) atomicOr(a.err, LLA_DEVERR_PAGE);
+        else off = (long long)page * pstride + grp * hstride + (pos % kPage) * R;
+      }
+    }
+    s_off[threadIdx.x] = off;
+  }
+
+  // this lane's x rows: tokens tok0 + 32 w + 16 rt + n (clamped; dropped at the end)
+  const uint16_t *xr[2];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    long long tk = tok0 + 32 * w + 16 * rt + n;
+    if (tk >= tokens) tk = tokens - 1;
+    xr[rt] = (const uint16_t *)x + ((li * tokens + tk) * a.groups + grp) * a.width;
+  }
+
+  f32x4 acc[2][CT];
+  f32x4 accm[MT];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int m = 0; m < MT; ++m) accm[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nchunks = a.width / KC;
+  for (int c = 0; c < nchunks; ++c) {
+    const int k0 = c * KC;
+    u32x4 xa[2][4];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) xa[rt][s] = *(const u32x4 *)(xr[rt] + k0 + 32 * g + 8 * s);
+    __syncthreads();  // previous chunk's operands are consumed
+    // W_down rows k0 .. k0 + 127 -> s_w[r][k]: 4 rows x 8 columns per task
+    for (int task = threadIdx.x; task < (KC / 4) * (R / 8); task += blockDim.x) {
+      const int k4 = task / (R / 8), r8 = task % (R / 8);
+      u32x4 v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = *(const u32x4 *)(wd + (long long)(k0 + 4 * k4 + i) * R + 8 * r8);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int sh = (j & 1) * 16;
+        const uint32_t e0 = (v[0][j >> 1] >> sh) & 0xFFFFu, e1 = (v[1][j >> 1] >> sh) & 0xFFFFu;
+        const uint32_t e2 = (v[2][j >> 1] >> sh) & 0xFFFFu, e3 = (v[3][j >> 1] >> sh) & 0xFFFFu;
+        uint32_t *dst = (uint32_t *)(s_w + (8 * r8 + j) * LROW + 4 * k4);
+        dst[0] = e0 | (e1 << 16);
+        dst[1] = e2 | (e3 << 16);
+      }
+    }
+    if (threadIdx.x < KC / 8) *(u32x4 *)(s_mu + 8 * threadIdx.x) = *(const u32x4 *)(mu + k0 + 8 * threadIdx.x);
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int kk = 32 * g + 8 * s;
+      const u32x4 mrow = *(const u32x4 *)(s_mu + kk);
+      const u32x4 am = n == 0 ? mrow : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const u32x4 bw = *(const u32x4 *)(s_w + (16 * ct + n) * LROW + kk);
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+          acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[rt][s]), as_bf16x8(bw),
+                                                                acc[rt][ct], 0, 0, 0);
+        if (ct % 4 == w)
+          accm[ct / 4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(am), as_bf16x8(bw),
+                                                                 accm[ct / 4], 0, 0, 0);
+      }
+    }
+  }
+
+  // mu W_down: row 0 of each mu tile = lanes g == 0, element 0
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+    if (4 * m + w < CT && g == 0) s_muw[16 * (4 * m + w) + n] = accm[m][0];
+  __syncthreads();  // s_muw ready, s_w free for output staging
+  uint16_t *s_out = s_w;  // [TOK][R] bf16
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const int r = 16 * ct + n;
+      const float mw = s_muw[r];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        s_out[(32 * w + 16 * rt + 4 * g + e) * R + r] = (uint16_t)f32_to_bf16(acc[rt][ct][e] - mw);
+    }
+  __syncthreads();
+  for (int q = threadIdx.x; q < TOK * (R / 8); q += blockDim.x) {
+    const int tl = q / (R / 8), c8 = q % (R / 8);
+    const long long off = s_off[tl];
+    if (off >= 0) *(u32x4 *)(pool + off + 8 * c8) = *(const u32x4 *)(s_out + tl * R + 8 * c8);
+  }
+}
+
+#define LLA_ENCODE_R(X) X(16) X(32) X(48) X(64) X(96) X(128) X(160) X(256)
+
+bool encode_mfma_r(int r) {
+#define X(RR) if (r == RR) return true;
+  LLA_ENCODE_R(X)
+#undef X
+  return false;
+}
+
+hipError_t launch_encode_mfma(int r, int kv, const EncodeArgs &a, hipStream_t stream) {
+  const long long tokens = (long long)a.batch * a.n_new;
+  const dim3 grid((unsigned)((tokens + 127) / 128), a.groups, a.n_layers);
+#define X(RR)                                                                               \
+  if (r == RR) {                                                                            \
+    hipLaunchKernelGGL(encode_mfma_kernel<RR>, grid, dim3(256), 0, stream, a, kv);          \
+    return hipGetLastError();                                                               \
+  }
+  LLA_ENCODE_R(X)
+#undef X
+  return hipErrorInvalidConfiguration;
+}
+
 bool encode_supported(int dtype, int width, int r_k, int r_v) {
   return (dtype == LLA_BF16 || dtype == LLA_F32) && width > 0 && r_k > 0 && r_v > 0;
 }
@@ -81,6 +254,13 @@ bool encode_supported(int dtype, int width, int r_k, int r_v) {
 hipError_t launch_encode(int dtype, int r_k, int r_v, const EncodeArgs &a, hipStream_t stream) {
   const long long tokens = (long long)a.batch * a.n_new;
   if (tokens == 0 || a.n_layers == 0) return hipSuccess;
+  // bf16 with whole 128-column chunks and an instantiated rank: matrix cores
+  if (dtype == LLA_BF16 && a.width % 128 == 0 && encode_mfma_r(r_k) && encode_mfma_r(r_v) &&
+      tokens <= 0x7FFFFFFFLL * 128) {
+    hipError_t e = launch_encode_mfma(r_k, 0, a, stream);
+    if (e != hipSuccess) return e;
+    return launch_encode_mfma(r_v, 1, a, stream);
+  }
   const dim3 g1(a.groups, a.n_layers, 2);
   const dim3 g2((unsigned)((tokens + 15) / 16), a.groups, 2 * a.n_layers);
   if (dtype == LLA_BF16) {
