@@ -165,7 +165,9 @@ def main():
     q_pos = ctx - 1
     ws_dec = lla.workspace(D, lla.OP_DECODE, w.batch, w.ctx)
     # the step's new token: its per-loop K/V for every layer, appended at ctx - 1
-    n_new = max(1, w.n_new if w.n_new <= 1 else 1)
+    # the step's new tokens: one per sequence for a decode step; workloads that
+    # name an append chunk (the 4x point: 512 tokens per sequence) append it
+    n_new = max(1, w.n_new)
     xs = (w.D, w.batch, n_new) + ((w.H, w.T, w.d_head) if w.variant == wl.PER_HEAD else (w.T, w.H, w.d_head))
     x_k = torch.empty(xs, dtype=dt_t, device=dev)
     x_v = torch.empty(xs, dtype=dt_t, device=dev)
@@ -177,8 +179,14 @@ def main():
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in calls]
 
+    ev_enc = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+
     def step(record):
+        if record:
+            ev_enc[0].record(stream)
         lla.encode_append(D, codec, cache, x_k, x_v, pos0, n_new, 0, w.D, ws_enc)
+        if record:
+            ev_enc[1].record(stream)
         for i, (t, l) in enumerate(calls):
             if record:
                 ev[i][0].record(stream)
@@ -189,12 +197,13 @@ def main():
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
-    kern_ms = []
+    kern_ms, enc_ms = [], []
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step(True)
         torch.cuda.synchronize()
         kern_ms += [a.elapsed_time(b) for a, b in ev]
+        enc_ms.append(ev_enc[0].elapsed_time(ev_enc[1]))
     elapsed = time.perf_counter() - t0
     assert lla.device_error_word(ws_dec) == 0 and lla.device_error_word(ws_enc) == 0
     assert torch.isfinite(out.float()).all().item()
@@ -236,9 +245,22 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "ctx": w.ctx, "T": w.T, "D": w.D,
                    "H": w.H, "d_head": w.d_head, "r_k": w.r_k, "r_v": w.r_v, "page_size": 16,
                    "page_table": "shuffled" if w.shuffled else "identity",
-                   "step": f"encode_append(1 token x {w.D} layers) + {len(calls)} lla_decode_attn calls"},
+                   "step": f"encode_append({n_new} token(s) per sequence x {w.D} layers) + {len(calls)} lla_decode_attn calls"},
         "roofline": roof,
     }
+    # encode + append of the step's tokens into every layer (HBM-bound GEMM):
+    # reads x_k, x_v and W_down, writes the latents
+    enc_avg = float(np.mean(enc_ms))
+    tok = w.batch * n_new * w.D
+    width = w.T * w.d_head * (w.H if w.variant == wl.TWO_D else 1)
+    enc_bytes = (tok * w.groups * width * 2 * w.esize + tok * w.groups * (w.r_k + w.r_v) * w.esize
+                 + w.D * w.groups * width * (w.r_k + w.r_v) * w.esize)
+    enc_flops = 2 * tok * w.groups * width * (w.r_k + w.r_v)
+    result["encode"] = {"kernel": "encode_mfma_kernel", "tokens_per_layer": w.batch * n_new,
+                        "layers": w.D, "avg_ms": enc_avg, "algorithmic_bytes": enc_bytes,
+                        "achieved_gbs": enc_bytes / (enc_avg / 1e3) / 1e9,
+                        "frac_hbm": enc_bytes / (enc_avg / 1e3) / 1e9 / HBM_PEAK_GBS,
+                        "tflops": enc_flops / (enc_avg / 1e3) / 1e12}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, codec_h, pt_h, layer=w.D - 1, loop=w.T - 1,
                                               target_s=args.cpu_seconds)

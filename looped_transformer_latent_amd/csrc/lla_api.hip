@@ -34,12 +34,11 @@ size_t esize(const lla_dims *d) { return d->dtype == LLA_BF16 ? 2 : 4; }
 struct AttnPlan {
   bool two_d;  // LLA-2D kernel (shared latent, 4 heads x 2 waves per workgroup)
   int hpw, waves, head_groups, splits, pages_per_split, chunk_pages;
-  size_t counters_off, partials_off, bytes;
+  size_t partials_off, bytes;
 };
 
 void plan_workspace(const lla_dims *d, long long rows, AttnPlan *p) {
-  p->counters_off = kHeaderBytes;
-  p->partials_off = align256(p->counters_off + sizeof(int) * (size_t)rows * p->head_groups);
+  p->partials_off = kHeaderBytes;
   p->bytes = p->splits > 1
                  ? align256(p->partials_off + sizeof(float) * (size_t)rows * d->H * p->splits * (d->r_v + 2))
                  : kHeaderBytes;
@@ -214,10 +213,11 @@ int32_t attn_call(const lla_dims *d, const lla_codec *c, const lla_cache *k, con
   const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)d->d_head);
   a.qscale = sc * 1.4426950408889634f;
   a.err = (int *)ws;
-  a.counters = (int *)((char *)ws + p.counters_off);
   a.partials = (float *)((char *)ws + p.partials_off);
-  if (p.two_d) return check_launch(launch_decode2d(d->d_head, d->r_k, d->r_v, a, stream));
-  return check_launch(launch_decode(d->dtype, d->d_head, d->r_k, d->r_v, a, stream));
+  const int32_t rc = check_launch(p.two_d ? launch_decode2d(d->d_head, d->r_k, d->r_v, a, stream)
+                                          : launch_decode(d->dtype, d->d_head, d->r_k, d->r_v, a, stream));
+  if (rc != LLA_OK || p.splits == 1) return rc;
+  return check_launch(launch_merge(d->dtype, d->d_head, d->r_v, a, stream));
 }
 
 }  // namespace

@@ -24,9 +24,9 @@
 //    cos/sin for its 16 pair indices and its token only: 2 FMAs per (i, token).
 //  * Online softmax in base 2 with deferred rescaling; V accumulated as
 //    sum_j p_j c_v,j in fp32 registers (lane = token x r_v/4 chunk).
-//  * Splits write (m, Z, acc) partials; the last workgroup of a row (atomic
-//    counter, reset by that workgroup) merges them in fixed split order --
-//    deterministic -- and up-projects through W_up,v,t.
+//  * With one split the workgroup normalises and up-projects through W_up,v,t
+//    itself; with several, each writes (m, Z, acc) partials and a separate
+//    merge launch combines them in fixed split order (lla_merge.hip).
 #include "lla_device.h"
 #include "lla_internal.h"
 
@@ -457,11 +457,10 @@ __global__ __launch_bounds__(64 * NW) void decode_ph_kernel(AttnArgs a) {
   if (errbits && threadIdx.x == 0) atomicOr(a.err, errbits);
   const bool bad = errbits != 0;
 
-  __shared__ int s_last;
   float *sh = (float *)(s_pt + a.pages_per_split);  // [waves][HPW][RV + 2]
   float *mine = sh + (wave * HPW) * (RV + 2);
 
-  if (a.splits > 1) {
+  if (a.splits > 1) {  // partials for the merge launch
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
       const int h = h0 + hh;
@@ -475,33 +474,7 @@ __global__ __launch_bounds__(64 * NW) void decode_ph_kernel(AttnArgs a) {
         part[RV + 1] = bad ? __builtin_nanf("") : z[hh];
       }
     }
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      const int prev = atomicAdd(&a.counters[row * a.head_groups + hg], 1);
-      s_last = (prev == a.splits - 1);
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    if (threadIdx.x == 0) a.counters[row * a.head_groups + hg] = 0;
-    // merge the splits in fixed order
-#pragma unroll
-    for (int hh = 0; hh < HPW; ++hh) {
-      const int h = h0 + hh;
-      const float *pb = a.partials + ((long long)row * a.H + h) * a.splits * (RV + 2);
-      float M = -INFINITY;
-      for (int s = 0; s < a.splits; ++s) M = fmaxf(M, pb[s * (RV + 2) + RV]);
-      float Z = 0.f;
-      for (int s = 0; s < a.splits; ++s)
-        Z = fmaf(exp2f(pb[s * (RV + 2) + RV] - M), pb[s * (RV + 2) + RV + 1], Z);
-      for (int r = lane; r < RV; r += 64) {
-        float s_acc = 0.f;
-        for (int s = 0; s < a.splits; ++s)
-          s_acc = fmaf(exp2f(pb[s * (RV + 2) + RV] - M), pb[s * (RV + 2) + r], s_acc);
-        mine[hh * (RV + 2) + r] = s_acc / Z;
-      }
-    }
+    return;
   } else {
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
@@ -560,7 +533,7 @@ hipError_t go(const AttnArgs &a, hipStream_t stream) {
   static bool lds_raised = false;  // allow more than the default 64 KiB of LDS once per kernel
   if (!lds_raised) {
     const hipError_t e = hipFuncSetAttribute((const void *)decode_ph_kernel<BF, DH, RK, RV, HPW, NW>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 256);
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 1024);
     if (e != hipSuccess) return e;
     lds_raised = true;
   }
@@ -581,17 +554,10 @@ hipError_t go(const AttnArgs &a, hipStream_t stream) {
   X(false, 64, 16, 32, 1, 8)   \
   X(false, 128, 16, 32, 1, 2)  \
   X(false, 128, 16, 32, 1, 8)  \
-  X(true, 64, 16, 32, 1, 2)    \
-  X(true, 64, 16, 32, 2, 8)    \
-  X(true, 128, 16, 32, 1, 2)   \
-  X(true, 128, 16, 32, 2, 2)   \
-  X(true, 128, 16, 32, 1, 8)   \
-  X(true, 128, 16, 32, 2, 8)   \
-  X(true, 128, 32, 64, 1, 8)   \
-  X(true, 128, 96, 160, 1, 8)  \
   X(false, 128, 96, 160, 1, 8)
 
 bool decode_supported(int dtype, int d_head, int r_k, int r_v, int hpw, int waves) {
+  if (dtype == LLA_BF16) return decode_g_supported(d_head, r_k, r_v, hpw, waves);
   const bool bf = dtype == LLA_BF16;
 #define X(BF, DH, RK, RV, HPW, NW) \
   if (bf == BF && d_head == DH && r_k == RK && r_v == RV && hpw == HPW && waves == NW) return true;
@@ -602,6 +568,7 @@ bool decode_supported(int dtype, int d_head, int r_k, int r_v, int hpw, int wave
 
 hipError_t launch_decode(int dtype, int d_head, int r_k, int r_v, const AttnArgs &a,
                          hipStream_t stream) {
+  if (dtype == LLA_BF16) return launch_decode_g(d_head, r_k, r_v, a, stream);
   const bool bf = dtype == LLA_BF16;
 #define X(BF, DH, RK, RV, HPW, NW)                                                  \
   if (bf == BF && d_head == DH && r_k == RK && r_v == RV && a.heads_per_wave == HPW && \

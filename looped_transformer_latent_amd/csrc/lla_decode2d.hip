@@ -30,8 +30,8 @@
 //  * V side, exact by linearity: sum_j p_j,h c_v,j for the 4 heads is one more
 //    MFMA product, P[tokens x 4 heads] (bf16 weights via LDS) times the c_v
 //    tile; wave w owns r_v/4 of the columns for all 4 heads.
-//  * Splits write (m, Z, acc) partials; the last workgroup of (row, head group)
-//    merges them in fixed order and up-projects once per head.
+//  * With one split the workgroup up-projects once per head; with several it
+//    writes (m, Z, acc) partials for the merge launch (lla_merge.hip).
 #include "lla_device.h"
 #include "lla_internal.h"
 
@@ -72,7 +72,6 @@ __global__ __launch_bounds__(512) void decode_2d_kernel(AttnArgs a) {
   __shared__ int s_pt[2048 + 2];
   __shared__ float s_red[NH][RV + 2];  // epilogue: normalised latent sums per head
   __shared__ float s_z[NH];
-  __shared__ int s_last;
 
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hl = w >> 1, rh = w & 1;         // head within the group, half of the pairs
@@ -329,30 +328,7 @@ __global__ __launch_bounds__(512) void decode_2d_kernel(AttnArgs a) {
       part[RV] = m_run;
       part[RV + 1] = bad ? __builtin_nanf("") : z_run;
     }
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      const int prev = atomicAdd(&a.counters[row * a.head_groups + hg], 1);
-      s_last = (prev == a.splits - 1);
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    if (threadIdx.x == 0) a.counters[row * a.head_groups + hg] = 0;
-    {  // waves (hl, rh) merge head h in fixed split order, columns rh * RV/2 ...
-      const float *pb = a.partials + ((long long)row * a.H + h) * a.splits * (RV + 2);
-      float M = -INFINITY;
-      for (int s = 0; s < a.splits; ++s) M = fmaxf(M, pb[s * (RV + 2) + RV]);
-      float Z = 0.f;
-      for (int s = 0; s < a.splits; ++s)
-        Z = fmaf(exp2f(pb[s * (RV + 2) + RV] - M), pb[s * (RV + 2) + RV + 1], Z);
-      for (int r = rh * (RV / 2) + lane; r < (rh + 1) * (RV / 2); r += 64) {
-        float acc_r = 0.f;
-        for (int s = 0; s < a.splits; ++s)
-          acc_r = fmaf(exp2f(pb[s * (RV + 2) + RV] - M), pb[s * (RV + 2) + r], acc_r);
-        s_red[hl][r] = acc_r / Z;
-      }
-    }
+    return;  // the merge launch combines the splits
   } else {
     if (rh == 0 && lane == 0) s_z[hl] = bad ? __builtin_nanf("") : z_run;
     __syncthreads();

@@ -1,0 +1,422 @@
+// Per-head LLA decode attention for bf16 storage, with the RoPE weighting on
+// the matrix cores (gfx950, wave64).
+//
+// What it computes is the same as the fp32 kernel (cc.laoqi.cc close reading,
+// 方法 items 1-3; gist.science "Kernmechanismus"): for layer l, loop t and
+// every (row, head),
+//   s_j = scale <R(q_pos) q, R(j) (mu_k,t + c_k,j W_up,k,t^T)>,
+//   out = mu_v,t + (sum_j e^{s_j - m} c_v,j) W_up,v,t^T / sum_j e^{s_j - m}.
+//
+// How.  With q' = scale log2(e) R(q_pos) q and RoPE pair i = (a, b) = (i, i + d/2),
+//   s_j log2(e) = sum_i cos_i(j) (alpha_i + A_i . c_j) + sin_i(j) (beta_i + B_i . c_j)
+// where A_ir = q'_a W[a][r] + q'_b W[b][r], B_ir = q'_b W[a][r] - q'_a W[b][r],
+// alpha_i = q'_a mu_a + q'_b mu_b and beta_i = q'_b mu_a - q'_a mu_b (exact algebra:
+// RoPE is linear in the reconstructed key).  Regrouping by latent column,
+//   s_j log2(e) = sum_r c_j[r] G[r][j] + G0[j],
+//   G[r][j]  = sum_i cos_i(j) A_ir + sin_i(j) B_ir,   G0[j] = sum_i cos_i(j) alpha_i + sin_i(j) beta_i.
+// G is a product of the folded decoder F (r_k x d, cos / sin slots interleaved)
+// with the RoPE rows of the page's 16 tokens (d x 16): one chain of fp16 MFMAs
+// (v_mfma_f32_16x16x32_f16) per 16 latent columns, K = d.  The RoPE rows are
+// already in LDS as fp16 (cos, sin) pairs, which is exactly the B-operand
+// layout, and are shared by all heads of the wave; G0 for the wave's heads is
+// one more MFMA chain with alpha / beta in rows 0 .. HPW-1.  What is left on the
+// vector ALUs per (token, head) is r_k / 4 FMAs per lane plus the softmax and
+// the latent-space value sum.
+//
+// fp16 keeps the decoder and cos / sin to 11 bits (bf16 has 8); products are
+// exact and accumulate in fp32.
+//
+// Work decomposition, latent streaming (ring of NBUF pages per wave, LOOK in
+// flight) and RoPE staging in LDS are as in the fp32 kernel.  With one split a
+// workgroup normalises and up-projects its heads itself; with several it
+// writes (m, Z, acc) partials for the merge launch (lla_merge.hip).
+#include "lla_device.h"
+#include "lla_internal.h"
+
+namespace lla {
+
+typedef _Float16 f16x8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
+typedef uint32_t u32x2 __attribute__((__vector_size__(2 * sizeof(uint32_t))));
+
+__device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+}
+
+template <int DH, int RK, int RV, int HPW, int NW>
+__global__ __launch_bounds__(64 * NW) void decode_g_kernel(AttnArgs a) {
+  constexpr int KS = DH / 32;   // K-steps: 16 RoPE pairs (32 cos / sin slots) each
+  constexpr int RT = RK / 16;   // 16-column tiles of the latent
+  constexpr int CV = RV / 4;    // V elements per lane per token
+  constexpr int KV = CV / 8;    // 16-byte V loads per lane per head
+  constexpr int HALF = DH / 2;
+  static_assert(DH % 32 == 0 && RK % 16 == 0 && RV % 32 == 0 && HPW <= 4, "shape");
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int NTH = 64 * NW;
+  const int g = lane >> 4, n = lane & 15;
+
+  int bid = blockIdx.x;
+  const int split = bid % a.splits;
+  bid /= a.splits;
+  const int hg = bid % a.head_groups;
+  const int row = bid / a.head_groups;
+  const int b = row / a.n_q, qi = row - b * a.n_q;
+
+  int qp, ctx;
+  if (a.prefill) {
+    qp = a.p0[b] + qi;
+    ctx = qp + 1;
+  } else {
+    qp = a.q_pos[b];
+    ctx = a.ctx_len[b];
+  }
+  int errbits = 0;
+  if (ctx < 1 || ctx > a.max_ctx || qp < 0 || qp >= a.rope_len) {
+    errbits |= LLA_DEVERR_CTX;
+    ctx = 0;
+    qp = 0;
+  }
+  const int npages = (ctx + kPage - 1) / kPage;
+  const int lp0 = split * a.pages_per_split;
+  const int lp1 = min(lp0 + a.pages_per_split, npages);
+  const int h0 = (hg * a.waves + wave) * HPW;
+
+  // ---- prologue: folded decoder as fp16 MFMA A-operands ----
+  // F[hh][rt][s]: lane (g, n) = row r = 16 rt + n, K-slots 2p, 2p + 1 = (A_ir, B_ir)
+  // of pair i = 16 s + 4 g + p.  Fa[s]: row hh (lanes n == hh) = (alpha_i, beta_i).
+  u32x4 F[HPW][RT][KS];
+  u32x4 Fa[KS];
+  {
+    const float *rq = a.rope + (long long)qp * DH;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) Fa[s] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      const int h = h0 + hh;
+      const uint16_t *qrow = (const uint16_t *)a.q + ((long long)row * a.H + h) * DH;
+      const uint16_t *w = (const uint16_t *)a.wup_k + (long long)h * a.wup_head_stride_k;
+      const uint16_t *mu = (const uint16_t *)a.mu_k + (long long)h * a.mu_head_stride;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int i = 16 * s + 4 * g + p;
+          const float c = rq[2 * i], sn = rq[2 * i + 1];
+          const float qa = bf16_to_f32(qrow[i]), qb = bf16_to_f32(qrow[i + HALF]);
+          const float pa = a.qscale * (qa * c - qb * sn);
+          const float pb = a.qscale * (qa * sn + qb * c);
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            const int r = 16 * rt + n;
+            const float wa = bf16_to_f32(w[(long long)i * RK + r]);
+            const float wb = bf16_to_f32(w[(long long)(i + HALF) * RK + r]);
+            F[hh][rt][s][p] = pack_f16(pa * wa + pb * wb, pb * wa - pa * wb);
+          }
+          const float ma = bf16_to_f32(mu[i]), mb = bf16_to_f32(mu[i + HALF]);
+          const uint32_t ab = pack_f16(pa * ma + pb * mb, pb * ma - pa * mb);
+          if (n == hh) Fa[s][p] = ab;
+        }
+      }
+    }
+  }
+
+  float m_run[HPW], z[HPW], acc[HPW][CV];
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    m_run[hh] = -INFINITY;
+    z[hh] = 0.f;
+#pragma unroll
+    for (int k = 0; k < CV; ++k) acc[hh][k] = 0.f;
+  }
+
+  // Per page and head, lane (g, n) loads latent row n: c_k columns
+  // 16 rt + 4 g .. + 3 (8 bytes per tile) and c_v columns CV g .. CV g + CV - 1.
+  // Rows past ctx_len (last page only) re-read the last valid row; their
+  // scores are forced to -inf.
+  struct Page {
+    u32x2 k[HPW][RT];
+    u32x4 v[HPW][KV];
+    int ok;
+    int last;  // last valid row of this page (15 unless the page is the last one)
+  };
+  // LDS: [RoPE rows: 2 chunk buffers][page-table entries of the split][epilogue]
+  constexpr int SPR = DH / 8;                  // 16-byte slots per position row (fp16 pairs)
+  constexpr int SWZ = SPR < 16 ? SPR - 1 : 15;  // XOR swizzle mask (row index low bits)
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  constexpr int LOOK = LLA_DECODE_LOOK;  // pages in flight beyond the one computed
+  constexpr int NBUF = LOOK + 2;        // page ring slots
+  constexpr int CH = NBUF;              // pages per RoPE chunk: one trip round the ring
+  constexpr int TS = CH * kPage * SPR;  // 16-byte slots of one chunk
+  constexpr int SLOTS = (TS + NTH - 1) / NTH;
+  constexpr int TSB = SLOTS * NTH;
+  char *s_trig = smem;
+  int *s_pt = (int *)(smem + 2 * TSB * 16);
+  {
+    const int *pt_row = a.page_table + (long long)b * a.max_pages;
+    for (int i = threadIdx.x; i < lp1 - lp0; i += blockDim.x) s_pt[i] = pt_row[lp0 + i];
+    __syncthreads();
+  }
+  auto page_at = [&](int lp) -> int { return __builtin_amdgcn_readfirstlane(s_pt[lp - lp0]); };
+
+  // RoPE staging: chunk c covers pages [lp0 + c CH, lp0 + (c + 1) CH); row R of
+  // a chunk buffer holds the fp16 (cos, sin) pairs of position 16 (lp0 + c CH) + R.
+  // Logical slot ls (pairs 4 ls .. 4 ls + 3) is stored at ls ^ (R % 16 & SWZ) so
+  // that 16 lanes reading one slot of 16 consecutive positions use distinct banks.
+  const char *rope_b = (const char *)a.rope;
+  f32x4 stg[SLOTS][2];
+  auto stage_load = [&](int c) {
+#pragma unroll
+    for (int j = 0; j < SLOTS; ++j) {
+      const int q = min((int)threadIdx.x + j * NTH, TS - 1);
+      const int R = q / SPR, ps = q % SPR, rn = R % kPage;
+      const int pos = min((lp0 + c * CH + R / kPage) * kPage + rn, ctx - 1);
+      const char *src = rope_b + (long long)pos * (DH * 4) + (ps ^ (rn & SWZ)) * 32;
+      stg[j][0] = *(const f32x4 *)(src);
+      stg[j][1] = *(const f32x4 *)(src + 16);
+    }
+  };
+  auto stage_store = [&](int c) {
+    char *dst = s_trig + (c & 1) * TSB * 16;
+#pragma unroll
+    for (int j = 0; j < SLOTS; ++j) {
+      const int q = threadIdx.x + j * NTH;  // q >= TS lands in the buffer's padding
+      u32x4 hv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        hv[e] = pack_f16(stg[j][e >> 1][(e & 1) * 2], stg[j][e >> 1][(e & 1) * 2 + 1]);
+      *(u32x4 *)(dst + q * 16) = hv;
+    }
+  };
+
+  auto load_page = [&](int lp, int pp_raw, Page &pg) {
+    pg.ok = (pp_raw >= 0 && pp_raw < a.num_pages);
+    const long long pp = pg.ok ? pp_raw : 0;
+    pg.last = min(kPage - 1, ctx - 1 - lp * kPage);
+    const int row_n = min(n, pg.last);
+    // uniform page bases + 32-bit lane offsets; latents are read exactly once
+    const char *kpage = a.k_pool + pp * a.pool_page_stride_k * 2;
+    const char *vpage = a.v_pool + pp * a.pool_page_stride_v * 2;
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      const int h = h0 + hh;
+      const uint32_t koff = (uint32_t)((h * a.pool_head_stride_k + row_n * RK + 4 * g) * 2);
+      const uint32_t voff = (uint32_t)((h * a.pool_head_stride_v + row_n * RV + CV * g) * 2);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        pg.k[hh][rt] = __builtin_nontemporal_load((const u32x2 *)(kpage + koff + 32 * rt));
+#pragma unroll
+      for (int kv = 0; kv < KV; ++kv)
+        pg.v[hh][kv] = __builtin_nontemporal_load((const u32x4 *)(vpage + voff + kv * 16));
+    }
+  };
+
+  // An invalid page-table entry was replaced by page 0 at load time; its
+  // tokens are masked out here and the row is poisoned through the error bits.
+  auto compute_page = [&](const Page &cur, int lp) {
+    errbits |= cur.ok ? 0 : LLA_DEVERR_PAGE;
+    const bool valid = cur.ok && n <= cur.last && lp < lp1;  // lp >= lp1: ring padding
+    const int row_n = min(n, cur.last);
+    const char *tb = s_trig + (((lp - lp0) / CH) & 1) * TSB * 16 +
+                     (((lp - lp0) % CH) * kPage + row_n) * SPR * 16;
+    // B-operands: RoPE pairs 16 s + 4 g .. + 3 of token n, (cos, sin) fp16
+    u32x4 th[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) th[s] = *(const u32x4 *)(tb + (((4 * s + g) ^ (row_n & SWZ)) * 16));
+    // G0 of the wave's heads: rows 0 .. HPW-1 (lane (0, n) element hh)
+    f32x4 Ga = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      Ga = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(Fa[s]), as_f16x8(th[s]), Ga, 0, 0, 0);
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      // score partial of lane (g, n): latent columns 16 rt + 4 g + e of token n
+      float sc = g == 0 ? Ga[hh] : 0.f;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        f32x4 G = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          G = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(F[hh][rt][s]), as_f16x8(th[s]), G, 0, 0, 0);
+        sc = fmaf(bf16_lo(cur.k[hh][rt][0]), G[0], sc);
+        sc = fmaf(bf16_hi(cur.k[hh][rt][0]), G[1], sc);
+        sc = fmaf(bf16_lo(cur.k[hh][rt][1]), G[2], sc);
+        sc = fmaf(bf16_hi(cur.k[hh][rt][1]), G[3], sc);
+      }
+      sc = sum_across_rows(sc);
+      sc = valid ? sc : -INFINITY;
+      const float mt = max_in_row(sc);
+      if (mt > m_run[hh]) {  // wave-uniform
+        const float corr = fast_exp2(m_run[hh] - mt);
+        z[hh] *= corr;
+#pragma unroll
+        for (int k = 0; k < CV; ++k) acc[hh][k] *= corr;
+        m_run[hh] = mt;
+      }
+      const float p = fast_exp2(sc - m_run[hh]);
+      z[hh] += p;
+#pragma unroll
+      for (int kv = 0; kv < KV; ++kv) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[hh][8 * kv + 2 * e] = fmaf(p, bf16_lo(cur.v[hh][kv][e]), acc[hh][8 * kv + 2 * e]);
+          acc[hh][8 * kv + 2 * e + 1] = fmaf(p, bf16_hi(cur.v[hh][kv][e]), acc[hh][8 * kv + 2 * e + 1]);
+        }
+      }
+    }
+  };
+
+  // Ring of NBUF page slots: while page p is computed, pages p+1 .. p+LOOK are
+  // in flight.  A slot is refilled LOOK steps after it was computed (NBUF =
+  // LOOK + 2), so the old and new contents of a slot never overlap and no
+  // register copies (which would wait for the loads in flight) are needed.
+  // Every trip computes exactly NBUF pages (pages past the split's end are
+  // masked) and every load is issued unconditionally (clamped to the split's
+  // last page); the next RoPE chunk is published at the end of the trip.  Both
+  // ways into the loop head thus leave the same loads outstanding, so the
+  // compiler's waits keep the ring's loads in flight.
+  if (lp0 < lp1) {
+    const int lp_end = lp0 + (lp1 - lp0 + NBUF - 1) / NBUF * NBUF;
+    Page ring[NBUF];
+    stage_load(0);
+#pragma unroll
+    for (int u = 0; u < LOOK; ++u) {
+      const int l = min(lp0 + u, lp1 - 1);
+      load_page(l, page_at(l), ring[u]);
+    }
+    stage_store(0);
+    __syncthreads();
+    stage_load(1);
+    for (int lp = lp0; lp < lp_end; lp += NBUF) {
+#pragma unroll
+      for (int u = 0; u < NBUF; ++u) {
+        const int l = min(lp + u + LOOK, lp1 - 1);
+        load_page(l, page_at(l), ring[(u + LOOK) % NBUF]);
+        compute_page(ring[u], lp + u);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const int c = (lp - lp0) / CH;  // chunk just computed
+      stage_store(c + 1);             // buffer of chunk c-1: every wave is past it
+      __syncthreads();
+      stage_load(c + 2);              // past the split's end: clamped rows, unused
+    }
+  }
+
+  // ---- reduce over the 16 token lanes of each row ----
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    z[hh] = sum_in_row(z[hh]);
+#pragma unroll
+    for (int k = 0; k < CV; ++k) acc[hh][k] = sum_in_row(acc[hh][k]);
+  }
+  if (errbits && threadIdx.x == 0) atomicOr(a.err, errbits);
+  const bool bad = __syncthreads_or(errbits != 0);
+
+  float *sh = (float *)(s_pt + a.pages_per_split);  // [waves][HPW][RV + 2]
+  float *mine = sh + (wave * HPW) * (RV + 2);
+
+  if (a.splits > 1) {  // partials for the merge launch
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      const int h = h0 + hh;
+      float *part = a.partials + (((long long)row * a.H + h) * a.splits + split) * (RV + 2);
+      if (n == 0) {
+#pragma unroll
+        for (int k = 0; k < CV; ++k) part[CV * g + k] = acc[hh][k];
+      }
+      if (lane == 0) {
+        part[RV] = m_run[hh];
+        part[RV + 1] = bad ? __builtin_nanf("") : z[hh];
+      }
+    }
+    return;
+  } else {
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      const float zz = bad ? __builtin_nanf("") : z[hh];
+      if (n == 0) {
+#pragma unroll
+        for (int k = 0; k < CV; ++k) mine[hh * (RV + 2) + CV * g + k] = acc[hh][k] / zz;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- V up-projection: out = mu_v,t + accn W_up,v,t^T ----
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    const int h = h0 + hh;
+    const char *w = a.wup_v + (long long)h * a.wup_head_stride_v * 2;
+    const uint16_t *mu = (const uint16_t *)a.mu_v + (long long)h * a.mu_head_stride;
+    const float *an = mine + hh * (RV + 2);
+    for (int e = lane; e < DH; e += 64) {
+      float o = bf16_to_f32(mu[e]);
+      const char *we = w + (long long)e * RV * 2;
+#pragma unroll
+      for (int r8 = 0; r8 < RV / 8; ++r8) {
+        const u32x4 v = *(const u32x4 *)(we + r8 * 16);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          o = fmaf(bf16_lo(v[k]), an[8 * r8 + 2 * k], o);
+          o = fmaf(bf16_hi(v[k]), an[8 * r8 + 2 * k + 1], o);
+        }
+      }
+      ((uint16_t *)a.out)[((long long)row * a.H + h) * DH + e] = (uint16_t)f32_to_bf16(o);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- dispatch
+
+namespace {
+template <int DH, int RK, int RV, int HPW, int NW>
+hipError_t go_g(const AttnArgs &a, hipStream_t stream) {
+  static bool lds_raised = false;  // allow more than the default 64 KiB of LDS once per kernel
+  if (!lds_raised) {
+    const hipError_t e = hipFuncSetAttribute((const void *)decode_g_kernel<DH, RK, RV, HPW, NW>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 1024);
+    if (e != hipSuccess) return e;
+    lds_raised = true;
+  }
+  const dim3 grid((unsigned)(a.rows * a.head_groups * a.splits));
+  const dim3 block((unsigned)(64 * NW));
+  constexpr int TS = (LLA_DECODE_LOOK + 2) * kPage * (DH / 8);  // one chunk = ring
+  constexpr int TSB = (TS + 64 * NW - 1) / (64 * NW) * (64 * NW);
+  const size_t shmem = 2 * (size_t)TSB * 16 + sizeof(int) * a.pages_per_split +
+                       sizeof(float) * NW * HPW * (RV + 2);
+  hipLaunchKernelGGL((decode_g_kernel<DH, RK, RV, HPW, NW>), grid, block, shmem, stream, a);
+  return hipGetLastError();
+}
+}  // namespace
+
+// (d_head, r_k, r_v, heads per wave, waves per workgroup)
+#define LLA_DECODE_G_SHAPES(X) \
+  X(64, 16, 32, 1, 2)          \
+  X(64, 16, 32, 2, 8)          \
+  X(128, 16, 32, 1, 2)         \
+  X(128, 16, 32, 2, 2)         \
+  X(128, 16, 32, 1, 8)         \
+  X(128, 16, 32, 2, 8)         \
+  X(128, 32, 64, 1, 8)         \
+  X(128, 96, 160, 1, 8)
+
+bool decode_g_supported(int d_head, int r_k, int r_v, int hpw, int waves) {
+#define X(DH, RK, RV, HPW, NW) \
+  if (d_head == DH && r_k == RK && r_v == RV && hpw == HPW && waves == NW) return true;
+  LLA_DECODE_G_SHAPES(X)
+#undef X
+  return false;
+}
+
+hipError_t launch_decode_g(int d_head, int r_k, int r_v, const AttnArgs &a, hipStream_t stream) {
+#define X(DH, RK, RV, HPW, NW)                                                                \
+  if (d_head == DH && r_k == RK && r_v == RV && a.heads_per_wave == HPW && a.waves == NW) \
+    return go_g<DH, RK, RV, HPW, NW>(a, stream);
+  LLA_DECODE_G_SHAPES(X)
+#undef X
+  return hipErrorInvalidConfiguration;
+}
+
+}  // namespace lla

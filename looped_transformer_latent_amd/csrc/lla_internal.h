@@ -39,7 +39,6 @@ struct AttnArgs {
   int chunk_pages;                       // pages per LDS-staged RoPE chunk
   float qscale;                          // softmax scale * log2(e)
   int *err;
-  int *counters;                         // [rows][head_groups], zero between calls
   float *partials;                       // [rows][H][splits][r_v + 2]
 };
 
@@ -62,10 +61,13 @@ struct EncodeArgs {
 bool decode_supported(int dtype, int d_head, int r_k, int r_v, int heads_per_wave, int waves);
 hipError_t launch_decode(int dtype, int d_head, int r_k, int r_v, const AttnArgs &a,
                          hipStream_t stream);
+bool decode_g_supported(int d_head, int r_k, int r_v, int heads_per_wave, int waves);
+hipError_t launch_decode_g(int d_head, int r_k, int r_v, const AttnArgs &a, hipStream_t stream);
 bool decode2d_supported(int dtype, int d_head, int r_k, int r_v);
 hipError_t launch_decode2d(int d_head, int r_k, int r_v, const AttnArgs &a, hipStream_t stream);
 bool encode_supported(int dtype, int width, int r_k, int r_v);
 hipError_t launch_encode(int dtype, int r_k, int r_v, const EncodeArgs &a, hipStream_t stream);
+hipError_t launch_merge(int dtype, int d_head, int r_v, const AttnArgs &a, hipStream_t stream);
 hipError_t launch_rope_table(int n_pos, int d_head, double base, float *table, hipStream_t s);
 
 }  // namespace lla
