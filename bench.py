@@ -28,7 +28,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
-DECODE_SOURCES = ("lla_decode.hip", "lla_device.h", "lla_internal.h")
+DECODE_SOURCES = ("lla_decode_g.hip", "lla_device.h", "lla_internal.h")
 
 
 def kernel_source_digest(names=DECODE_SOURCES) -> str:
@@ -40,11 +40,11 @@ def kernel_source_digest(names=DECODE_SOURCES) -> str:
     return h.hexdigest()
 
 
-def profiled_traffic(workload: str):
+def profiled_traffic(workload: str, kernel: str = "decode_g_kernel"):
     """HBM bytes per decode launch from the committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE summary of this workload, or None when the kernel sources have
     changed since those counters were taken (or no summary exists)."""
-    path = os.path.join(ROOT, "profiles", f"decode_ph_kernel_{workload}.md")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}.md")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -215,9 +215,10 @@ def main():
     bytes_per_launch = w.batch * w.ctx * w.read_bytes()
     if w.variant == wl.PER_HEAD:
         achieved = bytes_per_launch / (kern_avg_ms / 1e3) / 1e9
-        roof = {"kernel": "decode_ph_kernel", "bound": "hbm", "achieved": achieved,
+        kname = "decode_g_kernel" if w.dtype == wl.BF16 else "decode_ph_kernel"
+        roof = {"kernel": kname, "bound": "hbm", "achieved": achieved,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                "traffic": profiled_traffic(w.name), "traffic_unit": "HBM bytes per launch (rocprofv3)",
+                "traffic": profiled_traffic(w.name, kname), "traffic_unit": "HBM bytes per launch (rocprofv3)",
                 "algorithmic_bytes_per_launch": bytes_per_launch, "avg_launch_ms": kern_avg_ms}
     else:
         # LLA-2D is bound by the matrix cores: per token and head, rebuilding K is
