@@ -1,4 +1,4 @@
-// Fused split-K latent-cache decode attention for LLA (gfx950, wave64).
+// Per-head LLA decode attention for fp32 storage (gfx950, wave64).
 //
 // What it computes (cc.laoqi.cc close reading, 方法 items 1-3; gist.science
 // "Kernmechanismus"): for one (layer, loop t) and every query row,
@@ -8,7 +8,9 @@
 // The V side is exact by linearity of eq. (3): it is accumulated in latent
 // space (r_v wide) and up-projected once per (row, head).
 //
-// How, per (row, head group, split) workgroup; one wave per HPW heads:
+// fp32 storage is the exactness path (1e-4 relative); bf16 storage runs
+// decode_g_kernel (lla_decode_g.hip).  How, per (row, head group, split)
+// workgroup, one wave per HPW heads:
 //  * Prologue -- fold the rotated query into the K decoder.  For RoPE pair i
 //    (elements a = i, b = i + d/2) with q' = R(q_pos) q * scale * log2(e):
 //      X_i(j) = q'_a k_hat_a + q'_b k_hat_b = alpha_i + sum_r A[i][r] c_r
@@ -16,12 +18,12 @@
 //    with A[i][r] = q'_a W[a][r] + q'_b W[b][r], B[i][r] = q'_b W[a][r] - q'_a W[b][r],
 //    alpha_i = q'_a mu_a + q'_b mu_b, beta_i = q'_b mu_a - q'_a mu_b, and then
 //      s_j * log2(e) = sum_i cos(j w_i) X_i(j) + sin(j w_i) Y_i(j).
-//    [A alpha; B beta] (d x (r_k + 1)) is held in registers as MFMA A-operands
-//    (bf16: alpha/beta split into hi + lo bf16 parts; fp32: exact).
+//    [A alpha; B beta] (d x (r_k + 1)) is held in registers as the A-operands of
+//    v_mfma_f32_16x16x4f32 (exact fp32 products, alpha / beta in the last K-step).
 //  * Per 16-token page -- one MFMA 16x16 tile gives X (or Y) for 16 pair
-//    indices x 16 tokens; the latent tile [c_k, 1, 1] is the B-operand, read
-//    straight from the paged pool with 16-byte loads.  Each lane then needs
-//    cos/sin for its 16 pair indices and its token only: 2 FMAs per (i, token).
+//    indices x 16 tokens; the latent tile [c_k, 1] is the B-operand, read
+//    straight from the paged pool.  Each lane then needs cos/sin for its 16
+//    pair indices and its token only: 2 FMAs per (i, token).
 //  * Online softmax in base 2 with deferred rescaling; V accumulated as
 //    sum_j p_j c_v,j in fp32 registers (lane = token x r_v/4 chunk).
 //  * With one split the workgroup normalises and up-projects through W_up,v,t
@@ -32,42 +34,11 @@
 
 namespace lla {
 
-template <bool BF>
-struct St;
-template <>
-struct St<true> {
-  using Opnd = bf16x8;
-  static constexpr int esz = 2;
-  __device__ static f32x4 mma(Opnd a, Opnd b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-  }
-  __device__ static float ld(const char *p, long long i) {
-    return bf16_to_f32(((const uint16_t *)p)[i]);
-  }
-};
-template <>
-struct St<false> {
-  using Opnd = float;
-  static constexpr int esz = 4;
-  __device__ static f32x4 mma(Opnd a, Opnd b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-  }
-  __device__ static float ld(const char *p, long long i) { return ((const float *)p)[i]; }
-};
-
-// Number of MFMA K-steps for r_k latent columns plus the constant column(s).
-template <bool BF, int RK>
-constexpr int ksteps() {
-  return BF ? (RK + 2 + 31) / 32 : RK / 4 + 1;
-}
-
-template <bool BF, int DH, int RK, int RV, int HPW, int NW>
+template <int DH, int RK, int RV, int HPW, int NW>
 __global__ __launch_bounds__(64 * NW) void decode_ph_kernel(AttnArgs a) {
-  using S = St<BF>;
-  using Op = typename S::Opnd;
-  constexpr int NT = DH / 32;         // tile pairs: pair indices [16t, 16t + 16)
-  constexpr int KS = ksteps<BF, RK>();
-  constexpr int CV = RV / 4;          // V latent elements per lane per token
+  constexpr int NT = DH / 32;   // tile pairs: pair indices [16t, 16t + 16)
+  constexpr int KS = RK / 4 + 1;  // K-steps of 4 latent columns, plus the constant column
+  constexpr int CV = RV / 4;    // V latent elements per lane per token
   constexpr int HALF = DH / 2;
   static_assert(DH % 32 == 0 && RK % 16 == 0 && RV % 32 == 0, "shape");
 
@@ -102,64 +73,40 @@ __global__ __launch_bounds__(64 * NW) void decode_ph_kernel(AttnArgs a) {
   const int h0 = (hg * a.waves + wave) * HPW;
 
   // ---- prologue: query-folded K decoder as MFMA A-operands ----
-  Op A[HPW][NT][2][KS];
+  // Lane (g, n) holds row i = 16 t + n; K-step ks < RK/4 is latent column
+  // (RK/4) g + ks, the last K-step carries alpha / beta in lane group g = 0.
+  float A[HPW][NT][2][KS];
   {
     const float *rq = a.rope + (long long)qp * DH;
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
       const int h = h0 + hh;
-      const char *qrow = (const char *)a.q + ((long long)row * a.H + h) * DH * S::esz;
-      const char *w = a.wup_k + (long long)h * a.wup_head_stride_k * S::esz;
-      const char *mu = a.mu_k + (long long)h * a.mu_head_stride * S::esz;
+      const float *qrow = (const float *)a.q + ((long long)row * a.H + h) * DH;
+      const float *w = (const float *)a.wup_k + (long long)h * a.wup_head_stride_k;
+      const float *mu = (const float *)a.mu_k + (long long)h * a.mu_head_stride;
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const int i = 16 * t + n;
         const float c = rq[2 * i], s = rq[2 * i + 1];
-        const float qa = S::ld(qrow, i), qb = S::ld(qrow, i + HALF);
+        const float qa = qrow[i], qb = qrow[i + HALF];
         const float pa = a.qscale * (qa * c - qb * s);
         const float pb = a.qscale * (qa * s + qb * c);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          if constexpr (BF) {
-            const int r0 = 32 * ks + 8 * g;
-            u32x4 x = {0, 0, 0, 0}, y = {0, 0, 0, 0};
-            if (r0 + 8 <= RK) {
-              const u32x4 wa = *(const u32x4 *)(w + ((long long)i * RK + r0) * 2);
-              const u32x4 wb = *(const u32x4 *)(w + ((long long)(i + HALF) * RK + r0) * 2);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const float a0 = bf16_lo(wa[e]), a1 = bf16_hi(wa[e]);
-                const float b0 = bf16_lo(wb[e]), b1 = bf16_hi(wb[e]);
-                x[e] = pack_bf16(pa * a0 + pb * b0, pa * a1 + pb * b1);
-                y[e] = pack_bf16(pb * a0 - pa * b0, pb * a1 - pa * b1);
-              }
-            } else if (r0 == RK) {
-              const float ma = S::ld(mu, i), mb = S::ld(mu, i + HALF);
-              const float al = pa * ma + pb * mb, be = pb * ma - pa * mb;
-              const uint32_t ah = f32_to_bf16(al), bh = f32_to_bf16(be);
-              const uint32_t alo = f32_to_bf16(al - bf16_to_f32(ah));
-              const uint32_t blo = f32_to_bf16(be - bf16_to_f32(bh));
-              x[0] = ah | (alo << 16);
-              y[0] = bh | (blo << 16);
-            }
-            A[hh][t][0][ks] = as_bf16x8(x);
-            A[hh][t][1][ks] = as_bf16x8(y);
-          } else {
-            float x = 0.f, y = 0.f;
-            if (ks < RK / 4) {
-              const int r = (RK / 4) * g + ks;
-              const float wa = S::ld(w, (long long)i * RK + r);
-              const float wb = S::ld(w, (long long)(i + HALF) * RK + r);
-              x = pa * wa + pb * wb;
-              y = pb * wa - pa * wb;
-            } else if (g == 0) {
-              const float ma = S::ld(mu, i), mb = S::ld(mu, i + HALF);
-              x = pa * ma + pb * mb;
-              y = pb * ma - pa * mb;
-            }
-            A[hh][t][0][ks] = x;
-            A[hh][t][1][ks] = y;
+          float x = 0.f, y = 0.f;
+          if (ks < RK / 4) {
+            const int r = (RK / 4) * g + ks;
+            const float wa = w[(long long)i * RK + r];
+            const float wb = w[(long long)(i + HALF) * RK + r];
+            x = pa * wa + pb * wb;
+            y = pb * wa - pa * wb;
+          } else if (g == 0) {
+            const float ma = mu[i], mb = mu[i + HALF];
+            x = pa * ma + pb * mb;
+            y = pb * ma - pa * mb;
           }
+          A[hh][t][0][ks] = x;
+          A[hh][t][1][ks] = y;
         }
       }
     }
@@ -174,39 +121,26 @@ __global__ __launch_bounds__(64 * NW) void decode_ph_kernel(AttnArgs a) {
     for (int k = 0; k < CV; ++k) acc[hh][k] = 0.f;
   }
 
-  // ---- main loop over this split's pages, software-pipelined by one page ----
-  // Per page, lane (g, n) loads: cos/sin of its 16 pair indices at its token's
-  // position (2*NT x 16 B), and per head its K B-operand (KS x 16 B) and its
-  // r_v/4-wide V chunk.  Tokens past ctx_len (only on the last page) read the
-  // last valid row instead, so every loaded value is real data; their scores
-  // are forced to -inf and their weights are exactly zero.
-  constexpr int KV = BF ? CV / 8 : CV / 4;  // 16-byte V loads per lane per head
-  constexpr int KK = BF ? KS : RK / 16;     // 16-byte K loads per lane per head
-  // Two heads with r_k = 16 (bf16): one 64-lane load fetches both heads' K rows
-  // (lanes 0-31 head h0, lanes 32-63 head h0+1, each lane one 16-byte chunk of
-  // its token's row); a permlane32 swap later splits them into the two MFMA
-  // B-operands, bringing in the constant column from the other half.
-  constexpr bool KPAIR = BF && HPW == 2 && RK == 16;
+  // Per page, lane (g, n) loads latent row n: per head its RK/4 K columns
+  // (RK/4) g .. (RK/4) g + RK/4 - 1 and its CV V columns CV g ...  Tokens past
+  // ctx_len (last page only) read the last valid row instead; their scores are
+  // forced to -inf and their weights are exactly zero.
+  constexpr int KV = CV / 4;   // 16-byte V loads per lane per head
+  constexpr int KK = RK / 16;  // 16-byte K loads per lane per head
   struct Page {
-    u32x4 k[KPAIR ? 1 : HPW][KK];
+    u32x4 k[HPW][KK];
     u32x4 v[HPW][KV];
     int ok;
     int last;  // last valid row of this page (15 unless the page is the last one)
   };
-  // LDS: [trig: 2 chunk buffers][page-table entries of the split][epilogue floats]
-  // RoPE rows in LDS: fp32 (cos, sin) pairs for fp32 storage; for bf16 storage
-  // fp16 pairs (4 bytes), read straight into mixed-precision FMAs.  fp16 keeps
-  // cos/sin to 2^-12 absolute, adding ~3e-4 relative error to the scores -- far
-  // inside what bf16 latents already carry -- and halves registers and LDS.
-  constexpr bool T16 = BF;
-  constexpr int SPR = T16 ? DH / 8 : DH / 4;  // 16-byte LDS slots per position row
-  constexpr int SWZ = SPR < 16 ? SPR - 1 : 15; // XOR swizzle mask (row index low bits)
+  // LDS: [RoPE rows: 2 chunk buffers][page-table entries of the split][epilogue]
+  constexpr int SPR = DH / 4;                   // 16-byte slots per position row (fp32 pairs)
+  constexpr int SWZ = SPR < 16 ? SPR - 1 : 15;  // XOR swizzle mask (row index low bits)
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int LOOK = LLA_DECODE_LOOK;  // pages in flight beyond the one computed
   constexpr int NBUF = LOOK + 2;        // page ring slots (see the main loop)
-  constexpr int CH = NBUF;              // pages per trig chunk: one trip round the ring
+  constexpr int CH = NBUF;              // pages per RoPE chunk: one trip round the ring
   constexpr int TS = CH * kPage * SPR;  // 16-byte slots of one chunk
-  constexpr int GL = T16 ? 2 : 1;       // global 16-byte loads per LDS slot
   constexpr int SLOTS = (TS + NTH - 1) / NTH;  // slots staged per thread
   constexpr int TSB = SLOTS * NTH;      // slots per chunk buffer (surplus = padding)
   char *s_trig = smem;
@@ -218,25 +152,21 @@ __global__ __launch_bounds__(64 * NW) void decode_ph_kernel(AttnArgs a) {
   }
   auto page_at = [&](int lp) -> int { return __builtin_amdgcn_readfirstlane(s_pt[lp - lp0]); };
 
-  // Trig staging.  Chunk c covers pages [lp0 + c*CH, lp0 + (c+1)*CH); row R of a
+  // RoPE staging.  Chunk c covers pages [lp0 + c*CH, lp0 + (c+1)*CH); row R of a
   // chunk buffer holds the table row of token position 16*(lp0 + c*CH) + R.
-  // Within a row, logical 16-byte slot `ls` is stored at ls ^ (R % 16 & SWZ), so
-  // the 16 lanes of a row-group -- which read the same logical slot of 16
-  // consecutive positions -- hit different bank groups.  A logical slot holds 4
-  // pairs; in fp32 that is 2 slots of the global table, so each staged slot
-  // takes two 16-byte global loads.  Loads are unconditional (clamped slot) so
-  // the number in flight is the same on every path.
+  // Within a row, 16-byte slot `ls` (pairs 2 ls, 2 ls + 1) is stored at
+  // ls ^ (R % 16 & SWZ), so the 16 lanes of a row-group -- which read the same
+  // slot of 16 consecutive positions -- hit different bank groups.  Loads are
+  // unconditional (clamped slot) so the number in flight is the same on every path.
   const char *rope_b = (const char *)a.rope;
-  f32x4 stg[SLOTS][GL];
+  f32x4 stg[SLOTS];
   auto stage_load = [&](int c) {
 #pragma unroll
     for (int j = 0; j < SLOTS; ++j) {
       const int q = min((int)threadIdx.x + j * NTH, TS - 1);
       const int R = q / SPR, ps = q % SPR, rn = R % kPage;
       const int pos = min((lp0 + c * CH + R / kPage) * kPage + rn, ctx - 1);
-      const char *src = rope_b + (long long)pos * (DH * 4) + (ps ^ (rn & SWZ)) * 16 * GL;
-#pragma unroll
-      for (int u = 0; u < GL; ++u) stg[j][u] = *(const f32x4 *)(src + 16 * u);
+      stg[j] = *(const f32x4 *)(rope_b + (long long)pos * (DH * 4) + (ps ^ (rn & SWZ)) * 16);
     }
   };
   auto stage_store = [&](int c) {
@@ -244,20 +174,7 @@ __global__ __launch_bounds__(64 * NW) void decode_ph_kernel(AttnArgs a) {
 #pragma unroll
     for (int j = 0; j < SLOTS; ++j) {
       const int q = threadIdx.x + j * NTH;  // q >= TS lands in the buffer's padding
-      {
-        if constexpr (T16) {
-          u32x4 h;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float cval = stg[j][e >> 1][(e & 1) * 2], sval = stg[j][e >> 1][(e & 1) * 2 + 1];
-            const _Float16 ch = (_Float16)cval, sh = (_Float16)sval;  // round to nearest even
-            h[e] = (uint32_t)__builtin_bit_cast(uint16_t, ch) | ((uint32_t)__builtin_bit_cast(uint16_t, sh) << 16);
-          }
-          *(u32x4 *)(dst + q * 16) = h;
-        } else {
-          *(f32x4 *)(dst + q * 16) = stg[j][0];
-        }
-      }
+      *(f32x4 *)(dst + q * 16) = stg[j];
     }
   };
 
@@ -268,35 +185,16 @@ __global__ __launch_bounds__(64 * NW) void decode_ph_kernel(AttnArgs a) {
     const int row_n = min(n, pg.last);
     // uniform page bases (scalar registers) + 32-bit per-lane offsets; latents
     // are read exactly once per call, so they are loaded non-temporally
-    const char *kpage = a.k_pool + pp * a.pool_page_stride_k * S::esz;
-    const char *vpage = a.v_pool + pp * a.pool_page_stride_v * S::esz;
-    if constexpr (KPAIR) {
-      const uint32_t koff =
-          (uint32_t)(((h0 + (g >> 1)) * a.pool_head_stride_k + row_n * RK + 8 * (g & 1)) * 2);
-      pg.k[0][0] = *(const u32x4 *)(kpage + koff);
-    }
+    const char *kpage = a.k_pool + pp * a.pool_page_stride_k * 4;
+    const char *vpage = a.v_pool + pp * a.pool_page_stride_v * 4;
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
       const int h = h0 + hh;
-      const uint32_t koff = (uint32_t)((h * a.pool_head_stride_k + row_n * RK) * S::esz);
-      const uint32_t voff = (uint32_t)((h * a.pool_head_stride_v + row_n * RV + CV * g) * S::esz);
-      if constexpr (KPAIR) {
-      } else if constexpr (BF) {
+      const uint32_t koff = (uint32_t)((h * a.pool_head_stride_k + row_n * RK) * 4);
+      const uint32_t voff = (uint32_t)((h * a.pool_head_stride_v + row_n * RV + CV * g) * 4);
 #pragma unroll
-        for (int ks = 0; ks < KK; ++ks) {
-          const int r0 = 32 * ks + 8 * g;
-          if (r0 + 8 <= RK) {
-            pg.k[hh][ks] = __builtin_nontemporal_load((const u32x4 *)(kpage + koff + r0 * 2));
-          } else {  // constant column: bf16 (1, 1) picks up alpha hi + lo
-            const u32x4 c = {r0 == RK ? 0x3F803F80u : 0u, 0u, 0u, 0u};
-            pg.k[hh][ks] = c;
-          }
-        }
-      } else {
-#pragma unroll
-        for (int k4 = 0; k4 < KK; ++k4)
-          pg.k[hh][k4] = __builtin_nontemporal_load((const u32x4 *)(kpage + koff + ((RK / 4) * g + 4 * k4) * 4));
-      }
+      for (int k4 = 0; k4 < KK; ++k4)
+        pg.k[hh][k4] = __builtin_nontemporal_load((const u32x4 *)(kpage + koff + ((RK / 4) * g + 4 * k4) * 4));
 #pragma unroll
       for (int kv = 0; kv < KV; ++kv)
         pg.v[hh][kv] = __builtin_nontemporal_load((const u32x4 *)(vpage + voff + kv * 16));
@@ -312,48 +210,22 @@ __global__ __launch_bounds__(64 * NW) void decode_ph_kernel(AttnArgs a) {
     const int row_n = min(n, cur.last);
     const char *tb = s_trig + (((lp - lp0) / CH) & 1) * TSB * 16 +
                      (((lp - lp0) % CH) * kPage + row_n) * SPR * 16;
-    Op bpair[2][KS];
-    if constexpr (KPAIR) {
-      // lanes 0-15 / 32-47 of the constant hold bf16 (1, 1): after the swap they
-      // sit in the g = 2 lanes of both operands; g = 3 lanes get zeros.
-      const uint32_t one = ((lane >> 4) & 1) ? 0u : 0x3F803F80u;
-      u32x4 b0, b1;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const auto sw = __builtin_amdgcn_permlane32_swap(cur.k[0][0][e], e == 0 ? one : 0u, false, false);
-        b0[e] = sw[0];
-        b1[e] = sw[1];
-      }
-      bpair[0][0] = as_bf16x8(b0);
-      bpair[1][0] = as_bf16x8(b1);
-    }
-    // cos/sin of this lane's 16 pair indices at its token's position: fp16
-    // pairs (bf16 storage) feed mixed-precision FMAs directly; fp32 otherwise.
-    u32x4 th[NT];
+    // cos / sin of this lane's 16 pair indices 16 t + 4 g + e at its token
     float tc[NT][4], ts[NT][4];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      if constexpr (T16) {
-        th[t] = *(const u32x4 *)(tb + (((4 * t + g) ^ (row_n & SWZ)) * 16));
-      } else {
-        const int ls = 8 * t + 2 * g;
-        const f32x4 c0 = *(const f32x4 *)(tb + ((ls ^ (row_n & SWZ)) * 16));
-        const f32x4 c1 = *(const f32x4 *)(tb + (((ls + 1) ^ (row_n & SWZ)) * 16));
-        tc[t][0] = c0[0]; ts[t][0] = c0[1]; tc[t][1] = c0[2]; ts[t][1] = c0[3];
-        tc[t][2] = c1[0]; ts[t][2] = c1[1]; tc[t][3] = c1[2]; ts[t][3] = c1[3];
-      }
+      const int ls = 8 * t + 2 * g;
+      const f32x4 c0 = *(const f32x4 *)(tb + ((ls ^ (row_n & SWZ)) * 16));
+      const f32x4 c1 = *(const f32x4 *)(tb + (((ls + 1) ^ (row_n & SWZ)) * 16));
+      tc[t][0] = c0[0]; ts[t][0] = c0[1]; tc[t][1] = c0[2]; ts[t][1] = c0[3];
+      tc[t][2] = c1[0]; ts[t][2] = c1[1]; tc[t][3] = c1[2]; ts[t][3] = c1[3];
     }
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
-      Op bk[KS];
-      if constexpr (BF) {
+      float bk[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) bk[ks] = KPAIR ? bpair[hh][ks] : as_bf16x8(cur.k[hh][ks]);
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < RK / 4; ++ks) bk[ks] = __uint_as_float(cur.k[hh][ks / 4][ks % 4]);
-        bk[RK / 4] = (g == 0) ? 1.f : 0.f;
-      }
+      for (int ks = 0; ks < RK / 4; ++ks) bk[ks] = __uint_as_float(cur.k[hh][ks / 4][ks % 4]);
+      bk[RK / 4] = (g == 0) ? 1.f : 0.f;
       // X / Y tiles: rows = pair indices 16t + 4g + e, column = token n
       float sc0 = 0.f, sc1 = 0.f;
 #pragma unroll
@@ -361,18 +233,13 @@ __global__ __launch_bounds__(64 * NW) void decode_ph_kernel(AttnArgs a) {
         f32x4 X = {0.f, 0.f, 0.f, 0.f}, Y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          X = S::mma(A[hh][t][0][ks], bk[ks], X);
-          Y = S::mma(A[hh][t][1][ks], bk[ks], Y);
+          X = __builtin_amdgcn_mfma_f32_16x16x4f32(A[hh][t][0][ks], bk[ks], X, 0, 0, 0);
+          Y = __builtin_amdgcn_mfma_f32_16x16x4f32(A[hh][t][1][ks], bk[ks], Y, 0, 0, 0);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          if constexpr (T16) {  // the compiler emits v_fma_mix_f32 (no conversion)
-            sc0 = fmaf((float)__builtin_bit_cast(_Float16, (uint16_t)(th[t][e] & 0xFFFFu)), X[e], sc0);
-            sc1 = fmaf((float)__builtin_bit_cast(_Float16, (uint16_t)(th[t][e] >> 16)), Y[e], sc1);
-          } else {
-            sc0 = fmaf(tc[t][e], X[e], sc0);
-            sc1 = fmaf(ts[t][e], Y[e], sc1);
-          }
+          sc0 = fmaf(tc[t][e], X[e], sc0);
+          sc1 = fmaf(ts[t][e], Y[e], sc1);
         }
       }
       float sc = sum_across_rows(sc0 + sc1);
@@ -387,40 +254,21 @@ __global__ __launch_bounds__(64 * NW) void decode_ph_kernel(AttnArgs a) {
       }
       const float p = fast_exp2(sc - m_run[hh]);
       z[hh] += p;
-      if constexpr (BF) {
 #pragma unroll
-        for (int kv = 0; kv < KV; ++kv) {
+      for (int kv = 0; kv < KV; ++kv) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc[hh][8 * kv + 2 * e] = fmaf(p, bf16_lo(cur.v[hh][kv][e]), acc[hh][8 * kv + 2 * e]);
-            acc[hh][8 * kv + 2 * e + 1] = fmaf(p, bf16_hi(cur.v[hh][kv][e]), acc[hh][8 * kv + 2 * e + 1]);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int kv = 0; kv < KV; ++kv) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            acc[hh][4 * kv + e] = fmaf(p, __uint_as_float(cur.v[hh][kv][e]), acc[hh][4 * kv + e]);
-        }
+        for (int e = 0; e < 4; ++e)
+          acc[hh][4 * kv + e] = fmaf(p, __uint_as_float(cur.v[hh][kv][e]), acc[hh][4 * kv + e]);
       }
     }
   };
 
-  // Ping-pong over two page buffers.  Every half-iteration issues exactly one
-  // page of latent loads (past the end it re-reads the split's last page, which
-  // is never computed), so each compute has the next page's loads in flight.
-  // At a chunk boundary all waves drain, store the staged trig chunk to LDS,
-  // synchronise, and start staging the chunk after it.
   // Ring of NBUF page slots: while page p is computed, pages p+1 .. p+LOOK are
   // in flight.  A slot is refilled LOOK steps after it was computed (NBUF =
-  // LOOK + 2), so the old and new contents of a slot never overlap and no
-  // register copies (which would wait for the loads in flight) are needed.
-  // Every trip computes exactly NBUF pages (pages past the split's end are
-  // masked) and every load is issued unconditionally (clamped to the split's
-  // last page); the next RoPE chunk is published at the end of the trip.  Both
-  // ways into the loop head thus leave the same loads outstanding, so the
-  // compiler's waits keep the ring's loads in flight.
+  // LOOK + 2), so the old and new contents of a slot never overlap.  Every trip
+  // computes exactly NBUF pages (pages past the split's end are masked) and
+  // every load is issued unconditionally (clamped to the split's last page);
+  // the next RoPE chunk is published at the end of the trip.
   if (lp0 < lp1) {
     const int lp_end = lp0 + (lp1 - lp0 + NBUF - 1) / NBUF * NBUF;
     Page ring[NBUF];
@@ -455,10 +303,7 @@ __global__ __launch_bounds__(64 * NW) void decode_ph_kernel(AttnArgs a) {
     for (int k = 0; k < CV; ++k) acc[hh][k] = sum_in_row(acc[hh][k]);
   }
   if (errbits && threadIdx.x == 0) atomicOr(a.err, errbits);
-  const bool bad = errbits != 0;
-
-  float *sh = (float *)(s_pt + a.pages_per_split);  // [waves][HPW][RV + 2]
-  float *mine = sh + (wave * HPW) * (RV + 2);
+  const bool bad = __syncthreads_or(errbits != 0);
 
   if (a.splits > 1) {  // partials for the merge launch
 #pragma unroll
@@ -475,14 +320,15 @@ __global__ __launch_bounds__(64 * NW) void decode_ph_kernel(AttnArgs a) {
       }
     }
     return;
-  } else {
+  }
+
+  float *mine = (float *)(s_pt + a.pages_per_split) + (wave * HPW) * (RV + 2);  // [waves][HPW][RV + 2]
 #pragma unroll
-    for (int hh = 0; hh < HPW; ++hh) {
-      const float zz = bad ? __builtin_nanf("") : z[hh];
-      if (n == 0) {
+  for (int hh = 0; hh < HPW; ++hh) {
+    const float zz = bad ? __builtin_nanf("") : z[hh];
+    if (n == 0) {
 #pragma unroll
-        for (int k = 0; k < CV; ++k) mine[hh * (RV + 2) + CV * g + k] = acc[hh][k] / zz;
-      }
+      for (int k = 0; k < CV; ++k) mine[hh * (RV + 2) + CV * g + k] = acc[hh][k] / zz;
     }
   }
   __syncthreads();
@@ -491,32 +337,19 @@ __global__ __launch_bounds__(64 * NW) void decode_ph_kernel(AttnArgs a) {
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
     const int h = h0 + hh;
-    const char *w = a.wup_v + (long long)h * a.wup_head_stride_v * S::esz;
-    const char *mu = a.mu_v + (long long)h * a.mu_head_stride * S::esz;
+    const float *w = (const float *)a.wup_v + (long long)h * a.wup_head_stride_v;
+    const float *mu = (const float *)a.mu_v + (long long)h * a.mu_head_stride;
     const float *an = mine + hh * (RV + 2);
     for (int e = lane; e < DH; e += 64) {
-      float o = S::ld(mu, e);
-      const char *we = w + (long long)e * RV * S::esz;
-      if constexpr (BF) {
+      float o = mu[e];
+      const float *we = w + (long long)e * RV;
 #pragma unroll
-        for (int r8 = 0; r8 < RV / 8; ++r8) {
-          const u32x4 v = *(const u32x4 *)(we + r8 * 16);
+      for (int r4 = 0; r4 < RV / 4; ++r4) {
+        const f32x4 v = *(const f32x4 *)(we + 4 * r4);
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            o = fmaf(bf16_lo(v[k]), an[8 * r8 + 2 * k], o);
-            o = fmaf(bf16_hi(v[k]), an[8 * r8 + 2 * k + 1], o);
-          }
-        }
-        ((uint16_t *)a.out)[((long long)row * a.H + h) * DH + e] = (uint16_t)f32_to_bf16(o);
-      } else {
-#pragma unroll
-        for (int r4 = 0; r4 < RV / 4; ++r4) {
-          const f32x4 v = *(const f32x4 *)(we + r4 * 16);
-#pragma unroll
-          for (int k = 0; k < 4; ++k) o = fmaf(v[k], an[4 * r4 + k], o);
-        }
-        ((float *)a.out)[((long long)row * a.H + h) * DH + e] = o;
+        for (int k = 0; k < 4; ++k) o = fmaf(v[k], an[4 * r4 + k], o);
       }
+      ((float *)a.out)[((long long)row * a.H + h) * DH + e] = o;
     }
   }
 }
@@ -524,44 +357,39 @@ __global__ __launch_bounds__(64 * NW) void decode_ph_kernel(AttnArgs a) {
 // ---------------------------------------------------------------- dispatch
 
 namespace {
-struct Shape {
-  int bf, dh, rk, rv, hpw;
-};
-template <bool BF, int DH, int RK, int RV, int HPW, int NW>
+template <int DH, int RK, int RV, int HPW, int NW>
 hipError_t go(const AttnArgs &a, hipStream_t stream) {
-  if (a.waves != NW) return hipErrorInvalidConfiguration;
   static bool lds_raised = false;  // allow more than the default 64 KiB of LDS once per kernel
   if (!lds_raised) {
-    const hipError_t e = hipFuncSetAttribute((const void *)decode_ph_kernel<BF, DH, RK, RV, HPW, NW>,
+    const hipError_t e = hipFuncSetAttribute((const void *)decode_ph_kernel<DH, RK, RV, HPW, NW>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 1024);
     if (e != hipSuccess) return e;
     lds_raised = true;
   }
   const dim3 grid((unsigned)(a.rows * a.head_groups * a.splits));
-  const dim3 block((unsigned)(64 * a.waves));
-  constexpr int TS = (LLA_DECODE_LOOK + 2) * kPage * (BF ? DH / 8 : DH / 4);  // one chunk = ring
+  const dim3 block((unsigned)(64 * NW));
+  constexpr int TS = (LLA_DECODE_LOOK + 2) * kPage * (DH / 4);  // one chunk = ring
   constexpr int TSB = (TS + 64 * NW - 1) / (64 * NW) * (64 * NW);
   const size_t shmem = 2 * (size_t)TSB * 16 + sizeof(int) * a.pages_per_split +
-                       sizeof(float) * a.waves * HPW * (RV + 2);
-  hipLaunchKernelGGL((decode_ph_kernel<BF, DH, RK, RV, HPW, NW>), grid, block, shmem, stream, a);
+                       sizeof(float) * NW * HPW * (RV + 2);
+  hipLaunchKernelGGL((decode_ph_kernel<DH, RK, RV, HPW, NW>), grid, block, shmem, stream, a);
   return hipGetLastError();
 }
 }  // namespace
 
-// (bf16?, d_head, r_k, r_v, heads per wave, waves per workgroup)
-#define LLA_DECODE_SHAPES(X)   \
-  X(false, 64, 16, 32, 1, 2)   \
-  X(false, 64, 16, 32, 1, 8)   \
-  X(false, 128, 16, 32, 1, 2)  \
-  X(false, 128, 16, 32, 1, 8)  \
-  X(false, 128, 96, 160, 1, 8)
+// fp32 storage: (d_head, r_k, r_v, heads per wave, waves per workgroup)
+#define LLA_DECODE_F32_SHAPES(X) \
+  X(64, 16, 32, 1, 2)            \
+  X(64, 16, 32, 1, 8)            \
+  X(128, 16, 32, 1, 2)           \
+  X(128, 16, 32, 1, 8)           \
+  X(128, 96, 160, 1, 8)
 
 bool decode_supported(int dtype, int d_head, int r_k, int r_v, int hpw, int waves) {
   if (dtype == LLA_BF16) return decode_g_supported(d_head, r_k, r_v, hpw, waves);
-  const bool bf = dtype == LLA_BF16;
-#define X(BF, DH, RK, RV, HPW, NW) \
-  if (bf == BF && d_head == DH && r_k == RK && r_v == RV && hpw == HPW && waves == NW) return true;
-  LLA_DECODE_SHAPES(X)
+#define X(DH, RK, RV, HPW, NW) \
+  if (d_head == DH && r_k == RK && r_v == RV && hpw == HPW && waves == NW) return true;
+  LLA_DECODE_F32_SHAPES(X)
 #undef X
   return false;
 }
@@ -569,12 +397,10 @@ bool decode_supported(int dtype, int d_head, int r_k, int r_v, int hpw, int wave
 hipError_t launch_decode(int dtype, int d_head, int r_k, int r_v, const AttnArgs &a,
                          hipStream_t stream) {
   if (dtype == LLA_BF16) return launch_decode_g(d_head, r_k, r_v, a, stream);
-  const bool bf = dtype == LLA_BF16;
-#define X(BF, DH, RK, RV, HPW, NW)                                                  \
-  if (bf == BF && d_head == DH && r_k == RK && r_v == RV && a.heads_per_wave == HPW && \
-      a.waves == NW)                                                                   \
-    return go<BF, DH, RK, RV, HPW, NW>(a, stream);
-  LLA_DECODE_SHAPES(X)
+#define X(DH, RK, RV, HPW, NW)                                                                \
+  if (d_head == DH && r_k == RK && r_v == RV && a.heads_per_wave == HPW && a.waves == NW) \
+    return go<DH, RK, RV, HPW, NW>(a, stream);
+  LLA_DECODE_F32_SHAPES(X)
 #undef X
   return hipErrorInvalidConfiguration;
 }
