@@ -28,7 +28,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
-DECODE_SOURCES = ("lla_decode_g.hip", "lla_device.h", "lla_internal.h")
+DECODE_SOURCES = ("lla_decode_g.hip", "lla_device.h", "lla_internal.h", "lla_api.hip")
 
 
 def kernel_source_digest(names=DECODE_SOURCES) -> str:

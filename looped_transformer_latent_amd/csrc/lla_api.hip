@@ -79,7 +79,7 @@ bool plan_attn(const lla_dims *d, long long rows, int max_ctx, AttnPlan *p) {
   // 8 waves of 1 head, or 2 waves for small head counts.
   const int H = d->H;
   int hpw = 0, waves = 0;
-  const int cand[4][2] = {{2, 8}, {1, 8}, {2, 2}, {1, 2}};
+  const int cand[5][2] = {{2, 8}, {1, 8}, {1, 4}, {2, 2}, {1, 2}};
   for (const auto &c : cand) {
     if (H % (c[0] * c[1]) == 0 && decode_supported(d->dtype, d->d_head, d->r_k, d->r_v, c[0], c[1])) {
       hpw = c[0];
@@ -94,7 +94,10 @@ bool plan_attn(const lla_dims *d, long long rows, int max_ctx, AttnPlan *p) {
   p->chunk_pages = kDecodeRing;
   const int pages = (max_ctx + kPage - 1) / kPage;
   const long long base = rows * p->head_groups;
-  long long s = (1024 + base - 1) / base;
+  // One split per row once the grid already holds two rounds of workgroups
+  // (one 8-wave workgroup fits a CU): no partials, no merge launch.  Below
+  // that, split the context until about 1024 workgroups exist.
+  long long s = base >= 512 ? 1 : (1024 + base - 1) / base;
   const long long smax = pages / 4 > 1 ? pages / 4 : 1;
   if (s > smax) s = smax;
   const long long smin = (pages + kMaxPagesPerSplit - 1) / kMaxPagesPerSplit;  // LDS staging bound

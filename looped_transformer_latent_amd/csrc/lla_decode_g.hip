@@ -44,8 +44,10 @@ __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
          ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
 }
 
+// NW = 4 runs one wave per SIMD (up to 512 registers): the shape with the
+// widest latents (r_k = 96, r_v = 160) needs them for its decoder and page ring.
 template <int DH, int RK, int RV, int HPW, int NW>
-__global__ __launch_bounds__(64 * NW) void decode_g_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * NW, NW == 4 ? 1 : 2) void decode_g_kernel(AttnArgs a) {
   constexpr int KS = DH / 32;   // K-steps: 16 RoPE pairs (32 cos / sin slots) each
   constexpr int RT = RK / 16;   // 16-column tiles of the latent
   constexpr int CV = RV / 4;    // V elements per lane per token
@@ -400,7 +402,7 @@ hipError_t go_g(const AttnArgs &a, hipStream_t stream) {
   X(128, 16, 32, 1, 8)         \
   X(128, 16, 32, 2, 8)         \
   X(128, 32, 64, 1, 8)         \
-  X(128, 96, 160, 1, 8)
+  X(128, 96, 160, 1, 4)
 
 bool decode_g_supported(int d_head, int r_k, int r_v, int hpw, int waves) {
 #define X(DH, RK, RV, HPW, NW) \
