@@ -127,6 +127,38 @@ def cpu_baseline(w, codec_h, pt_h, layer, loop, target_s):
                       f"fp64 C oracle, OpenMP over (sequence, head); {dt:.1f} s"}
 
 
+def cpu_encode_baseline(w, codec_h, layer, target_s):
+    """Time the fp64 oracle's encode + append on a bounded sample: tokens of one
+    layer (all heads), drawn from the same generator streams as the GPU's x."""
+    import oracle
+    from looped_transformer_latent_amd import gen
+    from looped_transformer_latent_amd import workloads as wl
+
+    one = dict(w.dims, D=1)
+    codec1 = {k: np.ascontiguousarray(v[layer:layer + 1]) for k, v in codec_h.items()}
+    inner = (w.H, w.T, w.d_head) if w.variant == wl.PER_HEAD else (w.T, w.H, w.d_head)
+
+    def run(n_tok):
+        pages = (n_tok + 15) // 16
+        shp = (1, 1, n_tok) + inner
+        xk = gen.normal(w.seed, wl.STREAMS["x_k"], shp)
+        xv = gen.normal(w.seed, wl.STREAMS["x_v"], shp)
+        kp = np.zeros((1, pages) + w.pool_shape("k")[2:], np.uint16)
+        vp = np.zeros((1, pages) + w.pool_shape("v")[2:], np.uint16)
+        pt = np.arange(pages, dtype=np.int32)[None]
+        t0 = time.perf_counter()
+        rc = oracle.encode(one, codec1, kp, vp, pt, xk, xv, np.zeros(1, np.int32), n_tok, 0, 1)
+        dt = time.perf_counter() - t0
+        assert rc == 0
+        return dt
+
+    t1 = run(16)
+    n = int(max(16, min(1 << 16, round(16 * target_s / max(t1, 1e-4)))))
+    dt = run(n)
+    return {"value": n / dt, "unit": "appended token-layers/s (all heads)", "cores": 1, "kind": "oracle",
+            "sample": f"{n} tokens of one layer, all {w.H} heads; fp64 C oracle (single thread); {dt:.1f} s"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -258,13 +290,18 @@ def main():
                  + w.D * w.groups * width * (w.r_k + w.r_v) * w.esize)
     enc_flops = 2 * tok * w.groups * width * (w.r_k + w.r_v)
     result["encode"] = {"kernel": "encode_mfma_kernel", "tokens_per_layer": w.batch * n_new,
-                        "layers": w.D, "avg_ms": enc_avg, "algorithmic_bytes": enc_bytes,
+                        "layers": w.D, "avg_ms": enc_avg,
+                        "value": tok / (enc_avg / 1e3), "unit": "appended token-layers/s (all heads)",
+                        "algorithmic_bytes": enc_bytes,
                         "achieved_gbs": enc_bytes / (enc_avg / 1e3) / 1e9,
                         "frac_hbm": enc_bytes / (enc_avg / 1e3) / 1e9 / HBM_PEAK_GBS,
                         "tflops": enc_flops / (enc_avg / 1e3) / 1e12}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, codec_h, pt_h, layer=w.D - 1, loop=w.T - 1,
                                               target_s=args.cpu_seconds)
+        if n_new > 1:
+            result["encode"]["cpu_baseline"] = cpu_encode_baseline(w, codec_h, w.D - 1,
+                                                                   target_s=args.cpu_seconds / 3)
     print(json.dumps(result), flush=True)
 
 
