@@ -297,6 +297,8 @@ int32_t lla_encode_append(const lla_dims *d, const lla_codec *c, const lla_cache
   a.width = width;
   a.err = (int *)ws;
   a.muw = (float *)((char *)ws + kHeaderBytes);
+  a.muw_stride = d->r_k + d->r_v;
+  a.muw_v_off = d->r_k;
   return check_launch(launch_encode(d->dtype, d->r_k, d->r_v, a, stream));
 }
 

@@ -3,9 +3,9 @@
 // loop-concatenated pre-RoPE vector x = [x_1; ...; x_T], written to the paged
 // latent pool at the slot of logical position pos0[b] + n.
 //
-// Computed as x W_down - (mu W_down): mu W_down is a per-(layer, head) constant
-// (first kernel, fp32), the contraction accumulates exact bf16 x fp32 products
-// in fp32, and the result is rounded once to the storage type.
+// Computed as x W_down - (mu W_down): mu W_down is a per-(layer, group)
+// constant (first kernel, fp32), the contraction accumulates exact products in
+// fp32, and the result is rounded once to the storage type.
 #include "lla_device.h"
 #include "lla_internal.h"
 
@@ -17,19 +17,38 @@ __device__ __forceinline__ float ldx(const char *p, long long i) {
   else return ((const float *)p)[i];
 }
 
-// muw[li][grp][kv ? RK + r : r] = sum_i mu[i] W_down[i][r]
+// muw[li][grp][kv ? RK + r : r] = sum_i mu[i] W_down[i][r], fp32: a constant of
+// (layer, latent group), computed once per call and shared by every token tile.
+// Wave w sums rows i = w, w + 4, ... (lanes over r, coalesced rows of W_down);
+// the 4 partial sums are added in fixed order.
 template <bool BF>
 __global__ __launch_bounds__(256) void encode_muw_kernel(EncodeArgs a, int RK, int RV) {
+  __shared__ float part[4][256];
   const int grp = blockIdx.x, li = blockIdx.y, kv = blockIdx.z;
   const int R = kv ? RV : RK;
   const int esz = BF ? 2 : 4;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const long long gl = (long long)li * a.groups + grp;  // relative to layer0
   const char *mu = (kv ? a.mu_v : a.mu_k) + gl * a.width * esz;
   const char *wd = (kv ? a.wd_v : a.wd_k) + gl * a.width * (long long)R * esz;
-  for (int r = threadIdx.x; r < R; r += blockDim.x) {
-    float acc = 0.f;
-    for (int i = 0; i < a.width; ++i) acc = fmaf(ldx<BF>(mu, i), ldx<BF>(wd, (long long)i * R + r), acc);
-    a.muw[gl * (RK + RV) + (kv ? RK : 0) + r] = acc;
+  for (int r0 = 0; r0 < R; r0 += 256) {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int i = w; i < a.width; i += 4) {
+      const float m = ldx<BF>(mu, i);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = r0 + lane + 64 * j;
+        if (r < R) acc[j] = fmaf(m, ldx<BF>(wd, (long long)i * R + r), acc[j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) part[w][lane + 64 * j] = acc[j];
+    __syncthreads();
+    const int r = r0 + threadIdx.x;
+    if (r < R)
+      a.muw[gl * (RK + RV) + (kv ? RK : 0) + r] =
+          ((part[0][threadIdx.x] + part[1][threadIdx.x]) + part[2][threadIdx.x]) + part[3][threadIdx.x];
+    __syncthreads();
   }
 }
 
@@ -78,29 +97,25 @@ __global__ __launch_bounds__(256) void encode_append_kernel(EncodeArgs a, int RK
 //
 // Per (layer, latent group, K|V) the encoder is a plain GEMM,
 //   C[tokens x r] = X[tokens x width] W_down[width x r] - 1 (mu W_down),
-// run on v_mfma_f32_16x16x32_bf16.  A workgroup (4 waves) takes 128 tokens;
-// wave w owns 32 of them (two 16-row tiles) and all r columns.  W_down is
+// run on v_mfma_f32_16x16x32_bf16.  A workgroup (8 waves) takes 128 tokens;
+// wave w owns 16 of them (one 16-row tile) and all r columns: few registers
+// per wave and many waves per CU, which hides the x loads best.  W_down is
 // streamed in chunks of 128 rows, transposed into LDS ([r][k], rows padded so
 // the 16-byte B-operand reads of 16 consecutive r hit distinct banks) and
-// shared by the 4 waves.  Each lane reads its tokens' x as 64 contiguous bytes
+// shared by the 8 waves.  Each lane reads its token's x as 64 contiguous bytes
 // per chunk: K-slot e of K-step s in lane group g is chunk column
-// 32 g + 8 s + e, on both operands.  mu W_down is one more MFMA row tile
-// (mu in row 0, zeros below) per column tile, spread over the waves, so it is
-// computed with the same fp32 accumulation as the tokens.  The result (minus
-// mu W_down, rounded once to bf16) goes through LDS and leaves as 16-byte
-// stores into the paged pool.
+// 32 g + 8 s + e, on both operands.  mu W_down comes from encode_muw_kernel
+// (once per call).  The result (minus mu W_down, rounded once to bf16) goes
+// through LDS and leaves as 16-byte stores into the paged pool.
 template <int R>
-__global__ __launch_bounds__(256) void encode_mfma_kernel(EncodeArgs a, int kv) {
+__global__ __launch_bounds__(512) void encode_mfma_kernel(EncodeArgs a, int kv) {
   constexpr int TOK = 128;        // tokens per workgroup
   constexpr int KC = 128;         // W_down rows per chunk
   constexpr int LROW = KC + 8;    // padded LDS row (elements) of the transposed chunk
   constexpr int CT = R / 16;      // column tiles
-  constexpr int MT = (CT + 3) / 4;  // mu column tiles per wave
   static_assert(R % 16 == 0 && R <= 256, "r");
   static_assert(R * LROW >= TOK * R, "output staging reuses the chunk buffer");
   __shared__ __attribute__((aligned(16))) uint16_t s_w[R * LROW];
-  __shared__ __attribute__((aligned(16))) uint16_t s_mu[KC];
-  __shared__ float s_muw[R];
   __shared__ long long s_off[TOK];  // element offset of each token's latent row, -1 = dropped
 
   // wave index as a scalar: branches on it must be uniform scalar branches,
@@ -112,7 +127,6 @@ __global__ __launch_bounds__(256) void encode_mfma_kernel(EncodeArgs a, int kv) 
   const long long tok0 = (long long)blockIdx.x * TOK;
   const long long gl = (long long)li * a.groups + grp;
   const char *x = kv ? a.x_v : a.x_k;
-  const uint16_t *mu = (const uint16_t *)(kv ? a.mu_v : a.mu_k) + gl * a.width;
   const uint16_t *wd = (const uint16_t *)(kv ? a.wd_v : a.wd_k) + gl * a.width * (long long)R;
   uint16_t *pool = (uint16_t *)(kv ? a.v_pool : a.k_pool) +
                    (long long)li * (kv ? a.pool_layer_stride_v : a.pool_layer_stride_k);
@@ -137,32 +151,21 @@ __global__ __launch_bounds__(256) void encode_mfma_kernel(EncodeArgs a, int kv) 
     s_off[threadIdx.x] = off;
   }
 
-  // this lane's x rows: tokens tok0 + 32 w + 16 rt + n (clamped; dropped at the end)
-  const uint16_t *xr[2];
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    long long tk = tok0 + 32 * w + 16 * rt + n;
-    if (tk >= tokens) tk = tokens - 1;
-    xr[rt] = (const uint16_t *)x + ((li * tokens + tk) * a.groups + grp) * a.width;
-  }
+  // this lane's x row: token tok0 + 16 w + n (clamped; dropped at the end)
+  long long tk = tok0 + 16 * w + n;
+  if (tk >= tokens) tk = tokens - 1;
+  const uint16_t *xr = (const uint16_t *)x + ((li * tokens + tk) * a.groups + grp) * a.width;
 
-  f32x4 acc[2][CT];
-  f32x4 accm[MT];
+  f32x4 acc[CT];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int m = 0; m < MT; ++m) accm[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int ct = 0; ct < CT; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nchunks = a.width / KC;
   for (int c = 0; c < nchunks; ++c) {
     const int k0 = c * KC;
-    u32x4 xa[2][4];
+    u32x4 xa[4];
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) xa[rt][s] = *(const u32x4 *)(xr[rt] + k0 + 32 * g + 8 * s);
+    for (int s = 0; s < 4; ++s) xa[s] = *(const u32x4 *)(xr + k0 + 32 * g + 8 * s);
     __syncthreads();  // previous chunk's operands are consumed
     // W_down rows k0 .. k0 + 127 -> s_w[r][k]: 4 rows x 8 columns per task
     for (int task = threadIdx.x; task < (KC / 4) * (R / 8); task += blockDim.x) {
@@ -180,43 +183,29 @@ __global__ __launch_bounds__(256) void encode_mfma_kernel(EncodeArgs a, int kv) 
         dst[1] = e2 | (e3 << 16);
       }
     }
-    if (threadIdx.x < KC / 8) *(u32x4 *)(s_mu + 8 * threadIdx.x) = *(const u32x4 *)(mu + k0 + 8 * threadIdx.x);
     __syncthreads();
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int kk = 32 * g + 8 * s;
-      const u32x4 mrow = *(const u32x4 *)(s_mu + kk);
-      const u32x4 am = n == 0 ? mrow : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
         const u32x4 bw = *(const u32x4 *)(s_w + (16 * ct + n) * LROW + kk);
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-          acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[rt][s]), as_bf16x8(bw),
-                                                                acc[rt][ct], 0, 0, 0);
-        if (ct % 4 == w)
-          accm[ct / 4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(am), as_bf16x8(bw),
-                                                                 accm[ct / 4], 0, 0, 0);
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[s]), as_bf16x8(bw), acc[ct], 0, 0, 0);
       }
     }
   }
 
-  // mu W_down: row 0 of each mu tile = lanes g == 0, element 0
-#pragma unroll
-  for (int m = 0; m < MT; ++m)
-    if (4 * m + w < CT && g == 0) s_muw[16 * (4 * m + w) + n] = accm[m][0];
-  __syncthreads();  // s_muw ready, s_w free for output staging
+  __syncthreads();  // s_w free for output staging
   uint16_t *s_out = s_w;  // [TOK][R] bf16
+  const float *muw = a.muw + gl * (a.muw_stride) + (kv ? a.muw_v_off : 0);
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+  for (int ct = 0; ct < CT; ++ct) {
+    const int r = 16 * ct + n;
+    const float mw = muw[r];
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      const int r = 16 * ct + n;
-      const float mw = s_muw[r];
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        s_out[(32 * w + 16 * rt + 4 * g + e) * R + r] = (uint16_t)f32_to_bf16(acc[rt][ct][e] - mw);
-    }
+    for (int e = 0; e < 4; ++e)
+      s_out[(16 * w + 4 * g + e) * R + r] = (uint16_t)f32_to_bf16(acc[ct][e] - mw);
+  }
   __syncthreads();
   for (int q = threadIdx.x; q < TOK * (R / 8); q += blockDim.x) {
     const int tl = q / (R / 8), c8 = q % (R / 8);
@@ -239,7 +228,7 @@ hipError_t launch_encode_mfma(int r, int kv, const EncodeArgs &a, hipStream_t st
   const dim3 grid((unsigned)((tokens + 127) / 128), a.groups, a.n_layers);
 #define X(RR)                                                                               \
   if (r == RR) {                                                                            \
-    hipLaunchKernelGGL(encode_mfma_kernel<RR>, grid, dim3(256), 0, stream, a, kv);          \
+    hipLaunchKernelGGL(encode_mfma_kernel<RR>, grid, dim3(512), 0, stream, a, kv);          \
     return hipGetLastError();                                                               \
   }
   LLA_ENCODE_R(X)
@@ -255,13 +244,14 @@ hipError_t launch_encode(int dtype, int r_k, int r_v, const EncodeArgs &a, hipSt
   const long long tokens = (long long)a.batch * a.n_new;
   if (tokens == 0 || a.n_layers == 0) return hipSuccess;
   // bf16 with whole 128-column chunks and an instantiated rank: matrix cores
+  const dim3 g1(a.groups, a.n_layers, 2);
   if (dtype == LLA_BF16 && a.width % 128 == 0 && encode_mfma_r(r_k) && encode_mfma_r(r_v) &&
       tokens <= 0x7FFFFFFFLL * 128) {
+    hipLaunchKernelGGL(encode_muw_kernel<true>, g1, dim3(256), 0, stream, a, r_k, r_v);
     hipError_t e = launch_encode_mfma(r_k, 0, a, stream);
     if (e != hipSuccess) return e;
     return launch_encode_mfma(r_v, 1, a, stream);
   }
-  const dim3 g1(a.groups, a.n_layers, 2);
   const dim3 g2((unsigned)((tokens + 15) / 16), a.groups, 2 * a.n_layers);
   if (dtype == LLA_BF16) {
     hipLaunchKernelGGL(encode_muw_kernel<true>, g1, dim3(256), 0, stream, a, r_k, r_v);

@@ -52,7 +52,8 @@ struct EncodeArgs {
   long long pool_head_stride_k, pool_head_stride_v;
   const int32_t *page_table, *pos0;
   int max_pages, num_pages, batch, n_new, n_layers, groups, width;
-  float *muw;                  // workspace [n_layers][groups][r_k + r_v]
+  float *muw;                  // workspace [n_layers][groups][r_k + r_v]: mu W_down, K then V
+  int muw_stride, muw_v_off;   // r_k + r_v, r_k
   int *err;
 };
 

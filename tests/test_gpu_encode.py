@@ -104,6 +104,20 @@ def test_encode_per_head_ragged_positions(dtype):
     compare(m, got, ref, init, f"encode per-head dt={dtype}")
 
 
+@pytest.mark.parametrize("ranks", [(32, 48), (64, 128), (16, 256), (256, 160)])
+def test_encode_rank_tilings(ranks):
+    """Every instantiated rank pairing of K and V: the encoder's column tiles and
+    its mu W_down tiles are spread over the waves differently for each."""
+    rk, rv = ranks
+    m = dims(4, 2, 4, 128, rk, rv, PER_HEAD, BF16)
+    B, pps = 2, 3
+    pt = gen.shuffled_page_table(3401 + rk, B, pps)
+    codec = random_codec(m, seed=3402 + rv, ortho_down=True)
+    pos0 = np.array([5, 16])
+    got, ref, init = run_both(m, codec, pt, B * pps, pos0, 29, 0, 2, seed=3403)
+    compare(m, got, ref, init, f"encode r_k={rk} r_v={rv}")
+
+
 def test_encode_21x_single_token_all_layers():
     """The decode-step append: one token per sequence into every layer (r_k=16, r_v=32)."""
     m = dims(4, 24, 16, 128, 16, 32, PER_HEAD, BF16)
