@@ -32,7 +32,8 @@ size_t esize(const lla_dims *d) { return d->dtype == LLA_BF16 ? 2 : 4; }
 
 // How an attention call is cut into workgroups.
 struct AttnPlan {
-  bool two_d;  // LLA-2D kernel (shared latent, 4 heads x 2 waves per workgroup)
+  bool prefill;  // chunked prefill kernel (query blocks of 256, no partials)
+  bool two_d;    // LLA-2D kernel (shared latent, 4 heads x 2 waves per workgroup)
   int hpw, waves, head_groups, splits, pages_per_split, chunk_pages;
   size_t partials_off, bytes;
 };
@@ -72,7 +73,18 @@ bool plan_attn_2d(const lla_dims *d, long long rows, int max_ctx, AttnPlan *p) {
   return true;
 }
 
-bool plan_attn(const lla_dims *d, long long rows, int max_ctx, AttnPlan *p) {
+bool plan_attn(const lla_dims *d, long long rows, int max_ctx, AttnPlan *p, bool prefill = false) {
+  p->prefill = false;
+  if (prefill && prefill_supported(d->dtype, d->variant, d->d_head, d->r_k, d->r_v)) {
+    // A query chunk runs as a dense attention over rebuilt K tiles; otherwise
+    // every query is one decode row.
+    p->prefill = true;
+    p->two_d = false;
+    p->hpw = p->waves = p->head_groups = p->splits = p->pages_per_split = p->chunk_pages = 1;
+    p->partials_off = kHeaderBytes;
+    p->bytes = kHeaderBytes;
+    return true;
+  }
   if (plan_attn_2d(d, rows, max_ctx, p)) return true;
   p->two_d = false;
   // Workgroup shape: 8 waves of 2 heads (16 heads) where possible; otherwise
@@ -152,8 +164,8 @@ int32_t attn_call(const lla_dims *d, const lla_codec *c, const lla_cache *k, con
   const long long rows = (long long)k->batch * (prefill ? n_q : 1);
   if (rows > (1LL << 30)) return fail(LLA_ERR_INVALID_ARG, "too many query rows");
   AttnPlan p;
-  if (!plan_attn(d, rows > 0 ? rows : 1, max_ctx, &p))
-    return fail(LLA_ERR_UNSUPPORTED, "no decode kernel built for this (dtype, d_head, r_k, r_v)");
+  if (!plan_attn(d, rows > 0 ? rows : 1, max_ctx, &p, prefill != 0))
+    return fail(LLA_ERR_UNSUPPORTED, "no attention kernel built for this (dtype, d_head, r_k, r_v)");
   if (!ws || ws_bytes < p.bytes) return fail(LLA_ERR_WORKSPACE, "workspace missing or too small");
   if (rows == 0) return LLA_OK;
 
@@ -217,6 +229,7 @@ int32_t attn_call(const lla_dims *d, const lla_codec *c, const lla_cache *k, con
   a.qscale = sc * 1.4426950408889634f;
   a.err = (int *)ws;
   a.partials = (float *)((char *)ws + p.partials_off);
+  if (p.prefill) return check_launch(launch_prefill(d->d_head, d->r_k, d->r_v, a, stream));
   const int32_t rc = check_launch(p.two_d ? launch_decode2d(d->d_head, d->r_k, d->r_v, a, stream)
                                           : launch_decode(d->dtype, d->d_head, d->r_k, d->r_v, a, stream));
   if (rc != LLA_OK || p.splits == 1) return rc;
@@ -243,7 +256,7 @@ size_t lla_workspace_bytes(const lla_dims *d, int32_t op, int32_t batch, int32_t
   if (max_ctx < 1 || (op == LLA_OP_PREFILL && n < 0)) return 0;
   const long long rows = (long long)batch * (op == LLA_OP_PREFILL ? n : 1);
   AttnPlan p;
-  if (!plan_attn(d, rows > 0 ? rows : 1, max_ctx, &p)) return 0;
+  if (!plan_attn(d, rows > 0 ? rows : 1, max_ctx, &p, op == LLA_OP_PREFILL)) return 0;
   return p.bytes;
 }
 
@@ -334,7 +347,7 @@ int32_t lla_supported(const lla_dims *d, int32_t op) {
   }
   if (op == LLA_OP_DECODE || op == LLA_OP_PREFILL) {
     AttnPlan p;
-    return plan_attn(d, 1, kPage, &p) ? 1 : 0;
+    return plan_attn(d, 1, kPage, &p, op == LLA_OP_PREFILL) ? 1 : 0;
   }
   return 0;
 }

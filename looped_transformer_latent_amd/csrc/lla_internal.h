@@ -68,6 +68,8 @@ bool decode2d_supported(int dtype, int d_head, int r_k, int r_v);
 hipError_t launch_decode2d(int d_head, int r_k, int r_v, const AttnArgs &a, hipStream_t stream);
 bool encode_supported(int dtype, int width, int r_k, int r_v);
 hipError_t launch_encode(int dtype, int r_k, int r_v, const EncodeArgs &a, hipStream_t stream);
+bool prefill_supported(int dtype, int variant, int d_head, int r_k, int r_v);
+hipError_t launch_prefill(int d_head, int r_k, int r_v, const AttnArgs &a, hipStream_t stream);
 hipError_t launch_merge(int dtype, int d_head, int r_v, const AttnArgs &a, hipStream_t stream);
 hipError_t launch_rope_table(int n_pos, int d_head, double base, float *table, hipStream_t s);
 

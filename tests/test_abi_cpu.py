@@ -68,8 +68,14 @@ def test_workspace_bytes_planning():
     assert lla.workspace_bytes(d, lla.OP_DECODE, 1, 16) == 256          # one split: header only
     assert lla.workspace_bytes(d, lla.OP_DECODE, 32, 0) == 0            # invalid max_ctx
     assert lla.workspace_bytes(_dims(d_head=96), lla.OP_DECODE, 32, 4096) == 0
-    pre = lla.workspace_bytes(d, lla.OP_PREFILL, 4, 4096, 8)
-    assert pre == lla.workspace_bytes(d, lla.OP_DECODE, 32, 4096)      # 4 x 8 query rows
+    # bf16 per-head shapes with a chunked prefill kernel need only the header;
+    # other shapes run prefill as decode rows and plan like them (4 x 8 rows)
+    assert lla.workspace_bytes(d, lla.OP_PREFILL, 4, 4096, 8) == 256
+    assert lla.supported(_dims(H=2), lla.OP_PREFILL)                    # no decode grid needed
+    assert lla.workspace_bytes(_dims(H=2), lla.OP_PREFILL, 4, 4096, 300) == 256
+    df = _dims(dtype=lla.F32, d_head=64)
+    pre = lla.workspace_bytes(df, lla.OP_PREFILL, 4, 4096, 8)
+    assert pre == lla.workspace_bytes(df, lla.OP_DECODE, 32, 4096)
     enc = lla.workspace_bytes(d, lla.OP_ENCODE, 64, 0, 24)
     assert enc >= 256 + 4 * 24 * 16 * 48
 
