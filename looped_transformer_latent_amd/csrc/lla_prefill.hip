@@ -14,25 +14,29 @@
 // rebuild each K tile once per workgroup (the close reading's long-prefill
 // remark: rebuild per layer, keep nothing) and run a dense attention:
 //  * A workgroup = 8 waves = 256 consecutive queries of one (sequence, head);
-//    wave w owns 32 of them as two 16-query MFMA columns.
+//    wave w owns 32 of them as two 16-query MFMA columns (two waves per SIMD).
 //  * Keys go in 32-token tiles (two pages).  A tile's c_k and c_v rows are
-//    loaded into registers three tiles ahead and written to one of three LDS
-//    slots (rows padded against bank conflicts); rows past the last needed
+//    copied global -> LDS with direct-to-LDS loads three tiles ahead, into one
+//    of four slots (separate LDS objects, so that the compiler's waits stay
+//    per slot; rows padded against bank conflicts).  Rows past the last needed
 //    position, and rows of a page whose table entry is out of range, are
-//    written as zeros.
-//  * Rebuild: one tile before it is attended, every wave turns one 16-token x
-//    (16 + 16)-dim block of the tile into rotated K (v_mfma_f32_16x16x32_bf16
-//    with W_up,k rows, staged in LDS once, as the A-operand; mu and RoPE in fp32
-//    on the accumulator, which holds both halves of each RoPE pair in one
-//    lane) and stores it in bf16 to a double-buffered LDS tile.
-//  * S^T = K Q'^T per 16x16 block, with Q' = scale log2(e) R(p) q in bf16
+//    cleared to zero before use.  The page-table entries of the sequence are
+//    staged in LDS, 1024 at a time.
+//  * Rebuild, one tile ahead: every wave turns one 16-token x (16 + 16)-dim
+//    block of the tile into rotated K (v_mfma_f32_16x16x32_bf16 with W_up,k rows
+//    from LDS as the A-operand; mu and RoPE in fp32 on the accumulator, which
+//    holds both halves of each RoPE pair in one lane) and stores it in bf16 to
+//    a double-buffered LDS tile.
+//  * S^T = K Q'^T per 16x16 block with Q' = scale log2(e) R(p) q in bf16
 //    registers; each lane holds one query's column, so the online softmax
 //    needs only two cross-row swaps for the max.  The running max is moved
-//    only when a tile exceeds it by more than 2^8 (the weights stay <= 256, the
+//    only when a tile exceeds it by more than 8 (weights stay <= 2^8; the
 //    result is the same), which skips most rescales of the accumulator.
 //  * O^T[r][q] += C_v^T[r][t] P^T[t][q]: the bf16 weights come straight from
 //    the score accumulator as the B-operand; the c_v tile is read transposed
 //    with ds_read_b64_tr_b16 as the A-operand.
+//  * One barrier per tile: each wave first waits for its own copies of the
+//    tile the next step rebuilds, then all waves meet.
 //  * Epilogue: O / Z in bf16 times W_up,v on the matrix cores, plus mu_v.
 #include "lla_device.h"
 #include "lla_internal.h"
@@ -45,6 +49,8 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((__vector_size__(2 * sizeof(uint32_t))));
 typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
 typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
+
+#define LLA_LDS(p) ((__attribute__((address_space(3))) void *)(p))
 
 // Two fp32 values to packed bf16 (hardware round to nearest even).
 __device__ __forceinline__ uint32_t cvt2(float lo, float hi) {
@@ -68,26 +74,50 @@ __device__ __forceinline__ u32x2 lds_read_tr(const char *p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// Workgroup barrier that leaves the newest VM loads of this wave in flight:
+// wait until at most VM of them are outstanding and every LDS access is done,
+// then meet.  The empty asm statements keep the compiler from moving memory
+// accesses across the barrier.
+template <int VM>
+__device__ __forceinline__ void barrier_vm() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt");
+  // s_waitcnt: vmcnt bits [15:14] and [3:0], expcnt [6:4] (7 = no wait), lgkmcnt [11:8] = 0
+  __builtin_amdgcn_s_waitcnt(((VM >> 4) << 14) | (VM & 15) | 0x70);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 }  // namespace
 
 template <int DH, int RK, int RV>
 __global__ __launch_bounds__(512, 1) void prefill_kernel(AttnArgs a) {
-  constexpr int NW = 8, QB = NW * 32, KT = 32;  // queries per workgroup, tokens per tile
+  constexpr int NW = 8, NTH = NW * 64, QB = NW * 32, KT = 32;  // queries per workgroup, tokens per tile
   constexpr int HALF = DH / 2, NDT = DH / 16, KSD = DH / 32;
-  constexpr int NU = NDT;                        // rebuild units: 2 token halves x NDT / 2 tile pairs
+  constexpr int NU = NDT;                          // rebuild units: 2 token halves x NDT / 2 tile pairs
   constexpr int KS32 = RK / 32;
-  constexpr bool TAIL = (RK % 32) != 0;          // one extra 16-wide K-step
+  constexpr bool TAIL = (RK % 32) != 0;            // one extra 16-wide K-step
   constexpr int NRT = RV / 16, KSV = RV / 32;
-  constexpr int CK = 4 * RK, CT = 4 * (RK + RV);  // 16-byte chunks of a tile: c_k, all
-  constexpr int IPW = (CT + NW * 64 - 1) / (NW * 64);
-  constexpr int SK = 2 * RK + 16, SV = 2 * RV + 32, SKH = 2 * DH + 16;  // LDS row strides, bytes
-  constexpr int VOFF = KT * SK, SLOT = KT * (SK + SV);
+  // LDS rows of a slot, in 16-byte chunks: RK / 8 (+1 pad) for c_k, RV / 8 (+2 pad) for c_v
+  constexpr int CPK = RK / 8 + 1, CPV = RV / 8 + 2;
+  constexpr int SK = 16 * CPK, SV = 16 * CPV, SKH = 2 * DH + 16;  // row strides, bytes
+  constexpr int VOFF = KT * SK;
+  constexpr int NPOS = (KT * (CPK + CPV) + 63) / 64 * 64;  // copied chunks per tile (pad included)
+  constexpr int NCP = NPOS / 64;                            // wave-wide copies per tile
+  constexpr int IPW = (NCP + NW - 1) / NW;                  // copies per wave (the last ones partial)
+  constexpr int IPW_MIN = NCP / NW;                         // copies every wave issues
+  constexpr int SLOT = NPOS * 16;
   static_assert(RK % 16 == 0 && RV % 32 == 0 && (DH == 64 || DH == 128), "shape");
-  static_assert(NU <= NW, "rebuild units");
+  static_assert(NU <= NW && IPW <= 4, "tile split");
 
-  __shared__ __attribute__((aligned(16))) char s_c[3 * SLOT];      // c_k | c_v rows per slot
-  __shared__ __attribute__((aligned(16))) char s_kh[2][KT * SKH];  // rotated K, bf16
-  __shared__ __attribute__((aligned(16))) char s_wk[DH * SK];       // W_up,k,t rows, bf16
+  __shared__ __attribute__((aligned(16))) char s_c0[SLOT], s_c1[SLOT], s_c2[SLOT], s_c3[SLOT];
+  __shared__ __attribute__((aligned(16))) char s_kh0[KT * SKH], s_kh1[KT * SKH];  // rotated K, bf16
+  __shared__ __attribute__((aligned(16))) char s_wk[DH * SK];                      // W_up,k,t rows
+  __shared__ int s_pt[2][1024];  // page-table entries: chunk c (1024 logical pages) in s_pt[c % 2]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -159,14 +189,14 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(AttnArgs a) {
     }
   }
 
-  // ---- W_up,k,t of the head in LDS (rows padded like the c_k rows) ----
+  // ---- W_up,k,t of the head in LDS (rows padded like the c_k rows), mu_k ----
   // Rebuild unit (tau, T) of wave w: tokens 16 tau .. + 15 of each tile, dims
   // 16 T + n and 16 T + n + d/2 (tile T and its RoPE partner tile).
   const int tau = w & 1, T = w >> 1;
   float muk[2][4];
   {
     const char *wkh = a.wup_k + (long long)h * a.wup_head_stride_k * 2;
-    for (int c = tid; c < DH * RK / 8; c += NW * 64) {
+    for (int c = tid; c < DH * RK / 8; c += NTH) {
       const int d = c / (RK / 8), k8 = c - d * (RK / 8);
       *(u32x4 *)(s_wk + d * SK + k8 * 16) = *(const u32x4 *)(wkh + ((long long)d * RK + 8 * k8) * 2);
     }
@@ -183,89 +213,102 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(AttnArgs a) {
     }
   }
 
-  // ---- tile loads: registers now, LDS slot later ----
+  // ---- page table, tile copies ----
   const int *pt_row = a.page_table + (long long)b * a.max_pages;
   const char *kpool = a.k_pool + (long long)h * a.pool_head_stride_k * 2;
   const char *vpool = a.v_pool + (long long)h * a.pool_head_stride_v * 2;
+  const long long pstride_k = a.pool_page_stride_k * 2, pstride_v = a.pool_page_stride_v * 2;
   int bad_lp = 0x7FFFFFFF;  // first logical page with an out-of-range table entry
 
-  // chunk c of a tile -> (V?, page 0/1, row, column)
-  auto chunk = [&](int c, bool &isv, int &pi, int &row, int &col) {
-    if (c < CK) {
-      isv = false;
-      pi = c / (2 * RK);
-      const int wi = c - pi * 2 * RK;
-      row = wi / (RK / 8);
-      col = (wi - row * (RK / 8)) * 8;
-    } else {
-      isv = true;
-      const int c2 = c - CK;
-      pi = c2 / (2 * RV);
-      const int wi = c2 - pi * 2 * RV;
-      row = wi / (RV / 8);
-      col = (wi - row * (RV / 8)) * 8;
+  auto fill_pt = [&](int c) {
+    for (int i = tid; i < 1024; i += NTH) {
+      const int lp = 1024 * c + i;
+      s_pt[c & 1][i] = lp < npg ? pt_row[lp] : 0;
     }
   };
-  auto load_tile = [&](int x, u32x4 (&bank)[IPW], int &okm) {
+
+  // Copy it of this wave covers chunk positions 64 (it NW + w) .. + 63 of the
+  // slot; lane position pos -> (c_v?, row, chunk) is the same for every tile.
+  // Pad positions copy the row's first chunk (never read).
+  int cp_off[IPW];   // byte offset within the page (from the K or V page base)
+  int cp_row[IPW];   // tile row 0..31, or 32 for positions past the rows
+  bool cp_v[IPW];
+#pragma unroll
+  for (int it = 0; it < IPW; ++it) {
+    const int pos = 64 * (it * NW + w) + lane;
+    int row = 32, off = 0;
+    bool isv = false;
+    if (pos < KT * CPK) {
+      row = pos / CPK;
+      const int c = pos - row * CPK;
+      off = ((row & 15) * RK + 8 * (c < RK / 8 ? c : 0)) * 2;
+    } else if (pos < KT * (CPK + CPV)) {
+      isv = true;
+      const int p2 = pos - KT * CPK;
+      row = p2 / CPV;
+      const int c = p2 - row * CPV;
+      off = ((row & 15) * RV + 8 * (c < RV / 8 ? c : 0)) * 2;
+    }
+    cp_off[it] = off;
+    cp_row[it] = row;
+    cp_v[it] = isv;
+  }
+  // Direct-to-LDS copy of tile x (clamped to the last tile) into slot sb;
+  // returns the page-validity bits (bit 0: first page, bit 1: second).
+  auto copy_tile = [&](int x, char *sb) -> int {
+    x = min(x, nt - 1);
     const int l0 = min(2 * x, npg - 1), l1 = min(2 * x + 1, npg - 1);
-    const int e0 = pt_row[l0], e1 = pt_row[l1];
+    const int e0 = __builtin_amdgcn_readfirstlane(s_pt[(l0 >> 10) & 1][l0 & 1023]);
+    const int e1 = __builtin_amdgcn_readfirstlane(s_pt[(l1 >> 10) & 1][l1 & 1023]);
     const bool ok0 = e0 >= 0 && e0 < a.num_pages, ok1 = e1 >= 0 && e1 < a.num_pages;
     if (!ok0) bad_lp = min(bad_lp, l0);
     if (!ok1) bad_lp = min(bad_lp, l1);
-    okm = (ok0 ? 1 : 0) | (ok1 ? 2 : 0);
     const long long pg0 = ok0 ? e0 : 0, pg1 = ok1 ? e1 : 0;
+    const char *k0 = kpool + pg0 * pstride_k, *k1 = kpool + pg1 * pstride_k;
+    const char *v0p = vpool + pg0 * pstride_v, *v1p = vpool + pg1 * pstride_v;
 #pragma unroll
     for (int it = 0; it < IPW; ++it) {
-      const int c = it * NW * 64 + tid;
-      if (CT % (NW * 64) == 0 || c < CT) {
-        bool isv;
-        int pi, row, col;
-        chunk(c, isv, pi, row, col);
-        const long long pg = pi ? pg1 : pg0;
-        const char *src = isv ? vpool + (pg * a.pool_page_stride_v + row * RV + col) * 2
-                              : kpool + (pg * a.pool_page_stride_k + row * RK + col) * 2;
-        bank[it] = *(const u32x4 *)src;
+      if (it < IPW_MIN || it * NW + w < NCP) {
+        const bool p1 = cp_row[it] >= 16 && cp_row[it] < 32;
+        const char *base = cp_v[it] ? (p1 ? v1p : v0p) : (p1 ? k1 : k0);
+        __builtin_amdgcn_global_load_lds((const void *)(base + cp_off[it]), LLA_LDS(sb + 64 * 16 * (it * NW + w)), 16, 0, 0);
       }
     }
+    return (ok0 ? 1 : 0) | (ok1 ? 2 : 0);
   };
-  auto store_tile = [&](int x, const u32x4 (&bank)[IPW], int okm, int slot) {
-    char *sb = s_c + slot * SLOT;
+  // Clear the rows of tile x (in slot sb, copies landed) that are past kend or
+  // come from a bad page.
+  auto clear_tile = [&](int x, char *sb, int okm) {
 #pragma unroll
     for (int it = 0; it < IPW; ++it) {
-      const int c = it * NW * 64 + tid;
-      if (CT % (NW * 64) == 0 || c < CT) {
-        bool isv;
-        int pi, row, col;
-        chunk(c, isv, pi, row, col);
-        const int r = 16 * pi + row;
-        const bool zero = KT * x + r >= kend || !((okm >> pi) & 1);
-        const u32x4 v = zero ? u32x4{0u, 0u, 0u, 0u} : bank[it];
-        *(u32x4 *)(sb + (isv ? VOFF + r * SV : r * SK) + col * 2) = v;
+      if (it < IPW_MIN || it * NW + w < NCP) {
+        const int r = cp_row[it];
+        if (r < 32 && (KT * x + r >= kend || !((okm >> (r >> 4)) & 1)))
+          *(u32x4 *)(sb + 16 * (64 * (it * NW + w) + lane)) = u32x4{0u, 0u, 0u, 0u};
       }
     }
   };
 
-  // RoPE rows of a rebuild unit: pairs 16 T + 4 g .. + 3 at its lane's token.
-  auto load_rope = [&](int x, f32x4 (&rp)[2]) {
-    if (w < NU) {
-      const int pos = min(KT * x + 16 * tau + n, kend - 1);
-      const float *rr = a.rope + (long long)pos * DH + 2 * (16 * T + 4 * g);
-      rp[0] = *(const f32x4 *)rr;
-      rp[1] = *(const f32x4 *)(rr + 4);
-    }
+  // RoPE rows of this wave's rebuild unit: pairs 16 T + 4 g .. + 3 at its token.
+  f32x4 rp[2];
+  auto load_rope = [&](int x) {
+    const int pos = min(KT * min(x, nt - 1) + 16 * tau + n, kend - 1);
+    const float *rr = a.rope + (long long)pos * DH + 2 * (16 * (w < NU ? T : 0) + 4 * g);
+    rp[0] = *(const f32x4 *)rr;
+    rp[1] = *(const f32x4 *)(rr + 4);
   };
-  // Rotated K of tile x (from LDS slot `slot`) into K buffer kb.
-  auto rebuild = [&](int slot, char *kb, const f32x4 (&rp)[2]) {
+  // Rotated K of the tile in slot sb into K buffer kb.
+  auto rebuild = [&](const char *sb, char *kb) {
     if (w < NU) {
-      const char *ck = s_c + slot * SLOT + (16 * tau + n) * SK;
+      const char *ck = sb + (16 * tau + n) * SK;
       const char *wa = s_wk + (16 * T + n) * SK, *wb = wa + HALF * SK;
       f32x4 k0 = f32x4{0.f, 0.f, 0.f, 0.f}, k1 = k0;
 #pragma unroll
       for (int ks = 0; ks < KS32; ++ks) {
         const int off = (32 * ks + 8 * g) * 2;
         const u32x4 bop = *(const u32x4 *)(ck + off);
-        k0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(*(const u32x4 *)(wa + off)), as_bf16x8(bop), k0, 0, 0, 0);
-        k1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(*(const u32x4 *)(wb + off)), as_bf16x8(bop), k1, 0, 0, 0);
+        k0 = mfma16(*(const u32x4 *)(wa + off), bop, k0);
+        k1 = mfma16(*(const u32x4 *)(wb + off), bop, k1);
       }
       if constexpr (TAIL) {
         const int off = (32 * KS32 + 4 * g) * 2;
@@ -298,7 +341,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(AttnArgs a) {
     for (int rt = 0; rt < NRT; ++rt) o[f][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  auto attend = [&](int x, int slot, const char *kb) {
+  auto attend = [&](int x, const char *sb, const char *kb) {
     if (!wactive || KT * x > qmax) return;  // every key of the tile is in this wave's future
     f32x4 s[2][2];
 #pragma unroll
@@ -311,8 +354,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(AttnArgs a) {
       for (int t2 = 0; t2 < 2; ++t2) {
         const u32x4 ak = *(const u32x4 *)(kb + (16 * t2 + n) * SKH + (32 * ks + 8 * g) * 2);
 #pragma unroll
-        for (int f = 0; f < 2; ++f)
-          s[t2][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ak), as_bf16x8(qop[f][ks]), s[t2][f], 0, 0, 0);
+        for (int f = 0; f < 2; ++f) s[t2][f] = mfma16(ak, qop[f][ks], s[t2][f]);
       }
     }
     const bool masked = KT * x + KT - 1 > qmin;
@@ -338,60 +380,67 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(AttnArgs a) {
         m_ref[f] = mn;
       }
       const float mu = m_ref[f] == -INFINITY ? 0.f : m_ref[f];
-      uint32_t pk[4];
-      float ps = 0.f;
+      float e[8];
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-        for (int i2 = 0; i2 < 2; ++i2) {
-          const uint32_t u = cvt2(fast_exp2(s[t2][f][2 * i2] - mu), fast_exp2(s[t2][f][2 * i2 + 1] - mu));
-          pk[2 * t2 + i2] = u;
-          ps += bf16_lo(u) + bf16_hi(u);
-        }
-      l_run[f] += ps;
-      pop[f] = u32x4{pk[0], pk[1], pk[2], pk[3]};
+        for (int i = 0; i < 4; ++i) e[4 * t2 + i] = fast_exp2(s[t2][f][i] - mu);
+      l_run[f] += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+      pop[f] = u32x4{cvt2(e[0], e[1]), cvt2(e[2], e[3]), cvt2(e[4], e[5]), cvt2(e[6], e[7])};
     }
     // O^T += C_v^T P^T; K index 8 g + e <-> token 16 (e / 4) + 4 g + e % 4
-    const char *vb = s_c + slot * SLOT + VOFF + (4 * g + (n >> 2)) * SV + 8 * (n & 3);
+    const char *vb = sb + VOFF + (4 * g + (n >> 2)) * SV + 8 * (n & 3);
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
-      const u32x2 lo = lds_read_tr(vb + 32 * rt);
+      const u32x2 lo2 = lds_read_tr(vb + 32 * rt);
       const u32x2 hi2 = lds_read_tr(vb + 16 * SV + 32 * rt);
-      const u32x4 av = u32x4{lo[0], lo[1], hi2[0], hi2[1]};
+      const u32x4 av = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
 #pragma unroll
-      for (int f = 0; f < 2; ++f)
-        o[f][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(pop[f]), o[f][rt], 0, 0, 0);
+      for (int f = 0; f < 2; ++f) o[f][rt] = mfma16(av, pop[f], o[f][rt]);
     }
   };
 
-  // ---- main loop: 3 LDS slots, 2 register banks, rebuild one tile ahead ----
-  u32x4 bank0[IPW], bank1[IPW];
-  int okm0 = 0, okm1 = 0;
-  f32x4 rp[2];
+  // ---- main loop ----
+  // Step x: clear tile x + 1 if it needs it, load the RoPE rows for its
+  // rebuild, copy tile x + 3 into its slot, attend tile x, rebuild tile x + 1,
+  // barrier.  Tile y lives in slot y % 4 and K buffer y % 2; the copy of tile
+  // y (issued in step y - 3) is complete in every wave after the barrier of
+  // step y - 2 (each wave leaves only the copies of step y - 2 in flight).
+  int okm0 = 3, okm1 = 3, okm2 = 3, okm3 = 3;
   if (nt > 0) {
-    load_tile(0, bank0, okm0);
-    if (nt > 1) load_tile(1, bank1, okm1);
-    load_rope(0, rp);
-    store_tile(0, bank0, okm0, 0);
-    if (nt > 1) store_tile(1, bank1, okm1, 1);
-    if (nt > 2) load_tile(2, bank0, okm0);
-    __syncthreads();
-    rebuild(0, s_kh[0], rp);
-    __syncthreads();
+    fill_pt(0);
+    if (npg > 1024) fill_pt(1);
+    __syncthreads();  // s_pt, s_wk
+    okm0 = copy_tile(0, s_c0);
+    if (nt > 1) okm1 = copy_tile(1, s_c1);
+    if (nt > 2) okm2 = copy_tile(2, s_c2);
+    load_rope(0);
+    barrier_vm<0>();
+    clear_tile(0, s_c0, okm0);
+    if (nt > 1) clear_tile(1, s_c1, okm1);
+    barrier_vm<0>();
+    rebuild(s_c0, s_kh0);
+    barrier_vm<0>();
   }
-  auto step = [&](int x, u32x4 (&cur)[IPW], int &okc, u32x4 (&nxt)[IPW], int &okn, char *kb_x, char *kb_n) {
-    // cur holds tile x + 2 (loaded one step ago); nxt receives tile x + 3
-    if (x + 1 < nt) load_rope(x + 1, rp);
-    if (x + 3 < nt) load_tile(x + 3, nxt, okn);
-    attend(x, x % 3, kb_x);
-    if (x + 1 < nt) rebuild((x + 1) % 3, kb_n, rp);
-    if (x + 2 < nt) store_tile(x + 2, cur, okc, (x + 2) % 3);
-    __syncthreads();
+  auto step = [&](int x, char *sx, char *sx1, char *sx3, int okx1, int &okx3, char *kbx, char *kbx1) {
+    if (x + 1 < nt && x >= 1 && (x + 1 == nt - 1 || okx1 != 3)) {  // tiles 0 and 1 were cleared above
+      clear_tile(x + 1, sx1, okx1);
+      barrier_vm<63>();
+    }
+    if (((2 * (x + 3)) & 1023) == 0 && 2 * (x + 3) + 1024 < npg) fill_pt(((2 * (x + 3)) >> 10) + 1);
+    load_rope(x + 1);
+    okx3 = copy_tile(x + 3, sx3);
+    attend(x, sx, kbx);
+    if (x + 1 < nt) rebuild(sx1, kbx1);
+    barrier_vm<IPW_MIN>();
   };
-  for (int x = 0; x < nt; x += 2) {
-    step(x, bank0, okm0, bank1, okm1, s_kh[0], s_kh[1]);
-    if (x + 1 < nt) step(x + 1, bank1, okm1, bank0, okm0, s_kh[1], s_kh[0]);
+  for (int x = 0; x < nt; x += 4) {
+    step(x, s_c0, s_c1, s_c3, okm1, okm3, s_kh0, s_kh1);
+    if (x + 1 < nt) step(x + 1, s_c1, s_c2, s_c0, okm2, okm0, s_kh1, s_kh0);
+    if (x + 2 < nt) step(x + 2, s_c2, s_c3, s_c1, okm3, okm1, s_kh0, s_kh1);
+    if (x + 3 < nt) step(x + 3, s_c3, s_c0, s_c2, okm0, okm2, s_kh1, s_kh0);
   }
+  __syncthreads();  // no copy in flight past the loop
 
   // ---- epilogue: normalise, up-project with W_up,v, add mu_v ----
   if (bad_lp != 0x7FFFFFFF) errbits |= LLA_DEVERR_PAGE;
@@ -421,8 +470,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(AttnArgs a) {
       const u32x2 w1v = *(const u32x2 *)(wr + 64 * ks + 32);
       const u32x4 av = u32x4{w0v[0], w0v[1], w1v[0], w1v[1]};
 #pragma unroll
-      for (int f = 0; f < 2; ++f)
-        acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(bup[f][ks]), acc[f], 0, 0, 0);
+      for (int f = 0; f < 2; ++f) acc[f] = mfma16(av, bup[f][ks], acc[f]);
     }
     const u32x2 mu2 = *(const u32x2 *)(mvh + 16 * et + 4 * g);
 #pragma unroll
