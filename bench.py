@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 DECODE_SOURCES = ("lla_decode_g.hip", "lla_device.h", "lla_internal.h", "lla_api.hip")
+PREFILL_SOURCES = ("lla_prefill.hip", "lla_device.h", "lla_internal.h", "lla_api.hip")
 
 
 def kernel_source_digest(names=DECODE_SOURCES) -> str:
@@ -40,7 +41,7 @@ def kernel_source_digest(names=DECODE_SOURCES) -> str:
     return h.hexdigest()
 
 
-def profiled_traffic(workload: str, kernel: str = "decode_g_kernel"):
+def profiled_traffic(workload: str, kernel: str = "decode_g_kernel", sources=DECODE_SOURCES):
     """HBM bytes per decode launch from the committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE summary of this workload, or None when the kernel sources have
     changed since those counters were taken (or no summary exists)."""
@@ -53,7 +54,7 @@ def profiled_traffic(workload: str, kernel: str = "decode_g_kernel"):
             if ":" in line and line.split(":", 1)[0] in ("kernel_source_sha256", "traffic_bytes_per_launch"):
                 k, v = line.split(":", 1)
                 fields[k] = v.strip()
-    if fields.get("kernel_source_sha256") != kernel_source_digest():
+    if fields.get("kernel_source_sha256") != kernel_source_digest(sources):
         return None
     v = fields.get("traffic_bytes_per_launch")
     return int(v) if v else None
@@ -127,6 +128,41 @@ def cpu_baseline(w, codec_h, pt_h, layer, loop, target_s):
                       f"fp64 C oracle, OpenMP over (sequence, head); {dt:.1f} s"}
 
 
+def cpu_prefill_baseline(w, codec_h, pt_h, layer, loop, n_new, target_s):
+    """Time the fp64 oracle's causal prefill on a bounded sample: the first
+    queries of one sequence's chunk (all heads), each over its full causal
+    context p0 + i + 1."""
+    import oracle
+    from looped_transformer_latent_amd import gen
+    from looped_transformer_latent_amd import workloads as wl
+
+    one = dict(w.dims, D=1)
+    codec1 = {k: np.ascontiguousarray(v[layer:layer + 1]) for k, v in codec_h.items()}
+    pages = pt_h[0]
+    kp = wl.pool_pages_host(w, "k", layer, pages)[None]
+    vp = wl.pool_pages_host(w, "v", layer, pages)[None]
+    local = np.arange(len(pages), dtype=np.int32)[None]
+    p0 = np.array([w.ctx - n_new], np.int32)
+
+    def run(n_q):
+        q = gen.normal(w.seed, wl.STREAMS["q"], (1, n_q, w.H, w.d_head),
+                       dtype="bf16" if w.dtype == wl.BF16 else "f32")
+        t0 = time.perf_counter()
+        _, rc = oracle.prefill(one, codec1, kp, vp, local, 0, loop, n_q, q, p0)
+        dt = time.perf_counter() - t0
+        assert rc == 0
+        return dt
+
+    threads = oracle.max_threads(0)
+    t1 = run(1)
+    n = int(max(1, min(n_new, round(target_s / max(t1, 1e-3)))))
+    dt = run(n) if n > 1 else t1
+    return {"value": n / dt, "unit": "prefill query tokens/s (all heads)", "cores": threads, "kind": "oracle",
+            "sample": f"queries 0..{n - 1} of one sequence's {n_new}-token chunk at positions "
+                      f"{w.ctx - n_new}.., all {w.H} heads, one (layer, loop); fp64 C oracle, "
+                      f"OpenMP over (query, head); {dt:.1f} s"}
+
+
 def cpu_encode_baseline(w, codec_h, layer, target_s):
     """Time the fp64 oracle's encode + append on a bounded sample: tokens of one
     layer (all heads), drawn from the same generator streams as the GPU's x."""
@@ -157,6 +193,54 @@ def cpu_encode_baseline(w, codec_h, layer, target_s):
     dt = run(n)
     return {"value": n / dt, "unit": "appended token-layers/s (all heads)", "cores": 1, "kind": "oracle",
             "sample": f"{n} tokens of one layer, all {w.H} heads; fp64 C oracle (single thread); {dt:.1f} s"}
+
+
+def bench_prefill(w, D, codec, cache, rope, calls, n_new, dt_t, p0, stream):
+    """lla_prefill_attn over every (loop, layer) of the step, timed with HIP
+    events on the launch stream; roofline against the bf16 matrix-core peak."""
+    import torch
+    from looped_transformer_latent_amd import lla
+    from looped_transformer_latent_amd import workloads as wl
+
+    q = torch.empty((w.batch, n_new, w.H, w.d_head), dtype=dt_t, device="cuda")
+    lla.gen_normal_(q, w.seed, wl.STREAMS["q"], offset=1 << 40)
+    out = torch.empty_like(q)
+    ws = lla.workspace(D, lla.OP_PREFILL, w.batch, w.ctx, n_new)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
+
+    def one_pass(record):
+        for i, (t, l) in enumerate(calls):
+            if record:
+                ev[i][0].record(stream)
+            lla.prefill_attn(D, codec, cache, rope, l, t, n_new, q, p0, w.ctx, out, ws)
+            if record:
+                ev[i][1].record(stream)
+
+    one_pass(False)
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(2):
+        one_pass(True)
+        torch.cuda.synchronize()
+        ms += [a.elapsed_time(b) for a, b in ev]
+    assert lla.device_error_word(ws) == 0
+    assert torch.isfinite(out.float()).all().item()
+    avg = float(np.mean(ms))
+    # algorithmic work per call: K rebuilt once per cached token and head
+    # (2 d r_k), scores and latent-space value sums per (query, key) pair
+    # (2 d + 2 r_v), one up-projection per query and head (2 r_v d)
+    keys = float(np.sum(np.arange(w.ctx - n_new, w.ctx) + 1))
+    flops = w.batch * w.H * (w.ctx * 2.0 * w.d_head * w.r_k + keys * 2.0 * (w.d_head + w.r_v)
+                             + n_new * 2.0 * w.r_v * w.d_head)
+    tflops = flops / (avg / 1e3) / 1e12
+    return {"kernel": "prefill_kernel", "calls": len(calls), "queries_per_call": w.batch * n_new,
+            "positions": [w.ctx - n_new, w.ctx - 1], "avg_ms": avg,
+            "value": w.batch * n_new / (avg / 1e3), "unit": "prefill query tokens/s (all heads, one (loop, layer))",
+            "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+                         "traffic": profiled_traffic(w.name, "prefill_kernel", PREFILL_SOURCES),
+                         "traffic_unit": "HBM bytes per launch (rocprofv3)",
+                         "algorithmic_flops_per_launch": flops}}
 
 
 def main():
@@ -296,7 +380,14 @@ def main():
                         "achieved_gbs": enc_bytes / (enc_avg / 1e3) / 1e9,
                         "frac_hbm": enc_bytes / (enc_avg / 1e3) / 1e9 / HBM_PEAK_GBS,
                         "tflops": enc_flops / (enc_avg / 1e3) / 1e12}
+    # causal prefill of the appended chunk: its n_new queries at positions
+    # ctx - n_new .. ctx - 1 attend over the cache, one call per (loop, layer)
+    if n_new > 1 and lla.supported(D, lla.OP_PREFILL):
+        result["prefill"] = bench_prefill(w, D, codec, cache, rope, calls, n_new, dt_t, pos0, stream)
     if not args.no_cpu_baseline:
+        if "prefill" in result:
+            result["prefill"]["cpu_baseline"] = cpu_prefill_baseline(
+                w, codec_h, pt_h, w.D - 1, w.T - 1, n_new, target_s=args.cpu_seconds / 3)
         result["cpu_baseline"] = cpu_baseline(w, codec_h, pt_h, layer=w.D - 1, loop=w.T - 1,
                                               target_s=args.cpu_seconds)
         if n_new > 1:

@@ -40,9 +40,10 @@
  *     the affected latents are not written (encode), and a bit is OR-ed into the
  *     int32 error word at byte 0 of the workspace (LLA_DEVERR_*).  That word is
  *     sticky: the library never clears it.
- *   - Workspace: size it with lla_workspace_bytes() and ZERO it once after
- *     allocation (the split-merge counters must start at zero; every call
- *     leaves them at zero again).  One workspace must not be used by two calls
+ *   - Workspace: size it with lla_workspace_bytes() and zero it once after
+ *     allocation (the error word must start clear).  Beyond the 256-byte
+ *     header it holds per-call scratch (split partials, encode's mu W_down),
+ *     rewritten by every call.  One workspace must not be used by two calls
  *     that may run concurrently.
  */
 #ifndef LLA_H
@@ -166,8 +167,13 @@ int32_t lla_decode_attn(const lla_dims *dims, const lla_codec *codec, const lla_
  * p0[b] + i and attends over logical tokens [0, p0[b] + i]; those tokens must
  * already be appended.
  *   q, out   [batch][n_q][H][d_head];  p0 device int32 [batch];
- *   max_ctx  >= p0[b] + n_q for every b (bounds the split grid);
- *   other arguments as for lla_decode_attn. */
+ *   max_ctx  >= p0[b] + n_q for every b (rows past it are written as NaN);
+ *   other arguments as for lla_decode_attn.
+ * bf16 per-head shapes with a chunk kernel (lla_supported(.., LLA_OP_PREFILL)
+ * and d_head, r_k, r_v in (64,16,32), (128,16,32), (128,32,64), (128,96,160))
+ * rebuild each 32-token K tile once per 256 queries and run a dense attention
+ * on the matrix cores; other shapes run every query as one decode row.  Both
+ * give the same result within the storage type's rounding. */
 int32_t lla_prefill_attn(const lla_dims *dims, const lla_codec *codec, const lla_cache *cache,
                          const float *rope_table, int32_t rope_len, int32_t layer, int32_t loop,
                          int32_t n_q, const void *q, const int32_t *p0, int32_t max_ctx,
