@@ -342,7 +342,6 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(AttnArgs a) {
   }
 
   auto attend = [&](int x, const char *sb, const char *kb) {
-    if (!wactive || KT * x > qmax) return;  // every key of the tile is in this wave's future
     f32x4 s[2][2];
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2)
