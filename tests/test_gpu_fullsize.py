@@ -164,3 +164,36 @@ def test_ouro_4x_encode_then_decode_sampled(release):
     assert worst <= 2e-2
 
     check_rows(b, np.array([0, 37, 63]), 23, 3, from_device=True)
+
+    # chunked prefill of the appended chunk: query i of every sequence sits at
+    # position 7680 + i; sampled rows against the oracle's decode at that
+    # position (causal context 7681 + i), read from the GPU-written cache
+    layer, loop = 23, 3
+    q = torch.empty((w.batch, n_new, w.H, w.d_head), dtype=torch.bfloat16, device="cuda")
+    lla.gen_normal_(q, w.seed, wl.STREAMS["q"], offset=1 << 40)
+    out = torch.empty_like(q)
+    wsp = lla.workspace(b.D, lla.OP_PREFILL, w.batch, w.ctx, n_new)
+    lla.prefill_attn(b.D, b.codec, b.cache, b.rope, layer, loop, n_new, q, pos0, w.ctx, out, wsp)
+    torch.cuda.synchronize()
+    assert lla.device_error_word(wsp) == 0
+    got_all = out_to_f64(out)
+    assert np.isfinite(got_all).all()
+    q_h = to_host(q)
+    m1 = dict(w.dims, D=1)
+    codec1 = {k: np.ascontiguousarray(v[layer:layer + 1]) for k, v in b.codec_h.items()}
+    worst = 0.0
+    for bb, i in ((0, 0), (0, 511), (37, 255), (37, 256), (63, 100)):
+        pages = b.pt_h[bb]
+        idx = torch.from_numpy(pages.astype(np.int64)).cuda()
+        kp = to_host(b.k_pool[layer].index_select(0, idx))[None]
+        vp = to_host(b.v_pool[layer].index_select(0, idx))[None]
+        local = np.arange(len(pages), dtype=np.int32)[None]
+        pos = w.ctx - n_new + i
+        ref, rc = oracle.decode(m1, codec1, np.ascontiguousarray(kp), np.ascontiguousarray(vp), local, 0,
+                                loop, np.ascontiguousarray(q_h[bb:bb + 1, i]), np.int32([pos]),
+                                np.int32([pos + 1]))
+        assert rc == 0
+        worst = max(worst, float(row_rel_err(got_all[bb, i], ref[0]).max()))
+    print(f"[{w.name}] prefill of the 512-token chunk: 5 sampled (sequence, query) rows, "
+          f"max row rel err {worst:.3e}", flush=True)
+    assert worst <= TOL[w.dtype]
