@@ -68,7 +68,7 @@ enum {
 
 enum { LLA_PER_HEAD = 0, LLA_2D = 1 }; /* [CR] 方法 item 6: LLA-2D folds heads into one latent */
 enum { LLA_F32 = 0, LLA_BF16 = 1 };
-enum { LLA_OP_ENCODE = 0, LLA_OP_DECODE = 1, LLA_OP_PREFILL = 2 };
+enum { LLA_OP_ENCODE = 0, LLA_OP_DECODE = 1, LLA_OP_PREFILL = 2, LLA_OP_RECONSTRUCT = 3, LLA_OP_FULL_DECODE = 4 };
 
 /* Device-side error bits (workspace byte 0). */
 enum {
@@ -179,6 +179,40 @@ int32_t lla_prefill_attn(const lla_dims *dims, const lla_codec *codec, const lla
                          int32_t n_q, const void *q, const int32_t *p0, int32_t max_ctx,
                          float scale, void *out, void *workspace, size_t ws_bytes,
                          hipStream_t stream);
+
+/* Full ("teacher") K/V cache of one (layer, loop), the baseline the latent
+ * cache is measured against ([CR] 四:结果 item 9: the full-memory fast path keeps
+ * the complete reconstructed K/V; the capacity path rebuilds at read time).
+ * Layout, bf16 per-head, same page table as the latent cache:
+ *   k_full, v_full  [num_pages][H][page_size][d_head]
+ * where the K row of logical token j is already rotated by RoPE at position j.
+ *
+ * lla_reconstruct_kv rebuilds the slots of logical tokens [0, ctx_len[b]) of
+ * every sequence from the latent cache of (layer, loop), eq. (3) with RoPE
+ * after reconstruction ([CR] 方法 items 1 and 3):
+ *   k_j = R(j)(mu_k,t + c_k,j W_up,k,t^T),  v_j = mu_v,t + c_v,j W_up,v,t^T,
+ * fp32 accumulation, rounded once to bf16.  Other slots are not touched.
+ * ctx_len is device int32 [batch] (1 <= ctx_len <= max_ctx, else the row is
+ * skipped and LLA_DEVERR_CTX set); pages with out-of-range table entries are
+ * skipped and set LLA_DEVERR_PAGE.  Workspace: lla_workspace_bytes(..,
+ * LLA_OP_RECONSTRUCT, ..) (the error word only).  Supported: bf16 per-head,
+ * (d_head, r_k, r_v) in (64,16,32), (128,16,32), (128,32,64), (128,64,64). */
+int32_t lla_reconstruct_kv(const lla_dims *dims, const lla_codec *codec, const lla_cache *cache,
+                           const float *rope_table, int32_t rope_len, int32_t layer, int32_t loop,
+                           const int32_t *ctx_len, int32_t max_ctx, void *k_full, void *v_full,
+                           void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Decode attention over a full cache (textbook attention of R(q_pos) q over
+ * the stored K/V): out = softmax(scale <R(q_pos) q, k_j>) V over j < ctx_len.
+ * cache supplies the page table and sizes only (its pools are not read); q and
+ * out [batch][H][d_head] bf16; other arguments as for lla_decode_attn; workspace
+ * from lla_workspace_bytes(.., LLA_OP_FULL_DECODE, batch, max_ctx, 0).
+ * Supported: bf16 per-head, d_head 64 or 128, H a multiple of 4. */
+int32_t lla_full_decode_attn(const lla_dims *dims, const lla_cache *cache, const void *k_full,
+                             const void *v_full, const float *rope_table, int32_t rope_len,
+                             const void *q, const int32_t *q_pos, const int32_t *ctx_len,
+                             int32_t max_ctx, float scale, void *out, void *workspace,
+                             size_t ws_bytes, hipStream_t stream);
 
 /* Eq. (4): persistent cache scalars per token and layer, for the teacher
  * (2 T H d_head) and for the latent cache ((r_k + r_v) H, or r_k + r_v for

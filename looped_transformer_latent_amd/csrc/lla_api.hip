@@ -125,6 +125,32 @@ bool plan_attn(const lla_dims *d, long long rows, int max_ctx, AttnPlan *p, bool
   return true;
 }
 
+// Full-cache decode: 4 heads per workgroup, split the context until about
+// 1024 workgroups exist (HBM-bound like the latent decode).
+bool plan_full(const lla_dims *d, long long rows, int max_ctx, AttnPlan *p) {
+  if (!full_decode_supported(d->dtype, d->variant, d->d_head) || d->H % 4) return false;
+  p->prefill = false;
+  p->two_d = false;
+  p->hpw = 1;
+  p->waves = 4;
+  p->head_groups = d->H / 4;
+  p->chunk_pages = 1;
+  const int pages = (max_ctx + kPage - 1) / kPage;
+  const long long base = rows * p->head_groups;
+  long long s = base >= 512 ? 1 : (1024 + base - 1) / base;
+  const long long smax = pages / 2 > 1 ? pages / 2 : 1;
+  if (s > smax) s = smax;
+  if (s < 1) s = 1;
+  p->pages_per_split = (int)((pages + s - 1) / s);
+  p->splits = (pages + p->pages_per_split - 1) / p->pages_per_split;
+  if (p->splits < 1) p->splits = 1;
+  p->partials_off = kHeaderBytes;
+  p->bytes = p->splits > 1
+                 ? align256(kHeaderBytes + sizeof(float) * (size_t)rows * d->H * p->splits * (d->d_head + 2))
+                 : kHeaderBytes;
+  return true;
+}
+
 size_t encode_ws_bytes(const lla_dims *d, int n_layers) {
   const int groups = d->variant == LLA_PER_HEAD ? d->H : 1;
   return align256(kHeaderBytes + sizeof(float) * (size_t)n_layers * groups * (d->r_k + d->r_v));
@@ -252,6 +278,12 @@ int32_t lla_rope_table(const lla_dims *d, int32_t n_pos, float *table, hipStream
 size_t lla_workspace_bytes(const lla_dims *d, int32_t op, int32_t batch, int32_t max_ctx, int32_t n) {
   if (!dims_valid(d) || batch < 0) return 0;
   if (op == LLA_OP_ENCODE) return n >= 0 ? encode_ws_bytes(d, n) : 0;
+  if (op == LLA_OP_RECONSTRUCT) return kHeaderBytes;
+  if (op == LLA_OP_FULL_DECODE) {
+    AttnPlan p;
+    if (max_ctx < 1 || !plan_full(d, batch > 0 ? batch : 1, max_ctx, &p)) return 0;
+    return p.bytes;
+  }
   if (op != LLA_OP_DECODE && op != LLA_OP_PREFILL) return 0;
   if (max_ctx < 1 || (op == LLA_OP_PREFILL && n < 0)) return 0;
   const long long rows = (long long)batch * (op == LLA_OP_PREFILL ? n : 1);
@@ -332,6 +364,106 @@ int32_t lla_prefill_attn(const lla_dims *d, const lla_codec *c, const lla_cache 
                    max_ctx, scale, out, ws, ws_bytes, stream);
 }
 
+int32_t lla_reconstruct_kv(const lla_dims *d, const lla_codec *c, const lla_cache *k, const float *rope,
+                           int32_t rope_len, int32_t layer, int32_t loop, const int32_t *ctx_len,
+                           int32_t max_ctx, void *k_full, void *v_full, void *ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  if (!dims_valid(d)) return fail(LLA_ERR_INVALID_ARG, "invalid lla_dims");
+  if (!c || !k) return fail(LLA_ERR_INVALID_ARG, "null codec or cache");
+  if (!c->mu_k || !c->mu_v || !c->w_up_k || !c->w_up_v)
+    return fail(LLA_ERR_INVALID_ARG, "null decoder parameter (mu or W_up)");
+  if (!k->k_pool || !k->v_pool || !k->page_table) return fail(LLA_ERR_INVALID_ARG, "null pool or page table");
+  if (k->batch < 0 || k->max_pages_per_seq < 1 || k->num_pages < 1)
+    return fail(LLA_ERR_INVALID_ARG, "invalid cache sizes");
+  if (layer < 0 || layer >= d->D || loop < 0 || loop >= d->T)
+    return fail(LLA_ERR_INVALID_ARG, "layer or loop out of range");
+  if (!rope || rope_len < 1 || max_ctx < 1 || max_ctx > rope_len ||
+      (long long)max_ctx > (long long)k->max_pages_per_seq * kPage)
+    return fail(LLA_ERR_INVALID_ARG, "bad RoPE table or max_ctx");
+  if (!ctx_len || !k_full || !v_full) return fail(LLA_ERR_INVALID_ARG, "null ctx_len or full cache");
+  if (!reconstruct_supported(d->dtype, d->variant, d->d_head, d->r_k, d->r_v))
+    return fail(LLA_ERR_UNSUPPORTED, "no reconstruct kernel for this (dtype, variant, d_head, r_k, r_v)");
+  if (!ws || ws_bytes < kHeaderBytes) return fail(LLA_ERR_WORKSPACE, "workspace missing or too small");
+  if (k->batch == 0) return LLA_OK;
+  const long long T = d->T, H = d->H, dh = d->d_head, rk = d->r_k, rv = d->r_v, np = k->num_pages;
+  AttnArgs a = {};
+  a.k_pool = (const char *)k->k_pool + (size_t)layer * np * H * kPage * rk * 2;
+  a.v_pool = (const char *)k->v_pool + (size_t)layer * np * H * kPage * rv * 2;
+  a.pool_page_stride_k = H * kPage * rk;
+  a.pool_page_stride_v = H * kPage * rv;
+  a.pool_head_stride_k = kPage * rk;
+  a.pool_head_stride_v = kPage * rv;
+  const long long mu0 = ((long long)layer * H * T + loop) * dh;
+  a.mu_k = (const char *)c->mu_k + mu0 * 2;
+  a.mu_v = (const char *)c->mu_v + mu0 * 2;
+  a.wup_k = (const char *)c->w_up_k + mu0 * rk * 2;
+  a.wup_v = (const char *)c->w_up_v + mu0 * rv * 2;
+  a.mu_head_stride = T * dh;
+  a.wup_head_stride_k = T * dh * rk;
+  a.wup_head_stride_v = T * dh * rv;
+  a.page_table = k->page_table;
+  a.max_pages = k->max_pages_per_seq;             // page-table row length
+  a.pages_per_split = (max_ctx + kPage - 1) / kPage;  // pages a sequence can need (grid)
+  a.num_pages = k->num_pages;
+  a.rope = rope;
+  a.rope_len = rope_len;
+  a.ctx_len = ctx_len;
+  a.H = d->H;
+  a.max_ctx = max_ctx;
+  a.err = (int *)ws;
+  a.rows = k->batch;
+  return check_launch(launch_reconstruct(d->d_head, d->r_k, d->r_v, a, k_full, v_full, k->batch, stream));
+}
+
+int32_t lla_full_decode_attn(const lla_dims *d, const lla_cache *k, const void *k_full, const void *v_full,
+                             const float *rope, int32_t rope_len, const void *q, const int32_t *q_pos,
+                             const int32_t *ctx_len, int32_t max_ctx, float scale, void *out, void *ws,
+                             size_t ws_bytes, hipStream_t stream) {
+  if (!dims_valid(d)) return fail(LLA_ERR_INVALID_ARG, "invalid lla_dims");
+  if (!k || !k->page_table || !k_full || !v_full) return fail(LLA_ERR_INVALID_ARG, "null cache or full cache");
+  if (k->batch < 0 || k->max_pages_per_seq < 1 || k->num_pages < 1)
+    return fail(LLA_ERR_INVALID_ARG, "invalid cache sizes");
+  if (!rope || rope_len < 1 || max_ctx < 1 || max_ctx > rope_len ||
+      (long long)max_ctx > (long long)k->max_pages_per_seq * kPage)
+    return fail(LLA_ERR_INVALID_ARG, "bad RoPE table or max_ctx");
+  if (!q || !out || !q_pos || !ctx_len) return fail(LLA_ERR_INVALID_ARG, "null q, out or positions");
+  if (!(scale >= 0.f) || isinf(scale)) return fail(LLA_ERR_INVALID_ARG, "invalid scale");
+  AttnPlan p;
+  const long long rows = k->batch;
+  if (!plan_full(d, rows > 0 ? rows : 1, max_ctx, &p))
+    return fail(LLA_ERR_UNSUPPORTED, "no full-cache decode kernel for this (dtype, variant, d_head, H)");
+  if (!ws || ws_bytes < p.bytes) return fail(LLA_ERR_WORKSPACE, "workspace missing or too small");
+  if (rows == 0) return LLA_OK;
+  AttnArgs a = {};
+  a.q = q;
+  a.out = out;
+  a.k_pool = (const char *)k_full;
+  a.v_pool = (const char *)v_full;
+  a.page_table = k->page_table;
+  a.max_pages = k->max_pages_per_seq;
+  a.num_pages = k->num_pages;
+  a.rope = rope;
+  a.rope_len = rope_len;
+  a.q_pos = q_pos;
+  a.ctx_len = ctx_len;
+  a.n_q = 1;
+  a.rows = (int)rows;
+  a.H = d->H;
+  a.max_ctx = max_ctx;
+  a.splits = p.splits;
+  a.pages_per_split = p.pages_per_split;
+  a.head_groups = p.head_groups;
+  a.heads_per_wave = 1;
+  a.waves = 4;
+  const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)d->d_head);
+  a.qscale = sc * 1.4426950408889634f;
+  a.err = (int *)ws;
+  a.partials = (float *)((char *)ws + p.partials_off);
+  const int32_t rc = check_launch(launch_full_decode(d->d_head, a, stream));
+  if (rc != LLA_OK || p.splits == 1) return rc;
+  return check_launch(launch_merge_ident(d->d_head, a, stream));
+}
+
 int32_t lla_cache_scalars(const lla_dims *d, int64_t *teacher, int64_t *latent) {
   if (!dims_valid(d) || !teacher || !latent) return fail(LLA_ERR_INVALID_ARG, "invalid arguments");
   *teacher = 2LL * d->T * d->H * d->d_head;
@@ -348,6 +480,11 @@ int32_t lla_supported(const lla_dims *d, int32_t op) {
   if (op == LLA_OP_DECODE || op == LLA_OP_PREFILL) {
     AttnPlan p;
     return plan_attn(d, 1, kPage, &p, op == LLA_OP_PREFILL) ? 1 : 0;
+  }
+  if (op == LLA_OP_RECONSTRUCT) return reconstruct_supported(d->dtype, d->variant, d->d_head, d->r_k, d->r_v);
+  if (op == LLA_OP_FULL_DECODE) {
+    AttnPlan p;
+    return plan_full(d, 1, kPage, &p) ? 1 : 0;
   }
   return 0;
 }

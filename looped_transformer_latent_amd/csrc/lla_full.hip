@@ -1,0 +1,348 @@
+// Full ("teacher") K/V cache for one (layer, loop), bf16 per-head: the baseline
+// the latent path is measured against (cc.laoqi.cc close reading, 四:结果 item 9:
+// the full-memory fast path keeps complete reconstructed K/V; the capacity
+// path rebuilds from latents at read time).
+//
+//  * reconstruct_kernel: k_j = R(j)(mu_k,t + c_k,j W_up,k,t^T) and
+//    v_j = mu_v,t + c_v,j W_up,v,t^T (eq. (3), RoPE after reconstruction) for
+//    every cached token, written in bf16 to a paged full cache with the latent
+//    cache's page table ([num_pages][H][16][d_head]).  One wave rebuilds one
+//    16-token page of one head on the matrix cores: W_up rows are the
+//    A-operand (registers), the page's latent rows the B-operand, so the
+//    accumulator holds 4 consecutive dims of one token and both halves of each
+//    RoPE pair in one lane.
+//  * full_decode_kernel: ordinary decode attention over the full cache,
+//    s_j = scale <R(q_pos) q, k_j>, out = sum_j e^{s_j - m} v_j / sum_j e^{s_j - m}.
+//    Bound by HBM (2 d_head bf16 per token and head).  One wave per (row,
+//    head, split); lane (t, part) holds a quarter of token t's K and V row;
+//    pages are loaded two ahead; online softmax in base 2 with the running
+//    max moved only when it grows by more than 8.
+#include "lla_device.h"
+#include "lla_internal.h"
+
+namespace lla {
+
+namespace {
+
+typedef uint32_t u32x2 __attribute__((__vector_size__(2 * sizeof(uint32_t))));
+typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
+typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
+
+__device__ __forceinline__ uint32_t cvt2(float lo, float hi) {
+  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// dst rows d = 16 T + 4 g + i (i < 4), column t = lane & 15, of W_up[d][r] c[t][r]^T:
+// RK / 32 steps of 16x16x32 plus one 16x16x16 step when RK % 32 == 16.
+template <int RK>
+struct WupTile {
+  u32x4 a32[RK / 32 > 0 ? RK / 32 : 1];
+  u32x2 a16;
+};
+
+template <int RK>
+__device__ __forceinline__ void load_wup(WupTile<RK> &w, const uint16_t *row, int g) {
+#pragma unroll
+  for (int ks = 0; ks < RK / 32; ++ks) w.a32[ks] = *(const u32x4 *)(row + 32 * ks + 8 * g);
+  if constexpr (RK % 32) w.a16 = *(const u32x2 *)(row + 32 * (RK / 32) + 4 * g);
+}
+
+template <int RK>
+__device__ __forceinline__ f32x4 wup_times(const WupTile<RK> &w, const uint16_t *crow, int g) {
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < RK / 32; ++ks) {
+    const u32x4 b = *(const u32x4 *)(crow + 32 * ks + 8 * g);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w.a32[ks]), as_bf16x8(b), acc, 0, 0, 0);
+  }
+  if constexpr (RK % 32) {
+    const u32x2 b = *(const u32x2 *)(crow + 32 * (RK / 32) + 4 * g);
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, w.a16),
+                                                     __builtin_bit_cast(bf16x4, b), acc, 0, 0, 0);
+  }
+  return acc;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- reconstruct
+
+// Grid: x = batch * ceil(max pages / (4 * PPW)), y = H; 4 waves, each PPW pages.
+template <int DH, int RK, int RV>
+__global__ __launch_bounds__(256) void reconstruct_kernel(AttnArgs a, char *k_full, char *v_full, int ppw) {
+  constexpr int NDT = DH / 16, HALF = DH / 2;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int groups = (a.pages_per_split + 4 * ppw - 1) / (4 * ppw);  // pages_per_split: pages a row can need
+  const int b = blockIdx.x / groups, grp = blockIdx.x - b * groups;
+  const int h = blockIdx.y;
+  int ctx = a.ctx_len[b];
+  if (ctx < 1 || ctx > a.max_ctx) {
+    if (grp == 0 && threadIdx.x == 0 && h == 0) atomicOr(a.err, LLA_DEVERR_CTX);
+    return;
+  }
+  const int npg = (ctx + kPage - 1) / kPage;
+  const int lp0 = (grp * 4 + w) * ppw;
+  if (lp0 >= npg) return;  // whole wave
+
+  // W_up,k rows 16 T + n (T < NDT), W_up,v rows likewise; mu per output row
+  const uint16_t *wk = (const uint16_t *)a.wup_k + (long long)h * a.wup_head_stride_k;
+  const uint16_t *wv = (const uint16_t *)a.wup_v + (long long)h * a.wup_head_stride_v;
+  const uint16_t *mk = (const uint16_t *)a.mu_k + (long long)h * a.mu_head_stride;
+  const uint16_t *mv = (const uint16_t *)a.mu_v + (long long)h * a.mu_head_stride;
+  WupTile<RK> ak[NDT];
+  WupTile<RV> av[NDT];
+#pragma unroll
+  for (int T = 0; T < NDT; ++T) {
+    load_wup<RK>(ak[T], wk + (16 * T + n) * RK, g);
+    load_wup<RV>(av[T], wv + (16 * T + n) * RV, g);
+  }
+  const long long ls = (long long)kPage * DH;  // elements per (page, head)
+  int bad = 0;
+  for (int lp = lp0; lp < min(lp0 + ppw, npg); ++lp) {
+    const int e = a.page_table[(long long)b * a.max_pages + lp];
+    if (e < 0 || e >= a.num_pages) {  // uniform over the wave
+      bad |= LLA_DEVERR_PAGE;
+      continue;
+    }
+    const int pos = lp * kPage + n;  // this lane's token
+    const bool live = pos < ctx;
+    const uint16_t *ck = (const uint16_t *)a.k_pool + (long long)e * a.pool_page_stride_k +
+                         (long long)h * a.pool_head_stride_k + n * RK;
+    const uint16_t *cv = (const uint16_t *)a.v_pool + (long long)e * a.pool_page_stride_v +
+                         (long long)h * a.pool_head_stride_v + n * RV;
+    uint16_t *kd = (uint16_t *)k_full + ((long long)e * a.H + h) * ls + n * DH;
+    uint16_t *vd = (uint16_t *)v_full + ((long long)e * a.H + h) * ls + n * DH;
+    const float *rr = a.rope + (long long)min(pos, a.rope_len - 1) * DH;
+#pragma unroll
+    for (int T = 0; T < NDT / 2; ++T) {
+      const f32x4 x = wup_times<RK>(ak[T], ck, g);
+      const f32x4 y = wup_times<RK>(ak[T + NDT / 2], ck, g);
+      const int d0 = 16 * T + 4 * g;  // RoPE pairs d0 .. d0 + 3
+      const f32x4 c01 = *(const f32x4 *)(rr + 2 * d0), c23 = *(const f32x4 *)(rr + 2 * d0 + 4);
+      float ra[4], rb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float ka = x[i] + bf16_to_f32(mk[d0 + i]), kb = y[i] + bf16_to_f32(mk[d0 + i + HALF]);
+        const f32x4 &cq = i < 2 ? c01 : c23;
+        const float c = cq[2 * (i & 1)], s = cq[2 * (i & 1) + 1];
+        ra[i] = ka * c - kb * s;
+        rb[i] = ka * s + kb * c;
+      }
+      if (live) {
+        *(u32x2 *)(kd + d0) = u32x2{cvt2(ra[0], ra[1]), cvt2(ra[2], ra[3])};
+        *(u32x2 *)(kd + d0 + HALF) = u32x2{cvt2(rb[0], rb[1]), cvt2(rb[2], rb[3])};
+      }
+    }
+#pragma unroll
+    for (int T = 0; T < NDT; ++T) {
+      const f32x4 x = wup_times<RV>(av[T], cv, g);
+      const int d0 = 16 * T + 4 * g;
+      float o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = x[i] + bf16_to_f32(mv[d0 + i]);
+      if (live) *(u32x2 *)(vd + d0) = u32x2{cvt2(o[0], o[1]), cvt2(o[2], o[3])};
+    }
+  }
+  if (bad && lane == 0) atomicOr(a.err, bad);
+}
+
+// ---------------------------------------------------------------- full-cache decode
+
+template <int DH>
+__global__ __launch_bounds__(256, 2) void full_decode_kernel(AttnArgs a) {
+  constexpr int NW = 4;           // heads per workgroup
+  constexpr int QD = DH / 4;      // dims per lane (a quarter of a row)
+  constexpr int NV = QD / 8;      // 16-byte loads per lane per row
+  constexpr int HALF = DH / 2;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int t = lane >> 2, part = lane & 3;
+
+  int bid = blockIdx.x;
+  const int split = bid % a.splits;
+  bid /= a.splits;
+  const int hg = bid % a.head_groups;
+  const int row = bid / a.head_groups;
+  const int h = hg * NW + w;
+  int qp = a.q_pos[row], ctx = a.ctx_len[row];
+  int errbits = 0;
+  if (ctx < 1 || ctx > a.max_ctx || qp < 0 || qp >= a.rope_len) {
+    errbits |= LLA_DEVERR_CTX;
+    ctx = 0;
+    qp = 0;
+  }
+  const int npages = (ctx + kPage - 1) / kPage;
+  const int lp0 = split * a.pages_per_split;
+  const int lp1 = min(lp0 + a.pages_per_split, npages);
+
+  // q' = scale log2(e) R(q_pos) q: this lane's dims part*QD .. + QD - 1
+  float qr[QD];
+  {
+    const uint16_t *qrow = (const uint16_t *)a.q + ((long long)row * a.H + h) * DH;
+    const float *rq = a.rope + (long long)qp * DH;
+#pragma unroll
+    for (int j = 0; j < QD; ++j) {
+      const int d = part * QD + j;
+      const int i = d < HALF ? d : d - HALF;  // RoPE pair
+      const float qa = bf16_to_f32(qrow[i]), qb = bf16_to_f32(qrow[i + HALF]);
+      const float c = rq[2 * i], s = rq[2 * i + 1];
+      qr[j] = a.qscale * (d < HALF ? qa * c - qb * s : qa * s + qb * c);
+    }
+  }
+
+  const int *pt_row = a.page_table + (long long)row * a.max_pages;
+  const long long ls = (long long)kPage * DH;
+  auto load = [&](int lp, u32x4 (&kq)[NV], u32x4 (&vq)[NV], int &ok) {
+    const int e = pt_row[lp];
+    ok = e >= 0 && e < a.num_pages;
+    const long long off = ((long long)(ok ? e : 0) * a.H + h) * ls + t * DH + part * QD;
+    const uint16_t *kb = (const uint16_t *)a.k_pool + off;
+    const uint16_t *vb = (const uint16_t *)a.v_pool + off;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      kq[j] = __builtin_nontemporal_load((const u32x4 *)(kb + 8 * j));
+      vq[j] = __builtin_nontemporal_load((const u32x4 *)(vb + 8 * j));
+    }
+  };
+
+  float m_ref = -INFINITY, z = 0.f, acc[QD];
+#pragma unroll
+  for (int j = 0; j < QD; ++j) acc[j] = 0.f;
+
+  auto compute = [&](int lp, const u32x4 (&kq)[NV], const u32x4 (&vq)[NV], int ok) {
+    if (!ok) errbits |= LLA_DEVERR_PAGE;
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s = fmaf(qr[8 * j + 2 * e], bf16_lo(kq[j][e]), s);
+        s = fmaf(qr[8 * j + 2 * e + 1], bf16_hi(kq[j][e]), s);
+      }
+    s += dpp<kDppQuadSwap1>(s);
+    s += dpp<kDppQuadSwap2>(s);
+    // rows past ctx_len (last page) and rows of a bad page take no weight
+    if (!ok || lp * kPage + t >= ctx) s = -INFINITY;
+    float mx = s;
+    mx = fmaxf(mx, __shfl_xor(mx, 4));
+    mx = fmaxf(mx, __shfl_xor(mx, 8));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (mx > m_ref + 8.f) {  // uniform: mx is the wave's max
+      const float al = m_ref == -INFINITY ? 0.f : fast_exp2(m_ref - mx);
+#pragma unroll
+      for (int j = 0; j < QD; ++j) acc[j] *= al;
+      z *= al;
+      m_ref = mx;
+    }
+    const float p = m_ref == -INFINITY ? 0.f : fast_exp2(s - m_ref);
+    z += p;
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[8 * j + 2 * e] = fmaf(p, bf16_lo(vq[j][e]), acc[8 * j + 2 * e]);
+        acc[8 * j + 2 * e + 1] = fmaf(p, bf16_hi(vq[j][e]), acc[8 * j + 2 * e + 1]);
+      }
+  };
+
+  // two pages in flight beyond the one computed
+  u32x4 k0[NV], v0[NV], k1[NV], v1[NV], k2[NV], v2[NV];
+  int ok0 = 1, ok1 = 1, ok2 = 1;
+  const int n = lp1 - lp0;
+  if (n > 0) load(lp0, k0, v0, ok0);
+  if (n > 1) load(lp0 + 1, k1, v1, ok1);
+  for (int i = 0; i < n; i += 3) {
+    if (i + 2 < n) load(lp0 + i + 2, k2, v2, ok2);
+    compute(lp0 + i, k0, v0, ok0);
+    if (i + 1 >= n) break;
+    if (i + 3 < n) load(lp0 + i + 3, k0, v0, ok0);
+    compute(lp0 + i + 1, k1, v1, ok1);
+    if (i + 2 >= n) break;
+    if (i + 4 < n) load(lp0 + i + 4, k1, v1, ok1);
+    compute(lp0 + i + 2, k2, v2, ok2);
+  }
+
+  // z: every lane of a token added p, so the wave sum counts each token 4 times
+  for (int o = 4; o < 64; o <<= 1) z += __shfl_xor(z, o);
+  z += __shfl_xor(z, 1);
+  z += __shfl_xor(z, 2);
+  z *= 0.25f;
+#pragma unroll
+  for (int j = 0; j < QD; ++j)
+    for (int o = 4; o < 64; o <<= 1) acc[j] += __shfl_xor(acc[j], o);  // over the 16 tokens
+  if (errbits) atomicOr(a.err, errbits);
+  const bool bad = __syncthreads_or(errbits != 0);
+  if (a.splits > 1) {
+    float *part_p = a.partials + (((long long)row * a.H + h) * a.splits + split) * (DH + 2);
+    if (t == 0) {
+#pragma unroll
+      for (int j = 0; j < QD; ++j) part_p[part * QD + j] = acc[j];
+    }
+    if (lane == 0) {
+      part_p[DH] = m_ref;
+      part_p[DH + 1] = bad ? __builtin_nanf("") : z;
+    }
+    return;
+  }
+  if (t == 0) {
+    const float inv = bad ? __builtin_nanf("") : 1.f / z;
+    uint16_t *orow = (uint16_t *)a.out + ((long long)row * a.H + h) * DH + part * QD;
+#pragma unroll
+    for (int j = 0; j < QD; j += 2) *(uint32_t *)(orow + j) = cvt2(acc[j] * inv, acc[j + 1] * inv);
+  }
+}
+
+// ---------------------------------------------------------------- dispatch
+
+#define LLA_RECON_SHAPES(X) \
+  X(64, 16, 32)             \
+  X(128, 16, 32)            \
+  X(128, 32, 64)            \
+  X(128, 64, 64)
+
+bool reconstruct_supported(int dtype, int variant, int d_head, int r_k, int r_v) {
+  if (dtype != LLA_BF16 || variant != LLA_PER_HEAD) return false;
+#define X(DH, RK, RV) \
+  if (d_head == DH && r_k == RK && r_v == RV) return true;
+  LLA_RECON_SHAPES(X)
+#undef X
+  return false;
+}
+
+hipError_t launch_reconstruct(int d_head, int r_k, int r_v, const AttnArgs &a, void *k_full, void *v_full,
+                              int batch, hipStream_t stream) {
+  const int ppw = 4;
+  const long long groups = (a.pages_per_split + 4 * ppw - 1) / (4 * ppw);
+  const long long gx = (long long)batch * groups;
+  if (gx > 0x7FFFFFFF || a.H > 65535) return hipErrorInvalidConfiguration;
+#define X(DH, RK, RV)                                                                                   \
+  if (d_head == DH && r_k == RK && r_v == RV) {                                                         \
+    hipLaunchKernelGGL((reconstruct_kernel<DH, RK, RV>), dim3((unsigned)gx, (unsigned)a.H), dim3(256), 0, \
+                       stream, a, (char *)k_full, (char *)v_full, ppw);                                  \
+    return hipGetLastError();                                                                           \
+  }
+  LLA_RECON_SHAPES(X)
+#undef X
+  return hipErrorInvalidConfiguration;
+}
+
+bool full_decode_supported(int dtype, int variant, int d_head) {
+  return dtype == LLA_BF16 && variant == LLA_PER_HEAD && (d_head == 64 || d_head == 128);
+}
+
+hipError_t launch_full_decode(int d_head, const AttnArgs &a, hipStream_t stream) {
+  if (a.H % 4 || a.head_groups * 4 != a.H) return hipErrorInvalidConfiguration;
+  const long long grid = (long long)a.rows * a.head_groups * a.splits;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  if (d_head == 128)
+    hipLaunchKernelGGL(full_decode_kernel<128>, dim3((unsigned)grid), dim3(256), 0, stream, a);
+  else if (d_head == 64)
+    hipLaunchKernelGGL(full_decode_kernel<64>, dim3((unsigned)grid), dim3(256), 0, stream, a);
+  else
+    return hipErrorInvalidConfiguration;
+  return hipGetLastError();
+}
+
+}  // namespace lla

@@ -71,6 +71,12 @@ hipError_t launch_encode(int dtype, int r_k, int r_v, const EncodeArgs &a, hipSt
 bool prefill_supported(int dtype, int variant, int d_head, int r_k, int r_v);
 hipError_t launch_prefill(int d_head, int r_k, int r_v, const AttnArgs &a, hipStream_t stream);
 hipError_t launch_merge(int dtype, int d_head, int r_v, const AttnArgs &a, hipStream_t stream);
+hipError_t launch_merge_ident(int d_head, const AttnArgs &a, hipStream_t stream);
+bool reconstruct_supported(int dtype, int variant, int d_head, int r_k, int r_v);
+hipError_t launch_reconstruct(int d_head, int r_k, int r_v, const AttnArgs &a, void *k_full, void *v_full,
+                              int batch, hipStream_t stream);
+bool full_decode_supported(int dtype, int variant, int d_head);
+hipError_t launch_full_decode(int d_head, const AttnArgs &a, hipStream_t stream);
 hipError_t launch_rope_table(int n_pos, int d_head, double base, float *table, hipStream_t s);
 
 }  // namespace lla

@@ -18,8 +18,9 @@
 
 namespace lla {
 
-// One wave per (row, head); 4 per workgroup.
-template <bool BF>
+// One wave per (row, head); 4 per workgroup.  IDENT: the partials already hold
+// the output row (full-cache decode, r_v = d_head): no up-projection, no mu.
+template <bool BF, bool IDENT = false>
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int d_head, int r_v) {
   extern __shared__ float s_an[];  // [4][r_v]
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -46,7 +47,9 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int d_head, int 
       acc = fmaf(exp2f(m - M), pb[(long long)s * (r_v + 2) + r], acc);
     }
     an[r] = acc / Z;
+    if constexpr (IDENT) ((uint16_t *)a.out)[rh * d_head + r] = (uint16_t)f32_to_bf16(an[r]);
   }
+  if constexpr (IDENT) return;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -78,6 +81,15 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int d_head, int 
       ((float *)a.out)[rh * d_head + e] = o;
     }
   }
+}
+
+hipError_t launch_merge_ident(int d_head, const AttnArgs &a, hipStream_t stream) {
+  const long long waves = (long long)a.rows * a.H;
+  const long long blocks = (waves + 3) / 4;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((merge_kernel<true, true>), dim3((unsigned)blocks), dim3(256), sizeof(float) * 4 * d_head,
+                     stream, a, d_head, d_head);
+  return hipGetLastError();
 }
 
 hipError_t launch_merge(int dtype, int d_head, int r_v, const AttnArgs &a, hipStream_t stream) {

@@ -19,11 +19,11 @@ GEN_LIB_PATH = os.path.join(_PKG, "liblla_gen.so")
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH = 0, -1, -2, -3, -4
 PER_HEAD, TWO_D = 0, 1
 F32, BF16 = 0, 1
-OP_ENCODE, OP_DECODE, OP_PREFILL = 0, 1, 2
+OP_ENCODE, OP_DECODE, OP_PREFILL, OP_RECONSTRUCT, OP_FULL_DECODE = 0, 1, 2, 3, 4
 DEVERR_CTX, DEVERR_PAGE, DEVERR_APPEND = 1, 2, 4
 
 EXPORTS = ["lla_rope_table", "lla_workspace_bytes", "lla_encode_append", "lla_decode_attn",
-           "lla_prefill_attn", "lla_cache_scalars", "lla_supported", "lla_status_string",
+           "lla_prefill_attn", "lla_reconstruct_kv", "lla_full_decode_attn", "lla_cache_scalars", "lla_supported", "lla_status_string",
            "lla_last_error"]
 
 
@@ -72,6 +72,8 @@ def load() -> ctypes.CDLL:
     lib.lla_encode_append.argtypes = [pd, pc, pk, P, P, P, I, I, I, P, S, P]
     lib.lla_decode_attn.argtypes = [pd, pc, pk, P, I, I, I, P, P, P, I, F, P, P, S, P]
     lib.lla_prefill_attn.argtypes = [pd, pc, pk, P, I, I, I, I, P, P, I, F, P, P, S, P]
+    lib.lla_reconstruct_kv.argtypes = [pd, pc, pk, P, I, I, I, P, I, P, P, P, S, P]
+    lib.lla_full_decode_attn.argtypes = [pd, pk, P, P, P, I, P, P, P, I, F, P, P, S, P]
     lib.lla_cache_scalars.argtypes = [pd, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
     lib.lla_supported.argtypes = [pd, I]
     lib.lla_status_string.argtypes = [I]
@@ -79,6 +81,7 @@ def load() -> ctypes.CDLL:
     lib.lla_last_error.argtypes = []
     lib.lla_last_error.restype = ctypes.c_char_p
     for name in ("lla_rope_table", "lla_encode_append", "lla_decode_attn", "lla_prefill_attn",
+                 "lla_reconstruct_kv", "lla_full_decode_attn",
                  "lla_cache_scalars", "lla_supported"):
         getattr(lib, name).restype = I
     _lib = lib
@@ -188,6 +191,22 @@ def decode_attn(dims: Dims, codec: Codec, cache: Cache, rope: torch.Tensor, laye
                                   _ptr(rope), rope.shape[0], layer, loop, _ptr(q), _ptr(q_pos),
                                   _ptr(ctx_len), max_ctx, scale, _ptr(out), _ptr(ws), ws.numel(),
                                   _stream(stream)))
+
+
+def reconstruct_kv(dims: Dims, codec: Codec, cache: Cache, rope: torch.Tensor, layer: int, loop: int,
+                   ctx_len, max_ctx: int, k_full, v_full, ws: torch.Tensor, stream=None) -> None:
+    """Rebuild the full (rotated K, V) cache of (layer, loop) from the latents."""
+    _check(load().lla_reconstruct_kv(ctypes.byref(dims), ctypes.byref(codec), ctypes.byref(cache),
+                                     _ptr(rope), rope.shape[0], layer, loop, _ptr(ctx_len), max_ctx,
+                                     _ptr(k_full), _ptr(v_full), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def full_decode_attn(dims: Dims, cache: Cache, k_full, v_full, rope: torch.Tensor, q, q_pos, ctx_len,
+                     max_ctx: int, out, ws: torch.Tensor, scale: float = 0.0, stream=None) -> None:
+    """Decode attention over a full K/V cache (the cache's page table)."""
+    _check(load().lla_full_decode_attn(ctypes.byref(dims), ctypes.byref(cache), _ptr(k_full), _ptr(v_full),
+                                       _ptr(rope), rope.shape[0], _ptr(q), _ptr(q_pos), _ptr(ctx_len),
+                                       max_ctx, scale, _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def prefill_attn(dims: Dims, codec: Codec, cache: Cache, rope: torch.Tensor, layer: int, loop: int,

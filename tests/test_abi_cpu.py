@@ -130,3 +130,33 @@ def test_encode_and_prefill_validation_errors():
     assert pre == lla.ERR_INVALID_ARG
     assert lib.lla_rope_table(ctypes.byref(d), -1, FAKE, NULL) == lla.ERR_INVALID_ARG
     assert lla.load().lla_status_string(lla.ERR_WORKSPACE) == b"workspace missing or too small"
+
+
+def test_full_cache_validation_and_planning():
+    """Host-side checks of lla_reconstruct_kv / lla_full_decode_attn (no launch)."""
+    lib = lla.load()
+    d = _dims()
+    codec = lla.Codec(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
+    cache = lla.Cache(0x1000, 0x1000, 0x1000, 32, 256, 8192)
+    E = lla.ERR_INVALID_ARG
+    rec = lambda **kw: lib.lla_reconstruct_kv(
+        ctypes.byref(kw.get("dims", d)), ctypes.byref(codec), ctypes.byref(cache), kw.get("rope", FAKE), 4096,
+        kw.get("layer", 0), kw.get("loop", 0), kw.get("ctx", FAKE), kw.get("max_ctx", 4096),
+        kw.get("kf", FAKE), FAKE, kw.get("ws", FAKE), kw.get("ws_bytes", 16), NULL)
+    assert rec(layer=24) == E and rec(loop=4) == E
+    assert rec(rope=NULL) == E and rec(max_ctx=4097) == E and rec(ctx=NULL) == E and rec(kf=NULL) == E
+    assert rec(dims=_dims(dtype=lla.F32, d_head=64)) == lla.ERR_UNSUPPORTED
+    assert rec() == lla.ERR_WORKSPACE
+    full = lambda **kw: lib.lla_full_decode_attn(
+        ctypes.byref(kw.get("dims", d)), ctypes.byref(cache), FAKE, FAKE, FAKE, 4096, kw.get("q", FAKE),
+        FAKE, FAKE, kw.get("max_ctx", 4096), 0.0, FAKE, FAKE, kw.get("ws_bytes", 16), NULL)
+    assert full(q=NULL) == E and full(max_ctx=0) == E
+    assert full(dims=_dims(H=6)) == lla.ERR_UNSUPPORTED
+    assert full() == lla.ERR_WORKSPACE
+    # workspace: header only for the rebuild; split partials (d_head + 2 floats) for the decode
+    assert lla.workspace_bytes(d, lla.OP_RECONSTRUCT, 32, 4096) == 256
+    big = lla.workspace_bytes(d, lla.OP_FULL_DECODE, 32, 4096)
+    assert big > 256 and (big - 256) % (32 * 16 * (128 + 2) * 4) < 256
+    assert lla.workspace_bytes(d, lla.OP_FULL_DECODE, 1024, 4096) == 256   # one split at large batch
+    assert lla.supported(d, lla.OP_RECONSTRUCT) and lla.supported(d, lla.OP_FULL_DECODE)
+    assert not lla.supported(_dims(r_k=96, r_v=160), lla.OP_RECONSTRUCT)
