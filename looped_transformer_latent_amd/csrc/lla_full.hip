@@ -14,9 +14,11 @@
 //  * full_decode_kernel: ordinary decode attention over the full cache,
 //    s_j = scale <R(q_pos) q, k_j>, out = sum_j e^{s_j - m} v_j / sum_j e^{s_j - m}.
 //    Bound by HBM (2 d_head bf16 per token and head).  One wave per (row,
-//    head, split); lane (t, part) holds a quarter of token t's K and V row;
-//    pages are loaded two ahead; online softmax in base 2 with the running
-//    max moved only when it grows by more than 8.
+//    head, split); every load instruction reads 1 KiB of a page contiguously
+//    (lane l: bytes 16 l .. + 15), so a lane holds 8 dims of d_head / 16
+//    tokens; scores reduce within the token's lanes (DPP), the value sum per
+//    lane at the end.  Pages are loaded four ahead; online softmax in base 2
+//    with the running max moved only when it grows by more than 8.
 #include "lla_device.h"
 #include "lla_internal.h"
 
@@ -48,19 +50,19 @@ __device__ __forceinline__ void load_wup(WupTile<RK> &w, const uint16_t *row, in
   if constexpr (RK % 32) w.a16 = *(const u32x2 *)(row + 32 * (RK / 32) + 4 * g);
 }
 
+// The B-operand: this lane's token row of the latent page, same K slots.
 template <int RK>
-__device__ __forceinline__ f32x4 wup_times(const WupTile<RK> &w, const uint16_t *crow, int g) {
+using LatRow = WupTile<RK>;
+
+template <int RK>
+__device__ __forceinline__ f32x4 wup_times(const WupTile<RK> &w, const LatRow<RK> &b) {
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int ks = 0; ks < RK / 32; ++ks) {
-    const u32x4 b = *(const u32x4 *)(crow + 32 * ks + 8 * g);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w.a32[ks]), as_bf16x8(b), acc, 0, 0, 0);
-  }
-  if constexpr (RK % 32) {
-    const u32x2 b = *(const u32x2 *)(crow + 32 * (RK / 32) + 4 * g);
+  for (int ks = 0; ks < RK / 32; ++ks)
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w.a32[ks]), as_bf16x8(b.a32[ks]), acc, 0, 0, 0);
+  if constexpr (RK % 32)
     acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, w.a16),
-                                                     __builtin_bit_cast(bf16x4, b), acc, 0, 0, 0);
-  }
+                                                     __builtin_bit_cast(bf16x4, b.a16), acc, 0, 0, 0);
   return acc;
 }
 
@@ -98,52 +100,78 @@ __global__ __launch_bounds__(256) void reconstruct_kernel(AttnArgs a, char *k_fu
     load_wup<RK>(ak[T], wk + (16 * T + n) * RK, g);
     load_wup<RV>(av[T], wv + (16 * T + n) * RV, g);
   }
-  const long long ls = (long long)kPage * DH;  // elements per (page, head)
-  int bad = 0;
-  for (int lp = lp0; lp < min(lp0 + ppw, npg); ++lp) {
-    const int e = a.page_table[(long long)b * a.max_pages + lp];
-    if (e < 0 || e >= a.num_pages) {  // uniform over the wave
-      bad |= LLA_DEVERR_PAGE;
-      continue;
-    }
-    const int pos = lp * kPage + n;  // this lane's token
-    const bool live = pos < ctx;
-    const uint16_t *ck = (const uint16_t *)a.k_pool + (long long)e * a.pool_page_stride_k +
-                         (long long)h * a.pool_head_stride_k + n * RK;
-    const uint16_t *cv = (const uint16_t *)a.v_pool + (long long)e * a.pool_page_stride_v +
-                         (long long)h * a.pool_head_stride_v + n * RV;
-    uint16_t *kd = (uint16_t *)k_full + ((long long)e * a.H + h) * ls + n * DH;
-    uint16_t *vd = (uint16_t *)v_full + ((long long)e * a.H + h) * ls + n * DH;
-    const float *rr = a.rope + (long long)min(pos, a.rope_len - 1) * DH;
+  // RoPE of token 16 lp + n by angle addition: the page's first position is
+  // one table row shared by every lane (a broadcast read), the offset n is
+  // fixed per lane (fp32 products of two table rotations)
+  f32x4 rd[NDT / 2][2];
+  {
+    const float *r0 = a.rope + (long long)min(n, a.rope_len - 1) * DH;
 #pragma unroll
     for (int T = 0; T < NDT / 2; ++T) {
-      const f32x4 x = wup_times<RK>(ak[T], ck, g);
-      const f32x4 y = wup_times<RK>(ak[T + NDT / 2], ck, g);
-      const int d0 = 16 * T + 4 * g;  // RoPE pairs d0 .. d0 + 3
-      const f32x4 c01 = *(const f32x4 *)(rr + 2 * d0), c23 = *(const f32x4 *)(rr + 2 * d0 + 4);
-      float ra[4], rb[4];
+      rd[T][0] = *(const f32x4 *)(r0 + 2 * (16 * T + 4 * g));
+      rd[T][1] = *(const f32x4 *)(r0 + 2 * (16 * T + 4 * g) + 4);
+    }
+  }
+  const long long ls = (long long)kPage * DH;  // elements per (page, head)
+  int bad = 0;
+  // latent rows of page lp (lane n: token n of the page), one page ahead
+  const int lp_end = min(lp0 + ppw, npg);
+  auto page_of = [&](int lp) { return a.page_table[(long long)b * a.max_pages + lp]; };
+  auto fetch = [&](int e, LatRow<RK> &rk, LatRow<RV> &rv) {
+    const long long pe = e >= 0 && e < a.num_pages ? e : 0;
+    load_wup<RK>(rk, (const uint16_t *)a.k_pool + pe * a.pool_page_stride_k + (long long)h * a.pool_head_stride_k + n * RK, g);
+    load_wup<RV>(rv, (const uint16_t *)a.v_pool + pe * a.pool_page_stride_v + (long long)h * a.pool_head_stride_v + n * RV, g);
+  };
+  LatRow<RK> ck, ck_n;
+  LatRow<RV> cv, cv_n;
+  int e = page_of(lp0);
+  fetch(e, ck, cv);
+  for (int lp = lp0; lp < lp_end; ++lp) {
+    const int e_n = lp + 1 < lp_end ? page_of(lp + 1) : e;
+    if (lp + 1 < lp_end) fetch(e_n, ck_n, cv_n);
+    if (e < 0 || e >= a.num_pages) {  // uniform over the wave
+      bad |= LLA_DEVERR_PAGE;
+    } else {
+      const int pos = lp * kPage + n;  // this lane's token
+      const bool live = pos < ctx;
+      uint16_t *kd = (uint16_t *)k_full + ((long long)e * a.H + h) * ls + n * DH;
+      uint16_t *vd = (uint16_t *)v_full + ((long long)e * a.H + h) * ls + n * DH;
+      const float *rr = a.rope + (long long)(lp * kPage) * DH;  // page's first position (< ctx)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float ka = x[i] + bf16_to_f32(mk[d0 + i]), kb = y[i] + bf16_to_f32(mk[d0 + i + HALF]);
-        const f32x4 &cq = i < 2 ? c01 : c23;
-        const float c = cq[2 * (i & 1)], s = cq[2 * (i & 1) + 1];
-        ra[i] = ka * c - kb * s;
-        rb[i] = ka * s + kb * c;
+      for (int T = 0; T < NDT / 2; ++T) {
+        const f32x4 x = wup_times<RK>(ak[T], ck);
+        const f32x4 y = wup_times<RK>(ak[T + NDT / 2], ck);
+        const int d0 = 16 * T + 4 * g;  // RoPE pairs d0 .. d0 + 3
+        const f32x4 c01 = *(const f32x4 *)(rr + 2 * d0), c23 = *(const f32x4 *)(rr + 2 * d0 + 4);
+        float ra[4], rb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float ka = x[i] + bf16_to_f32(mk[d0 + i]), kb = y[i] + bf16_to_f32(mk[d0 + i + HALF]);
+          const f32x4 &cq = i < 2 ? c01 : c23;
+          const float cb = cq[2 * (i & 1)], sb = cq[2 * (i & 1) + 1];
+          const float cd = rd[T][i >> 1][2 * (i & 1)], sd = rd[T][i >> 1][2 * (i & 1) + 1];
+          const float c = cb * cd - sb * sd, s = sb * cd + cb * sd;
+          ra[i] = ka * c - kb * s;
+          rb[i] = ka * s + kb * c;
+        }
+        if (live) {
+          *(u32x2 *)(kd + d0) = u32x2{cvt2(ra[0], ra[1]), cvt2(ra[2], ra[3])};
+          *(u32x2 *)(kd + d0 + HALF) = u32x2{cvt2(rb[0], rb[1]), cvt2(rb[2], rb[3])};
+        }
       }
-      if (live) {
-        *(u32x2 *)(kd + d0) = u32x2{cvt2(ra[0], ra[1]), cvt2(ra[2], ra[3])};
-        *(u32x2 *)(kd + d0 + HALF) = u32x2{cvt2(rb[0], rb[1]), cvt2(rb[2], rb[3])};
+#pragma unroll
+      for (int T = 0; T < NDT; ++T) {
+        const f32x4 x = wup_times<RV>(av[T], cv);
+        const int d0 = 16 * T + 4 * g;
+        float o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = x[i] + bf16_to_f32(mv[d0 + i]);
+        if (live) *(u32x2 *)(vd + d0) = u32x2{cvt2(o[0], o[1]), cvt2(o[2], o[3])};
       }
     }
-#pragma unroll
-    for (int T = 0; T < NDT; ++T) {
-      const f32x4 x = wup_times<RV>(av[T], cv, g);
-      const int d0 = 16 * T + 4 * g;
-      float o[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = x[i] + bf16_to_f32(mv[d0 + i]);
-      if (live) *(u32x2 *)(vd + d0) = u32x2{cvt2(o[0], o[1]), cvt2(o[2], o[3])};
-    }
+    e = e_n;
+    ck = ck_n;
+    cv = cv_n;
   }
   if (bad && lane == 0) atomicOr(a.err, bad);
 }
@@ -152,12 +180,16 @@ __global__ __launch_bounds__(256) void reconstruct_kernel(AttnArgs a, char *k_fu
 
 template <int DH>
 __global__ __launch_bounds__(256, 2) void full_decode_kernel(AttnArgs a) {
-  constexpr int NW = 4;           // heads per workgroup
-  constexpr int QD = DH / 4;      // dims per lane (a quarter of a row)
-  constexpr int NV = QD / 8;      // 16-byte loads per lane per row
+  constexpr int NW = 4;              // heads per workgroup
+  constexpr int LPR = DH / 8;        // lanes per token row (8 dims = 16 bytes each)
+  constexpr int TPL = 16 * LPR / 64; // tokens per lane per page (one per 16-byte load)
+  constexpr int RPW = 64 / LPR;      // token rows covered by one load instruction
   constexpr int HALF = DH / 2;
+  constexpr int LOOK = 4, NB = LOOK + 1;  // pages in flight beyond the one computed
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int t = lane >> 2, part = lane & 3;
+  // load j of a page reads bytes 1024 j + 16 lane: token RPW j + lane / LPR,
+  // dims 8 (lane % LPR) .. + 7
+  const int tr = lane / LPR, d0 = 8 * (lane % LPR);
 
   int bid = blockIdx.x;
   const int split = bid % a.splits;
@@ -176,109 +208,122 @@ __global__ __launch_bounds__(256, 2) void full_decode_kernel(AttnArgs a) {
   const int lp0 = split * a.pages_per_split;
   const int lp1 = min(lp0 + a.pages_per_split, npages);
 
-  // q' = scale log2(e) R(q_pos) q: this lane's dims part*QD .. + QD - 1
-  float qr[QD];
+  // q' = scale log2(e) R(q_pos) q for dims d0 .. d0 + 7
+  float qr[8];
   {
     const uint16_t *qrow = (const uint16_t *)a.q + ((long long)row * a.H + h) * DH;
     const float *rq = a.rope + (long long)qp * DH;
 #pragma unroll
-    for (int j = 0; j < QD; ++j) {
-      const int d = part * QD + j;
+    for (int e = 0; e < 8; ++e) {
+      const int d = d0 + e;
       const int i = d < HALF ? d : d - HALF;  // RoPE pair
       const float qa = bf16_to_f32(qrow[i]), qb = bf16_to_f32(qrow[i + HALF]);
       const float c = rq[2 * i], s = rq[2 * i + 1];
-      qr[j] = a.qscale * (d < HALF ? qa * c - qb * s : qa * s + qb * c);
+      qr[e] = a.qscale * (d < HALF ? qa * c - qb * s : qa * s + qb * c);
     }
   }
 
   const int *pt_row = a.page_table + (long long)row * a.max_pages;
   const long long ls = (long long)kPage * DH;
-  auto load = [&](int lp, u32x4 (&kq)[NV], u32x4 (&vq)[NV], int &ok) {
+  auto load = [&](int lp, u32x4 (&kq)[TPL], u32x4 (&vq)[TPL], int &ok) {
     const int e = pt_row[lp];
     ok = e >= 0 && e < a.num_pages;
-    const long long off = ((long long)(ok ? e : 0) * a.H + h) * ls + t * DH + part * QD;
+    const long long off = ((long long)(ok ? e : 0) * a.H + h) * ls + 8 * lane;
     const uint16_t *kb = (const uint16_t *)a.k_pool + off;
     const uint16_t *vb = (const uint16_t *)a.v_pool + off;
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      kq[j] = __builtin_nontemporal_load((const u32x4 *)(kb + 8 * j));
-      vq[j] = __builtin_nontemporal_load((const u32x4 *)(vb + 8 * j));
+    for (int j = 0; j < TPL; ++j) {
+      kq[j] = __builtin_nontemporal_load((const u32x4 *)(kb + 512 * j));
+      vq[j] = __builtin_nontemporal_load((const u32x4 *)(vb + 512 * j));
     }
   };
 
-  float m_ref = -INFINITY, z = 0.f, acc[QD];
+  float m_ref = -INFINITY, z = 0.f, acc[8];
 #pragma unroll
-  for (int j = 0; j < QD; ++j) acc[j] = 0.f;
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
 
-  auto compute = [&](int lp, const u32x4 (&kq)[NV], const u32x4 (&vq)[NV], int ok) {
+  // sum over the LPR lanes of a token row (LPR = 16: one DPP row; 8: half a row)
+  auto row_sum = [&](float x) {
+    x += dpp<kDppQuadSwap1>(x);
+    x += dpp<kDppQuadSwap2>(x);
+    x += dpp<kDppHalfMirror>(x);
+    if constexpr (LPR == 16) x += dpp<kDppMirror>(x);
+    return x;
+  };
+
+  auto compute = [&](int lp, const u32x4 (&kq)[TPL], const u32x4 (&vq)[TPL], int ok) {
     if (!ok) errbits |= LLA_DEVERR_PAGE;
-    float s = 0.f;
+    float s[TPL];
+    float mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < NV; ++j)
+    for (int j = 0; j < TPL; ++j) {
+      float x = 0.f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        s = fmaf(qr[8 * j + 2 * e], bf16_lo(kq[j][e]), s);
-        s = fmaf(qr[8 * j + 2 * e + 1], bf16_hi(kq[j][e]), s);
+        x = fmaf(qr[2 * e], bf16_lo(kq[j][e]), x);
+        x = fmaf(qr[2 * e + 1], bf16_hi(kq[j][e]), x);
       }
-    s += dpp<kDppQuadSwap1>(s);
-    s += dpp<kDppQuadSwap2>(s);
-    // rows past ctx_len (last page) and rows of a bad page take no weight
-    if (!ok || lp * kPage + t >= ctx) s = -INFINITY;
-    float mx = s;
-    mx = fmaxf(mx, __shfl_xor(mx, 4));
-    mx = fmaxf(mx, __shfl_xor(mx, 8));
+      x = row_sum(x);
+      // rows past ctx_len (last page) and rows of a bad page take no weight
+      if (!ok || lp * kPage + RPW * j + tr >= ctx) x = -INFINITY;
+      s[j] = x;
+      mx = fmaxf(mx, x);
+    }
+    // the page's max: over this lane's tokens, then over the other token rows
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if constexpr (LPR == 8) mx = fmaxf(mx, __shfl_xor(mx, 8));
     if (mx > m_ref + 8.f) {  // uniform: mx is the wave's max
       const float al = m_ref == -INFINITY ? 0.f : fast_exp2(m_ref - mx);
 #pragma unroll
-      for (int j = 0; j < QD; ++j) acc[j] *= al;
+      for (int e = 0; e < 8; ++e) acc[e] *= al;
       z *= al;
       m_ref = mx;
     }
-    const float p = m_ref == -INFINITY ? 0.f : fast_exp2(s - m_ref);
-    z += p;
 #pragma unroll
-    for (int j = 0; j < NV; ++j)
+    for (int j = 0; j < TPL; ++j) {
+      const float p = m_ref == -INFINITY ? 0.f : fast_exp2(s[j] - m_ref);
+      z += p;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        acc[8 * j + 2 * e] = fmaf(p, bf16_lo(vq[j][e]), acc[8 * j + 2 * e]);
-        acc[8 * j + 2 * e + 1] = fmaf(p, bf16_hi(vq[j][e]), acc[8 * j + 2 * e + 1]);
+        acc[2 * e] = fmaf(p, bf16_lo(vq[j][e]), acc[2 * e]);
+        acc[2 * e + 1] = fmaf(p, bf16_hi(vq[j][e]), acc[2 * e + 1]);
       }
+    }
   };
 
-  // two pages in flight beyond the one computed
-  u32x4 k0[NV], v0[NV], k1[NV], v1[NV], k2[NV], v2[NV];
-  int ok0 = 1, ok1 = 1, ok2 = 1;
+  u32x4 kb[NB][TPL], vb[NB][TPL];
+  int okb[NB];
+#pragma unroll
+  for (int u = 0; u < NB; ++u) okb[u] = 1;
   const int n = lp1 - lp0;
-  if (n > 0) load(lp0, k0, v0, ok0);
-  if (n > 1) load(lp0 + 1, k1, v1, ok1);
-  for (int i = 0; i < n; i += 3) {
-    if (i + 2 < n) load(lp0 + i + 2, k2, v2, ok2);
-    compute(lp0 + i, k0, v0, ok0);
-    if (i + 1 >= n) break;
-    if (i + 3 < n) load(lp0 + i + 3, k0, v0, ok0);
-    compute(lp0 + i + 1, k1, v1, ok1);
-    if (i + 2 >= n) break;
-    if (i + 4 < n) load(lp0 + i + 4, k1, v1, ok1);
-    compute(lp0 + i + 2, k2, v2, ok2);
+#pragma unroll
+  for (int u = 0; u < LOOK; ++u)
+    if (u < n) load(lp0 + u, kb[u], vb[u], okb[u]);
+  for (int i = 0; i < n; i += NB) {
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      if (i + u < n) {
+        if (i + u + LOOK < n) load(lp0 + i + u + LOOK, kb[(u + LOOK) % NB], vb[(u + LOOK) % NB], okb[(u + LOOK) % NB]);
+        compute(lp0 + i + u, kb[u], vb[u], okb[u]);
+      }
+    }
   }
 
-  // z: every lane of a token added p, so the wave sum counts each token 4 times
-  for (int o = 4; o < 64; o <<= 1) z += __shfl_xor(z, o);
-  z += __shfl_xor(z, 1);
-  z += __shfl_xor(z, 2);
-  z *= 0.25f;
+  // z: every lane of a token row added that token's weight, so the wave sum
+  // counts each token LPR times; acc sums over this lane's tokens only
+  for (int o = 1; o < 64; o <<= 1) z += __shfl_xor(z, o);
+  z *= 1.f / LPR;
 #pragma unroll
-  for (int j = 0; j < QD; ++j)
-    for (int o = 4; o < 64; o <<= 1) acc[j] += __shfl_xor(acc[j], o);  // over the 16 tokens
+  for (int e = 0; e < 8; ++e)
+    for (int o = LPR; o < 64; o <<= 1) acc[e] += __shfl_xor(acc[e], o);  // over the token rows
   if (errbits) atomicOr(a.err, errbits);
   const bool bad = __syncthreads_or(errbits != 0);
   if (a.splits > 1) {
     float *part_p = a.partials + (((long long)row * a.H + h) * a.splits + split) * (DH + 2);
-    if (t == 0) {
+    if (tr == 0) {
 #pragma unroll
-      for (int j = 0; j < QD; ++j) part_p[part * QD + j] = acc[j];
+      for (int e = 0; e < 8; ++e) part_p[d0 + e] = acc[e];
     }
     if (lane == 0) {
       part_p[DH] = m_ref;
@@ -286,11 +331,11 @@ __global__ __launch_bounds__(256, 2) void full_decode_kernel(AttnArgs a) {
     }
     return;
   }
-  if (t == 0) {
+  if (tr == 0) {
     const float inv = bad ? __builtin_nanf("") : 1.f / z;
-    uint16_t *orow = (uint16_t *)a.out + ((long long)row * a.H + h) * DH + part * QD;
-#pragma unroll
-    for (int j = 0; j < QD; j += 2) *(uint32_t *)(orow + j) = cvt2(acc[j] * inv, acc[j + 1] * inv);
+    uint16_t *orow = (uint16_t *)a.out + ((long long)row * a.H + h) * DH + d0;
+    *(u32x4 *)orow = u32x4{cvt2(acc[0] * inv, acc[1] * inv), cvt2(acc[2] * inv, acc[3] * inv),
+                           cvt2(acc[4] * inv, acc[5] * inv), cvt2(acc[6] * inv, acc[7] * inv)};
   }
 }
 
