@@ -30,6 +30,8 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 DECODE_SOURCES = ("lla_decode_g.hip", "lla_device.h", "lla_internal.h", "lla_api.hip")
 PREFILL_SOURCES = ("lla_prefill.hip", "lla_device.h", "lla_internal.h", "lla_api.hip")
+FULL_SOURCES = ("lla_full.hip", "lla_merge.hip", "lla_device.h", "lla_internal.h", "lla_api.hip")
+HBM_BYTES = 288e9
 
 
 def kernel_source_digest(names=DECODE_SOURCES) -> str:
@@ -69,6 +71,7 @@ def parse():
                    help="decode workload: ouro1.4b-21x-b768-paged (default), ouro1.4b-21x-b32, "
                         "ouro1.4b-21x-b768-contig, lla2d-t8-h32-b128")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-full-cache", action="store_true", help="skip the full K/V cache baseline")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle sample time")
     p.add_argument("--calibrate-copy", type=float, default=0.0, metavar="GIB",
                    help="only run a plain device copy of GIB gibibytes, three times (a known "
@@ -243,6 +246,77 @@ def bench_prefill(w, D, codec, cache, rope, calls, n_new, dt_t, p0, stream):
                          "algorithmic_flops_per_launch": flops}}
 
 
+def bench_full_cache(w, D, codec, cache, rope, calls, q, q_pos, ctx, out_lat, lat_ms, stream):
+    """The full-memory baseline on the same step: each (loop, layer) call's K/V
+    rebuilt as a full bf16 cache (lla_reconstruct_kv) and attended by a plain
+    decode over it (lla_full_decode_attn), against the latent decode's time.
+    One (loop, layer) slice of the full cache is resident at a time; the whole
+    model's full cache is reported with whether it would fit in HBM."""
+    import torch
+    from looped_transformer_latent_amd import lla
+    from looped_transformer_latent_amd import workloads as wl
+
+    sub = list(range(len(calls)))[-4:]            # the last four (loop, layer) calls of the step
+    shape = (w.num_pages, w.H, wl.PAGE, w.d_head)
+    kf = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    vf = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    ws_r = lla.workspace(D, lla.OP_RECONSTRUCT, w.batch, w.ctx)
+    ws_f = lla.workspace(D, lla.OP_FULL_DECODE, w.batch, w.ctx)
+    out = torch.empty_like(out_lat[0])
+    mk = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    ev = [(mk(), mk()) for _ in sub]
+    rel = 0.0
+
+    def one_pass(record):
+        nonlocal rel
+        for j, i in enumerate(sub):
+            t, l = calls[i]
+            if record:
+                ev[j][0][0].record(stream)
+            lla.reconstruct_kv(D, codec, cache, rope, l, t, ctx, w.ctx, kf, vf, ws_r)
+            if record:
+                ev[j][0][1].record(stream)
+                ev[j][1][0].record(stream)
+            lla.full_decode_attn(D, cache, kf, vf, rope, q[i], q_pos, ctx, w.ctx, out, ws_f)
+            if record:
+                ev[j][1][1].record(stream)
+            # same query, same latents: the two paths agree to bf16 rounding
+            a, b = out.float(), out_lat[i].float()
+            rel = max(rel, ((a - b).abs().amax(-1) / b.abs().amax(-1)).max().item())
+
+    one_pass(False)
+    torch.cuda.synchronize()
+    rec_ms, full_ms = [], []
+    for _ in range(2):
+        one_pass(True)
+        torch.cuda.synchronize()
+        rec_ms += [r[0].elapsed_time(r[1]) for r, _ in ev]
+        full_ms += [f[0].elapsed_time(f[1]) for _, f in ev]
+    assert lla.device_error_word(ws_r) == 0 and lla.device_error_word(ws_f) == 0
+    assert rel < 2e-2, rel
+    rec, full = float(np.mean(rec_ms)), float(np.mean(full_ms))
+    tokens = w.batch * w.ctx
+    full_bytes = tokens * w.H * w.d_head * 2 * 2          # K and V, bf16, one (loop, layer)
+    lat_bytes = tokens * w.read_bytes()
+    gbs = full_bytes / (full / 1e3) / 1e9
+    whole = tokens * w.D * w.T * w.H * w.d_head * 2 * 2    # every layer's per-loop K/V
+    return {"kernels": ["reconstruct_kernel", "full_decode_kernel"], "calls": len(sub),
+            "latent_decode_ms": lat_ms, "full_decode_ms": full, "reconstruct_ms": rec,
+            "reconstruct_then_attend_ms": rec + full,
+            "latent_speedup_vs_full_decode": full / lat_ms,
+            "latent_speedup_vs_reconstruct_then_attend": (rec + full) / lat_ms,
+            "reconstruct_gbs": (full_bytes + lat_bytes) / (rec / 1e3) / 1e9,
+            "bytes_per_token_per_call": {"full": w.H * w.d_head * 4, "latent": w.read_bytes()},
+            "full_cache_bytes_whole_model": whole, "full_cache_fits_hbm": whole <= HBM_BYTES,
+            "max_row_rel_diff_vs_latent_decode": rel,
+            "roofline": {"kernel": "full_decode_kernel", "bound": "hbm", "achieved": gbs,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                         "traffic": profiled_traffic(w.name, "full_decode_kernel", FULL_SOURCES),
+                         "traffic_unit": "HBM bytes per launch (rocprofv3)",
+                         "algorithmic_bytes_per_launch": full_bytes},
+            "cpu_baseline": "the oracle's decode is this same reconstruct-then-attend: see cpu_baseline"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -384,6 +458,10 @@ def main():
     # ctx - n_new .. ctx - 1 attend over the cache, one call per (loop, layer)
     if n_new > 1 and lla.supported(D, lla.OP_PREFILL):
         result["prefill"] = bench_prefill(w, D, codec, cache, rope, calls, n_new, dt_t, pos0, stream)
+    # the full-memory baseline of the same calls (per-head bf16 shapes it covers)
+    if not args.no_full_cache and lla.supported(D, lla.OP_RECONSTRUCT) and lla.supported(D, lla.OP_FULL_DECODE):
+        result["full_cache"] = bench_full_cache(w, D, codec, cache, rope, calls, q, q_pos, ctx, out,
+                                                kern_avg_ms, stream)
     if not args.no_cpu_baseline:
         if "prefill" in result:
             result["prefill"]["cpu_baseline"] = cpu_prefill_baseline(
