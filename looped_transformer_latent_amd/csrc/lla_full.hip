@@ -6,11 +6,13 @@
 //  * reconstruct_kernel: k_j = R(j)(mu_k,t + c_k,j W_up,k,t^T) and
 //    v_j = mu_v,t + c_v,j W_up,v,t^T (eq. (3), RoPE after reconstruction) for
 //    every cached token, written in bf16 to a paged full cache with the latent
-//    cache's page table ([num_pages][H][16][d_head]).  One wave rebuilds one
-//    16-token page of one head on the matrix cores: W_up rows are the
-//    A-operand (registers), the page's latent rows the B-operand, so the
-//    accumulator holds 4 consecutive dims of one token and both halves of each
-//    RoPE pair in one lane.
+//    cache's page table ([num_pages][H][16][d_head]).  One wave rebuilds 16
+//    consecutive pages of one head, one page at a time on the matrix cores:
+//    W_up rows are the A-operand (registers), the page's latent rows the
+//    B-operand, so the accumulator holds 4 consecutive dims of one token and
+//    both halves of each RoPE pair in one lane.  The bf16 page tile goes
+//    through LDS and leaves in 1 KiB-contiguous stores (the write stream is
+//    most of the traffic).
 //  * full_decode_kernel: ordinary decode attention over the full cache,
 //    s_j = scale <R(q_pos) q, k_j>, out = sum_j e^{s_j - m} v_j / sum_j e^{s_j - m}.
 //    Bound by HBM (2 d_head bf16 per token and head).  One wave per (row,
@@ -113,6 +115,11 @@ __global__ __launch_bounds__(256) void reconstruct_kernel(AttnArgs a, char *k_fu
     }
   }
   const long long ls = (long long)kPage * DH;  // elements per (page, head)
+  // each wave's page tile of K and of V is staged in LDS, so that it leaves in
+  // 1 KiB-contiguous stores (16-byte pad per row)
+  constexpr int SROW = DH + 8;
+  __shared__ __align__(16) uint16_t s_stage[4][2][kPage * SROW];
+  uint16_t *sk = s_stage[w][0], *sv = s_stage[w][1];
   int bad = 0;
   // latent rows of page lp (lane n: token n of the page), one page ahead
   const int lp_end = min(lp0 + ppw, npg);
@@ -132,10 +139,8 @@ __global__ __launch_bounds__(256) void reconstruct_kernel(AttnArgs a, char *k_fu
     if (e < 0 || e >= a.num_pages) {  // uniform over the wave
       bad |= LLA_DEVERR_PAGE;
     } else {
-      const int pos = lp * kPage + n;  // this lane's token
-      const bool live = pos < ctx;
-      uint16_t *kd = (uint16_t *)k_full + ((long long)e * a.H + h) * ls + n * DH;
-      uint16_t *vd = (uint16_t *)v_full + ((long long)e * a.H + h) * ls + n * DH;
+      uint16_t *kd = (uint16_t *)k_full + ((long long)e * a.H + h) * ls;
+      uint16_t *vd = (uint16_t *)v_full + ((long long)e * a.H + h) * ls;
       const float *rr = a.rope + (long long)(lp * kPage) * DH;  // page's first position (< ctx)
 #pragma unroll
       for (int T = 0; T < NDT / 2; ++T) {
@@ -154,10 +159,8 @@ __global__ __launch_bounds__(256) void reconstruct_kernel(AttnArgs a, char *k_fu
           ra[i] = ka * c - kb * s;
           rb[i] = ka * s + kb * c;
         }
-        if (live) {
-          *(u32x2 *)(kd + d0) = u32x2{cvt2(ra[0], ra[1]), cvt2(ra[2], ra[3])};
-          *(u32x2 *)(kd + d0 + HALF) = u32x2{cvt2(rb[0], rb[1]), cvt2(rb[2], rb[3])};
-        }
+        *(u32x2 *)(sk + n * SROW + d0) = u32x2{cvt2(ra[0], ra[1]), cvt2(ra[2], ra[3])};
+        *(u32x2 *)(sk + n * SROW + d0 + HALF) = u32x2{cvt2(rb[0], rb[1]), cvt2(rb[2], rb[3])};
       }
 #pragma unroll
       for (int T = 0; T < NDT; ++T) {
@@ -166,7 +169,20 @@ __global__ __launch_bounds__(256) void reconstruct_kernel(AttnArgs a, char *k_fu
         float o[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[i] = x[i] + bf16_to_f32(mv[d0 + i]);
-        if (live) *(u32x2 *)(vd + d0) = u32x2{cvt2(o[0], o[1]), cvt2(o[2], o[3])};
+        *(u32x2 *)(sv + n * SROW + d0) = u32x2{cvt2(o[0], o[1]), cvt2(o[2], o[3])};
+      }
+      // store j, lane l: elements 512 j + 8 l .. + 7 of the tile, i.e. token
+      // (512 j + 8 l) / DH; slots of tokens at or past ctx_len stay untouched
+      // (the stage is wave-private and LDS accesses of one wave stay in order)
+#pragma unroll
+      for (int j = 0; j < kPage * DH / 512; ++j) {
+        const int el = 512 * j + 8 * lane, t = el / DH, c = el % DH;
+        const u32x4 kv = *(const u32x4 *)(sk + t * SROW + c);
+        const u32x4 vv = *(const u32x4 *)(sv + t * SROW + c);
+        if (lp * kPage + t < ctx) {
+          __builtin_nontemporal_store(kv, (u32x4 *)(kd + el));
+          __builtin_nontemporal_store(vv, (u32x4 *)(vd + el));
+        }
       }
     }
     e = e_n;
@@ -358,7 +374,7 @@ bool reconstruct_supported(int dtype, int variant, int d_head, int r_k, int r_v)
 
 hipError_t launch_reconstruct(int d_head, int r_k, int r_v, const AttnArgs &a, void *k_full, void *v_full,
                               int batch, hipStream_t stream) {
-  const int ppw = 4;
+  const int ppw = 16;
   const long long groups = (a.pages_per_split + 4 * ppw - 1) / (4 * ppw);
   const long long gx = (long long)batch * groups;
   if (gx > 0x7FFFFFFF || a.H > 65535) return hipErrorInvalidConfiguration;
