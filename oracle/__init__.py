@@ -65,6 +65,12 @@ def lib():
         _lib.lla_oracle_prefill.restype = _i
         _lib.lla_oracle_prefill.argtypes = ([_i] * 9 + [_d] + [_p] * 7 + [_i] * 6 +
                                             [_p, _p, _d, _p, _i])
+        _lib.lla_oracle_rope_key_append.restype = _i
+        _lib.lla_oracle_rope_key_append.argtypes = [_i, _i, _i, _d, _i, _p, _p, _i, _i, _i, _p, _p,
+                                                    _i, _i, _i]
+        _lib.lla_oracle_decoupled_decode.restype = _i
+        _lib.lla_oracle_decoupled_decode.argtypes = ([_i] * 9 + [_d] + [_p] * 8 + [_i] * 5 +
+                                                     [_p, _p, _p, _d, _p, _i])
         _lib.lla_oracle_max_threads.restype = _i
         _lib.lla_oracle_max_threads.argtypes = [_i]
     return _lib
@@ -168,6 +174,48 @@ def prefill(dims: dict, codec: dict, k_pool, v_pool, page_table, layer: int, loo
     rc = lib().lla_oracle_prefill(*head, *[_ptr(a) for a in params], *[_ptr(a) for a in pools],
                                   _ptr(pt), B, pt.shape[1], pools[0].shape[1], layer, loop,
                                   n_q, _ptr(qs), _ptr(pp), scale, _ptr(out), threads)
+    return out, rc
+
+
+def rope_key_append(dims: dict, d_rope: int, kr_pool: np.ndarray, page_table: np.ndarray,
+                    kr_new: np.ndarray, pos0: np.ndarray, layer0: int) -> int:
+    """Decoupled-RoPE rotary keys: rotate kr_new [n_layers][B][n_new][d_rope] at
+    positions pos0[b] + n and store them in kr_pool [D][num_pages][P][d_rope]
+    (in place, storage arrays)."""
+    dt = dims["dtype"]
+    pt = np.ascontiguousarray(page_table, dtype=np.int32)
+    p0 = np.ascontiguousarray(pos0, dtype=np.int32)
+    assert kr_pool.flags["C_CONTIGUOUS"] and kr_pool.shape[-1] == d_rope
+    kn = _stored(kr_new, dt)
+    n_layers, B, n_new = kn.shape[0], kn.shape[1], kn.shape[2]
+    assert B == pt.shape[0]
+    return lib().lla_oracle_rope_key_append(
+        dims["D"], dims["page_size"], d_rope, float(dims.get("rope_base", 10000.0)), dt,
+        _ptr(kr_pool), _ptr(pt), B, pt.shape[1], kr_pool.shape[1], _ptr(kn), _ptr(p0),
+        n_new, layer0, n_layers)
+
+
+def decoupled_decode(dims: dict, codec: dict, k_pool, v_pool, kr_pool, page_table, layer: int,
+                     loop: int, q: np.ndarray, q_pos: np.ndarray, ctx_len: np.ndarray,
+                     d_rope: int, scale: float | None = None,
+                     threads: int = 0) -> tuple[np.ndarray, int]:
+    """Decode with a NoPE content path and a rotary branch of width d_rope.
+    q [B][H][d + d_rope].  Returns (out [B][H][d] float64, status)."""
+    head, params, pools, pt = _attn_common(dims, codec, k_pool, v_pool, page_table)
+    assert dims["variant"] == PER_HEAD
+    B, H, d = pt.shape[0], dims["H"], dims["d_head"]
+    qs = _stored(q, dims["dtype"])
+    krs = _stored(kr_pool, dims["dtype"])
+    assert qs.size == B * H * (d + d_rope) and krs.shape[1] == pools[0].shape[1]
+    qp = np.ascontiguousarray(q_pos, dtype=np.int32)
+    cl = np.ascontiguousarray(ctx_len, dtype=np.int32)
+    out = np.empty((B, H, d), dtype=np.float64)
+    scale = (1.0 / np.sqrt(d + d_rope)) if scale is None else float(scale)
+    T, D, H_, d_, r_k, r_v, _variant, dt, P, base = head
+    rc = lib().lla_oracle_decoupled_decode(
+        T, D, H_, d_, r_k, r_v, d_rope, dt, P, base, *[_ptr(a) for a in params],
+        *[_ptr(a) for a in pools], _ptr(krs), _ptr(pt), B, pt.shape[1], pools[0].shape[1],
+        layer, loop, _ptr(qs), _ptr(qp), _ptr(cl), scale, _ptr(out), threads)
     return out, rc
 
 

@@ -360,6 +360,122 @@ int lla_oracle_prefill(int T, int D, int H, int d, int r_k, int r_v, int variant
   return rc;
 }
 
+/* ---------- decoupled RoPE: NoPE content path + explicit rotary branch ---------- */
+/*
+ * [CR] 四:结果 item 10 (appendix J): full RoPE depends on position and blocks
+ * absorbing the K decoder into attention, so the absorbed variant scores with
+ * a NoPE content path plus an explicit rotary branch of width d_rope (64 or
+ * 32).  Readings (listed in the design doc): the content key of loop t is the eq. (3)
+ * reconstruction, not rotated; the rotary key is one d_rope-vector per
+ * (token, layer), shared by all heads and loops, stored after rotation at the
+ * token's position with RoPE over d_rope dims (pairs (i, i + d_rope/2), angle
+ * p * base^(-2i/d_rope)); a query row holds [q_content (d) ; q_rotary (d_rope)],
+ * and q_rotary is rotated at q_pos; the score is
+ *   s_j = scale (<q_content, k_hat_j> + <R(q_pos) q_rotary, kr_j>),
+ * scale defaulting to 1/sqrt(d + d_rope); V is rebuilt by eq. (3) as in decode.
+ * Layouts: kr_pool [D][num_pages][P][d_rope]; kr_new [n_layers][B][n_new][d_rope];
+ * q [B][H][d + d_rope]; out [B][H][d].  Per-head LLA only.
+ */
+
+/* Rotate kr_new at position pos0[b] + n and store it (rounded once to the
+ * storage type) in the slot of that logical token, for layers layer0 .. +n_layers-1.
+ * Tokens whose slot is outside the page table (or whose entry is invalid) are
+ * skipped and reported with OR_BAD_INDEX. */
+int lla_oracle_rope_key_append(int D, int P, int d_rope, double rope_base, int dtype,
+                               void *kr_pool, const int32_t *page_table, int batch,
+                               int max_pages, int num_pages, const void *kr_new,
+                               const int32_t *pos0, int n_new, int layer0, int n_layers) {
+  if (D <= 0 || P <= 0 || d_rope <= 0 || d_rope % 2 || layer0 < 0 || n_layers < 0 ||
+      layer0 + n_layers > D || n_new < 0 || (dtype != OR_F32 && dtype != OR_BF16))
+    return OR_BAD_ARG;
+  int rc = OR_OK;
+  double *x = (double *)malloc(sizeof(double) * d_rope);
+  double *y = (double *)malloc(sizeof(double) * d_rope);
+  for (int l = 0; l < n_layers; ++l)
+    for (int b = 0; b < batch; ++b)
+      for (int n = 0; n < n_new; ++n) {
+        int64_t pos = (int64_t)pos0[b] + n;
+        int64_t slot = lla_oracle_slot(page_table, max_pages, num_pages, P, b, pos);
+        if (slot < 0) { rc = OR_BAD_INDEX; continue; }
+        size_t src = (((size_t)l * batch + b) * n_new + n) * d_rope;
+        for (int e = 0; e < d_rope; ++e) x[e] = ld(kr_new, dtype, src + e);
+        lla_oracle_rope(x, d_rope, (double)pos, rope_base, y);
+        size_t dst = ((size_t)(layer0 + l) * num_pages * P + (size_t)slot) * d_rope;
+        for (int e = 0; e < d_rope; ++e) st(kr_pool, dtype, dst + e, y[e]);
+      }
+  free(x); free(y);
+  return rc;
+}
+
+/* Decode with the decoupled score above: one query row per sequence. */
+int lla_oracle_decoupled_decode(int T, int D, int H, int d, int r_k, int r_v, int d_rope,
+                                int dtype, int P, double rope_base, const void *mu_k,
+                                const void *mu_v, const void *wup_k, const void *wup_v,
+                                const void *k_pool, const void *v_pool, const void *kr_pool,
+                                const int32_t *page_table, int batch, int max_pages,
+                                int num_pages, int layer, int loop, const void *q,
+                                const int32_t *q_pos, const int32_t *ctx_len, double scale,
+                                double *out, int threads) {
+  odims m = {T, D, H, d, r_k, r_v, OR_PER_HEAD, dtype, P, rope_base};
+  if (!dims_ok(&m) || d_rope <= 0 || d_rope % 2 || layer < 0 || layer >= D || loop < 0 || loop >= T)
+    return OR_BAD_ARG;
+  set_threads(threads);
+  const int dq = d + d_rope;
+  int rc = OR_OK;
+#pragma omp parallel for schedule(dynamic) reduction(min : rc)
+  for (int bh = 0; bh < batch * H; ++bh) {
+    int b = bh / H, h = bh % H;
+    double *o = out + (size_t)bh * d;
+    for (int e = 0; e < d; ++e) o[e] = NAN;
+    int64_t ctx = ctx_len[b];
+    if (ctx < 1 || ctx > (int64_t)max_pages * P) { rc = OR_BAD_INDEX; continue; }
+    double *qc = (double *)malloc(sizeof(double) * d);
+    double *qr = (double *)malloc(sizeof(double) * d_rope);
+    double *qrr = (double *)malloc(sizeof(double) * d_rope);
+    double *ck = (double *)malloc(sizeof(double) * r_k);
+    double *cv = (double *)malloc(sizeof(double) * r_v);
+    double *kh = (double *)malloc(sizeof(double) * d);
+    double *vh = (double *)malloc(sizeof(double) * d * (size_t)ctx);
+    double *s = (double *)malloc(sizeof(double) * (size_t)ctx);
+    for (int e = 0; e < d; ++e) qc[e] = ld(q, dtype, (size_t)bh * dq + e);
+    for (int e = 0; e < d_rope; ++e) qr[e] = ld(q, dtype, (size_t)bh * dq + d + e);
+    lla_oracle_rope(qr, d_rope, (double)q_pos[b], rope_base, qrr); /* rotary branch of q */
+    size_t muo = mu_off(&m, layer, h, loop);
+    size_t wko = wup_off(&m, layer, h, loop, r_k), wvo = wup_off(&m, layer, h, loop, r_v);
+    int r1 = OR_OK;
+    for (int64_t j = 0; j < ctx; ++j) {
+      int64_t slot = lla_oracle_slot(page_table, max_pages, num_pages, P, b, j);
+      if (slot < 0) { r1 = OR_BAD_INDEX; break; }
+      size_t pk = pool_off(&m, num_pages, layer, h, slot, r_k);
+      size_t pv = pool_off(&m, num_pages, layer, h, slot, r_v);
+      size_t pr = ((size_t)layer * num_pages * P + (size_t)slot) * d_rope;
+      for (int k = 0; k < r_k; ++k) ck[k] = ld(k_pool, dtype, pk + k);
+      for (int k = 0; k < r_v; ++k) cv[k] = ld(v_pool, dtype, pv + k);
+      reconstruct(&m, mu_k, wup_k, muo, wko, r_k, ck, kh);                /* eq. (3), K, no RoPE */
+      reconstruct(&m, mu_v, wup_v, muo, wvo, r_v, cv, vh + (size_t)j * d); /* eq. (3), V */
+      double dot = 0.0;
+      for (int e = 0; e < d; ++e) dot += qc[e] * kh[e];
+      for (int e = 0; e < d_rope; ++e) dot += qrr[e] * ld(kr_pool, dtype, pr + e);
+      s[j] = scale * dot;
+    }
+    if (r1 == OR_OK) {
+      double mx = -INFINITY;
+      for (int64_t j = 0; j < ctx; ++j) mx = s[j] > mx ? s[j] : mx;
+      double z = 0.0;
+      for (int64_t j = 0; j < ctx; ++j) { s[j] = exp(s[j] - mx); z += s[j]; }
+      for (int e = 0; e < d; ++e) {
+        double acc = 0.0;
+        for (int64_t j = 0; j < ctx; ++j) acc += s[j] * vh[(size_t)j * d + e];
+        o[e] = acc / z;
+      }
+    } else {
+      rc = r1 < rc ? r1 : rc;
+    }
+    free(qc); free(qr); free(qrr); free(ck); free(cv); free(kh); free(vh); free(s);
+  }
+  return rc;
+}
+
 /* Number of OpenMP threads a parallel region would use (for reporting). */
 int lla_oracle_max_threads(int threads) {
   set_threads(threads);
