@@ -8,7 +8,7 @@
  * section:
  *   [CR] "Looped Latent Attention: 跨循环 KV 压缩精读" (cc.laoqi.cc close reading of
  *        arXiv 2607.15456v2), section 二:方法 items 1-3 and 6, section 四:结果 item 9
- *        (Table 5).
+ *        (Table 5) and item 10 (appendix J: decoupled RoPE).
  *   [GS] gist.science summary of arXiv 2607.15456, "Technisches Resümee" /
  *        "Kernmechanismus" (text form of eq. (2)-(4)).
  *   encoder  eq. (2): c = (x - mu) W_down, x = [x_1; ...; x_T] (loop-major).
@@ -68,7 +68,15 @@ enum {
 
 enum { LLA_PER_HEAD = 0, LLA_2D = 1 }; /* [CR] 方法 item 6: LLA-2D folds heads into one latent */
 enum { LLA_F32 = 0, LLA_BF16 = 1 };
-enum { LLA_OP_ENCODE = 0, LLA_OP_DECODE = 1, LLA_OP_PREFILL = 2, LLA_OP_RECONSTRUCT = 3, LLA_OP_FULL_DECODE = 4 };
+enum {
+  LLA_OP_ENCODE = 0,
+  LLA_OP_DECODE = 1,
+  LLA_OP_PREFILL = 2,
+  LLA_OP_RECONSTRUCT = 3,
+  LLA_OP_FULL_DECODE = 4,
+  LLA_OP_ROPE_KEY_APPEND = 5,
+  LLA_OP_DECOUPLED_DECODE = 6
+};
 
 /* Device-side error bits (workspace byte 0). */
 enum {
@@ -126,7 +134,8 @@ int32_t lla_rope_table(const lla_dims *dims, int32_t n_pos, float *table, hipStr
 /* Bytes of workspace that `op` needs.  batch = sequences; max_ctx = the
  * host-known upper bound on every context the call may read (decode: on
  * ctx_len; prefill: on p0[b] + n); n = n_q for prefill, n_layers for encode,
- * ignored for decode.  Returns 0 for invalid arguments. */
+ * d_rope for the decoupled decode, ignored otherwise.  Returns 0 for invalid
+ * arguments or shapes without a kernel. */
 size_t lla_workspace_bytes(const lla_dims *dims, int32_t op, int32_t batch, int32_t max_ctx,
                            int32_t n);
 
@@ -213,6 +222,52 @@ int32_t lla_full_decode_attn(const lla_dims *dims, const lla_cache *cache, const
                              const void *q, const int32_t *q_pos, const int32_t *ctx_len,
                              int32_t max_ctx, float scale, void *out, void *workspace,
                              size_t ws_bytes, hipStream_t stream);
+
+/* Decoupled RoPE ([CR] 四:结果 item 10, appendix J).  Full RoPE rotates each
+ * rebuilt key by its own position, which keeps the K decoder out of the query;
+ * the decoupled variant scores with a NoPE content path (the eq. (3) key, not
+ * rotated) plus an explicit rotary branch of width d_rope:
+ *   s_j = scale (<q_c, mu_k,t + c_k,j W_up,k,t^T> + <R_r(q_pos) q_r, kr_j>),
+ *   out = sum_j softmax_j(s) v_hat_j   (v_hat_j as in lla_decode_attn),
+ * where kr_j is one rotary key per (token, layer), shared by all heads and
+ * loops and stored after rotation at its position, and R_r is RoPE over the
+ * d_rope dims (pairs (i, i + d_rope/2), angle p * rope_base^(-2i/d_rope)).
+ * The RoPE table for the branch is lla_rope_table() of a copy of dims with
+ * d_head = d_rope: [rope_r_len][d_rope/2][2].
+ *   kr_pool  bf16 [D][num_pages][page_size][d_rope], paged by cache->page_table.
+ *
+ * lla_rope_key_append writes the rotary keys of tokens pos0[b] + n
+ * (n < n_new) for layers layer0 .. layer0 + n_layers - 1:
+ *   kr_pool[layer][slot] = R_r(pos) kr_new[layer - layer0][b][n],  fp32, rounded once to bf16.
+ *   kr_new  bf16 [n_layers][batch][n_new][d_rope] (before rotation).
+ * A token whose position is outside the page table row is skipped with
+ * LLA_DEVERR_APPEND, one past the table with LLA_DEVERR_CTX, one on an invalid
+ * page with LLA_DEVERR_PAGE.  Workspace: the error word (LLA_OP_ROPE_KEY_APPEND).
+ * bf16 only; d_rope even, 2..1024. */
+int32_t lla_rope_key_append(const lla_dims *dims, const lla_cache *cache, int32_t d_rope, void *kr_pool,
+                            const float *rope_r, int32_t rope_r_len, const void *kr_new, const int32_t *pos0,
+                            int32_t n_new, int32_t layer0, int32_t n_layers, void *workspace,
+                            size_t ws_bytes, hipStream_t stream);
+
+/* Decode attention with the decoupled score above, one query per sequence,
+ * for one (layer, loop).  The content path is absorbed into the query
+ * (q~ = W_up,k,t^T q_c, r_k wide; the <q_c, mu_k,t> term is the same for every
+ * token of a row and cancels in the softmax), so no key is rebuilt; V is
+ * summed in latent space and up-projected once.
+ *   q        bf16 [batch][H][d_head + d_rope]: content part, then rotary part
+ *   out      bf16 [batch][H][d_head]
+ *   q_pos    device int32 [batch], in [0, rope_r_len) (else LLA_DEVERR_CTX)
+ *   ctx_len  device int32 [batch], in [1, max_ctx]; max_ctx <= max_pages_per_seq * page_size
+ *   scale    0 selects 1/sqrt(d_head + d_rope)
+ * codec->mu_k is not read.  Workspace: lla_workspace_bytes(.., LLA_OP_DECOUPLED_DECODE,
+ * batch, max_ctx, d_rope).  Supported: bf16 per-head, (d_head, r_k, r_v) in
+ * (128,16,32) with H a multiple of 16 and (128,96,160) with H a multiple of 4,
+ * d_rope 32 or 64.  Device errors as lla_decode_attn. */
+int32_t lla_decoupled_decode_attn(const lla_dims *dims, const lla_codec *codec, const lla_cache *cache,
+                                  int32_t d_rope, const void *kr_pool, const float *rope_r, int32_t rope_r_len,
+                                  int32_t layer, int32_t loop, const void *q, const int32_t *q_pos,
+                                  const int32_t *ctx_len, int32_t max_ctx, float scale, void *out,
+                                  void *workspace, size_t ws_bytes, hipStream_t stream);
 
 /* Eq. (4): persistent cache scalars per token and layer, for the teacher
  * (2 T H d_head) and for the latent cache ((r_k + r_v) H, or r_k + r_v for

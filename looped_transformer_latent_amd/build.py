@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-LLA_SOURCES = ["lla_api.hip", "lla_decode.hip", "lla_decode_g.hip", "lla_decode2d.hip", "lla_encode.hip", "lla_full.hip", "lla_merge.hip", "lla_prefill.hip", "lla_rope.hip"]
+LLA_SOURCES = ["lla_api.hip", "lla_absorbed.hip", "lla_decode.hip", "lla_decode_g.hip", "lla_decode2d.hip", "lla_encode.hip", "lla_full.hip", "lla_merge.hip", "lla_prefill.hip", "lla_rope.hip"]
 GEN_SOURCES = ["gen/lla_gen.hip"]
 
 # Packed-fp32 VALU ops are disabled for every HIP source; hipcc's host pass

@@ -73,6 +73,8 @@ bool plan_attn_2d(const lla_dims *d, long long rows, int max_ctx, AttnPlan *p) {
   return true;
 }
 
+void plan_decode_splits(const lla_dims *d, long long rows, int max_ctx, int hpw, int waves, AttnPlan *p);
+
 bool plan_attn(const lla_dims *d, long long rows, int max_ctx, AttnPlan *p, bool prefill = false) {
   p->prefill = false;
   if (prefill && prefill_supported(d->dtype, d->variant, d->d_head, d->r_k, d->r_v)) {
@@ -100,9 +102,30 @@ bool plan_attn(const lla_dims *d, long long rows, int max_ctx, AttnPlan *p, bool
     }
   }
   if (!hpw) return false;
+  plan_decode_splits(d, rows, max_ctx, hpw, waves, p);
+  return true;
+}
+
+// Decoupled-RoPE absorbed decode: the same grid and splits as the latent
+// decode, with the workgroup shapes built for (d_head, r_k, r_v, d_rope).
+bool plan_decoupled(const lla_dims *d, long long rows, int max_ctx, int d_rope, AttnPlan *p) {
+  if (d->variant != LLA_PER_HEAD || d->dtype != LLA_BF16) return false;
+  const int cand[3][2] = {{2, 8}, {1, 8}, {1, 4}};
+  for (const auto &c : cand) {
+    if (d->H % (c[0] * c[1]) == 0 && absorbed_supported(d->d_head, d->r_k, d->r_v, d_rope, c[0], c[1])) {
+      p->prefill = false;
+      p->two_d = false;
+      plan_decode_splits(d, rows, max_ctx, c[0], c[1], p);
+      return true;
+    }
+  }
+  return false;
+}
+
+void plan_decode_splits(const lla_dims *d, long long rows, int max_ctx, int hpw, int waves, AttnPlan *p) {
   p->hpw = hpw;
   p->waves = waves;
-  p->head_groups = H / (hpw * waves);
+  p->head_groups = d->H / (hpw * waves);
   p->chunk_pages = kDecodeRing;
   const int pages = (max_ctx + kPage - 1) / kPage;
   const long long base = rows * p->head_groups;
@@ -122,7 +145,6 @@ bool plan_attn(const lla_dims *d, long long rows, int max_ctx, AttnPlan *p, bool
   p->splits = (pages + pps - 1) / pps;
   if (p->splits < 1) p->splits = 1;
   plan_workspace(d, rows, p);
-  return true;
 }
 
 // Full-cache decode: 4 heads per workgroup, split the context until about
@@ -163,6 +185,8 @@ int32_t check_launch(hipError_t e) {
   return LLA_ERR_LAUNCH;
 }
 
+void fill_layer(const lla_dims *d, const lla_codec *c, const lla_cache *k, int layer, int loop, AttnArgs *a);
+
 // Common validation + argument filling for decode and prefill.
 int32_t attn_call(const lla_dims *d, const lla_codec *c, const lla_cache *k, const float *rope,
                   int32_t rope_len, int32_t layer, int32_t loop, const void *q,
@@ -195,12 +219,46 @@ int32_t attn_call(const lla_dims *d, const lla_codec *c, const lla_cache *k, con
   if (!ws || ws_bytes < p.bytes) return fail(LLA_ERR_WORKSPACE, "workspace missing or too small");
   if (rows == 0) return LLA_OK;
 
-  const size_t es = esize(d);
-  const long long T = d->T, H = d->H, dh = d->d_head, rk = d->r_k, rv = d->r_v;
-  const long long np = k->num_pages;
   AttnArgs a = {};
   a.q = q;
   a.out = out;
+  fill_layer(d, c, k, layer, loop, &a);
+  a.page_table = k->page_table;
+  a.max_pages = k->max_pages_per_seq;
+  a.num_pages = k->num_pages;
+  a.rope = rope;
+  a.rope_len = rope_len;
+  a.q_pos = q_pos;
+  a.ctx_len = ctx_len;
+  a.p0 = p0;
+  a.n_q = prefill ? n_q : 1;
+  a.prefill = prefill;
+  a.rows = (int)rows;
+  a.H = d->H;
+  a.max_ctx = max_ctx;
+  a.splits = p.splits;
+  a.pages_per_split = p.pages_per_split;
+  a.head_groups = p.head_groups;
+  a.heads_per_wave = p.hpw;
+  a.waves = p.waves;
+  a.chunk_pages = p.chunk_pages;
+  const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)d->d_head);
+  a.qscale = sc * 1.4426950408889634f;
+  a.err = (int *)ws;
+  a.partials = (float *)((char *)ws + p.partials_off);
+  if (p.prefill) return check_launch(launch_prefill(d->d_head, d->r_k, d->r_v, a, stream));
+  const int32_t rc = check_launch(p.two_d ? launch_decode2d(d->d_head, d->r_k, d->r_v, a, stream)
+                                          : launch_decode(d->dtype, d->d_head, d->r_k, d->r_v, a, stream));
+  if (rc != LLA_OK || p.splits == 1) return rc;
+  return check_launch(launch_merge(d->dtype, d->d_head, d->r_v, a, stream));
+}
+
+// Pool and codec pointers of (layer, loop), for both variants.
+void fill_layer(const lla_dims *d, const lla_codec *c, const lla_cache *k, int layer, int loop, AttnArgs *ap) {
+  AttnArgs &a = *ap;
+  const size_t es = esize(d);
+  const long long T = d->T, H = d->H, dh = d->d_head, rk = d->r_k, rv = d->r_v;
+  const long long np = k->num_pages;
   if (d->variant == LLA_PER_HEAD) {
     a.k_pool = (const char *)k->k_pool + (size_t)layer * np * H * kPage * rk * es;
     a.v_pool = (const char *)k->v_pool + (size_t)layer * np * H * kPage * rv * es;
@@ -232,34 +290,6 @@ int32_t attn_call(const lla_dims *d, const lla_codec *c, const lla_cache *k, con
     a.wup_head_stride_k = dh * rk;
     a.wup_head_stride_v = dh * rv;
   }
-  a.page_table = k->page_table;
-  a.max_pages = k->max_pages_per_seq;
-  a.num_pages = k->num_pages;
-  a.rope = rope;
-  a.rope_len = rope_len;
-  a.q_pos = q_pos;
-  a.ctx_len = ctx_len;
-  a.p0 = p0;
-  a.n_q = prefill ? n_q : 1;
-  a.prefill = prefill;
-  a.rows = (int)rows;
-  a.H = d->H;
-  a.max_ctx = max_ctx;
-  a.splits = p.splits;
-  a.pages_per_split = p.pages_per_split;
-  a.head_groups = p.head_groups;
-  a.heads_per_wave = p.hpw;
-  a.waves = p.waves;
-  a.chunk_pages = p.chunk_pages;
-  const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)d->d_head);
-  a.qscale = sc * 1.4426950408889634f;
-  a.err = (int *)ws;
-  a.partials = (float *)((char *)ws + p.partials_off);
-  if (p.prefill) return check_launch(launch_prefill(d->d_head, d->r_k, d->r_v, a, stream));
-  const int32_t rc = check_launch(p.two_d ? launch_decode2d(d->d_head, d->r_k, d->r_v, a, stream)
-                                          : launch_decode(d->dtype, d->d_head, d->r_k, d->r_v, a, stream));
-  if (rc != LLA_OK || p.splits == 1) return rc;
-  return check_launch(launch_merge(d->dtype, d->d_head, d->r_v, a, stream));
 }
 
 }  // namespace
@@ -278,7 +308,12 @@ int32_t lla_rope_table(const lla_dims *d, int32_t n_pos, float *table, hipStream
 size_t lla_workspace_bytes(const lla_dims *d, int32_t op, int32_t batch, int32_t max_ctx, int32_t n) {
   if (!dims_valid(d) || batch < 0) return 0;
   if (op == LLA_OP_ENCODE) return n >= 0 ? encode_ws_bytes(d, n) : 0;
-  if (op == LLA_OP_RECONSTRUCT) return kHeaderBytes;
+  if (op == LLA_OP_RECONSTRUCT || op == LLA_OP_ROPE_KEY_APPEND) return kHeaderBytes;
+  if (op == LLA_OP_DECOUPLED_DECODE) {
+    AttnPlan p;
+    if (max_ctx < 1 || !plan_decoupled(d, batch > 0 ? batch : 1, max_ctx, n, &p)) return 0;
+    return p.bytes;
+  }
   if (op == LLA_OP_FULL_DECODE) {
     AttnPlan p;
     if (max_ctx < 1 || !plan_full(d, batch > 0 ? batch : 1, max_ctx, &p)) return 0;
@@ -464,6 +499,96 @@ int32_t lla_full_decode_attn(const lla_dims *d, const lla_cache *k, const void *
   return check_launch(launch_merge_ident(d->d_head, a, stream));
 }
 
+int32_t lla_rope_key_append(const lla_dims *d, const lla_cache *k, int32_t d_rope, void *kr_pool,
+                            const float *rope_r, int32_t rope_r_len, const void *kr_new, const int32_t *pos0,
+                            int32_t n_new, int32_t layer0, int32_t n_layers, void *ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  if (!dims_valid(d)) return fail(LLA_ERR_INVALID_ARG, "invalid lla_dims");
+  if (!k || !k->page_table || k->batch < 0 || k->max_pages_per_seq < 1 || k->num_pages < 1)
+    return fail(LLA_ERR_INVALID_ARG, "null or invalid cache");
+  if (d_rope < 2 || d_rope % 2 || d_rope > 1024) return fail(LLA_ERR_INVALID_ARG, "d_rope must be even, 2..1024");
+  if (n_new < 0 || n_layers < 0 || layer0 < 0 || layer0 + n_layers > d->D)
+    return fail(LLA_ERR_INVALID_ARG, "layer range or n_new out of range");
+  if (!kr_pool || !rope_r || rope_r_len < 1) return fail(LLA_ERR_INVALID_ARG, "null rotary pool or table");
+  if ((!kr_new || !pos0) && n_new > 0 && n_layers > 0 && k->batch > 0)
+    return fail(LLA_ERR_INVALID_ARG, "null kr_new or pos0");
+  if (d->dtype != LLA_BF16) return fail(LLA_ERR_UNSUPPORTED, "rotary keys are stored in bf16 only");
+  if (!ws || ws_bytes < kHeaderBytes) return fail(LLA_ERR_WORKSPACE, "workspace missing or too small");
+  RopeAppendArgs a = {};
+  a.layer_stride = (long long)k->num_pages * kPage * d_rope;
+  a.kr_pool = (char *)kr_pool + (size_t)layer0 * a.layer_stride * 2;
+  a.kr_new = (const char *)kr_new;
+  a.rope = rope_r;
+  a.rope_len = rope_r_len;
+  a.page_table = k->page_table;
+  a.pos0 = pos0;
+  a.max_pages = k->max_pages_per_seq;
+  a.num_pages = k->num_pages;
+  a.batch = k->batch;
+  a.n_new = n_new;
+  a.n_layers = n_layers;
+  a.d_rope = d_rope;
+  a.err = (int *)ws;
+  return check_launch(launch_rope_key_append(a, stream));
+}
+
+int32_t lla_decoupled_decode_attn(const lla_dims *d, const lla_codec *c, const lla_cache *k, int32_t d_rope,
+                                  const void *kr_pool, const float *rope_r, int32_t rope_r_len, int32_t layer,
+                                  int32_t loop, const void *q, const int32_t *q_pos, const int32_t *ctx_len,
+                                  int32_t max_ctx, float scale, void *out, void *ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  if (!dims_valid(d)) return fail(LLA_ERR_INVALID_ARG, "invalid lla_dims");
+  if (!c || !k) return fail(LLA_ERR_INVALID_ARG, "null codec or cache");
+  if (!c->mu_v || !c->w_up_k || !c->w_up_v) return fail(LLA_ERR_INVALID_ARG, "null decoder parameter");
+  if (!k->k_pool || !k->v_pool || !k->page_table || !kr_pool)
+    return fail(LLA_ERR_INVALID_ARG, "null pool, rotary pool or page table");
+  if (k->batch < 0 || k->max_pages_per_seq < 1 || k->num_pages < 1)
+    return fail(LLA_ERR_INVALID_ARG, "invalid cache sizes");
+  if (layer < 0 || layer >= d->D || loop < 0 || loop >= d->T)
+    return fail(LLA_ERR_INVALID_ARG, "layer or loop out of range");
+  if (!rope_r || rope_r_len < 1) return fail(LLA_ERR_INVALID_ARG, "null rotary RoPE table");
+  if (max_ctx < 1 || (long long)max_ctx > (long long)k->max_pages_per_seq * kPage)
+    return fail(LLA_ERR_INVALID_ARG, "max_ctx out of range");
+  if (!q || !out || !q_pos || !ctx_len) return fail(LLA_ERR_INVALID_ARG, "null q, out or positions");
+  if (!(scale >= 0.f) || isinf(scale)) return fail(LLA_ERR_INVALID_ARG, "invalid scale");
+  if (d_rope < 2 || d_rope % 2) return fail(LLA_ERR_INVALID_ARG, "d_rope must be even");
+  const long long rows = k->batch;
+  AttnPlan p;
+  if (!plan_decoupled(d, rows > 0 ? rows : 1, max_ctx, d_rope, &p))
+    return fail(LLA_ERR_UNSUPPORTED, "no decoupled-RoPE kernel for this (dtype, d_head, r_k, r_v, d_rope, H)");
+  if (!ws || ws_bytes < p.bytes) return fail(LLA_ERR_WORKSPACE, "workspace missing or too small");
+  if (rows == 0) return LLA_OK;
+  AttnArgs a = {};
+  a.q = q;
+  a.out = out;
+  fill_layer(d, c, k, layer, loop, &a);
+  a.kr_pool = (const char *)kr_pool + (size_t)layer * k->num_pages * kPage * d_rope * 2;
+  a.kr_page_stride = (long long)kPage * d_rope;
+  a.page_table = k->page_table;
+  a.max_pages = k->max_pages_per_seq;
+  a.num_pages = k->num_pages;
+  a.rope = rope_r;
+  a.rope_len = rope_r_len;
+  a.q_pos = q_pos;
+  a.ctx_len = ctx_len;
+  a.n_q = 1;
+  a.rows = (int)rows;
+  a.H = d->H;
+  a.max_ctx = max_ctx;
+  a.splits = p.splits;
+  a.pages_per_split = p.pages_per_split;
+  a.head_groups = p.head_groups;
+  a.heads_per_wave = p.hpw;
+  a.waves = p.waves;
+  const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)(d->d_head + d_rope));
+  a.qscale = sc * 1.4426950408889634f;
+  a.err = (int *)ws;
+  a.partials = (float *)((char *)ws + p.partials_off);
+  const int32_t rc = check_launch(launch_absorbed(d->d_head, d->r_k, d->r_v, d_rope, a, stream));
+  if (rc != LLA_OK || p.splits == 1) return rc;
+  return check_launch(launch_merge(d->dtype, d->d_head, d->r_v, a, stream));
+}
+
 int32_t lla_cache_scalars(const lla_dims *d, int64_t *teacher, int64_t *latent) {
   if (!dims_valid(d) || !teacher || !latent) return fail(LLA_ERR_INVALID_ARG, "invalid arguments");
   *teacher = 2LL * d->T * d->H * d->d_head;
@@ -482,6 +607,11 @@ int32_t lla_supported(const lla_dims *d, int32_t op) {
     return plan_attn(d, 1, kPage, &p, op == LLA_OP_PREFILL) ? 1 : 0;
   }
   if (op == LLA_OP_RECONSTRUCT) return reconstruct_supported(d->dtype, d->variant, d->d_head, d->r_k, d->r_v);
+  if (op == LLA_OP_ROPE_KEY_APPEND) return d->dtype == LLA_BF16 ? 1 : 0;
+  if (op == LLA_OP_DECOUPLED_DECODE) {
+    AttnPlan p;
+    return plan_decoupled(d, 1, kPage, 64, &p) && plan_decoupled(d, 1, kPage, 32, &p) ? 1 : 0;
+  }
   if (op == LLA_OP_FULL_DECODE) {
     AttnPlan p;
     return plan_full(d, 1, kPage, &p) ? 1 : 0;

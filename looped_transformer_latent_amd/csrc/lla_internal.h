@@ -40,6 +40,20 @@ struct AttnArgs {
   float qscale;                          // softmax scale * log2(e)
   int *err;
   float *partials;                       // [rows][H][splits][r_v + 2]
+  const char *kr_pool;                   // decoupled RoPE: rotary keys of the layer
+  long long kr_page_stride;              // elements between physical pages (16 d_rope)
+};
+
+// Decoupled RoPE: rotate and append rotary keys.
+struct RopeAppendArgs {
+  char *kr_pool;                         // layer0 base, [num_pages][16][d_rope] per layer
+  long long layer_stride;                // elements between layers
+  const char *kr_new;                    // [n_layers][batch][n_new][d_rope]
+  const float *rope;                     // [rope_len][d_rope/2][2]
+  int rope_len;
+  const int32_t *page_table, *pos0;
+  int max_pages, num_pages, batch, n_new, n_layers, d_rope;
+  int *err;
 };
 
 struct EncodeArgs {
@@ -77,6 +91,9 @@ hipError_t launch_reconstruct(int d_head, int r_k, int r_v, const AttnArgs &a, v
                               int batch, hipStream_t stream);
 bool full_decode_supported(int dtype, int variant, int d_head);
 hipError_t launch_full_decode(int d_head, const AttnArgs &a, hipStream_t stream);
+bool absorbed_supported(int d_head, int r_k, int r_v, int d_rope, int heads_per_wave, int waves);
+hipError_t launch_absorbed(int d_head, int r_k, int r_v, int d_rope, const AttnArgs &a, hipStream_t stream);
+hipError_t launch_rope_key_append(const RopeAppendArgs &a, hipStream_t stream);
 hipError_t launch_rope_table(int n_pos, int d_head, double base, float *table, hipStream_t s);
 
 }  // namespace lla

@@ -20,10 +20,12 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH = 0, -1, -2, -3,
 PER_HEAD, TWO_D = 0, 1
 F32, BF16 = 0, 1
 OP_ENCODE, OP_DECODE, OP_PREFILL, OP_RECONSTRUCT, OP_FULL_DECODE = 0, 1, 2, 3, 4
+OP_ROPE_KEY_APPEND, OP_DECOUPLED_DECODE = 5, 6
 DEVERR_CTX, DEVERR_PAGE, DEVERR_APPEND = 1, 2, 4
 
 EXPORTS = ["lla_rope_table", "lla_workspace_bytes", "lla_encode_append", "lla_decode_attn",
-           "lla_prefill_attn", "lla_reconstruct_kv", "lla_full_decode_attn", "lla_cache_scalars", "lla_supported", "lla_status_string",
+           "lla_prefill_attn", "lla_reconstruct_kv", "lla_full_decode_attn", "lla_rope_key_append",
+           "lla_decoupled_decode_attn", "lla_cache_scalars", "lla_supported", "lla_status_string",
            "lla_last_error"]
 
 
@@ -74,6 +76,8 @@ def load() -> ctypes.CDLL:
     lib.lla_prefill_attn.argtypes = [pd, pc, pk, P, I, I, I, I, P, P, I, F, P, P, S, P]
     lib.lla_reconstruct_kv.argtypes = [pd, pc, pk, P, I, I, I, P, I, P, P, P, S, P]
     lib.lla_full_decode_attn.argtypes = [pd, pk, P, P, P, I, P, P, P, I, F, P, P, S, P]
+    lib.lla_rope_key_append.argtypes = [pd, pk, I, P, P, I, P, P, I, I, I, P, S, P]
+    lib.lla_decoupled_decode_attn.argtypes = [pd, pc, pk, I, P, P, I, I, I, P, P, P, I, F, P, P, S, P]
     lib.lla_cache_scalars.argtypes = [pd, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
     lib.lla_supported.argtypes = [pd, I]
     lib.lla_status_string.argtypes = [I]
@@ -207,6 +211,28 @@ def full_decode_attn(dims: Dims, cache: Cache, k_full, v_full, rope: torch.Tenso
     _check(load().lla_full_decode_attn(ctypes.byref(dims), ctypes.byref(cache), _ptr(k_full), _ptr(v_full),
                                        _ptr(rope), rope.shape[0], _ptr(q), _ptr(q_pos), _ptr(ctx_len),
                                        max_ctx, scale, _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def rope_key_append(dims: Dims, cache: Cache, kr_pool, rope_r: torch.Tensor, kr_new, pos0, n_new: int,
+                    layer0: int, n_layers: int, ws: torch.Tensor, stream=None) -> None:
+    """Rotate the rotary-branch keys kr_new [n_layers][B][n_new][d_rope] at
+    positions pos0[b] + n and write them into kr_pool [D][num_pages][16][d_rope]."""
+    d_rope = kr_pool.shape[-1]
+    _check(load().lla_rope_key_append(ctypes.byref(dims), ctypes.byref(cache), d_rope, _ptr(kr_pool),
+                                      _ptr(rope_r), rope_r.shape[0], _ptr(kr_new), _ptr(pos0), n_new,
+                                      layer0, n_layers, _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def decoupled_decode_attn(dims: Dims, codec: Codec, cache: Cache, kr_pool, rope_r: torch.Tensor, layer: int,
+                          loop: int, q, q_pos, ctx_len, max_ctx: int, out, ws: torch.Tensor,
+                          scale: float = 0.0, stream=None) -> None:
+    """Decode with a NoPE content path absorbed into q plus a rotary branch;
+    q [B][H][d_head + d_rope], out [B][H][d_head]."""
+    d_rope = kr_pool.shape[-1]
+    _check(load().lla_decoupled_decode_attn(ctypes.byref(dims), ctypes.byref(codec), ctypes.byref(cache),
+                                            d_rope, _ptr(kr_pool), _ptr(rope_r), rope_r.shape[0], layer, loop,
+                                            _ptr(q), _ptr(q_pos), _ptr(ctx_len), max_ctx, scale, _ptr(out),
+                                            _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def prefill_attn(dims: Dims, codec: Codec, cache: Cache, rope: torch.Tensor, layer: int, loop: int,

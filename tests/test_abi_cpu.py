@@ -160,3 +160,37 @@ def test_full_cache_validation_and_planning():
     assert lla.workspace_bytes(d, lla.OP_FULL_DECODE, 1024, 4096) == 256   # one split at large batch
     assert lla.supported(d, lla.OP_RECONSTRUCT) and lla.supported(d, lla.OP_FULL_DECODE)
     assert not lla.supported(_dims(r_k=96, r_v=160), lla.OP_RECONSTRUCT)
+
+
+def test_decoupled_validation_and_planning():
+    """Host-side checks of lla_rope_key_append / lla_decoupled_decode_attn (no launch)."""
+    lib = lla.load()
+    d = _dims()
+    codec = lla.Codec(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
+    cache = lla.Cache(0x1000, 0x1000, 0x1000, 32, 256, 8192)
+    E = lla.ERR_INVALID_ARG
+    app = lambda **kw: lib.lla_rope_key_append(
+        ctypes.byref(kw.get("dims", d)), ctypes.byref(cache), kw.get("d_rope", 64), kw.get("pool", FAKE), FAKE,
+        kw.get("rope_len", 4096), FAKE, FAKE, kw.get("n_new", 1), kw.get("layer0", 0), kw.get("n_layers", 1),
+        kw.get("ws", FAKE), kw.get("ws_bytes", 16), NULL)
+    assert app(d_rope=63) == E and app(d_rope=0) == E and app(pool=NULL) == E and app(rope_len=0) == E
+    assert app(layer0=24) == E and app(n_new=-1) == E
+    assert app(dims=_dims(dtype=lla.F32, d_head=64)) == lla.ERR_UNSUPPORTED
+    assert app() == lla.ERR_WORKSPACE
+    dec = lambda **kw: lib.lla_decoupled_decode_attn(
+        ctypes.byref(kw.get("dims", d)), ctypes.byref(codec), ctypes.byref(cache), kw.get("d_rope", 64),
+        kw.get("kr", FAKE), FAKE, 4096, kw.get("layer", 0), 0, kw.get("q", FAKE), FAKE, FAKE,
+        kw.get("max_ctx", 4096), 0.0, FAKE, FAKE, kw.get("ws_bytes", 16), NULL)
+    assert dec(kr=NULL) == E and dec(q=NULL) == E and dec(layer=24) == E and dec(max_ctx=0) == E
+    assert dec(max_ctx=256 * 16 + 1) == E
+    assert dec(d_rope=48) == lla.ERR_UNSUPPORTED and dec(dims=_dims(H=8)) == lla.ERR_UNSUPPORTED
+    assert dec() == lla.ERR_WORKSPACE
+    # planning: as the latent decode (16 heads per workgroup), partials r_v + 2 when split
+    assert lla.workspace_bytes(d, lla.OP_ROPE_KEY_APPEND, 32, 0) == 256
+    big = lla.workspace_bytes(d, lla.OP_DECOUPLED_DECODE, 1, 262144, 64)
+    assert big > 256 and (big - 256) % (16 * 34 * 4) < 256
+    assert lla.workspace_bytes(d, lla.OP_DECOUPLED_DECODE, 1024, 4096, 64) == 256
+    assert lla.workspace_bytes(d, lla.OP_DECOUPLED_DECODE, 1, 4096, 48) == 0
+    assert lla.supported(d, lla.OP_DECOUPLED_DECODE) and lla.supported(_dims(r_k=96, r_v=160, H=4),
+                                                                       lla.OP_DECOUPLED_DECODE)
+    assert not lla.supported(_dims(r_k=32, r_v=64), lla.OP_DECOUPLED_DECODE)
