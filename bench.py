@@ -108,6 +108,7 @@ def cpu_baseline(w, codec_h, pt_h, layer, loop, target_s):
     pages = pt_h[:n_data].reshape(-1)
     kp = wl.pool_pages_host(w, "k", layer, pages)[None]
     vp = wl.pool_pages_host(w, "v", layer, pages)[None]
+    kr = wl.pool_pages_host(w, "kr", layer, pages)[None] if w.d_rope else None
     local = np.arange(len(pages), dtype=np.int32).reshape(n_data, -1)
 
     def run(n_seq):
@@ -115,7 +116,10 @@ def cpu_baseline(w, codec_h, pt_h, layer, loop, target_s):
         q = wl.q_host(w, n_seq)
         ctx = np.full(n_seq, w.ctx, np.int32)
         t0 = time.perf_counter()
-        _, rc = oracle.decode(one, codec1, kp, vp, pt_local, 0, loop, q, ctx - 1, ctx)
+        if w.d_rope:
+            _, rc = oracle.decoupled_decode(one, codec1, kp, vp, kr, pt_local, 0, loop, q, ctx - 1, ctx, w.d_rope)
+        else:
+            _, rc = oracle.decode(one, codec1, kp, vp, pt_local, 0, loop, q, ctx - 1, ctx)
         dt = time.perf_counter() - t0
         assert rc == 0
         return dt
@@ -297,7 +301,7 @@ def bench_full_cache(w, D, codec, cache, rope, calls, q, q_pos, ctx, out_lat, la
     rec, full = float(np.mean(rec_ms)), float(np.mean(full_ms))
     tokens = w.batch * w.ctx
     full_bytes = tokens * w.H * w.d_head * 2 * 2          # K and V, bf16, one (loop, layer)
-    lat_bytes = tokens * w.read_bytes()
+    lat_bytes = tokens * w.groups * (w.r_k + w.r_v) * w.esize   # the rebuild reads c_k, c_v
     gbs = full_bytes / (full / 1e3) / 1e9
     whole = tokens * w.D * w.T * w.H * w.d_head * 2 * 2    # every layer's per-loop K/V
     return {"kernels": ["reconstruct_kernel", "full_decode_kernel"], "calls": len(sub),
@@ -306,7 +310,7 @@ def bench_full_cache(w, D, codec, cache, rope, calls, q, q_pos, ctx, out_lat, la
             "latent_speedup_vs_full_decode": full / lat_ms,
             "latent_speedup_vs_reconstruct_then_attend": (rec + full) / lat_ms,
             "reconstruct_gbs": (full_bytes + lat_bytes) / (rec / 1e3) / 1e9,
-            "bytes_per_token_per_call": {"full": w.H * w.d_head * 4, "latent": w.read_bytes()},
+            "bytes_per_token_per_call": {"full": w.H * w.d_head * 4, "latent": w.groups * (w.r_k + w.r_v) * w.esize},
             "full_cache_bytes_whole_model": whole, "full_cache_fits_hbm": whole <= HBM_BYTES,
             "max_row_rel_diff_vs_latent_decode": rel,
             "roofline": {"kernel": "full_decode_kernel", "bound": "hbm", "achieved": gbs,
@@ -347,13 +351,24 @@ def main():
     cache = lla.make_cache(k_pool, v_pool, pt, w.num_pages)
     rope = lla.rope_table(D, w.ctx)
 
+    decoupled = w.d_rope > 0
     calls = [(t, l) for t in range(w.T) for l in range(w.D)]
-    q = torch.empty((len(calls), w.batch, w.H, w.d_head), dtype=dt_t, device=dev)
+    q = torch.empty((len(calls), w.batch, w.H, w.q_width), dtype=dt_t, device=dev)
     lla.gen_normal_(q, w.seed, wl.STREAMS["q"])
-    out = torch.empty_like(q)
+    out = torch.empty((len(calls), w.batch, w.H, w.d_head), dtype=dt_t, device=dev)
+    if decoupled:
+        # rotary keys of every cached token (stored rotated), the RoPE table of the
+        # d_rope-wide branch, and the step's new rotary keys
+        kr_pool = wl.device_pool(w, "kr", dev)
+        rope_r = lla.rope_table(lla.dims_from_dict(dict(w.dims, d_head=w.d_rope)), w.ctx)
+        x_r = torch.empty((w.D, w.batch, max(1, w.n_new), w.d_rope), dtype=dt_t, device=dev)
+        lla.gen_normal_(x_r, w.seed, wl.STREAMS["x_r"])
+        ws_app = lla.workspace(D, lla.OP_ROPE_KEY_APPEND, w.batch, 0)
+        ws_dec = lla.workspace(D, lla.OP_DECOUPLED_DECODE, w.batch, w.ctx, w.d_rope)
     ctx = torch.full((w.batch,), w.ctx, dtype=torch.int32, device=dev)
     q_pos = ctx - 1
-    ws_dec = lla.workspace(D, lla.OP_DECODE, w.batch, w.ctx)
+    if not decoupled:
+        ws_dec = lla.workspace(D, lla.OP_DECODE, w.batch, w.ctx)
     # the step's new token: its per-loop K/V for every layer, appended at ctx - 1
     # the step's new tokens: one per sequence for a decode step; workloads that
     # name an append chunk (the 4x point: 512 tokens per sequence) append it
@@ -375,12 +390,18 @@ def main():
         if record:
             ev_enc[0].record(stream)
         lla.encode_append(D, codec, cache, x_k, x_v, pos0, n_new, 0, w.D, ws_enc)
+        if decoupled:
+            lla.rope_key_append(D, cache, kr_pool, rope_r, x_r, pos0, n_new, 0, w.D, ws_app)
         if record:
             ev_enc[1].record(stream)
         for i, (t, l) in enumerate(calls):
             if record:
                 ev[i][0].record(stream)
-            lla.decode_attn(D, codec, cache, rope, l, t, q[i], q_pos, ctx, w.ctx, out[i], ws_dec)
+            if decoupled:
+                lla.decoupled_decode_attn(D, codec, cache, kr_pool, rope_r, l, t, q[i], q_pos, ctx, w.ctx,
+                                          out[i], ws_dec)
+            else:
+                lla.decode_attn(D, codec, cache, rope, l, t, q[i], q_pos, ctx, w.ctx, out[i], ws_dec)
             if record:
                 ev[i][1].record(stream)
 
@@ -396,6 +417,7 @@ def main():
         enc_ms.append(ev_enc[0].elapsed_time(ev_enc[1]))
     elapsed = time.perf_counter() - t0
     assert lla.device_error_word(ws_dec) == 0 and lla.device_error_word(ws_enc) == 0
+    assert not decoupled or lla.device_error_word(ws_app) == 0
     assert torch.isfinite(out.float()).all().item()
 
     ms_step = 1e3 * elapsed / args.steps
@@ -406,6 +428,8 @@ def main():
     if w.variant == wl.PER_HEAD:
         achieved = bytes_per_launch / (kern_avg_ms / 1e3) / 1e9
         kname = "decode_g_kernel" if w.dtype == wl.BF16 else "decode_ph_kernel"
+        if decoupled:
+            kname = "absorbed_kernel"
         roof = {"kernel": kname, "bound": "hbm", "achieved": achieved,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                 "traffic": profiled_traffic(w.name, kname), "traffic_unit": "HBM bytes per launch (rocprofv3)",
@@ -436,7 +460,9 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "ctx": w.ctx, "T": w.T, "D": w.D,
                    "H": w.H, "d_head": w.d_head, "r_k": w.r_k, "r_v": w.r_v, "page_size": 16,
                    "page_table": "shuffled" if w.shuffled else "identity",
-                   "step": f"encode_append({n_new} token(s) per sequence x {w.D} layers) + {len(calls)} lla_decode_attn calls"},
+                   "step": (f"encode_append({n_new} token(s) per sequence x {w.D} layers) + " +
+                            (f"rope_key_append (d_rope {w.d_rope}) + {len(calls)} lla_decoupled_decode_attn calls"
+                             if decoupled else f"{len(calls)} lla_decode_attn calls"))},
         "roofline": roof,
     }
     # encode + append of the step's tokens into every layer (HBM-bound GEMM):
@@ -459,7 +485,33 @@ def main():
     if n_new > 1 and lla.supported(D, lla.OP_PREFILL):
         result["prefill"] = bench_prefill(w, D, codec, cache, rope, calls, n_new, dt_t, pos0, stream)
     # the full-memory baseline of the same calls (per-head bf16 shapes it covers)
-    if not args.no_full_cache and lla.supported(D, lla.OP_RECONSTRUCT) and lla.supported(D, lla.OP_FULL_DECODE):
+    full_ok = lla.supported(D, lla.OP_RECONSTRUCT) and lla.supported(D, lla.OP_FULL_DECODE)
+    if decoupled:
+        # the pages' comparison set for the absorbed kernel: the full-RoPE latent
+        # decode, the full-cache ("teacher") decode and reconstruct-then-attend,
+        # all with the content part of the same queries
+        qc = q[..., :w.d_head].contiguous()
+        out_fr = torch.empty_like(out)
+        ws_fr = lla.workspace(D, lla.OP_DECODE, w.batch, w.ctx)
+        evf = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
+        for rep_ in range(2):
+            for i, (t, l) in enumerate(calls):
+                evf[i][0].record(stream)
+                lla.decode_attn(D, codec, cache, rope, l, t, qc[i], q_pos, ctx, w.ctx, out_fr[i], ws_fr)
+                evf[i][1].record(stream)
+            torch.cuda.synchronize()
+        assert lla.device_error_word(ws_fr) == 0
+        fr_ms = float(np.mean([a_.elapsed_time(b_) for a_, b_ in evf]))
+        result["full_rope_latent_decode"] = {
+            "kernel": "decode_g_kernel", "avg_ms": fr_ms, "bytes_per_launch": w.batch * w.ctx * w.groups * (w.r_k + w.r_v) * w.esize,
+            "absorbed_speedup": fr_ms / kern_avg_ms}
+        if not args.no_full_cache and full_ok:
+            fc = bench_full_cache(w, D, codec, cache, rope, calls, qc, q_pos, ctx, out_fr, fr_ms, stream)
+            fc["absorbed_ms"] = kern_avg_ms
+            fc["absorbed_speedup_vs_full_decode"] = fc["full_decode_ms"] / kern_avg_ms
+            fc["absorbed_speedup_vs_reconstruct_then_attend"] = fc["reconstruct_then_attend_ms"] / kern_avg_ms
+            result["full_cache"] = fc
+    elif not args.no_full_cache and full_ok:
         result["full_cache"] = bench_full_cache(w, D, codec, cache, rope, calls, q, q_pos, ctx, out,
                                                 kern_avg_ms, stream)
     if not args.no_cpu_baseline:

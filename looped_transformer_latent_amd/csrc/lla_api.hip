@@ -20,6 +20,7 @@ int32_t fail(int32_t code, const char *msg) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 constexpr int kMaxPagesPerSplit = 2048;  // page-table entries a workgroup stages in LDS
+constexpr long long kCUs = 256;          // compute units of an MI355X
 
 bool dims_valid(const lla_dims *d) {
   return d && d->T > 0 && d->D > 0 && d->H > 0 && d->d_head > 0 && d->d_head % 2 == 0 &&
@@ -129,18 +130,20 @@ void plan_decode_splits(const lla_dims *d, long long rows, int max_ctx, int hpw,
   p->chunk_pages = kDecodeRing;
   const int pages = (max_ctx + kPage - 1) / kPage;
   const long long base = rows * p->head_groups;
-  // One split per row once the grid already holds two rounds of workgroups
-  // (one 8-wave workgroup fits a CU): no partials, no merge launch.  Below
-  // that, split the context until about 1024 workgroups exist.
-  long long s = base >= 512 ? 1 : (1024 + base - 1) / base;
-  const long long smax = pages / 4 > 1 ? pages / 4 : 1;
+  // One round of workgroups over the chip: with fewer (row, head group)
+  // workgroups than CUs, split each row's context until about one workgroup
+  // per CU exists, and no further.  Each workgroup pays its start-up (page
+  // table, folded query, pipeline fill) once, so the longest splits that still
+  // occupy every CU win (measured at batch 1 x 262144 tokens, batch 32 x 4096
+  // and batch 64 x 8192).  A split that is not a whole number of ring trips
+  // masks the padding pages of its last trip.
+  long long s = base >= kCUs ? 1 : (kCUs + base - 1) / base;
+  const long long smax = pages / 4 > 1 ? pages / 4 : 1;  // at least 4 pages per split
   if (s > smax) s = smax;
   const long long smin = (pages + kMaxPagesPerSplit - 1) / kMaxPagesPerSplit;  // LDS staging bound
   if (s < smin) s = smin;
   if (s < 1) s = 1;
-  int pps = (int)((pages + s - 1) / s);
-  pps = (pps + kDecodeRing - 1) / kDecodeRing * kDecodeRing;  // whole trips of the page ring
-  if (pps < kDecodeRing) pps = kDecodeRing;
+  const int pps = (int)((pages + s - 1) / s);
   p->pages_per_split = pps;
   p->splits = (pages + pps - 1) / pps;
   if (p->splits < 1) p->splits = 1;

@@ -3,8 +3,8 @@
 //
 // A split of the context leaves, per (row, head), its running max m (base 2),
 // its weight sum Z and its latent-space value sum acc[r_v] (partials layout
-// [rows][H][splits][r_v + 2]).  The merge is the usual log-sum-exp combination
-// in fixed split order (deterministic):
+// [rows][H][splits][r_v + 2]).  The merge is the usual log-sum-exp combination,
+// reduced in a fixed order (deterministic):
 //   M = max_s m_s,   Z = sum_s 2^{m_s - M} Z_s,   a[r] = sum_s 2^{m_s - M} acc_s[r] / Z,
 // followed by the one up-projection per (row, head) that linearity of the
 // decoder allows (cc.laoqi.cc close reading, 方法 item 1, eq. (3)):
@@ -18,46 +18,103 @@
 
 namespace lla {
 
-// One wave per (row, head); 4 per workgroup.  IDENT: the partials already hold
-// the output row (full-cache decode, r_v = d_head): no up-projection, no mu.
-template <bool BF, bool IDENT = false>
+// Work split: lanes run over splits (a row's splits are independent), so the
+// cost per (row, head) is ceil(S / threads) partial rows per thread plus one
+// cross-lane reduction per output column.  WPR waves share one (row, head):
+// 4 (the whole workgroup) when a row has many splits (long contexts at small
+// batch), else 1 (4 (row, head) pairs per workgroup).  IDENT: the partials
+// already hold the output row (full-cache decode, r_v = d_head): no
+// up-projection, no mu.
+template <bool BF, bool IDENT, int WPR>
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int d_head, int r_v) {
-  extern __shared__ float s_an[];  // [4][r_v]
+  extern __shared__ float s_an[];  // [4 / WPR][r_v]
+  __shared__ float s_red[4][33];
+  constexpr int G = 64 * WPR;      // threads per (row, head)
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const long long rh = (long long)blockIdx.x * 4 + w;  // row * H + head
-  if (rh >= (long long)a.rows * a.H) return;           // whole wave leaves together
-  const int h = (int)(rh % a.H);
-  const int S = a.splits;
-  const float *pb = a.partials + rh * S * (r_v + 2);
-  float *an = s_an + w * r_v;
+  const int grp = threadIdx.x / G, u = threadIdx.x % G, wg = w % WPR;
+  const long long rh = (long long)blockIdx.x * (4 / WPR) + grp;  // row * H + head
+  const bool live = rh < (long long)a.rows * a.H;                // uniform per group
+  const int h = live ? (int)(rh % a.H) : 0;
+  const int S = a.splits, stride = r_v + 2;
+  const float *pb = a.partials + (live ? rh : 0) * S * stride;
+  float *an = s_an + grp * r_v;
+
+  // group-wide max / sum: wave reduction, then (WPR = 4) across the 4 waves
+  auto group_sum = [&](float x, int slot) -> float {
+    x = sum_across_rows(sum_in_row(x));
+    if constexpr (WPR == 1) return x;
+    if (lane == 0) s_red[wg][slot] = x;
+    __syncthreads();
+    const float t = s_red[0][slot] + s_red[1][slot] + s_red[2][slot] + s_red[3][slot];
+    __syncthreads();
+    return t;
+  };
 
   float M = -INFINITY;
-  for (int s = lane; s < S; s += 64) M = fmaxf(M, pb[(long long)s * (r_v + 2) + r_v]);
+  if (live)
+    for (int s = u; s < S; s += G) M = fmaxf(M, pb[(long long)s * stride + r_v]);
   M = max_in_wave(M);
+  if constexpr (WPR == 4) {
+    if (lane == 0) s_red[wg][32] = M;
+    __syncthreads();
+    M = fmaxf(fmaxf(s_red[0][32], s_red[1][32]), fmaxf(s_red[2][32], s_red[3][32]));
+    __syncthreads();
+  }
   float Z = 0.f;
-  for (int s = lane; s < S; s += 64) {
-    const float m = pb[(long long)s * (r_v + 2) + r_v];
-    Z += exp2f(m - M) * pb[(long long)s * (r_v + 2) + r_v + 1];  // NaN Z poisons the row
-  }
-  for (int o = 32; o >= 1; o >>= 1) Z += __shfl_xor(Z, o);
-  for (int r = lane; r < r_v; r += 64) {
-    float acc = 0.f;
-    for (int s = 0; s < S; ++s) {
-      const float m = pb[(long long)s * (r_v + 2) + r_v];
-      acc = fmaf(exp2f(m - M), pb[(long long)s * (r_v + 2) + r], acc);
+  if (live)
+    for (int s = u; s < S; s += G) {
+      const float m = pb[(long long)s * stride + r_v];
+      Z += exp2f(m - M) * pb[(long long)s * stride + r_v + 1];  // NaN Z poisons the row
     }
-    an[r] = acc / Z;
-    if constexpr (IDENT) ((uint16_t *)a.out)[rh * d_head + r] = (uint16_t)f32_to_bf16(an[r]);
-  }
-  if constexpr (IDENT) return;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  Z = group_sum(Z, 32);
 
+  // value sums, 32 columns at a time: each thread folds its splits' columns
+  for (int c0 = 0; c0 < r_v; c0 += 32) {
+    float acc[32];
+#pragma unroll
+    for (int k = 0; k < 32; ++k) acc[k] = 0.f;
+    if (live)
+      for (int s = u; s < S; s += G) {
+        const float *row = pb + (long long)s * stride;
+        const float wgt = exp2f(row[r_v] - M);
+#pragma unroll
+        for (int k = 0; k < 32; k += 2) {
+          if (c0 + k < r_v) {  // r_v is a multiple of 8: pairs stay whole
+            const float2 v = *(const float2 *)(row + c0 + k);
+            acc[k] = fmaf(wgt, v.x, acc[k]);
+            acc[k + 1] = fmaf(wgt, v.y, acc[k + 1]);
+          }
+        }
+      }
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      const float t = sum_across_rows(sum_in_row(acc[k]));
+      if constexpr (WPR == 1) {
+        if (lane == k && c0 + k < r_v) an[c0 + k] = t / Z;
+      } else {
+        if (lane == 0) s_red[wg][k] = t;
+      }
+    }
+    if constexpr (WPR == 4) {
+      __syncthreads();
+      if (threadIdx.x < 32 && c0 + (int)threadIdx.x < r_v) {
+        const int k = threadIdx.x;
+        an[c0 + k] = (s_red[0][k] + s_red[1][k] + s_red[2][k] + s_red[3][k]) / Z;
+      }
+      __syncthreads();
+    }
+  }
+  __syncthreads();
+  if (!live) return;  // after the last barrier
+
+  if constexpr (IDENT) {
+    for (int e = u; e < d_head; e += G) ((uint16_t *)a.out)[rh * d_head + e] = (uint16_t)f32_to_bf16(an[e]);
+    return;
+  }
   const int esz = BF ? 2 : 4;
   const char *wv = a.wup_v + (long long)h * a.wup_head_stride_v * esz;
   const char *mu = a.mu_v + (long long)h * a.mu_head_stride * esz;
-  for (int e = lane; e < d_head; e += 64) {
+  for (int e = u; e < d_head; e += G) {
     const char *we = wv + (long long)e * r_v * esz;
     float o;
     if constexpr (BF) {
@@ -83,26 +140,32 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int d_head, int 
   }
 }
 
-hipError_t launch_merge_ident(int d_head, const AttnArgs &a, hipStream_t stream) {
-  const long long waves = (long long)a.rows * a.H;
-  const long long blocks = (waves + 3) / 4;
+namespace {
+constexpr int kWholeGroupSplits = 64;  // more splits than this: 4 waves per (row, head)
+
+template <bool BF, bool IDENT>
+hipError_t go_merge(const AttnArgs &a, int d_head, int r_v, hipStream_t stream) {
+  if (r_v % 8) return hipErrorInvalidConfiguration;
+  const long long pairs = (long long)a.rows * a.H;
+  const bool whole = a.splits > kWholeGroupSplits;
+  const long long blocks = whole ? pairs : (pairs + 3) / 4;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((merge_kernel<true, true>), dim3((unsigned)blocks), dim3(256), sizeof(float) * 4 * d_head,
-                     stream, a, d_head, d_head);
+  const size_t shmem = sizeof(float) * (whole ? 1 : 4) * r_v;
+  if (whole)
+    hipLaunchKernelGGL((merge_kernel<BF, IDENT, 4>), dim3((unsigned)blocks), dim3(256), shmem, stream, a, d_head, r_v);
+  else
+    hipLaunchKernelGGL((merge_kernel<BF, IDENT, 1>), dim3((unsigned)blocks), dim3(256), shmem, stream, a, d_head, r_v);
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_merge_ident(int d_head, const AttnArgs &a, hipStream_t stream) {
+  return go_merge<true, true>(a, d_head, d_head, stream);
 }
 
 hipError_t launch_merge(int dtype, int d_head, int r_v, const AttnArgs &a, hipStream_t stream) {
-  if (r_v % 8) return hipErrorInvalidConfiguration;
-  const long long waves = (long long)a.rows * a.H;
-  const long long blocks = (waves + 3) / 4;
-  if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  const size_t shmem = sizeof(float) * 4 * r_v;
-  if (dtype == LLA_BF16)
-    hipLaunchKernelGGL(merge_kernel<true>, dim3((unsigned)blocks), dim3(256), shmem, stream, a, d_head, r_v);
-  else
-    hipLaunchKernelGGL(merge_kernel<false>, dim3((unsigned)blocks), dim3(256), shmem, stream, a, d_head, r_v);
-  return hipGetLastError();
+  return dtype == LLA_BF16 ? go_merge<true, false>(a, d_head, r_v, stream)
+                           : go_merge<false, false>(a, d_head, r_v, stream);
 }
 
 }  // namespace lla

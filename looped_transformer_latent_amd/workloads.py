@@ -21,7 +21,7 @@ PER_HEAD, TWO_D = 0, 1
 PAGE = 16
 
 STREAMS = dict(mu_k=101, mu_v=102, w_up_k=103, w_up_v=104, w_down_k=111, w_down_v=112,
-               k_pool=201, v_pool=202, q=301, x_k=401, x_v=402)
+               k_pool=201, v_pool=202, kr_pool=203, q=301, x_k=401, x_v=402, x_r=403)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -41,6 +41,7 @@ class Workload:
     n_new: int          # tokens appended per sequence by one encode call
     seed: int
     ortho_down: bool = False  # W_down orthonormal (QR) and W_up,t its loop-t row slice
+    d_rope: int = 0           # > 0: decoupled RoPE (NoPE content + rotary branch of this width)
 
     @property
     def dims(self) -> dict:
@@ -66,10 +67,17 @@ class Workload:
 
     def read_bytes(self) -> int:
         """Algorithmic latent bytes of one cached-token read: all heads' (c_k, c_v)
-        for per-head LLA, the one shared latent for LLA-2D."""
-        return self.groups * (self.r_k + self.r_v) * self.esize
+        for per-head LLA, the one shared latent for LLA-2D; plus the token's
+        rotary key with decoupled RoPE."""
+        return (self.groups * (self.r_k + self.r_v) + self.d_rope) * self.esize
+
+    @property
+    def q_width(self) -> int:
+        return self.d_head + self.d_rope
 
     def pool_shape(self, kv: str) -> tuple:
+        if kv == "kr":  # decoupled RoPE: one rotary key per (token, layer)
+            return (self.D, self.num_pages, PAGE, self.d_rope)
         r = self.r_k if kv == "k" else self.r_v
         if self.variant == PER_HEAD:
             return (self.D, self.num_pages, self.H, PAGE, r)
@@ -106,6 +114,9 @@ WORKLOADS = {
     # 4x compression plus encode/append of 512 tokens per sequence, 8k context
     "ouro1.4b-4x-b64-encode": Workload("ouro1.4b-4x-b64-encode", 4, 24, 16, 128, 96, 160,
                                        PER_HEAD, BF16, 64, 8192, False, 512, 1004, True),
+    # decoupled RoPE (appendix J's absorbed kernel), one sequence at 262144 tokens
+    "ouro1.4b-21x-ctx256k-decoupled": Workload("ouro1.4b-21x-ctx256k-decoupled", 4, 24, 16, 128, 16, 32,
+                                               PER_HEAD, BF16, 1, 262144, True, 1, 1006, d_rope=64),
     # LLA-2D: heads folded into one latent per token and layer
     "lla2d-t8-h32-b128": Workload("lla2d-t8-h32-b128", 8, 4, 32, 128, 256, 256, TWO_D, BF16,
                                   128, 16384, True, 0, 1005),
@@ -163,7 +174,7 @@ def pool_pages_host(w: Workload, kv: str, layer: int, pages) -> np.ndarray:
 
 def q_host(w: Workload, rows: int | None = None, stream: str = "q") -> np.ndarray:
     rows = w.batch if rows is None else rows
-    return gen.normal(w.seed, STREAMS[stream], (rows, w.H, w.d_head), dtype=_gdt(w))
+    return gen.normal(w.seed, STREAMS[stream], (rows, w.H, w.q_width), dtype=_gdt(w))
 
 
 # ---------------------------------------------------------------- device side

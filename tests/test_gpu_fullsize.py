@@ -197,3 +197,40 @@ def test_ouro_4x_encode_then_decode_sampled(release):
     print(f"[{w.name}] prefill of the 512-token chunk: 5 sampled (sequence, query) rows, "
           f"max row rel err {worst:.3e}", flush=True)
     assert worst <= TOL[w.dtype]
+
+
+def test_decoupled_ctx256k_in_the_benchmark_configuration(release):
+    """Decoupled RoPE at the pages' micro-benchmark context: one sequence of
+    262144 tokens, 24 layers of latents and rotary keys resident, the split and
+    merge configuration the benchmark times (about a thousand splits).  Both
+    calls (two (layer, loop) pairs) against the oracle's plain definition over
+    the whole context, all 16 heads."""
+    w = wl.WORKLOADS["ouro1.4b-21x-ctx256k-decoupled"]
+    b = Built(w)
+    kr_pool = wl.device_pool(w, "kr")
+    rope_r = lla.rope_table(lla.dims_from_dict(dict(w.dims, d_head=w.d_rope)), w.ctx)
+    ctx = torch.full((w.batch,), w.ctx, dtype=torch.int32, device="cuda")
+    ws = lla.workspace(b.D, lla.OP_DECOUPLED_DECODE, w.batch, w.ctx, w.d_rope)
+    m1 = dict(w.dims, D=1)
+    pages = b.pt_h[0]
+    for layer, loop in ((23, 3), (4, 0)):
+        q = torch.empty((w.batch, w.H, w.q_width), dtype=torch.bfloat16, device="cuda")
+        lla.gen_normal_(q, w.seed, wl.STREAMS["q"], offset=layer * 7919 + loop)
+        out = torch.empty((w.batch, w.H, w.d_head), dtype=torch.bfloat16, device="cuda")
+        lla.decoupled_decode_attn(b.D, b.codec, b.cache, kr_pool, rope_r, layer, loop, q, ctx - 1, ctx, w.ctx,
+                                  out, ws)
+        torch.cuda.synchronize()
+        assert lla.device_error_word(ws) == 0
+        got = out_to_f64(out)
+        codec1 = {k: np.ascontiguousarray(v[layer:layer + 1]) for k, v in b.codec_h.items()}
+        kp = wl.pool_pages_host(w, "k", layer, pages)[None]
+        vp = wl.pool_pages_host(w, "v", layer, pages)[None]
+        kr = wl.pool_pages_host(w, "kr", layer, pages)[None]
+        local = np.arange(len(pages), dtype=np.int32)[None]
+        c = np.full(1, w.ctx, np.int32)
+        ref, rc = oracle.decoupled_decode(m1, codec1, kp, vp, kr, local, 0, loop, to_host(q), c - 1, c, w.d_rope)
+        assert rc == 0
+        err = row_rel_err(got, ref)
+        print(f"[{w.name}] layer {layer} loop {loop}: all 16 heads over 262144 tokens, "
+              f"max row rel err {err.max():.3e}", flush=True)
+        assert err.max() <= TOL[w.dtype]
