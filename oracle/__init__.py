@@ -62,6 +62,9 @@ def lib():
         _lib.lla_oracle_decode.restype = _i
         _lib.lla_oracle_decode.argtypes = ([_i] * 9 + [_d] + [_p] * 7 + [_i] * 5 +
                                            [_p, _p, _p, _d, _p, _i])
+        _lib.lla_oracle_decode_window.restype = _i
+        _lib.lla_oracle_decode_window.argtypes = ([_i] * 9 + [_d] + [_p] * 7 + [_i] * 5 +
+                                                  [_p, _p, _p, _i, _i, _d, _p, _i])
         _lib.lla_oracle_prefill.restype = _i
         _lib.lla_oracle_prefill.argtypes = ([_i] * 9 + [_d] + [_p] * 7 + [_i] * 6 +
                                             [_p, _p, _d, _p, _i])
@@ -157,6 +160,27 @@ def decode(dims: dict, codec: dict, k_pool, v_pool, page_table, layer: int, loop
     rc = lib().lla_oracle_decode(*head, *[_ptr(a) for a in params], *[_ptr(a) for a in pools],
                                  _ptr(pt), B, pt.shape[1], pools[0].shape[1], layer, loop,
                                  _ptr(qs), _ptr(qp), _ptr(cl), scale, _ptr(out), threads)
+    return out, rc
+
+
+def decode_window(dims: dict, codec: dict, k_pool, v_pool, page_table, layer: int, loop: int,
+                  q: np.ndarray, q_pos: np.ndarray, ctx_len: np.ndarray, n_sink: int, window: int,
+                  scale: float | None = None, threads: int = 0) -> tuple[np.ndarray, int]:
+    """Decode over the sink + window retained set: tokens j < n_sink and
+    j >= ctx_len - window of each sequence (original positions).  Returns
+    (out [B][H][d] float64, status)."""
+    head, params, pools, pt = _attn_common(dims, codec, k_pool, v_pool, page_table)
+    B, H, d = pt.shape[0], dims["H"], dims["d_head"]
+    qs = _stored(q, dims["dtype"])
+    assert qs.size == B * H * d
+    qp = np.ascontiguousarray(q_pos, dtype=np.int32)
+    cl = np.ascontiguousarray(ctx_len, dtype=np.int32)
+    out = np.empty((B, H, d), dtype=np.float64)
+    scale = (1.0 / np.sqrt(d)) if scale is None else float(scale)
+    rc = lib().lla_oracle_decode_window(*head, *[_ptr(a) for a in params], *[_ptr(a) for a in pools],
+                                        _ptr(pt), B, pt.shape[1], pools[0].shape[1], layer, loop,
+                                        _ptr(qs), _ptr(qp), _ptr(cl), n_sink, window, scale, _ptr(out),
+                                        threads)
     return out, rc
 
 

@@ -242,12 +242,15 @@ int lla_oracle_encode(int T, int D, int H, int d, int r_k, int r_v, int variant,
 /* ---------- attention of one query over ctx cached tokens ---------- */
 
 /* Textbook attention of query vector q (pre-RoPE, position qpos) of head h
- * over logical tokens [0, ctx) of sequence b, all in double.  Writes out[d]. */
+ * over the retained logical tokens of [0, ctx) of sequence b, all in double:
+ * token j takes part iff j < keep_lo or j >= keep_hi (keep_lo = keep_hi = ctx:
+ * every token).  Tokens that do not take part are never looked up.  Writes
+ * out[d]. */
 static int attend_one(const odims *m, const void *mu_k, const void *mu_v, const void *wup_k,
                       const void *wup_v, const void *k_pool, const void *v_pool,
                       const int32_t *page_table, int max_pages, int num_pages, int layer,
                       int loop, int b, int h, const double *q, int64_t qpos, int64_t ctx,
-                      double scale, double *out) {
+                      int64_t keep_lo, int64_t keep_hi, double scale, double *out) {
   const int d = m->d;
   double *qr = (double *)malloc(sizeof(double) * d);
   double *ck = (double *)malloc(sizeof(double) * m->r_k);
@@ -261,6 +264,8 @@ static int attend_one(const odims *m, const void *mu_k, const void *mu_v, const 
   size_t muko = mu_off(m, layer, h, loop), muvo = mu_off(m, layer, h, loop);
   size_t wko = wup_off(m, layer, h, loop, m->r_k), wvo = wup_off(m, layer, h, loop, m->r_v);
   for (int64_t j = 0; j < ctx; ++j) {
+    s[j] = -INFINITY; /* weight 0 unless the token takes part */
+    if (j >= keep_lo && j < keep_hi) continue;
     int64_t slot = lla_oracle_slot(page_table, max_pages, num_pages, m->P, b, j);
     if (slot < 0) { rc = OR_BAD_INDEX; break; }
     size_t pk = pool_off(m, num_pages, layer, h, slot, m->r_k);
@@ -281,7 +286,8 @@ static int attend_one(const odims *m, const void *mu_k, const void *mu_v, const 
     for (int64_t j = 0; j < ctx; ++j) { s[j] = exp(s[j] - mx); z += s[j]; }
     for (int e = 0; e < d; ++e) {
       double acc = 0.0;
-      for (int64_t j = 0; j < ctx; ++j) acc += s[j] * vh[(size_t)j * d + e];
+      for (int64_t j = 0; j < ctx; ++j)
+        if (s[j] != 0.0) acc += s[j] * vh[(size_t)j * d + e]; /* skipped tokens have no v_hat */
       out[e] = acc / z;
     }
   }
@@ -321,7 +327,46 @@ int lla_oracle_decode(int T, int D, int H, int d, int r_k, int r_v, int variant,
     double *qv = (double *)malloc(sizeof(double) * d);
     for (int e = 0; e < d; ++e) qv[e] = ld(q, dtype, (size_t)bh * d + e);
     int r1 = attend_one(&m, mu_k, mu_v, wup_k, wup_v, k_pool, v_pool, page_table, max_pages,
-                        num_pages, layer, loop, b, h, qv, q_pos[b], ctx_len[b], scale, o);
+                        num_pages, layer, loop, b, h, qv, q_pos[b], ctx_len[b], ctx_len[b],
+                        ctx_len[b], scale, o);
+    if (r1 != OR_OK) { rc = r1 < rc ? r1 : rc; for (int e = 0; e < d; ++e) o[e] = NAN; }
+    free(qv);
+  }
+  return rc;
+}
+
+/* ---------- decode over a sink + window retained set ([CR] 四:结果 item 10, Table 9) ---------- */
+
+/* As lla_oracle_decode, but with token eviction: of the ctx_len[b] tokens of
+ * sequence b only the first n_sink (the attention sink) and the last `window`
+ * take part; the rest are evicted, never looked up (their page-table entries
+ * may be invalid).  Retained tokens keep their logical positions for RoPE. */
+int lla_oracle_decode_window(int T, int D, int H, int d, int r_k, int r_v, int variant, int dtype,
+                             int P, double rope_base, const void *mu_k, const void *mu_v,
+                             const void *wup_k, const void *wup_v, const void *k_pool,
+                             const void *v_pool, const int32_t *page_table, int batch, int max_pages,
+                             int num_pages, int layer, int loop, const void *q, const int32_t *q_pos,
+                             const int32_t *ctx_len, int n_sink, int window, double scale,
+                             double *out, int threads) {
+  odims m = {T, D, H, d, r_k, r_v, variant, dtype, P, rope_base};
+  if (!dims_ok(&m) || layer < 0 || layer >= D || loop < 0 || loop >= T || n_sink < 0 || window < 0 ||
+      n_sink + window < 1)
+    return OR_BAD_ARG;
+  set_threads(threads);
+  int rc = OR_OK;
+#pragma omp parallel for schedule(dynamic) reduction(min : rc)
+  for (int bh = 0; bh < batch * H; ++bh) {
+    int b = bh / H, h = bh % H;
+    double *o = out + (size_t)bh * d;
+    for (int e = 0; e < d; ++e) o[e] = NAN;
+    int64_t ctx = ctx_len[b];
+    if (ctx < 1 || ctx > (int64_t)max_pages * P) { rc = OR_BAD_INDEX; continue; }
+    int64_t lo = n_sink < ctx ? n_sink : ctx;           /* sink: [0, lo) */
+    int64_t hi = ctx - window > lo ? ctx - window : lo;  /* window: [hi, ctx) */
+    double *qv = (double *)malloc(sizeof(double) * d);
+    for (int e = 0; e < d; ++e) qv[e] = ld(q, dtype, (size_t)bh * d + e);
+    int r1 = attend_one(&m, mu_k, mu_v, wup_k, wup_v, k_pool, v_pool, page_table, max_pages,
+                        num_pages, layer, loop, b, h, qv, q_pos[b], ctx, lo, hi, scale, o);
     if (r1 != OR_OK) { rc = r1 < rc ? r1 : rc; for (int e = 0; e < d; ++e) o[e] = NAN; }
     free(qv);
   }
@@ -353,7 +398,7 @@ int lla_oracle_prefill(int T, int D, int H, int d, int r_k, int r_v, int variant
     double *qv = (double *)malloc(sizeof(double) * d);
     for (int e = 0; e < d; ++e) qv[e] = ld(q, dtype, (size_t)row * d + e);
     int r1 = attend_one(&m, mu_k, mu_v, wup_k, wup_v, k_pool, v_pool, page_table, max_pages,
-                        num_pages, layer, loop, b, h, qv, pos, pos + 1, scale, o);
+                        num_pages, layer, loop, b, h, qv, pos, pos + 1, pos + 1, pos + 1, scale, o);
     if (r1 != OR_OK) { rc = r1 < rc ? r1 : rc; for (int e = 0; e < d; ++e) o[e] = NAN; }
     free(qv);
   }
