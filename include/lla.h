@@ -75,7 +75,8 @@ enum {
   LLA_OP_RECONSTRUCT = 3,
   LLA_OP_FULL_DECODE = 4,
   LLA_OP_ROPE_KEY_APPEND = 5,
-  LLA_OP_DECOUPLED_DECODE = 6
+  LLA_OP_DECOUPLED_DECODE = 6,
+  LLA_OP_WINDOW_DECODE = 7
 };
 
 /* Device-side error bits (workspace byte 0). */
@@ -134,7 +135,8 @@ int32_t lla_rope_table(const lla_dims *dims, int32_t n_pos, float *table, hipStr
 /* Bytes of workspace that `op` needs.  batch = sequences; max_ctx = the
  * host-known upper bound on every context the call may read (decode: on
  * ctx_len; prefill: on p0[b] + n); n = n_q for prefill, n_layers for encode,
- * d_rope for the decoupled decode, ignored otherwise.  Returns 0 for invalid
+ * d_rope for the decoupled decode, n_sink + window for the windowed decode,
+ * ignored otherwise.  Returns 0 for invalid
  * arguments or shapes without a kernel. */
 size_t lla_workspace_bytes(const lla_dims *dims, int32_t op, int32_t batch, int32_t max_ctx,
                            int32_t n);
@@ -170,6 +172,26 @@ int32_t lla_decode_attn(const lla_dims *dims, const lla_codec *codec, const lla_
                         const void *q, const int32_t *q_pos, const int32_t *ctx_len,
                         int32_t max_ctx, float scale, void *out, void *workspace,
                         size_t ws_bytes, hipStream_t stream);
+
+/* Decode attention with token eviction composed with LLA ([CR] 四:结果 item 10,
+ * Table 9: a 4-token attention sink plus a 256-token window; item 9: 1024
+ * retained tokens of the 21.3x cache take 36 KiB x 1024).  Of the ctx_len[b]
+ * tokens of sequence b only logical tokens j < n_sink and j >= ctx_len[b] -
+ * window take part, each at its own logical position j for RoPE; the softmax
+ * runs over that set:
+ *   out = sum_{j retained} softmax_j(scale <R(q_pos) q, R(j) k_hat_j>) v_hat_j.
+ * Page-table entries of pages that hold no retained token are never read, so
+ * the caller may release those pages (set their entries to anything).  A page
+ * that holds a retained token must be valid (else LLA_DEVERR_PAGE, row NaN).
+ *   n_sink, window  host ints, >= 0, 1 <= n_sink + window <= max_ctx
+ * Other arguments as for lla_decode_attn; workspace from lla_workspace_bytes(..,
+ * LLA_OP_WINDOW_DECODE, batch, max_ctx, n_sink + window).  Supported: bf16
+ * per-head shapes of lla_decode_attn. */
+int32_t lla_decode_window_attn(const lla_dims *dims, const lla_codec *codec, const lla_cache *cache,
+                               const float *rope_table, int32_t rope_len, int32_t layer, int32_t loop,
+                               const void *q, const int32_t *q_pos, const int32_t *ctx_len, int32_t n_sink,
+                               int32_t window, int32_t max_ctx, float scale, void *out, void *workspace,
+                               size_t ws_bytes, hipStream_t stream);
 
 /* Causal prefill attention over the latent cache ([CR] 方法 item 6: long
  * prefill reconstructs per layer).  Query i of sequence b sits at position

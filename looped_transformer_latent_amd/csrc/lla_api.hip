@@ -191,11 +191,18 @@ int32_t check_launch(hipError_t e) {
 void fill_layer(const lla_dims *d, const lla_codec *c, const lla_cache *k, int layer, int loop, AttnArgs *a);
 
 // Common validation + argument filling for decode and prefill.
+// Pages a token-eviction call can touch per row: the sink's, the window's and
+// one partial page at each edge.
+int window_plan_ctx(int max_ctx, int n_keep) {
+  const long long t = (long long)kPage * ((n_keep + kPage - 1) / kPage + 2);
+  return t < max_ctx ? (int)t : max_ctx;
+}
+
 int32_t attn_call(const lla_dims *d, const lla_codec *c, const lla_cache *k, const float *rope,
                   int32_t rope_len, int32_t layer, int32_t loop, const void *q,
                   const int32_t *q_pos, const int32_t *ctx_len, const int32_t *p0, int32_t n_q,
                   int32_t prefill, int32_t max_ctx, float scale, void *out, void *ws,
-                  size_t ws_bytes, hipStream_t stream) {
+                  size_t ws_bytes, hipStream_t stream, int evict = 0, int n_sink = 0, int window = 0) {
   if (!dims_valid(d)) return fail(LLA_ERR_INVALID_ARG, "invalid lla_dims");
   if (!c || !k) return fail(LLA_ERR_INVALID_ARG, "null codec or cache");
   if (!c->mu_k || !c->mu_v || !c->w_up_k || !c->w_up_v)
@@ -216,8 +223,15 @@ int32_t attn_call(const lla_dims *d, const lla_codec *c, const lla_cache *k, con
   if (!(scale >= 0.f) || isinf(scale)) return fail(LLA_ERR_INVALID_ARG, "invalid scale");
   const long long rows = (long long)k->batch * (prefill ? n_q : 1);
   if (rows > (1LL << 30)) return fail(LLA_ERR_INVALID_ARG, "too many query rows");
+  if (evict) {
+    if (n_sink < 0 || window < 0 || (long long)n_sink + window < 1 || (long long)n_sink + window > max_ctx)
+      return fail(LLA_ERR_INVALID_ARG, "need n_sink, window >= 0 and 1 <= n_sink + window <= max_ctx");
+    if (d->dtype != LLA_BF16 || d->variant != LLA_PER_HEAD)
+      return fail(LLA_ERR_UNSUPPORTED, "token eviction is built for bf16 per-head LLA only");
+  }
   AttnPlan p;
-  if (!plan_attn(d, rows > 0 ? rows : 1, max_ctx, &p, prefill != 0))
+  if (!plan_attn(d, rows > 0 ? rows : 1, evict ? window_plan_ctx(max_ctx, n_sink + window) : max_ctx, &p,
+                 prefill != 0))
     return fail(LLA_ERR_UNSUPPORTED, "no attention kernel built for this (dtype, d_head, r_k, r_v)");
   if (!ws || ws_bytes < p.bytes) return fail(LLA_ERR_WORKSPACE, "workspace missing or too small");
   if (rows == 0) return LLA_OK;
@@ -245,6 +259,9 @@ int32_t attn_call(const lla_dims *d, const lla_codec *c, const lla_cache *k, con
   a.heads_per_wave = p.hpw;
   a.waves = p.waves;
   a.chunk_pages = p.chunk_pages;
+  a.evict = evict;
+  a.n_sink = n_sink;
+  a.window = window;
   const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)d->d_head);
   a.qscale = sc * 1.4426950408889634f;
   a.err = (int *)ws;
@@ -315,6 +332,13 @@ size_t lla_workspace_bytes(const lla_dims *d, int32_t op, int32_t batch, int32_t
   if (op == LLA_OP_DECOUPLED_DECODE) {
     AttnPlan p;
     if (max_ctx < 1 || !plan_decoupled(d, batch > 0 ? batch : 1, max_ctx, n, &p)) return 0;
+    return p.bytes;
+  }
+  if (op == LLA_OP_WINDOW_DECODE) {
+    AttnPlan p;
+    if (max_ctx < 1 || n < 1 || d->dtype != LLA_BF16 || d->variant != LLA_PER_HEAD ||
+        !plan_attn(d, batch > 0 ? batch : 1, window_plan_ctx(max_ctx, n), &p))
+      return 0;
     return p.bytes;
   }
   if (op == LLA_OP_FULL_DECODE) {
@@ -392,6 +416,15 @@ int32_t lla_decode_attn(const lla_dims *d, const lla_codec *c, const lla_cache *
                         hipStream_t stream) {
   return attn_call(d, c, k, rope, rope_len, layer, loop, q, q_pos, ctx_len, nullptr, 1, 0,
                    max_ctx, scale, out, ws, ws_bytes, stream);
+}
+
+int32_t lla_decode_window_attn(const lla_dims *d, const lla_codec *c, const lla_cache *k,
+                               const float *rope, int32_t rope_len, int32_t layer, int32_t loop,
+                               const void *q, const int32_t *q_pos, const int32_t *ctx_len, int32_t n_sink,
+                               int32_t window, int32_t max_ctx, float scale, void *out, void *ws,
+                               size_t ws_bytes, hipStream_t stream) {
+  return attn_call(d, c, k, rope, rope_len, layer, loop, q, q_pos, ctx_len, nullptr, 1, 0, max_ctx, scale,
+                   out, ws, ws_bytes, stream, 1, n_sink, window);
 }
 
 int32_t lla_prefill_attn(const lla_dims *d, const lla_codec *c, const lla_cache *k,
@@ -611,6 +644,10 @@ int32_t lla_supported(const lla_dims *d, int32_t op) {
   }
   if (op == LLA_OP_RECONSTRUCT) return reconstruct_supported(d->dtype, d->variant, d->d_head, d->r_k, d->r_v);
   if (op == LLA_OP_ROPE_KEY_APPEND) return d->dtype == LLA_BF16 ? 1 : 0;
+  if (op == LLA_OP_WINDOW_DECODE) {
+    AttnPlan p;
+    return d->dtype == LLA_BF16 && d->variant == LLA_PER_HEAD && plan_attn(d, 1, kPage, &p) ? 1 : 0;
+  }
   if (op == LLA_OP_DECOUPLED_DECODE) {
     AttnPlan p;
     return plan_decoupled(d, 1, kPage, 64, &p) && plan_decoupled(d, 1, kPage, 32, &p) ? 1 : 0;

@@ -81,8 +81,21 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 1 : 2) void decode_g_kernel(Attn
     qp = 0;
   }
   const int npages = (ctx + kPage - 1) / kPage;
+  // Retained tokens: [0, keep_lo) and [keep_hi, ctx) (token eviction), or the
+  // whole context.  Splits run over the pages that hold retained tokens
+  // ("virtual" pages v: the sink pages [0, n_a), then the window pages from
+  // page p_b on); the other pages' table entries are never read.
+  int keep_lo = ctx, keep_hi = ctx;
+  if (a.evict) {
+    keep_lo = min(a.n_sink, ctx);
+    keep_hi = max(ctx - a.window, keep_lo);
+  }
+  const int n_a = (keep_lo + kPage - 1) / kPage;
+  const int p_b = max(keep_hi / kPage, n_a);
+  const int nvirt = n_a + (npages - p_b);
+  auto logical = [&](int v) -> int { return v < n_a ? v : p_b + (v - n_a); };
   const int lp0 = split * a.pages_per_split;
-  const int lp1 = min(lp0 + a.pages_per_split, npages);
+  const int lp1 = min(lp0 + a.pages_per_split, nvirt);
   const int h0 = (hg * a.waves + wave) * HPW;
 
   // ---- prologue: folded decoder as fp16 MFMA A-operands ----
@@ -157,13 +170,14 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 1 : 2) void decode_g_kernel(Attn
   int *s_pt = (int *)(smem + 2 * TSB * 16);
   {
     const int *pt_row = a.page_table + (long long)b * a.max_pages;
-    for (int i = threadIdx.x; i < lp1 - lp0; i += blockDim.x) s_pt[i] = pt_row[lp0 + i];
+    for (int i = threadIdx.x; i < lp1 - lp0; i += blockDim.x) s_pt[i] = pt_row[logical(lp0 + i)];
     __syncthreads();
   }
   auto page_at = [&](int lp) -> int { return __builtin_amdgcn_readfirstlane(s_pt[lp - lp0]); };
 
-  // RoPE staging: chunk c covers pages [lp0 + c CH, lp0 + (c + 1) CH); row R of
-  // a chunk buffer holds the fp16 (cos, sin) pairs of position 16 (lp0 + c CH) + R.
+  // RoPE staging: chunk c covers (virtual) pages [lp0 + c CH, lp0 + (c + 1) CH);
+  // row R of a chunk buffer holds the fp16 (cos, sin) pairs of position
+  // 16 logical(lp0 + c CH + R / 16) + R % 16.
   // Logical slot ls (pairs 4 ls .. 4 ls + 3) is stored at ls ^ (R % 16 & SWZ) so
   // that 16 lanes reading one slot of 16 consecutive positions use distinct banks.
   const char *rope_b = (const char *)a.rope;
@@ -173,7 +187,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 1 : 2) void decode_g_kernel(Attn
     for (int j = 0; j < SLOTS; ++j) {
       const int q = min((int)threadIdx.x + j * NTH, TS - 1);
       const int R = q / SPR, ps = q % SPR, rn = R % kPage;
-      const int pos = min((lp0 + c * CH + R / kPage) * kPage + rn, ctx - 1);
+      const int pos = min(logical(lp0 + c * CH + R / kPage) * kPage + rn, ctx - 1);
       const char *src = rope_b + (long long)pos * (DH * 4) + (ps ^ (rn & SWZ)) * 32;
       stg[j][0] = *(const f32x4 *)(src);
       stg[j][1] = *(const f32x4 *)(src + 16);
@@ -195,7 +209,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 1 : 2) void decode_g_kernel(Attn
   auto load_page = [&](int lp, int pp_raw, Page &pg) {
     pg.ok = (pp_raw >= 0 && pp_raw < a.num_pages);
     const long long pp = pg.ok ? pp_raw : 0;
-    pg.last = min(kPage - 1, ctx - 1 - lp * kPage);
+    pg.last = min(kPage - 1, ctx - 1 - logical(lp) * kPage);
     const int row_n = min(n, pg.last);
     // uniform page bases + 32-bit lane offsets; latents are read exactly once
     const char *kpage = a.k_pool + pp * a.pool_page_stride_k * 2;
@@ -218,7 +232,9 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 1 : 2) void decode_g_kernel(Attn
   // tokens are masked out here and the row is poisoned through the error bits.
   auto compute_page = [&](const Page &cur, int lp) {
     errbits |= cur.ok ? 0 : LLA_DEVERR_PAGE;
-    const bool valid = cur.ok && n <= cur.last && lp < lp1;  // lp >= lp1: ring padding
+    const int j = logical(lp) * kPage + n;  // this lane's token
+    const bool valid = cur.ok && n <= cur.last && lp < lp1 &&  // lp >= lp1: ring padding
+                       (j < keep_lo || j >= keep_hi);         // evicted rows of edge pages
     const int row_n = min(n, cur.last);
     const char *tb = s_trig + (((lp - lp0) / CH) & 1) * TSB * 16 +
                      (((lp - lp0) % CH) * kPage + row_n) * SPR * 16;

@@ -40,6 +40,7 @@ struct AttnArgs {
   float qscale;                          // softmax scale * log2(e)
   int *err;
   float *partials;                       // [rows][H][splits][r_v + 2]
+  int evict, n_sink, window;             // token eviction: retained [0, n_sink) and the last `window`
   const char *kr_pool;                   // decoupled RoPE: rotary keys of the layer
   long long kr_page_stride;              // elements between physical pages (16 d_rope)
 };

@@ -20,12 +20,12 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH = 0, -1, -2, -3,
 PER_HEAD, TWO_D = 0, 1
 F32, BF16 = 0, 1
 OP_ENCODE, OP_DECODE, OP_PREFILL, OP_RECONSTRUCT, OP_FULL_DECODE = 0, 1, 2, 3, 4
-OP_ROPE_KEY_APPEND, OP_DECOUPLED_DECODE = 5, 6
+OP_ROPE_KEY_APPEND, OP_DECOUPLED_DECODE, OP_WINDOW_DECODE = 5, 6, 7
 DEVERR_CTX, DEVERR_PAGE, DEVERR_APPEND = 1, 2, 4
 
 EXPORTS = ["lla_rope_table", "lla_workspace_bytes", "lla_encode_append", "lla_decode_attn",
            "lla_prefill_attn", "lla_reconstruct_kv", "lla_full_decode_attn", "lla_rope_key_append",
-           "lla_decoupled_decode_attn", "lla_cache_scalars", "lla_supported", "lla_status_string",
+           "lla_decoupled_decode_attn", "lla_decode_window_attn", "lla_cache_scalars", "lla_supported", "lla_status_string",
            "lla_last_error"]
 
 
@@ -78,6 +78,7 @@ def load() -> ctypes.CDLL:
     lib.lla_full_decode_attn.argtypes = [pd, pk, P, P, P, I, P, P, P, I, F, P, P, S, P]
     lib.lla_rope_key_append.argtypes = [pd, pk, I, P, P, I, P, P, I, I, I, P, S, P]
     lib.lla_decoupled_decode_attn.argtypes = [pd, pc, pk, I, P, P, I, I, I, P, P, P, I, F, P, P, S, P]
+    lib.lla_decode_window_attn.argtypes = [pd, pc, pk, P, I, I, I, P, P, P, I, I, I, F, P, P, S, P]
     lib.lla_cache_scalars.argtypes = [pd, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
     lib.lla_supported.argtypes = [pd, I]
     lib.lla_status_string.argtypes = [I]
@@ -195,6 +196,16 @@ def decode_attn(dims: Dims, codec: Codec, cache: Cache, rope: torch.Tensor, laye
                                   _ptr(rope), rope.shape[0], layer, loop, _ptr(q), _ptr(q_pos),
                                   _ptr(ctx_len), max_ctx, scale, _ptr(out), _ptr(ws), ws.numel(),
                                   _stream(stream)))
+
+
+def decode_window_attn(dims: Dims, codec: Codec, cache: Cache, rope: torch.Tensor, layer: int, loop: int,
+                       q, q_pos, ctx_len, n_sink: int, window: int, max_ctx: int, out, ws: torch.Tensor,
+                       scale: float = 0.0, stream=None) -> None:
+    """Decode over the retained tokens j < n_sink and j >= ctx_len - window."""
+    _check(load().lla_decode_window_attn(ctypes.byref(dims), ctypes.byref(codec), ctypes.byref(cache),
+                                         _ptr(rope), rope.shape[0], layer, loop, _ptr(q), _ptr(q_pos),
+                                         _ptr(ctx_len), n_sink, window, max_ctx, scale, _ptr(out), _ptr(ws),
+                                         ws.numel(), _stream(stream)))
 
 
 def reconstruct_kv(dims: Dims, codec: Codec, cache: Cache, rope: torch.Tensor, layer: int, loop: int,

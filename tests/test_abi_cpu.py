@@ -194,3 +194,26 @@ def test_decoupled_validation_and_planning():
     assert lla.supported(d, lla.OP_DECOUPLED_DECODE) and lla.supported(_dims(r_k=96, r_v=160, H=4),
                                                                        lla.OP_DECOUPLED_DECODE)
     assert not lla.supported(_dims(r_k=32, r_v=64), lla.OP_DECOUPLED_DECODE)
+
+
+def test_window_validation_and_planning():
+    """Host-side checks of lla_decode_window_attn (no launch)."""
+    lib = lla.load()
+    d = _dims()
+    codec = lla.Codec(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
+    cache = lla.Cache(0x1000, 0x1000, 0x1000, 32, 256, 8192)
+    E = lla.ERR_INVALID_ARG
+    win = lambda **kw: lib.lla_decode_window_attn(
+        ctypes.byref(kw.get("dims", d)), ctypes.byref(codec), ctypes.byref(cache), FAKE, 4096, 0, 0, FAKE, FAKE,
+        FAKE, kw.get("n_sink", 4), kw.get("window", 256), kw.get("max_ctx", 4096), 0.0, FAKE, FAKE,
+        kw.get("ws_bytes", 16), NULL)
+    assert win(n_sink=-1) == E and win(window=-2) == E and win(n_sink=0, window=0) == E
+    assert win(n_sink=100, window=5000) == E                           # budget beyond max_ctx
+    assert win(dims=_dims(dtype=lla.F32, d_head=64)) == lla.ERR_UNSUPPORTED
+    assert win() == lla.ERR_WORKSPACE
+    # a 260-token budget plans like a 260 + 2 page context, not like 4096
+    assert lla.workspace_bytes(d, lla.OP_WINDOW_DECODE, 1, 4096, 260) == \
+        lla.workspace_bytes(d, lla.OP_DECODE, 1, 16 * (17 + 2))
+    assert lla.workspace_bytes(d, lla.OP_WINDOW_DECODE, 1, 4096, 0) == 0
+    assert lla.supported(d, lla.OP_WINDOW_DECODE) and not lla.supported(_dims(dtype=lla.F32, d_head=64),
+                                                                         lla.OP_WINDOW_DECODE)
