@@ -30,6 +30,7 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 DECODE_SOURCES = ("lla_decode_g.hip", "lla_device.h", "lla_internal.h", "lla_api.hip")
 PREFILL_SOURCES = ("lla_prefill.hip", "lla_device.h", "lla_internal.h", "lla_api.hip")
+ABSORBED_SOURCES = ("lla_absorbed.hip", "lla_merge.hip", "lla_device.h", "lla_internal.h", "lla_api.hip")
 FULL_SOURCES = ("lla_full.hip", "lla_merge.hip", "lla_device.h", "lla_internal.h", "lla_api.hip")
 HBM_BYTES = 288e9
 
@@ -168,6 +169,77 @@ def cpu_prefill_baseline(w, codec_h, pt_h, layer, loop, n_new, target_s):
             "sample": f"queries 0..{n - 1} of one sequence's {n_new}-token chunk at positions "
                       f"{w.ctx - n_new}.., all {w.H} heads, one (layer, loop); fp64 C oracle, "
                       f"OpenMP over (query, head); {dt:.1f} s"}
+
+
+def bench_window(w, D, codec, cache, rope, calls, q, q_pos, ctx, codec_h, pt_h, stream, n_sink=4, window=256,
+                 cpu_s=0.0):
+    """Token eviction composed with LLA: every (loop, layer) call of the step
+    attends over a 4-token sink plus the last 256 tokens (lla_decode_window_attn),
+    timed with HIP events; roofline on the retained tokens' latent bytes."""
+    import torch
+    from looped_transformer_latent_amd import lla
+
+    out = torch.empty((len(calls), w.batch, w.H, w.d_head), dtype=q.dtype, device="cuda")
+    ws = lla.workspace(D, lla.OP_WINDOW_DECODE, w.batch, w.ctx, n_sink + window)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
+
+    def one_pass(record):
+        for i, (t, l) in enumerate(calls):
+            if record:
+                ev[i][0].record(stream)
+            lla.decode_window_attn(D, codec, cache, rope, l, t, q[i], q_pos, ctx, n_sink, window, w.ctx, out[i], ws)
+            if record:
+                ev[i][1].record(stream)
+
+    one_pass(False)
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(2):
+        one_pass(True)
+        torch.cuda.synchronize()
+        ms += [a.elapsed_time(b) for a, b in ev]
+    assert lla.device_error_word(ws) == 0
+    assert torch.isfinite(out.float()).all().item()
+    avg = float(np.mean(ms))
+    kept = min(w.ctx, n_sink + window)
+    nbytes = w.batch * kept * w.read_bytes()
+    gbs = nbytes / (avg / 1e3) / 1e9
+    res = {"kernel": "decode_g_kernel (eviction)", "n_sink": n_sink, "window": window, "calls": len(calls),
+           "avg_ms": avg, "value": w.batch * kept / (avg / 1e3), "unit": "retained-token reads/s",
+           "retained_latent_bytes_per_sequence_all_layers": kept * w.read_bytes() * w.D,
+           "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": gbs / HBM_PEAK_GBS,
+                        "traffic": profiled_traffic(w.name + "-window", "decode_g_kernel"),
+                        "traffic_unit": "HBM bytes per launch (rocprofv3)", "algorithmic_bytes_per_launch": nbytes}}
+    if cpu_s > 0:
+        import oracle
+        from looped_transformer_latent_amd import workloads as wl
+        layer, loop = calls[-1][1], calls[-1][0]
+        one = dict(w.dims, D=1)
+        codec1 = {k: np.ascontiguousarray(v[layer:layer + 1]) for k, v in codec_h.items()}
+        n_data = min(4, w.batch)
+        pages = pt_h[:n_data].reshape(-1)
+        kp = wl.pool_pages_host(w, "k", layer, pages)[None]
+        vp = wl.pool_pages_host(w, "v", layer, pages)[None]
+        local = np.arange(len(pages), dtype=np.int32).reshape(n_data, -1)
+
+        def run(n_seq):
+            pt_local = np.ascontiguousarray(local[np.arange(n_seq) % n_data])
+            qh = wl.q_host(w, n_seq)
+            c = np.full(n_seq, w.ctx, np.int32)
+            t0 = time.perf_counter()
+            _, rc = oracle.decode_window(one, codec1, kp, vp, pt_local, 0, loop, qh, c - 1, c, n_sink, window)
+            assert rc == 0
+            return time.perf_counter() - t0
+
+        t1 = run(1)
+        n = int(max(1, min(w.batch, round(cpu_s / max(t1, 1e-3)))))
+        dt = run(n) if n > 1 else t1
+        res["cpu_baseline"] = {"value": n * kept / dt, "unit": "retained-token reads/s",
+                               "cores": oracle.max_threads(0), "kind": "oracle",
+                               "sample": f"{n} of {w.batch} sequences x {kept} retained tokens x all {w.H} heads, "
+                                         f"one (layer, loop) call; fp64 C oracle; {dt:.1f} s"}
+    return res
 
 
 def cpu_encode_baseline(w, codec_h, layer, target_s):
@@ -432,7 +504,7 @@ def main():
             kname = "absorbed_kernel"
         roof = {"kernel": kname, "bound": "hbm", "achieved": achieved,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                "traffic": profiled_traffic(w.name, kname), "traffic_unit": "HBM bytes per launch (rocprofv3)",
+                "traffic": profiled_traffic(w.name, kname, ABSORBED_SOURCES if decoupled else DECODE_SOURCES), "traffic_unit": "HBM bytes per launch (rocprofv3)",
                 "algorithmic_bytes_per_launch": bytes_per_launch, "avg_launch_ms": kern_avg_ms}
     else:
         # LLA-2D is bound by the matrix cores: per token and head, rebuilding K is
@@ -484,6 +556,10 @@ def main():
     # ctx - n_new .. ctx - 1 attend over the cache, one call per (loop, layer)
     if n_new > 1 and lla.supported(D, lla.OP_PREFILL):
         result["prefill"] = bench_prefill(w, D, codec, cache, rope, calls, n_new, dt_t, pos0, stream)
+    # token eviction on top of the latent cache: sink 4 + window 256 per call
+    if not decoupled and w.ctx > 260 and lla.supported(D, lla.OP_WINDOW_DECODE):
+        result["window"] = bench_window(w, D, codec, cache, rope, calls, q, q_pos, ctx, codec_h, pt_h, stream,
+                                        cpu_s=0.0 if args.no_cpu_baseline else args.cpu_seconds / 4)
     # the full-memory baseline of the same calls (per-head bf16 shapes it covers)
     full_ok = lla.supported(D, lla.OP_RECONSTRUCT) and lla.supported(D, lla.OP_FULL_DECODE)
     if decoupled:
