@@ -44,6 +44,17 @@ __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
          ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
 }
 
+// LDS layout of decode_g_kernel: [RoPE chunk buffers: 2 x TSB x 16 B][page-table
+// entries of the split][epilogue: NW x HPW x (RV + 2) floats][W_up,k stage:
+// NW x HPW x DH x RK bf16].  Offset of the last part (16-byte aligned).
+template <int DH, int RK, int RV, int HPW, int NW>
+__host__ __device__ constexpr size_t w_stage_offset(int pages_per_split) {
+  constexpr int TS = (LLA_DECODE_LOOK + 2) * kPage * (DH / 8);
+  constexpr int TSB = (TS + 64 * NW - 1) / (64 * NW) * (64 * NW);
+  return (2 * (size_t)TSB * 16 + sizeof(int) * (size_t)pages_per_split +
+          sizeof(float) * NW * HPW * (RV + 2) + 15) / 16 * 16;
+}
+
 // NW = 4 runs one wave per SIMD (up to 512 registers): the shape with the
 // widest latents (r_k = 96, r_v = 160) needs them for its decoder and page ring.
 template <int DH, int RK, int RV, int HPW, int NW>
@@ -101,35 +112,59 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 1 : 2) void decode_g_kernel(Attn
   // ---- prologue: folded decoder as fp16 MFMA A-operands ----
   // F[hh][rt][s]: lane (g, n) = row r = 16 rt + n, K-slots 2p, 2p + 1 = (A_ir, B_ir)
   // of pair i = 16 s + 4 g + p.  Fa[s]: row hh (lanes n == hh) = (alpha_i, beta_i).
+  // The wave's W_up,k,t (HPW x d x r_k bf16) is first copied into its own LDS
+  // region with 16-byte loads: the fold reads it by (pair, column), which as
+  // global loads would be one 2-byte load per element and lane.  The RoPE row
+  // of q_pos, q and mu_k are read 4 pairs per load.
+  extern __shared__ __attribute__((aligned(16))) char smem[];
   u32x4 F[HPW][RT][KS];
   u32x4 Fa[KS];
   {
+    uint16_t *s_w = (uint16_t *)(smem + w_stage_offset<DH, RK, RV, HPW, NW>(a.pages_per_split)) +
+                    wave * (HPW * DH * RK);
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      const u32x4 *src = (const u32x4 *)((const uint16_t *)a.wup_k + (long long)(h0 + hh) * a.wup_head_stride_k);
+      u32x4 *dst = (u32x4 *)(s_w + hh * DH * RK);
+#pragma unroll
+      for (int c = 0; c < DH * RK / 8 / 64; ++c) dst[c * 64 + lane] = src[c * 64 + lane];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const float *rq = a.rope + (long long)qp * DH;
 #pragma unroll
     for (int s = 0; s < KS; ++s) Fa[s] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int hh = 0; hh < HPW; ++hh) {
-      const int h = h0 + hh;
-      const uint16_t *qrow = (const uint16_t *)a.q + ((long long)row * a.H + h) * DH;
-      const uint16_t *w = (const uint16_t *)a.wup_k + (long long)h * a.wup_head_stride_k;
-      const uint16_t *mu = (const uint16_t *)a.mu_k + (long long)h * a.mu_head_stride;
+    for (int s = 0; s < KS; ++s) {
+      const int i0 = 16 * s + 4 * g;  // pairs i0 .. i0 + 3 of this lane
+      const f32x4 cs01 = *(const f32x4 *)(rq + 2 * i0), cs23 = *(const f32x4 *)(rq + 2 * i0 + 4);
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
+      for (int hh = 0; hh < HPW; ++hh) {
+        const int h = h0 + hh;
+        const uint16_t *qrow = (const uint16_t *)a.q + ((long long)row * a.H + h) * DH;
+        const uint16_t *mu = (const uint16_t *)a.mu_k + (long long)h * a.mu_head_stride;
+        const u32x2 qa4 = *(const u32x2 *)(qrow + i0), qb4 = *(const u32x2 *)(qrow + i0 + HALF);
+        const u32x2 ma4 = *(const u32x2 *)(mu + i0), mb4 = *(const u32x2 *)(mu + i0 + HALF);
+        const uint16_t *w = s_w + hh * DH * RK;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          const int i = 16 * s + 4 * g + p;
-          const float c = rq[2 * i], sn = rq[2 * i + 1];
-          const float qa = bf16_to_f32(qrow[i]), qb = bf16_to_f32(qrow[i + HALF]);
+          const int i = i0 + p;
+          const f32x4 &cq = p < 2 ? cs01 : cs23;
+          const float c = cq[2 * (p & 1)], sn = cq[2 * (p & 1) + 1];
+          const float qa = p & 1 ? bf16_hi(qa4[p >> 1]) : bf16_lo(qa4[p >> 1]);
+          const float qb = p & 1 ? bf16_hi(qb4[p >> 1]) : bf16_lo(qb4[p >> 1]);
           const float pa = a.qscale * (qa * c - qb * sn);
           const float pb = a.qscale * (qa * sn + qb * c);
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt) {
             const int r = 16 * rt + n;
-            const float wa = bf16_to_f32(w[(long long)i * RK + r]);
-            const float wb = bf16_to_f32(w[(long long)(i + HALF) * RK + r]);
+            const float wa = bf16_to_f32(w[i * RK + r]);
+            const float wb = bf16_to_f32(w[(i + HALF) * RK + r]);
             F[hh][rt][s][p] = pack_f16(pa * wa + pb * wb, pb * wa - pa * wb);
           }
-          const float ma = bf16_to_f32(mu[i]), mb = bf16_to_f32(mu[i + HALF]);
+          const float ma = p & 1 ? bf16_hi(ma4[p >> 1]) : bf16_lo(ma4[p >> 1]);
+          const float mb = p & 1 ? bf16_hi(mb4[p >> 1]) : bf16_lo(mb4[p >> 1]);
           const uint32_t ab = pack_f16(pa * ma + pb * mb, pb * ma - pa * mb);
           if (n == hh) Fa[s][p] = ab;
         }
@@ -159,7 +194,6 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 1 : 2) void decode_g_kernel(Attn
   // LDS: [RoPE rows: 2 chunk buffers][page-table entries of the split][epilogue]
   constexpr int SPR = DH / 8;                  // 16-byte slots per position row (fp16 pairs)
   constexpr int SWZ = SPR < 16 ? SPR - 1 : 15;  // XOR swizzle mask (row index low bits)
-  extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int LOOK = LLA_DECODE_LOOK;  // pages in flight beyond the one computed
   constexpr int NBUF = LOOK + 2;        // page ring slots
   constexpr int CH = NBUF;              // pages per RoPE chunk: one trip round the ring
@@ -400,10 +434,8 @@ hipError_t go_g(const AttnArgs &a, hipStream_t stream) {
   }
   const dim3 grid((unsigned)(a.rows * a.head_groups * a.splits));
   const dim3 block((unsigned)(64 * NW));
-  constexpr int TS = (LLA_DECODE_LOOK + 2) * kPage * (DH / 8);  // one chunk = ring
-  constexpr int TSB = (TS + 64 * NW - 1) / (64 * NW) * (64 * NW);
-  const size_t shmem = 2 * (size_t)TSB * 16 + sizeof(int) * a.pages_per_split +
-                       sizeof(float) * NW * HPW * (RV + 2);
+  const size_t shmem = w_stage_offset<DH, RK, RV, HPW, NW>(a.pages_per_split) +
+                       sizeof(uint16_t) * NW * HPW * DH * RK;
   hipLaunchKernelGGL((decode_g_kernel<DH, RK, RV, HPW, NW>), grid, block, shmem, stream, a);
   return hipGetLastError();
 }
