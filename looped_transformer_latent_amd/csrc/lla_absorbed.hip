@@ -93,13 +93,26 @@ __global__ __launch_bounds__(64 * NW, 1) void absorbed_kernel(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) qk[hh][rt][e] = a.qscale * sum_in_row(p[e]);
       }
+      // rotary columns CR g + k: pairs i0 + k, the first (g < 2) or second half
+      const int i0 = CR * (g & 1);
+      const bool upper = g >= 2;
+      u32x4 xa8[CR / 8], xb8[CR / 8];
 #pragma unroll
-      for (int k = 0; k < CR; ++k) {
-        const int c = CR * g + k;  // rotary column of this lane
-        const int i = c < HALF ? c : c - HALF;
-        const float cs = rq[2 * i], sn = rq[2 * i + 1];
-        const float xa = bf16_to_f32(qrow[DH + i]), xb = bf16_to_f32(qrow[DH + i + HALF]);
-        qr[hh][k] = a.qscale * (c < HALF ? xa * cs - xb * sn : xa * sn + xb * cs);
+      for (int k8 = 0; k8 < CR / 8; ++k8) {
+        xa8[k8] = *(const u32x4 *)(qrow + DH + i0 + 8 * k8);
+        xb8[k8] = *(const u32x4 *)(qrow + DH + HALF + i0 + 8 * k8);
+      }
+#pragma unroll
+      for (int k4 = 0; k4 < CR / 2; ++k4) {
+        const f32x4 t = *(const f32x4 *)(rq + 2 * (i0 + 2 * k4));  // (cos, sin) of pairs i0 + 2 k4, + 1
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int k = 2 * k4 + e;
+          const uint32_t wa = xa8[k / 8][(k % 8) / 2], wb = xb8[k / 8][(k % 8) / 2];
+          const float xa = k & 1 ? bf16_hi(wa) : bf16_lo(wa), xb = k & 1 ? bf16_hi(wb) : bf16_lo(wb);
+          const float cs = t[2 * e], sn = t[2 * e + 1];
+          qr[hh][k] = a.qscale * (upper ? xa * sn + xb * cs : xa * cs - xb * sn);
+        }
       }
     }
   }
