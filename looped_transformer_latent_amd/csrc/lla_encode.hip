@@ -97,25 +97,28 @@ __global__ __launch_bounds__(256) void encode_append_kernel(EncodeArgs a, int RK
 //
 // Per (layer, latent group, K|V) the encoder is a plain GEMM,
 //   C[tokens x r] = X[tokens x width] W_down[width x r] - 1 (mu W_down),
-// run on v_mfma_f32_16x16x32_bf16.  A workgroup (8 waves) takes 128 tokens;
-// wave w owns 16 of them (one 16-row tile) and all r columns: few registers
-// per wave and many waves per CU, which hides the x loads best.  W_down is
-// streamed in chunks of 128 rows, transposed into LDS ([r][k], rows padded so
-// the 16-byte B-operand reads of 16 consecutive r hit distinct banks) and
-// shared by the 8 waves.  Each lane reads its token's x as 64 contiguous bytes
-// per chunk: K-slot e of K-step s in lane group g is chunk column
-// 32 g + 8 s + e, on both operands.  mu W_down comes from encode_muw_kernel
+// run on v_mfma_f32_16x16x32_bf16.  A workgroup (8 waves) takes 256 tokens
+// (128 for r > 160); wave w owns two 16-row tiles (one) and all r columns, so
+// every W_down operand read from LDS feeds two products.  W_down is streamed in
+// chunks of 128 rows, transposed into LDS ([r][k], rows padded so the 16-byte
+// B-operand reads of 16 consecutive r hit distinct banks) and shared by the 8
+// waves; the chunks are software-pipelined: while chunk c multiplies out of
+// one LDS buffer, the x rows and W_down rows of chunk c + 1 are in flight and
+// land in the other buffer, one barrier per chunk.  K-slot e of K-step s in
+// lane group g is chunk column 32 s + 8 g + e on both operands, so each x load
+// instruction reads 64 contiguous bytes of every token's row.  mu W_down comes from encode_muw_kernel
 // (once per call).  The result (minus mu W_down, rounded once to bf16) goes
 // through LDS and leaves as 16-byte stores into the paged pool.
 template <int R>
 __global__ __launch_bounds__(512) void encode_mfma_kernel(EncodeArgs a, int kv) {
-  constexpr int TOK = 128;        // tokens per workgroup
+  constexpr int TPW = R <= 160 ? 2 : 1;  // 16-token row tiles per wave (registers bound it)
+  constexpr int TOK = 128 * TPW;         // tokens per workgroup
   constexpr int KC = 128;         // W_down rows per chunk
   constexpr int LROW = KC + 8;    // padded LDS row (elements) of the transposed chunk
   constexpr int CT = R / 16;      // column tiles
   static_assert(R % 16 == 0 && R <= 256, "r");
-  static_assert(R * LROW >= TOK * R, "output staging reuses the chunk buffer");
-  __shared__ __attribute__((aligned(16))) uint16_t s_w[R * LROW];
+  constexpr int WBUF = R * LROW;  // one transposed chunk
+  __shared__ __attribute__((aligned(16))) uint16_t s_w[(2 * WBUF > TOK * R ? 2 * WBUF : TOK * R)];
   __shared__ long long s_off[TOK];  // element offset of each token's latent row, -1 = dropped
 
   // wave index as a scalar: branches on it must be uniform scalar branches,
@@ -151,48 +154,89 @@ __global__ __launch_bounds__(512) void encode_mfma_kernel(EncodeArgs a, int kv) 
     s_off[threadIdx.x] = off;
   }
 
-  // this lane's x row: token tok0 + 16 w + n (clamped; dropped at the end)
-  long long tk = tok0 + 16 * w + n;
-  if (tk >= tokens) tk = tokens - 1;
-  const uint16_t *xr = (const uint16_t *)x + ((li * tokens + tk) * a.groups + grp) * a.width;
-
-  f32x4 acc[CT];
+  // this lane's x rows: tokens tok0 + 16 (TPW w + tt) + n (clamped; dropped at the end)
+  const uint16_t *xr[TPW];
 #pragma unroll
-  for (int ct = 0; ct < CT; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int tt = 0; tt < TPW; ++tt) {
+    long long tk = tok0 + 16 * (TPW * w + tt) + n;
+    if (tk >= tokens) tk = tokens - 1;
+    xr[tt] = (const uint16_t *)x + ((li * tokens + tk) * a.groups + grp) * a.width;
+  }
+
+  f32x4 acc[TPW][CT];
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) acc[tt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nchunks = a.width / KC;
-  for (int c = 0; c < nchunks; ++c) {
-    const int k0 = c * KC;
-    u32x4 xa[4];
+  // Software pipeline over 128-row chunks: while chunk c multiplies out of LDS
+  // buffer c % 2, the x rows and W_down rows of chunk c + 1 are in flight in
+  // registers; W_down goes into the other buffer after the products, then one
+  // barrier per chunk.
+  constexpr int WT = ((KC / 4) * (R / 8) + 511) / 512;  // transpose tasks per thread
+  u32x4 xa[TPW][4], xn[TPW][4], wv[WT][4];
+  auto load_x = [&](int c, u32x4 (&dst)[TPW][4]) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) xa[s] = *(const u32x4 *)(xr + k0 + 32 * g + 8 * s);
-    __syncthreads();  // previous chunk's operands are consumed
-    // W_down rows k0 .. k0 + 127 -> s_w[r][k]: 4 rows x 8 columns per task
-    for (int task = threadIdx.x; task < (KC / 4) * (R / 8); task += blockDim.x) {
+    for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) dst[tt][s] = *(const u32x4 *)(xr[tt] + c * KC + 32 * s + 8 * g);
+  };
+  auto load_w = [&](int c) {
+#pragma unroll
+    for (int j = 0; j < WT; ++j) {
+      const int task = min((int)threadIdx.x + 512 * j, (KC / 4) * (R / 8) - 1);
       const int k4 = task / (R / 8), r8 = task % (R / 8);
-      u32x4 v[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = *(const u32x4 *)(wd + (long long)(k0 + 4 * k4 + i) * R + 8 * r8);
+      for (int i = 0; i < 4; ++i) wv[j][i] = *(const u32x4 *)(wd + (long long)(c * KC + 4 * k4 + i) * R + 8 * r8);
+    }
+  };
+  auto store_w = [&](uint16_t *buf) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int sh = (j & 1) * 16;
-        const uint32_t e0 = (v[0][j >> 1] >> sh) & 0xFFFFu, e1 = (v[1][j >> 1] >> sh) & 0xFFFFu;
-        const uint32_t e2 = (v[2][j >> 1] >> sh) & 0xFFFFu, e3 = (v[3][j >> 1] >> sh) & 0xFFFFu;
-        uint32_t *dst = (uint32_t *)(s_w + (8 * r8 + j) * LROW + 4 * k4);
-        dst[0] = e0 | (e1 << 16);
-        dst[1] = e2 | (e3 << 16);
+    for (int j = 0; j < WT; ++j) {
+      const int task = (int)threadIdx.x + 512 * j;
+      if (task < (KC / 4) * (R / 8)) {
+        const int k4 = task / (R / 8), r8 = task % (R / 8);
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const int sh = (jj & 1) * 16;
+          const uint32_t e0 = (wv[j][0][jj >> 1] >> sh) & 0xFFFFu, e1 = (wv[j][1][jj >> 1] >> sh) & 0xFFFFu;
+          const uint32_t e2 = (wv[j][2][jj >> 1] >> sh) & 0xFFFFu, e3 = (wv[j][3][jj >> 1] >> sh) & 0xFFFFu;
+          uint32_t *dst = (uint32_t *)(buf + (8 * r8 + jj) * LROW + 4 * k4);
+          dst[0] = e0 | (e1 << 16);
+          dst[1] = e2 | (e3 << 16);
+        }
       }
     }
-    __syncthreads();
+  };
+  load_x(0, xa);
+  load_w(0);
+  store_w(s_w);
+  __syncthreads();
+  for (int c = 0; c < nchunks; ++c) {
+    const bool more = c + 1 < nchunks;
+    if (more) {
+      load_x(c + 1, xn);
+      load_w(c + 1);
+    }
+    const uint16_t *buf = s_w + (c & 1) * WBUF;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const int kk = 32 * g + 8 * s;
+      const int kk = 32 * s + 8 * g;  // K-step s: 64 contiguous bytes of each token's x row
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
-        const u32x4 bw = *(const u32x4 *)(s_w + (16 * ct + n) * LROW + kk);
-        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[s]), as_bf16x8(bw), acc[ct], 0, 0, 0);
+        const u32x4 bw = *(const u32x4 *)(buf + (16 * ct + n) * LROW + kk);
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt)
+          acc[tt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[tt][s]), as_bf16x8(bw), acc[tt][ct], 0, 0, 0);
       }
     }
+    if (more) store_w(s_w + ((c + 1) & 1) * WBUF);
+    __syncthreads();
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) xa[tt][s] = xn[tt][s];
   }
 
   __syncthreads();  // s_w free for output staging
@@ -203,8 +247,10 @@ __global__ __launch_bounds__(512) void encode_mfma_kernel(EncodeArgs a, int kv) 
     const int r = 16 * ct + n;
     const float mw = muw[r];
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      s_out[(16 * w + 4 * g + e) * R + r] = (uint16_t)f32_to_bf16(acc[ct][e] - mw);
+    for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        s_out[(16 * (TPW * w + tt) + 4 * g + e) * R + r] = (uint16_t)f32_to_bf16(acc[tt][ct][e] - mw);
   }
   __syncthreads();
   for (int q = threadIdx.x; q < TOK * (R / 8); q += blockDim.x) {
@@ -225,11 +271,12 @@ bool encode_mfma_r(int r) {
 
 hipError_t launch_encode_mfma(int r, int kv, const EncodeArgs &a, hipStream_t stream) {
   const long long tokens = (long long)a.batch * a.n_new;
-  const dim3 grid((unsigned)((tokens + 127) / 128), a.groups, a.n_layers);
-#define X(RR)                                                                               \
-  if (r == RR) {                                                                            \
-    hipLaunchKernelGGL(encode_mfma_kernel<RR>, grid, dim3(512), 0, stream, a, kv);          \
-    return hipGetLastError();                                                               \
+#define X(RR)                                                                                     \
+  if (r == RR) {                                                                                  \
+    constexpr int tok = RR <= 160 ? 256 : 128;                                                    \
+    const dim3 grid((unsigned)((tokens + tok - 1) / tok), a.groups, a.n_layers);                  \
+    hipLaunchKernelGGL(encode_mfma_kernel<RR>, grid, dim3(512), 0, stream, a, kv);                \
+    return hipGetLastError();                                                                     \
   }
   LLA_ENCODE_R(X)
 #undef X
