@@ -20,7 +20,10 @@
 //    (alpha / beta as hi + lo bf16 in one extra K-step).
 //  * Tokens go in blocks of 32 (two 16-token pages).  The block's c_k, c_v and
 //    RoPE rows are copied global -> LDS with direct-to-LDS loads (no register
-//    staging), double-buffered: block b+1 is in flight while block b computes.
+//    staging) into three buffers: the copy of block b+2 is in flight while the
+//    K-side products of block b+1 share a barrier interval with the softmax of
+//    block b, and the value sum of block b with the cos / sin weighting of
+//    block b+1 (two barriers per block).
 //    The tile is shared by the 4 waves, so each latent is fetched from L2 once
 //    per workgroup.  Workgroups of the same (row, split) but different head
 //    groups are dispatched to the same XCD so that they share its L2.
@@ -41,6 +44,17 @@ typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
 typedef uint32_t u32x2 __attribute__((__vector_size__(2 * sizeof(uint32_t))));
 
 #define LLA_LDS(p) ((__attribute__((address_space(3))) void *)(p))
+
+// Barrier that first waits for this wave's LDS writes and for all but its VM
+// most recent vector-memory operations (direct-to-LDS copies still in flight).
+template <int VM>
+__device__ __forceinline__ void barrier_vm() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(((VM >> 4) << 14) | (VM & 15) | 0x70);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 template <int DH, int RK, int RV>
 struct Tile2d {
@@ -65,7 +79,7 @@ __global__ __launch_bounds__(512) void decode_2d_kernel(AttnArgs a) {
   static_assert(PW % 16 == 0 && RK % 128 == 0 && VR == 32 && VT == 2, "shape");
   static_assert(CKQ % NW == 0 && CVQ % NW == 0 && TRQ % NW == 0, "tile split");
 
-  __shared__ Tile2d<DH, RK, RV> tile0, tile1;
+  __shared__ Tile2d<DH, RK, RV> tile0, tile1, tile2;
   __shared__ __attribute__((aligned(16))) uint16_t s_p[16][32];  // bf16 weights; rows >= 4 stay 0
   __shared__ float s_alpha[16];                                   // rescale per head; >= 4 stay 1
   __shared__ float s_part[NH][2][32];                             // half-scores per head
@@ -207,17 +221,16 @@ __global__ __launch_bounds__(512) void decode_2d_kernel(AttnArgs a) {
 #pragma unroll
   for (int v = 0; v < VT; ++v) accv[v] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto run_block = [&](int blk, Tile2d<DH, RK, RV> &T, Tile2d<DH, RK, RV> &N) {
-    if (blk + 1 < nblk) issue(blk + 1, N);
-    __builtin_amdgcn_sched_barrier(0);
-    const int j0 = j_lo + 32 * blk;
-    const int nvalid = min(32, j_hi - j0);
-
-    // K side: X / Y of this wave's 32 pairs x 32 tokens
-    f32x16 acc[RTW];
+  // The block loop is software-pipelined over three tile buffers so that the
+  // K-side products of block b + 1 sit in the same barrier interval as the
+  // softmax of block b (the matrix cores run while the vector units reduce):
+  //   interval A(b): issue copies of block b + 2; softmax(b); K side(b + 1)
+  //   interval B(b): value sum(b); cos / sin weighting(b + 1) -> s_part
+  // A(b) ends with a barrier that leaves this wave's copies of block b + 2 in
+  // flight; B(b) ends with a barrier after all copies have landed.
+  auto kside = [&](Tile2d<DH, RK, RV> &T, f32x16 (&acc)[RTW]) {
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) acc[rt] = f32x16{};
-    // B-operands two K-steps ahead of their MFMAs
     u32x4 bk[3];
     bk[0] = T.ck[(kh * KS + 0) * 32 + t];
     bk[1] = T.ck[(kh * KS + 1) * 32 + t];
@@ -232,7 +245,8 @@ __global__ __launch_bounds__(512) void decode_2d_kernel(AttnArgs a) {
     for (int rt = 0; rt < RTW; ++rt)
       acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(u32x4{A1[rt], 0u, 0u, 0u}), bone,
                                                          acc[rt], 0, 0, 0);
-
+  };
+  auto weigh = [&](Tile2d<DH, RK, RV> &T, const f32x16 (&acc)[RTW]) {
     float sp = 0.f;
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) {
@@ -246,13 +260,14 @@ __global__ __launch_bounds__(512) void decode_2d_kernel(AttnArgs a) {
         sp = fmaf(tr[3], acc[rt][4 * q + 3], sp);
       }
     }
-    {
-      const uint32_t us = __float_as_uint(sp);
-      const auto sw = __builtin_amdgcn_permlane32_swap(us, us, false, false);
-      sp = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    }
+    const uint32_t us = __float_as_uint(sp);
+    const auto sw = __builtin_amdgcn_permlane32_swap(us, us, false, false);
+    sp = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
     if (kh == 0) s_part[hl][rh][t] = sp;
-    __syncthreads();
+  };
+  auto softmax = [&](int blk) {
+    const int j0 = j_lo + 32 * blk;
+    const int nvalid = min(32, j_hi - j0);
     // both halves of a head add the two half-scores in the same order
     const float sfull = s_part[hl][0][t] + s_part[hl][1][t];
     const float s = t < nvalid ? sfull : -INFINITY;
@@ -275,9 +290,11 @@ __global__ __launch_bounds__(512) void decode_2d_kernel(AttnArgs a) {
     m_run = m_new;
     if (rh == 0 && kh == 0) s_p[hl][t] = (uint16_t)pbits;
     if (rh == 0 && lane == 0) s_alpha[hl] = alpha;
-    __syncthreads();
-
-    // V side: accv[head n][r] = accv * alpha_n + sum_t p[n][t] c_v[t][r]
+  };
+  auto vside = [&](int blk, Tile2d<DH, RK, RV> &T) {
+    const int j0 = j_lo + 32 * blk;
+    const int nvalid = min(32, j_hi - j0);
+    // accv[head n][r] = accv * alpha_n + sum_t p[n][t] c_v[t][r]
     const float al = s_alpha[n16];
     const u32x4 pv = *(const u32x4 *)&s_p[n16][8 * g16];
     const int rb = w * VR + 2 * n16;  // lane's 2 columns: rb, rb + 1 (one per tile)
@@ -299,14 +316,37 @@ __global__ __launch_bounds__(512) void decode_2d_kernel(AttnArgs a) {
       accv[v] = accv[v] * al;
       accv[v] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(pv), accv[v], 0, 0, 0);
     }
-    __syncthreads();  // tile T, s_part and s_p free; block blk+1 landed in N
+  };
+  // this wave's copy instructions per block (all of them count on vmcnt)
+  constexpr int NCOPY = CKQ / NW + CVQ / NW + TRQ / NW;
+  auto step = [&](int blk, Tile2d<DH, RK, RV> &Tb, Tile2d<DH, RK, RV> &Tn, Tile2d<DH, RK, RV> &Tnn) {
+    issue(min(blk + 2, nblk - 1), Tnn);  // past the end: a harmless re-copy of the last block
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 acc[RTW];
+    kside(Tn, acc);  // block b + 1 (past the end: ignored)
+    softmax(blk);
+    barrier_vm<NCOPY>();
+    weigh(Tn, acc);
+    vside(blk, Tb);
+    barrier_vm<0>();
   };
 
-  if (nblk > 0) issue(0, tile0);
-  __syncthreads();
-  for (int blk = 0; blk < nblk; blk += 2) {
-    run_block(blk, tile0, tile1);
-    if (blk + 1 < nblk) run_block(blk + 1, tile1, tile0);
+  if (nblk > 0) {
+    issue(0, tile0);
+    issue(min(1, nblk - 1), tile1);
+    barrier_vm<0>();
+    f32x16 acc0[RTW];
+    kside(tile0, acc0);
+    weigh(tile0, acc0);
+    barrier_vm<0>();
+    int blk = 0;
+    for (; blk + 3 <= nblk; blk += 3) {
+      step(blk, tile0, tile1, tile2);
+      step(blk + 1, tile1, tile2, tile0);
+      step(blk + 2, tile2, tile0, tile1);
+    }
+    if (blk < nblk) step(blk, tile0, tile1, tile2);
+    if (blk + 1 < nblk) step(blk + 1, tile1, tile2, tile0);
   }
 
   // ---- epilogue ----
