@@ -123,7 +123,18 @@ __global__ __launch_bounds__(256) void reconstruct_kernel(AttnArgs a, char *k_fu
   int bad = 0;
   // latent rows of page lp (lane n: token n of the page), one page ahead
   const int lp_end = min(lp0 + ppw, npg);
-  auto page_of = [&](int lp) { return a.page_table[(long long)b * a.max_pages + lp]; };
+  // mu_k, mu_v at this lane's output dims, read once (bf16 pairs)
+  u32x2 mk2[NDT / 2][2], mv2[NDT];
+#pragma unroll
+  for (int T = 0; T < NDT / 2; ++T) {
+    mk2[T][0] = *(const u32x2 *)(mk + 16 * T + 4 * g);
+    mk2[T][1] = *(const u32x2 *)(mk + 16 * T + 4 * g + HALF);
+  }
+#pragma unroll
+  for (int T = 0; T < NDT; ++T) mv2[T] = *(const u32x2 *)(mv + 16 * T + 4 * g);
+  // the wave's page-table entries, one per lane, read once (lane i: page lp0 + i)
+  const int pt_lane = lane < lp_end - lp0 ? a.page_table[(long long)b * a.max_pages + lp0 + lane] : 0;
+  auto page_of = [&](int lp) { return __builtin_amdgcn_readlane(pt_lane, lp - lp0); };
   auto fetch = [&](int e, LatRow<RK> &rk, LatRow<RV> &rv) {
     const long long pe = e >= 0 && e < a.num_pages ? e : 0;
     load_wup<RK>(rk, (const uint16_t *)a.k_pool + pe * a.pool_page_stride_k + (long long)h * a.pool_head_stride_k + n * RK, g);
@@ -131,11 +142,25 @@ __global__ __launch_bounds__(256) void reconstruct_kernel(AttnArgs a, char *k_fu
   };
   LatRow<RK> ck, ck_n;
   LatRow<RV> cv, cv_n;
+  // RoPE of the page's first position for this lane's pairs, one page ahead
+  f32x4 rb4[NDT / 2][2], rb4_n[NDT / 2][2];
+  auto fetch_rope = [&](int lp, f32x4 (&dst)[NDT / 2][2]) {
+    const float *rr = a.rope + (long long)(lp * kPage) * DH;
+#pragma unroll
+    for (int T = 0; T < NDT / 2; ++T) {
+      dst[T][0] = *(const f32x4 *)(rr + 2 * (16 * T + 4 * g));
+      dst[T][1] = *(const f32x4 *)(rr + 2 * (16 * T + 4 * g) + 4);
+    }
+  };
   int e = page_of(lp0);
   fetch(e, ck, cv);
+  fetch_rope(lp0, rb4);
   for (int lp = lp0; lp < lp_end; ++lp) {
     const int e_n = lp + 1 < lp_end ? page_of(lp + 1) : e;
-    if (lp + 1 < lp_end) fetch(e_n, ck_n, cv_n);
+    if (lp + 1 < lp_end) {
+      fetch(e_n, ck_n, cv_n);
+      fetch_rope(lp + 1, rb4_n);
+    }
     if (e < 0 || e >= a.num_pages) {  // uniform over the wave
       bad |= LLA_DEVERR_PAGE;
     } else {
@@ -147,11 +172,12 @@ __global__ __launch_bounds__(256) void reconstruct_kernel(AttnArgs a, char *k_fu
         const f32x4 x = wup_times<RK>(ak[T], ck);
         const f32x4 y = wup_times<RK>(ak[T + NDT / 2], ck);
         const int d0 = 16 * T + 4 * g;  // RoPE pairs d0 .. d0 + 3
-        const f32x4 c01 = *(const f32x4 *)(rr + 2 * d0), c23 = *(const f32x4 *)(rr + 2 * d0 + 4);
+        const f32x4 c01 = rb4[T][0], c23 = rb4[T][1];
         float ra[4], rb[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float ka = x[i] + bf16_to_f32(mk[d0 + i]), kb = y[i] + bf16_to_f32(mk[d0 + i + HALF]);
+          const float ka = x[i] + (i & 1 ? bf16_hi(mk2[T][0][i >> 1]) : bf16_lo(mk2[T][0][i >> 1]));
+          const float kb = y[i] + (i & 1 ? bf16_hi(mk2[T][1][i >> 1]) : bf16_lo(mk2[T][1][i >> 1]));
           const f32x4 &cq = i < 2 ? c01 : c23;
           const float cb = cq[2 * (i & 1)], sb = cq[2 * (i & 1) + 1];
           const float cd = rd[T][i >> 1][2 * (i & 1)], sd = rd[T][i >> 1][2 * (i & 1) + 1];
@@ -168,7 +194,7 @@ __global__ __launch_bounds__(256) void reconstruct_kernel(AttnArgs a, char *k_fu
         const int d0 = 16 * T + 4 * g;
         float o[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = x[i] + bf16_to_f32(mv[d0 + i]);
+        for (int i = 0; i < 4; ++i) o[i] = x[i] + (i & 1 ? bf16_hi(mv2[T][i >> 1]) : bf16_lo(mv2[T][i >> 1]));
         *(u32x2 *)(sv + n * SROW + d0) = u32x2{cvt2(o[0], o[1]), cvt2(o[2], o[3])};
       }
       // store j, lane l: elements 512 j + 8 l .. + 7 of the tile, i.e. token
@@ -188,6 +214,11 @@ __global__ __launch_bounds__(256) void reconstruct_kernel(AttnArgs a, char *k_fu
     e = e_n;
     ck = ck_n;
     cv = cv_n;
+#pragma unroll
+    for (int T = 0; T < NDT / 2; ++T) {
+      rb4[T][0] = rb4_n[T][0];
+      rb4[T][1] = rb4_n[T][1];
+    }
   }
   if (bad && lane == 0) atomicOr(a.err, bad);
 }
