@@ -178,7 +178,9 @@ bool plan_full(const lla_dims *d, long long rows, int max_ctx, AttnPlan *p) {
 
 size_t encode_ws_bytes(const lla_dims *d, int n_layers) {
   const int groups = d->variant == LLA_PER_HEAD ? d->H : 1;
-  return align256(kHeaderBytes + sizeof(float) * (size_t)n_layers * groups * (d->r_k + d->r_v));
+  const int width = d->variant == LLA_PER_HEAD ? d->T * d->d_head : d->T * d->H * d->d_head;
+  const size_t one = sizeof(float) * (size_t)n_layers * groups * (d->r_k + d->r_v);
+  return align256(kHeaderBytes + one) + align256(one * encode_muw_parts(width));
 }
 
 int32_t check_launch(hipError_t e) {
@@ -404,6 +406,9 @@ int32_t lla_encode_append(const lla_dims *d, const lla_codec *c, const lla_cache
   a.width = width;
   a.err = (int *)ws;
   a.muw = (float *)((char *)ws + kHeaderBytes);
+  a.muw_parts = encode_muw_parts(width);
+  a.muw_part = (float *)((char *)ws + align256(kHeaderBytes + sizeof(float) * (size_t)n_layers * groups *
+                                                                    (d->r_k + d->r_v)));
   a.muw_stride = d->r_k + d->r_v;
   a.muw_v_off = d->r_k;
   return check_launch(launch_encode(d->dtype, d->r_k, d->r_v, a, stream));

@@ -19,21 +19,31 @@ __device__ __forceinline__ float ldx(const char *p, long long i) {
 
 // muw[li][grp][kv ? RK + r : r] = sum_i mu[i] W_down[i][r], fp32: a constant of
 // (layer, latent group), computed once per call and shared by every token tile.
-// Wave w sums rows i = w, w + 4, ... (lanes over r, coalesced rows of W_down);
-// the 4 partial sums are added in fixed order.
+// The rows of W_down are cut into muw_parts ranges of kMuwRows rows, summed by
+// separate workgroups (one per (range, group), layer, K|V) into muw_part; a
+// second launch adds the ranges in fixed order.  Within a range, wave w sums
+// rows w, w + 4, ... (lanes over r, coalesced rows of W_down) and the 4 wave
+// sums are added in fixed order.
+constexpr int kMuwRows = 64;
+
+int encode_muw_parts(int width) { return (width + kMuwRows - 1) / kMuwRows; }
+
 template <bool BF>
 __global__ __launch_bounds__(256) void encode_muw_kernel(EncodeArgs a, int RK, int RV) {
   __shared__ float part[4][256];
-  const int grp = blockIdx.x, li = blockIdx.y, kv = blockIdx.z;
+  const int grp = blockIdx.x % a.groups, pr = blockIdx.x / a.groups;
+  const int li = blockIdx.y, kv = blockIdx.z;
   const int R = kv ? RV : RK;
   const int esz = BF ? 2 : 4;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const long long gl = (long long)li * a.groups + grp;  // relative to layer0
   const char *mu = (kv ? a.mu_v : a.mu_k) + gl * a.width * esz;
   const char *wd = (kv ? a.wd_v : a.wd_k) + gl * a.width * (long long)R * esz;
+  const int i0 = pr * kMuwRows, i1 = min(i0 + kMuwRows, a.width);
+  float *dst = a.muw_part + ((long long)pr * a.n_layers * a.groups + gl) * (RK + RV) + (kv ? RK : 0);
   for (int r0 = 0; r0 < R; r0 += 256) {
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int i = w; i < a.width; i += 4) {
+    for (int i = i0 + w; i < i1; i += 4) {
       const float m = ldx<BF>(mu, i);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -45,12 +55,32 @@ __global__ __launch_bounds__(256) void encode_muw_kernel(EncodeArgs a, int RK, i
     for (int j = 0; j < 4; ++j) part[w][lane + 64 * j] = acc[j];
     __syncthreads();
     const int r = r0 + threadIdx.x;
-    if (r < R)
-      a.muw[gl * (RK + RV) + (kv ? RK : 0) + r] =
-          ((part[0][threadIdx.x] + part[1][threadIdx.x]) + part[2][threadIdx.x]) + part[3][threadIdx.x];
+    if (r < R) dst[r] = ((part[0][threadIdx.x] + part[1][threadIdx.x]) + part[2][threadIdx.x]) + part[3][threadIdx.x];
     __syncthreads();
   }
 }
+
+// muw = sum over the row ranges, in range order.  One thread per
+// (layer, group, column).
+__global__ __launch_bounds__(256) void encode_muw_reduce_kernel(EncodeArgs a) {
+  const long long n = (long long)a.n_layers * a.groups * a.muw_stride;
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n) return;
+  float s = 0.f;
+  for (int pr = 0; pr < a.muw_parts; ++pr) s += a.muw_part[(long long)pr * n + idx];
+  a.muw[idx] = s;
+}
+
+namespace {
+template <bool BF>
+hipError_t launch_muw(int r_k, int r_v, const EncodeArgs &a, hipStream_t stream) {
+  const dim3 g1((unsigned)(a.groups * a.muw_parts), a.n_layers, 2);
+  hipLaunchKernelGGL(encode_muw_kernel<BF>, g1, dim3(256), 0, stream, a, r_k, r_v);
+  const long long n = (long long)a.n_layers * a.groups * a.muw_stride;
+  hipLaunchKernelGGL(encode_muw_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+}  // namespace
 
 // One workgroup per (16-token tile, group, layer*2 + kv).
 template <bool BF>
@@ -291,20 +321,22 @@ hipError_t launch_encode(int dtype, int r_k, int r_v, const EncodeArgs &a, hipSt
   const long long tokens = (long long)a.batch * a.n_new;
   if (tokens == 0 || a.n_layers == 0) return hipSuccess;
   // bf16 with whole 128-column chunks and an instantiated rank: matrix cores
-  const dim3 g1(a.groups, a.n_layers, 2);
   if (dtype == LLA_BF16 && a.width % 128 == 0 && encode_mfma_r(r_k) && encode_mfma_r(r_v) &&
       tokens <= 0x7FFFFFFFLL * 128) {
-    hipLaunchKernelGGL(encode_muw_kernel<true>, g1, dim3(256), 0, stream, a, r_k, r_v);
-    hipError_t e = launch_encode_mfma(r_k, 0, a, stream);
+    hipError_t e = launch_muw<true>(r_k, r_v, a, stream);
+    if (e != hipSuccess) return e;
+    e = launch_encode_mfma(r_k, 0, a, stream);
     if (e != hipSuccess) return e;
     return launch_encode_mfma(r_v, 1, a, stream);
   }
   const dim3 g2((unsigned)((tokens + 15) / 16), a.groups, 2 * a.n_layers);
   if (dtype == LLA_BF16) {
-    hipLaunchKernelGGL(encode_muw_kernel<true>, g1, dim3(256), 0, stream, a, r_k, r_v);
+    const hipError_t e = launch_muw<true>(r_k, r_v, a, stream);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(encode_append_kernel<true>, g2, dim3(256), 0, stream, a, r_k, r_v);
   } else {
-    hipLaunchKernelGGL(encode_muw_kernel<false>, g1, dim3(256), 0, stream, a, r_k, r_v);
+    const hipError_t e = launch_muw<false>(r_k, r_v, a, stream);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(encode_append_kernel<false>, g2, dim3(256), 0, stream, a, r_k, r_v);
   }
   return hipGetLastError();

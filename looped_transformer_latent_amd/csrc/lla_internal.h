@@ -69,6 +69,8 @@ struct EncodeArgs {
   int max_pages, num_pages, batch, n_new, n_layers, groups, width;
   float *muw;                  // workspace [n_layers][groups][r_k + r_v]: mu W_down, K then V
   int muw_stride, muw_v_off;   // r_k + r_v, r_k
+  float *muw_part;             // workspace [muw_parts][n_layers][groups][r_k + r_v]: partial sums
+  int muw_parts;               // row ranges of W_down summed independently
   int *err;
 };
 
@@ -95,6 +97,7 @@ hipError_t launch_full_decode(int d_head, const AttnArgs &a, hipStream_t stream)
 bool absorbed_supported(int d_head, int r_k, int r_v, int d_rope, int heads_per_wave, int waves);
 hipError_t launch_absorbed(int d_head, int r_k, int r_v, int d_rope, const AttnArgs &a, hipStream_t stream);
 hipError_t launch_rope_key_append(const RopeAppendArgs &a, hipStream_t stream);
+int encode_muw_parts(int width);
 hipError_t launch_rope_table(int n_pos, int d_head, double base, float *table, hipStream_t s);
 
 }  // namespace lla
