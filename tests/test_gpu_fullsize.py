@@ -106,10 +106,36 @@ def test_ouro_b32_ctx4096_full(release):
 
 
 def test_ouro_b768_ctx4096_shuffled_sampled(release):
-    """The high-capacity point: batch 768, 4k context, 116 GB shuffled pool."""
+    """The high-capacity point: batch 768, 4k context, 116 GB shuffled pool; then
+    the same calls with a 4-token sink and a 256-token window, as the benchmark
+    runs them."""
     b = Built(wl.WORKLOADS["ouro1.4b-21x-b768-paged"])
     check_rows(b, np.array([0, 1, 383, 500, 766, 767]), 23, 3)
     check_rows(b, np.array([2, 640]), 11, 0)
+    w = b.w
+    layer, loop, rows = 23, 3, np.array([0, 383, 767])
+    q = torch.empty((w.batch, w.H, w.d_head), dtype=torch.bfloat16, device="cuda")
+    lla.gen_normal_(q, w.seed, wl.STREAMS["q"], offset=12345)
+    ctx = torch.full((w.batch,), w.ctx, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    ws = lla.workspace(b.D, lla.OP_WINDOW_DECODE, w.batch, w.ctx, 260)
+    lla.decode_window_attn(b.D, b.codec, b.cache, b.rope, layer, loop, q, ctx - 1, ctx, 4, 256, w.ctx, out, ws)
+    torch.cuda.synchronize()
+    assert lla.device_error_word(ws) == 0
+    got = out_to_f64(out)
+    m1 = dict(w.dims, D=1)
+    codec1 = {k: np.ascontiguousarray(v[layer:layer + 1]) for k, v in b.codec_h.items()}
+    pages = b.pt_h[rows].reshape(-1)
+    kp = wl.pool_pages_host(w, "k", layer, pages)[None]
+    vp = wl.pool_pages_host(w, "v", layer, pages)[None]
+    local = np.arange(len(pages), dtype=np.int32).reshape(len(rows), -1)
+    c = np.full(len(rows), w.ctx, np.int32)
+    ref, rc = oracle.decode_window(m1, codec1, kp, vp, local, 0, loop, np.ascontiguousarray(to_host(q)[rows]),
+                                   c - 1, c, 4, 256)
+    assert rc == 0
+    err = row_rel_err(got[rows], ref)
+    print(f"[{w.name}] sink 4 + window 256, rows {list(rows)}: max row rel err {err.max():.3e}", flush=True)
+    assert err.max() <= TOL[w.dtype]
 
 
 def test_ouro_4x_encode_then_decode_sampled(release):
