@@ -183,7 +183,8 @@ int32_t lla_decode_attn(const lla_dims *dims, const lla_codec *codec, const lla_
  * Page-table entries of pages that hold no retained token are never read, so
  * the caller may release those pages (set their entries to anything).  A page
  * that holds a retained token must be valid (else LLA_DEVERR_PAGE, row NaN).
- *   n_sink, window  host ints, >= 0, 1 <= n_sink + window <= max_ctx
+ *   n_sink, window  host ints, >= 0, 1 <= n_sink + window <= 2^30 (a budget at
+ *                   or above a sequence's context keeps all of it)
  * Other arguments as for lla_decode_attn; workspace from lla_workspace_bytes(..,
  * LLA_OP_WINDOW_DECODE, batch, max_ctx, n_sink + window).  Supported: bf16
  * per-head shapes of lla_decode_attn. */

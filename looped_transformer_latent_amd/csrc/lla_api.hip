@@ -226,8 +226,8 @@ int32_t attn_call(const lla_dims *d, const lla_codec *c, const lla_cache *k, con
   const long long rows = (long long)k->batch * (prefill ? n_q : 1);
   if (rows > (1LL << 30)) return fail(LLA_ERR_INVALID_ARG, "too many query rows");
   if (evict) {
-    if (n_sink < 0 || window < 0 || (long long)n_sink + window < 1 || (long long)n_sink + window > max_ctx)
-      return fail(LLA_ERR_INVALID_ARG, "need n_sink, window >= 0 and 1 <= n_sink + window <= max_ctx");
+    if (n_sink < 0 || window < 0 || (long long)n_sink + window < 1 || (long long)n_sink + window > (1LL << 30))
+      return fail(LLA_ERR_INVALID_ARG, "need n_sink, window >= 0 and 1 <= n_sink + window <= 2^30");
     if (d->dtype != LLA_BF16 || d->variant != LLA_PER_HEAD)
       return fail(LLA_ERR_UNSUPPORTED, "token eviction is built for bf16 per-head LLA only");
   }

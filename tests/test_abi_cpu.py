@@ -208,7 +208,8 @@ def test_window_validation_and_planning():
         FAKE, kw.get("n_sink", 4), kw.get("window", 256), kw.get("max_ctx", 4096), 0.0, FAKE, FAKE,
         kw.get("ws_bytes", 16), NULL)
     assert win(n_sink=-1) == E and win(window=-2) == E and win(n_sink=0, window=0) == E
-    assert win(n_sink=100, window=5000) == E                           # budget beyond max_ctx
+    assert win(n_sink=1 << 29, window=(1 << 29) + 1) == E                # budget beyond 2^30
+    assert win(n_sink=100, window=5000) == lla.ERR_WORKSPACE             # a budget above max_ctx is valid
     assert win(dims=_dims(dtype=lla.F32, d_head=64)) == lla.ERR_UNSUPPORTED
     assert win() == lla.ERR_WORKSPACE
     # a 260-token budget plans like a 260 + 2 page context, not like 4096

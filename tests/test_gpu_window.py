@@ -48,7 +48,8 @@ def problem(shape, B, ctx_max, seed):
 
 
 CASES = [((128, 16, 32, 16), 4, 256), ((128, 16, 32, 16), 0, 16), ((128, 16, 32, 16), 20, 37),
-         ((128, 96, 160, 16), 4, 256), ((64, 16, 32, 16), 4, 256), ((128, 32, 64, 8), 4, 1024)]
+         ((128, 96, 160, 16), 4, 256), ((64, 16, 32, 16), 4, 256), ((128, 32, 64, 8), 4, 1024),
+         ((128, 16, 32, 16), 4, 8000)]  # a budget above max_ctx keeps every token
 
 
 @pytest.mark.parametrize("shape,n_sink,window", CASES, ids=lambda v: str(v))
