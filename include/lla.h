@@ -228,7 +228,8 @@ int32_t lla_prefill_attn(const lla_dims *dims, const lla_codec *codec, const lla
  * skipped and LLA_DEVERR_CTX set); pages with out-of-range table entries are
  * skipped and set LLA_DEVERR_PAGE.  Workspace: lla_workspace_bytes(..,
  * LLA_OP_RECONSTRUCT, ..) (the error word only).  Supported: bf16 per-head,
- * (d_head, r_k, r_v) in (64,16,32), (128,16,32), (128,32,64), (128,64,64). */
+ * (d_head, r_k, r_v) in (64,16,32), (128,16,32), (128,32,64), (128,64,64),
+ * (128,96,160). */
 int32_t lla_reconstruct_kv(const lla_dims *dims, const lla_codec *codec, const lla_cache *cache,
                            const float *rope_table, int32_t rope_len, int32_t layer, int32_t loop,
                            const int32_t *ctx_len, int32_t max_ctx, void *k_full, void *v_full,

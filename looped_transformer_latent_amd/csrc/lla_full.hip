@@ -68,17 +68,35 @@ __device__ __forceinline__ f32x4 wup_times(const WupTile<RK> &w, const LatRow<RK
   return acc;
 }
 
+// The same product with the W_up rows read from LDS (row stride R + 8
+// elements): for ranks whose decoder does not fit in registers.
+template <int RK>
+__device__ __forceinline__ f32x4 wup_times_lds(const uint16_t *w_row, const LatRow<RK> &b, int g) {
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < RK / 32; ++ks)
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(*(const u32x4 *)(w_row + 32 * ks + 8 * g)),
+                                                  as_bf16x8(b.a32[ks]), acc, 0, 0, 0);
+  if constexpr (RK % 32)
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+        __builtin_bit_cast(bf16x4, *(const u32x2 *)(w_row + 32 * (RK / 32) + 4 * g)),
+        __builtin_bit_cast(bf16x4, b.a16), acc, 0, 0, 0);
+  return acc;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- reconstruct
 
-// Grid: x = batch * ceil(max pages / (4 * PPW)), y = H; 4 waves, each PPW pages.
-template <int DH, int RK, int RV>
-__global__ __launch_bounds__(256) void reconstruct_kernel(AttnArgs a, char *k_full, char *v_full, int ppw) {
+// Grid: x = batch * ceil(max pages / (NW * PPW)), y = H; NW waves, each PPW
+// pages.  WLDS: W_up,k and W_up,v of the head are staged in LDS (shared by the
+// workgroup's waves) instead of registers, for ranks whose decoder does not fit.
+template <int DH, int RK, int RV, bool WLDS, int NW>
+__global__ __launch_bounds__(64 * NW) void reconstruct_kernel(AttnArgs a, char *k_full, char *v_full, int ppw) {
   constexpr int NDT = DH / 16, HALF = DH / 2;
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g = lane >> 4;
-  const int groups = (a.pages_per_split + 4 * ppw - 1) / (4 * ppw);  // pages_per_split: pages a row can need
+  const int groups = (a.pages_per_split + NW * ppw - 1) / (NW * ppw);  // pages_per_split: pages a row can need
   const int b = blockIdx.x / groups, grp = blockIdx.x - b * groups;
   const int h = blockIdx.y;
   int ctx = a.ctx_len[b];
@@ -87,21 +105,31 @@ __global__ __launch_bounds__(256) void reconstruct_kernel(AttnArgs a, char *k_fu
     return;
   }
   const int npg = (ctx + kPage - 1) / kPage;
-  const int lp0 = (grp * 4 + w) * ppw;
-  if (lp0 >= npg) return;  // whole wave
+  const int lp0 = (grp * NW + w) * ppw;
 
   // W_up,k rows 16 T + n (T < NDT), W_up,v rows likewise; mu per output row
   const uint16_t *wk = (const uint16_t *)a.wup_k + (long long)h * a.wup_head_stride_k;
   const uint16_t *wv = (const uint16_t *)a.wup_v + (long long)h * a.wup_head_stride_v;
   const uint16_t *mk = (const uint16_t *)a.mu_k + (long long)h * a.mu_head_stride;
   const uint16_t *mv = (const uint16_t *)a.mu_v + (long long)h * a.mu_head_stride;
-  WupTile<RK> ak[NDT];
-  WupTile<RV> av[NDT];
+  constexpr int WKR = RK + 8, WVR = RV + 8;  // LDS row strides of the staged decoder
+  __shared__ __align__(16) uint16_t s_w[WLDS ? DH * (WKR + WVR) : 8];
+  WupTile<RK> ak[WLDS ? 1 : NDT];
+  WupTile<RV> av[WLDS ? 1 : NDT];
+  if constexpr (WLDS) {
+    for (int i = threadIdx.x; i < DH * RK / 8; i += 64 * NW)
+      *(u32x4 *)(s_w + (i / (RK / 8)) * WKR + 8 * (i % (RK / 8))) = *(const u32x4 *)(wk + 8 * i);
+    for (int i = threadIdx.x; i < DH * RV / 8; i += 64 * NW)
+      *(u32x4 *)(s_w + DH * WKR + (i / (RV / 8)) * WVR + 8 * (i % (RV / 8))) = *(const u32x4 *)(wv + 8 * i);
+    __syncthreads();
+  } else {
 #pragma unroll
-  for (int T = 0; T < NDT; ++T) {
-    load_wup<RK>(ak[T], wk + (16 * T + n) * RK, g);
-    load_wup<RV>(av[T], wv + (16 * T + n) * RV, g);
+    for (int T = 0; T < NDT; ++T) {
+      load_wup<RK>(ak[T], wk + (16 * T + n) * RK, g);
+      load_wup<RV>(av[T], wv + (16 * T + n) * RV, g);
+    }
   }
+  if (lp0 >= npg) return;  // whole wave, after the workgroup's only barrier
   // RoPE of token 16 lp + n by angle addition: the page's first position is
   // one table row shared by every lane (a broadcast read), the offset n is
   // fixed per lane (fp32 products of two table rotations)
@@ -118,7 +146,7 @@ __global__ __launch_bounds__(256) void reconstruct_kernel(AttnArgs a, char *k_fu
   // each wave's page tile of K and of V is staged in LDS, so that it leaves in
   // 1 KiB-contiguous stores (16-byte pad per row)
   constexpr int SROW = DH + 8;
-  __shared__ __align__(16) uint16_t s_stage[4][2][kPage * SROW];
+  __shared__ __align__(16) uint16_t s_stage[NW][2][kPage * SROW];
   uint16_t *sk = s_stage[w][0], *sv = s_stage[w][1];
   int bad = 0;
   // latent rows of page lp (lane n: token n of the page), one page ahead
@@ -169,8 +197,14 @@ __global__ __launch_bounds__(256) void reconstruct_kernel(AttnArgs a, char *k_fu
       const float *rr = a.rope + (long long)(lp * kPage) * DH;  // page's first position (< ctx)
 #pragma unroll
       for (int T = 0; T < NDT / 2; ++T) {
-        const f32x4 x = wup_times<RK>(ak[T], ck);
-        const f32x4 y = wup_times<RK>(ak[T + NDT / 2], ck);
+        f32x4 x, y;
+        if constexpr (WLDS) {
+          x = wup_times_lds<RK>(s_w + (16 * T + n) * WKR, ck, g);
+          y = wup_times_lds<RK>(s_w + (16 * (T + NDT / 2) + n) * WKR, ck, g);
+        } else {
+          x = wup_times<RK>(ak[T], ck);
+          y = wup_times<RK>(ak[T + NDT / 2], ck);
+        }
         const int d0 = 16 * T + 4 * g;  // RoPE pairs d0 .. d0 + 3
         const f32x4 c01 = rb4[T][0], c23 = rb4[T][1];
         float ra[4], rb[4];
@@ -190,7 +224,9 @@ __global__ __launch_bounds__(256) void reconstruct_kernel(AttnArgs a, char *k_fu
       }
 #pragma unroll
       for (int T = 0; T < NDT; ++T) {
-        const f32x4 x = wup_times<RV>(av[T], cv);
+        f32x4 x;
+        if constexpr (WLDS) x = wup_times_lds<RV>(s_w + DH * WKR + (16 * T + n) * WVR, cv, g);
+        else x = wup_times<RV>(av[T], cv);
         const int d0 = 16 * T + 4 * g;
         float o[4];
 #pragma unroll
@@ -388,15 +424,17 @@ __global__ __launch_bounds__(256, 2) void full_decode_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------- dispatch
 
-#define LLA_RECON_SHAPES(X) \
-  X(64, 16, 32)             \
-  X(128, 16, 32)            \
-  X(128, 32, 64)            \
-  X(128, 64, 64)
+// (d_head, r_k, r_v, decoder in LDS, waves per workgroup)
+#define LLA_RECON_SHAPES(X)      \
+  X(64, 16, 32, false, 4)        \
+  X(128, 16, 32, false, 4)       \
+  X(128, 32, 64, false, 4)       \
+  X(128, 64, 64, false, 4)       \
+  X(128, 96, 160, true, 8)
 
 bool reconstruct_supported(int dtype, int variant, int d_head, int r_k, int r_v) {
   if (dtype != LLA_BF16 || variant != LLA_PER_HEAD) return false;
-#define X(DH, RK, RV) \
+#define X(DH, RK, RV, WL, NW) \
   if (d_head == DH && r_k == RK && r_v == RV) return true;
   LLA_RECON_SHAPES(X)
 #undef X
@@ -406,13 +444,12 @@ bool reconstruct_supported(int dtype, int variant, int d_head, int r_k, int r_v)
 hipError_t launch_reconstruct(int d_head, int r_k, int r_v, const AttnArgs &a, void *k_full, void *v_full,
                               int batch, hipStream_t stream) {
   const int ppw = 16;
-  const long long groups = (a.pages_per_split + 4 * ppw - 1) / (4 * ppw);
-  const long long gx = (long long)batch * groups;
-  if (gx > 0x7FFFFFFF || a.H > 65535) return hipErrorInvalidConfiguration;
-#define X(DH, RK, RV)                                                                                   \
+#define X(DH, RK, RV, WL, NW)                                                                           \
   if (d_head == DH && r_k == RK && r_v == RV) {                                                         \
-    hipLaunchKernelGGL((reconstruct_kernel<DH, RK, RV>), dim3((unsigned)gx, (unsigned)a.H), dim3(256), 0, \
-                       stream, a, (char *)k_full, (char *)v_full, ppw);                                  \
+    const long long gx = (long long)batch * ((a.pages_per_split + NW * ppw - 1) / (NW * ppw));          \
+    if (gx > 0x7FFFFFFF || a.H > 65535) return hipErrorInvalidConfiguration;                            \
+    hipLaunchKernelGGL((reconstruct_kernel<DH, RK, RV, WL, NW>), dim3((unsigned)gx, (unsigned)a.H),     \
+                       dim3(64 * NW), 0, stream, a, (char *)k_full, (char *)v_full, ppw);              \
     return hipGetLastError();                                                                           \
   }
   LLA_RECON_SHAPES(X)

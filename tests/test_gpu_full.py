@@ -56,7 +56,7 @@ def problem(shape, B, H, ctx, seed, extra_pages=1):
     return m, codec, kp, vp, pt, q
 
 
-@pytest.mark.parametrize("shape", [(128, 16, 32), (64, 16, 32), (128, 32, 64), (128, 64, 64)],
+@pytest.mark.parametrize("shape", [(128, 16, 32), (64, 16, 32), (128, 32, 64), (128, 64, 64), (128, 96, 160)],
                          ids=lambda s: "d%d_rk%d_rv%d" % s)
 def test_full_cache_decode_matches_oracle(shape):
     """Rebuilt full cache + full-cache decode against the oracle's LLA decode:
