@@ -181,10 +181,25 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 1 : 2) void decode_g_kernel(Attn
     for (int k = 0; k < CV; ++k) acc[hh][k] = 0.f;
   }
 
-  // Per page and head, lane (g, n) loads latent row n: c_k columns
+  // Per page and head, lane (g, n) computes with latent row n: c_k columns
   // 16 rt + 4 g .. + 3 (8 bytes per tile) and c_v columns CV g .. CV g + CV - 1.
-  // Rows past ctx_len (last page only) re-read the last valid row; their
-  // scores are forced to -inf.
+  // Rows past ctx_len (last page only) use the last valid row; their scores
+  // are forced to -inf.
+  //
+  // Narrow latents (r_k <= 32) are loaded in that layout directly: a load
+  // instruction then covers 512 or 1024 contiguous bytes.  For wider rows the
+  // same layout would spread each instruction over 16 rows (one 8- or 16-byte
+  // piece per row) and the address unit, not HBM, sets the pace.  XP: the
+  // (page, head) block is loaded in address order instead (lane l: bytes
+  // 8 l of each 512-byte K piece, 16 l of each 1 KiB V piece), written to the
+  // wave's own LDS region with padded rows, and read back in the compute
+  // layout.  The region is the wave's W_up,k stage of the prologue, which is
+  // no longer used by then.
+  constexpr bool XP = RK > 32;
+  constexpr int SKP = RK + 8, SVP = RV + 8;  // padded LDS rows (elements): conflict-free reads
+  static_assert(!XP || (HPW == 1 && RK % 4 == 0 && RV % 8 == 0 && (kPage * RK) % 256 == 0 &&
+                        (kPage * RV) % 512 == 0 && kPage * (SKP + SVP) <= DH * RK),
+                "transposed page layout");
   struct Page {
     u32x2 k[HPW][RT];
     u32x4 v[HPW][KV];
@@ -248,6 +263,17 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 1 : 2) void decode_g_kernel(Attn
     // uniform page bases + 32-bit lane offsets; latents are read exactly once
     const char *kpage = a.k_pool + pp * a.pool_page_stride_k * 2;
     const char *vpage = a.v_pool + pp * a.pool_page_stride_v * 2;
+    if constexpr (XP) {  // whole (page, head) block in address order
+      const uint32_t koff = (uint32_t)(h0 * a.pool_head_stride_k * 2 + 8 * lane);
+      const uint32_t voff = (uint32_t)(h0 * a.pool_head_stride_v * 2 + 16 * lane);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        pg.k[0][rt] = __builtin_nontemporal_load((const u32x2 *)(kpage + koff + 512 * rt));
+#pragma unroll
+      for (int kv = 0; kv < KV; ++kv)
+        pg.v[0][kv] = __builtin_nontemporal_load((const u32x4 *)(vpage + voff + 1024 * kv));
+      return;
+    }
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
       const int h = h0 + hh;
@@ -264,12 +290,37 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 1 : 2) void decode_g_kernel(Attn
 
   // An invalid page-table entry was replaced by page 0 at load time; its
   // tokens are masked out here and the row is poisoned through the error bits.
-  auto compute_page = [&](const Page &cur, int lp) {
+  auto compute_page = [&](Page &cur, int lp) {
     errbits |= cur.ok ? 0 : LLA_DEVERR_PAGE;
     const int j = logical(lp) * kPage + n;  // this lane's token
     const bool valid = cur.ok && n <= cur.last && lp < lp1 &&  // lp >= lp1: ring padding
                        (j < keep_lo || j >= keep_hi);         // evicted rows of edge pages
     const int row_n = min(n, cur.last);
+    if constexpr (XP) {  // address order -> compute layout, through the wave's LDS region
+      uint16_t *xb = (uint16_t *)(smem + w_stage_offset<DH, RK, RV, HPW, NW>(a.pages_per_split)) +
+                     wave * (HPW * DH * RK);
+      uint16_t *xv = xb + kPage * SKP;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const int e = 256 * rt + 4 * lane, r = e / RK;
+        *(u32x2 *)(xb + r * SKP + (e - r * RK)) = cur.k[0][rt];
+      }
+#pragma unroll
+      for (int kv = 0; kv < KV; ++kv) {
+        const int e = 512 * kv + 8 * lane, r = e / RV;
+        *(u32x4 *)(xv + r * SVP + (e - r * RV)) = cur.v[0][kv];
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) cur.k[0][rt] = *(const u32x2 *)(xb + row_n * SKP + 16 * rt + 4 * g);
+#pragma unroll
+      for (int kv = 0; kv < KV; ++kv) cur.v[0][kv] = *(const u32x4 *)(xv + row_n * SVP + CV * g + 8 * kv);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
     const char *tb = s_trig + (((lp - lp0) / CH) & 1) * TSB * 16 +
                      (((lp - lp0) % CH) * kPage + row_n) * SPR * 16;
     // B-operands: RoPE pairs 16 s + 4 g .. + 3 of token n, (cos, sin) fp16
