@@ -127,28 +127,80 @@ __global__ __launch_bounds__(256) void encode_append_kernel(EncodeArgs a, int RK
 //
 // Per (layer, latent group, K|V) the encoder is a plain GEMM,
 //   C[tokens x r] = X[tokens x width] W_down[width x r] - 1 (mu W_down),
-// run on v_mfma_f32_16x16x32_bf16.  A workgroup (8 waves) takes 256 tokens
-// (128 for r > 160); wave w owns two 16-row tiles (one) and all r columns, so
-// every W_down operand read from LDS feeds two products.  W_down is streamed in
-// chunks of 128 rows, transposed into LDS ([r][k], rows padded so the 16-byte
-// B-operand reads of 16 consecutive r hit distinct banks) and shared by the 8
-// waves; the chunks are software-pipelined: while chunk c multiplies out of
-// one LDS buffer, the x rows and W_down rows of chunk c + 1 are in flight and
-// land in the other buffer, one barrier per chunk.  K-slot e of K-step s in
-// lane group g is chunk column 32 s + 8 g + e on both operands, so each x load
-// instruction reads 64 contiguous bytes of every token's row.  mu W_down comes from encode_muw_kernel
-// (once per call).  The result (minus mu W_down, rounded once to bf16) goes
-// through LDS and leaves as 16-byte stores into the paged pool.
+// on v_mfma_f32_16x16x32_bf16.  A workgroup (8 waves) takes 256 tokens (128
+// for r > 160); wave w owns two 16-row tiles (one) and all r columns.  The
+// contraction runs over chunks of 64 rows of W_down (32 for r > 160):
+//  * x: each wave loads its rows x chunk bytes in address order (for 64-row
+//    chunks one load instruction covers 8 whole 128-byte row pieces), two
+//    chunks ahead in registers, and passes them through its own LDS region
+//    (16-byte slots XOR-swizzled by row) into the A-operand layout;
+//  * W_down: the chunk's rows are copied as stored (r contiguous; rows padded
+//    so that the transposing reads below hit distinct banks) straight into
+//    LDS by the 8 waves together (global_load_lds_dwordx4), two chunks ahead
+//    in three buffers, one barrier per chunk;
+//  * B-operands come from ds_read_b64_tr_b16, which hands lane (g, n) column n
+//    of four consecutive rows: K-slot 8 g + 4 h + e of K-step s is chunk row
+//    32 s + 16 h + 4 g + e, on both operands.
+// mu W_down comes from encode_muw_kernel (once per call).  The result (minus
+// mu W_down, rounded once to bf16) goes through LDS and leaves as 16-byte
+// stores into the paged pool.
+namespace {
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((__vector_size__(2 * sizeof(uint32_t))));
+#define LLA_LDS(p) ((__attribute__((address_space(3))) void *)(p))
+
+// Transposing LDS read: within each 16-lane group, lane i receives element i % 4
+// of the 8-byte rows addressed by lanes i / 4, 4 + i / 4, 8 + i / 4, 12 + i / 4.
+__device__ __forceinline__ u32x2 lds_read_tr(const char *p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// 16 bytes per lane from global memory straight into LDS at lds (+ 16 x lane).
+// Written as assembly on purpose: the compiler does not see that it writes
+// LDS, so it does not hold every later LDS access until all copies in flight
+// have landed (which would undo the prefetch); the copies are instead ordered
+// by the explicit vmcnt waits of barrier_vm.  No register is written; M0 is
+// set inside the block (this kernel keeps nothing else in M0).
+__device__ __forceinline__ void copy16_to_lds(const void *src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src) : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(__attribute__((address_space(3))) const char *)p);
+}
+
+// Wait until at most VM vector-memory operations of this wave are outstanding,
+// then meet the other waves.
+template <int VM>
+__device__ __forceinline__ void barrier_vm() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(((VM >> 4) << 14) | (VM & 15) | 0x70);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+}  // namespace
+
+// 16-row tiles per wave (registers bound it), tokens per workgroup and W_down
+// rows per chunk
+__host__ __device__ constexpr int enc_tpw(int r) { return r <= 160 ? 2 : 1; }
+__host__ __device__ constexpr int enc_tok(int r) { return 128 * enc_tpw(r); }
+__host__ __device__ constexpr int enc_kc(int r) { return r <= 160 ? 64 : 32; }
+
 template <int R>
 __global__ __launch_bounds__(512) void encode_mfma_kernel(EncodeArgs a, int kv) {
-  constexpr int TPW = R <= 160 ? 2 : 1;  // 16-token row tiles per wave (registers bound it)
-  constexpr int TOK = 128 * TPW;         // tokens per workgroup
-  constexpr int KC = 128;         // W_down rows per chunk
-  constexpr int LROW = KC + 8;    // padded LDS row (elements) of the transposed chunk
-  constexpr int CT = R / 16;      // column tiles
-  static_assert(R % 16 == 0 && R <= 256, "r");
-  constexpr int WBUF = R * LROW;  // one transposed chunk
-  __shared__ __attribute__((aligned(16))) uint16_t s_w[(2 * WBUF > TOK * R ? 2 * WBUF : TOK * R)];
+  constexpr int TPW = enc_tpw(R), TOK = enc_tok(R), KC = enc_kc(R);
+  constexpr int XP = KC / 8;                               // 16-byte pieces of a token's chunk row
+  constexpr int NXI = 16 * TPW * XP / 64;                  // x load instructions per wave and chunk
+  constexpr int CT = R / 16;                               // column tiles
+  constexpr int PW = R / 8 + ((R / 8) % 4 == 0 ? 2 : 0);   // 16-byte pieces per LDS row of W_down
+  constexpr int NWI = (KC * PW + 511) / 512;               // W_down copy instructions per wave and chunk
+  constexpr int WBUF = NWI * 512 * 16;                     // bytes of one W_down buffer
+  constexpr int XW = 16 * TPW * KC * 2;                    // bytes of a wave's x region
+  static_assert(R % 16 == 0 && R <= 256 && KC % 32 == 0 && (16 * TPW * XP) % 64 == 0, "r");
+  // The x slots double as the output staging area at the end.
+  __shared__ __attribute__((aligned(16))) char s_xo[8 * XW > TOK * R * 2 ? 8 * XW : TOK * R * 2];
+  __shared__ __attribute__((aligned(16))) char s_w0[WBUF], s_w1[WBUF], s_w2[WBUF];
   __shared__ long long s_off[TOK];  // element offset of each token's latent row, -1 = dropped
 
   // wave index as a scalar: branches on it must be uniform scalar branches,
@@ -184,14 +236,41 @@ __global__ __launch_bounds__(512) void encode_mfma_kernel(EncodeArgs a, int kv) 
     s_off[threadIdx.x] = off;
   }
 
-  // this lane's x rows: tokens tok0 + 16 (TPW w + tt) + n (clamped; dropped at the end)
-  const uint16_t *xr[TPW];
+  // this wave's x slots: row tl, piece p at tl XP + (p ^ (tl / 2 % XP))
+  char *s_x = s_xo + w * XW;
+
+  // x loads: instruction i, lane l -> local row (64 i + l) / XP (token
+  // 16 TPW w + that, clamped; dropped at the end), piece l % XP of the chunk
+  const char *xsrc[NXI];
+  int xslot[NXI];
 #pragma unroll
-  for (int tt = 0; tt < TPW; ++tt) {
-    long long tk = tok0 + 16 * (TPW * w + tt) + n;
+  for (int i = 0; i < NXI; ++i) {
+    const int tl = (64 * i + lane) / XP, p = lane % XP;
+    long long tk = tok0 + 16 * TPW * w + tl;
     if (tk >= tokens) tk = tokens - 1;
-    xr[tt] = (const uint16_t *)x + ((li * tokens + tk) * a.groups + grp) * a.width;
+    xsrc[i] = x + (((li * tokens + tk) * a.groups + grp) * a.width) * 2 + 16 * p;
+    xslot[i] = (tl * XP + (p ^ ((tl >> 1) & (XP - 1)))) * 16;
   }
+  auto load_x = [&](int c, u32x4 (&d)[NXI]) {
+#pragma unroll
+    for (int i = 0; i < NXI; ++i) d[i] = __builtin_nontemporal_load((const u32x4 *)(xsrc[i] + c * (KC * 2)));
+  };
+  auto put_x = [&](const u32x4 (&d)[NXI]) {
+#pragma unroll
+    for (int i = 0; i < NXI; ++i) *(u32x4 *)(s_x + xslot[i]) = d[i];
+  };
+  // W_down rows c KC .. c KC + KC - 1 into buffer buf; pad and surplus slots
+  // copy the chunk's first piece (never read)
+  auto copy_w = [&](int c, char *dst) {
+#pragma unroll
+    for (int i = 0; i < NWI; ++i) {
+      const int slot = (i * 8 + w) * 64 + lane;
+      const int k = slot / PW, pc = slot - k * PW;
+      const bool ok = k < KC && pc < R / 8;
+      const uint16_t *src = wd + (long long)(c * KC + (ok ? k : 0)) * R + (ok ? 8 * pc : 0);
+      copy16_to_lds(src, lds_addr(dst + (i * 8 + w) * 1024));
+    }
+  };
 
   f32x4 acc[TPW][CT];
 #pragma unroll
@@ -199,78 +278,65 @@ __global__ __launch_bounds__(512) void encode_mfma_kernel(EncodeArgs a, int kv) 
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) acc[tt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nchunks = a.width / KC;
-  // Software pipeline over 128-row chunks: while chunk c multiplies out of LDS
-  // buffer c % 2, the x rows and W_down rows of chunk c + 1 are in flight in
-  // registers; W_down goes into the other buffer after the products, then one
-  // barrier per chunk.
-  constexpr int WT = ((KC / 4) * (R / 8) + 511) / 512;  // transpose tasks per thread
-  u32x4 xa[TPW][4], xn[TPW][4], wv[WT][4];
-  auto load_x = [&](int c, u32x4 (&dst)[TPW][4]) {
+  auto compute = [&](const char *wb) {
 #pragma unroll
-    for (int tt = 0; tt < TPW; ++tt)
+    for (int s = 0; s < KC / 32; ++s) {
+      u32x4 av[TPW];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) dst[tt][s] = *(const u32x4 *)(xr[tt] + c * KC + 32 * s + 8 * g);
-  };
-  auto load_w = [&](int c) {
-#pragma unroll
-    for (int j = 0; j < WT; ++j) {
-      const int task = min((int)threadIdx.x + 512 * j, (KC / 4) * (R / 8) - 1);
-      const int k4 = task / (R / 8), r8 = task % (R / 8);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) wv[j][i] = *(const u32x4 *)(wd + (long long)(c * KC + 4 * k4 + i) * R + 8 * r8);
-    }
-  };
-  auto store_w = [&](uint16_t *buf) {
-#pragma unroll
-    for (int j = 0; j < WT; ++j) {
-      const int task = (int)threadIdx.x + 512 * j;
-      if (task < (KC / 4) * (R / 8)) {
-        const int k4 = task / (R / 8), r8 = task % (R / 8);
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const int sh = (jj & 1) * 16;
-          const uint32_t e0 = (wv[j][0][jj >> 1] >> sh) & 0xFFFFu, e1 = (wv[j][1][jj >> 1] >> sh) & 0xFFFFu;
-          const uint32_t e2 = (wv[j][2][jj >> 1] >> sh) & 0xFFFFu, e3 = (wv[j][3][jj >> 1] >> sh) & 0xFFFFu;
-          uint32_t *dst = (uint32_t *)(buf + (8 * r8 + jj) * LROW + 4 * k4);
-          dst[0] = e0 | (e1 << 16);
-          dst[1] = e2 | (e3 << 16);
-        }
+      for (int tt = 0; tt < TPW; ++tt) {
+        const char *xr = s_x + (16 * tt + n) * (XP * 16) + 8 * (g & 1);
+        const u32x2 lo = *(const u32x2 *)(xr + ((4 * s + (g >> 1)) ^ ((n >> 1) & (XP - 1))) * 16);
+        const u32x2 hi = *(const u32x2 *)(xr + ((4 * s + 2 + (g >> 1)) ^ ((n >> 1) & (XP - 1))) * 16);
+        av[tt] = u32x4{lo[0], lo[1], hi[0], hi[1]};
       }
-    }
-  };
-  load_x(0, xa);
-  load_w(0);
-  store_w(s_w);
-  __syncthreads();
-  for (int c = 0; c < nchunks; ++c) {
-    const bool more = c + 1 < nchunks;
-    if (more) {
-      load_x(c + 1, xn);
-      load_w(c + 1);
-    }
-    const uint16_t *buf = s_w + (c & 1) * WBUF;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int kk = 32 * s + 8 * g;  // K-step s: 64 contiguous bytes of each token's x row
+      const char *wr = wb + (32 * s + 4 * g + (n >> 2)) * (PW * 16) + 8 * (n & 3);
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
-        const u32x4 bw = *(const u32x4 *)(buf + (16 * ct + n) * LROW + kk);
+        const u32x2 lo = lds_read_tr(wr + 32 * ct);
+        const u32x2 hi = lds_read_tr(wr + 16 * (PW * 16) + 32 * ct);
+        const u32x4 bw = u32x4{lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt)
-          acc[tt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[tt][s]), as_bf16x8(bw), acc[tt][ct], 0, 0, 0);
+          acc[tt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[tt]), as_bf16x8(bw), acc[tt][ct], 0, 0, 0);
       }
     }
-    if (more) store_w(s_w + ((c + 1) & 1) * WBUF);
-    __syncthreads();
-#pragma unroll
-    for (int tt = 0; tt < TPW; ++tt)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) xa[tt][s] = xn[tt][s];
-  }
+  };
 
-  __syncthreads();  // s_w free for output staging
-  uint16_t *s_out = s_w;  // [TOK][R] bf16
+  // Chunk c (W_down buffer c % 3): its x rows, in registers since two chunks
+  // ago, go to the wave's slots.  The W_down copies of chunk c were issued
+  // just before those x loads, so once only the copies and loads of chunk
+  // c + 1 may be outstanding, this wave's part of chunk c is in LDS; all waves
+  // meet, which also frees buffer (c + 2) % 3; then the copies and x loads of
+  // chunk c + 2 are issued and chunk c is multiplied.
+  const int nch = a.width / KC;
+  auto step = [&](int c, const char *buf, char *buf2, u32x4 (&cur)[NXI], u32x4 (&nx2)[NXI]) {
+    put_x(cur);
+    if (c + 1 < nch) barrier_vm<NWI + NXI>();
+    else barrier_vm<0>();
+    if (c + 2 < nch) {
+      copy_w(c + 2, buf2);
+      load_x(c + 2, nx2);
+    }
+    compute(buf);
+  };
+  u32x4 xa[NXI], xb[NXI], xc[NXI];
+  copy_w(0, s_w0);
+  load_x(0, xa);
+  if (nch > 1) {
+    copy_w(1, s_w1);
+    load_x(1, xb);
+  }
+  int c = 0;
+  for (; c + 3 <= nch; c += 3) {
+    step(c, s_w0, s_w2, xa, xc);
+    step(c + 1, s_w1, s_w0, xb, xa);
+    step(c + 2, s_w2, s_w1, xc, xb);
+  }
+  if (c < nch) step(c, s_w0, s_w2, xa, xc);
+  if (c + 1 < nch) step(c + 1, s_w1, s_w0, xb, xa);
+
+  __syncthreads();  // LDS free for output staging
+  uint16_t *s_out = (uint16_t *)s_xo;  // [TOK][R] bf16
   const float *muw = a.muw + gl * (a.muw_stride) + (kv ? a.muw_v_off : 0);
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
@@ -303,8 +369,7 @@ hipError_t launch_encode_mfma(int r, int kv, const EncodeArgs &a, hipStream_t st
   const long long tokens = (long long)a.batch * a.n_new;
 #define X(RR)                                                                                     \
   if (r == RR) {                                                                                  \
-    constexpr int tok = RR <= 160 ? 256 : 128;                                                    \
-    const dim3 grid((unsigned)((tokens + tok - 1) / tok), a.groups, a.n_layers);                  \
+    const dim3 grid((unsigned)((tokens + enc_tok(RR) - 1) / enc_tok(RR)), a.groups, a.n_layers);  \
     hipLaunchKernelGGL(encode_mfma_kernel<RR>, grid, dim3(512), 0, stream, a, kv);                \
     return hipGetLastError();                                                                     \
   }
@@ -320,8 +385,8 @@ bool encode_supported(int dtype, int width, int r_k, int r_v) {
 hipError_t launch_encode(int dtype, int r_k, int r_v, const EncodeArgs &a, hipStream_t stream) {
   const long long tokens = (long long)a.batch * a.n_new;
   if (tokens == 0 || a.n_layers == 0) return hipSuccess;
-  // bf16 with whole 128-column chunks and an instantiated rank: matrix cores
-  if (dtype == LLA_BF16 && a.width % 128 == 0 && encode_mfma_r(r_k) && encode_mfma_r(r_v) &&
+  // bf16 with whole 64-row chunks of W_down and an instantiated rank: matrix cores
+  if (dtype == LLA_BF16 && a.width % 64 == 0 && encode_mfma_r(r_k) && encode_mfma_r(r_v) &&
       tokens <= 0x7FFFFFFFLL * 128) {
     hipError_t e = launch_muw<true>(r_k, r_v, a, stream);
     if (e != hipSuccess) return e;

@@ -118,6 +118,20 @@ def test_encode_rank_tilings(ranks):
     compare(m, got, ref, init, f"encode r_k={rk} r_v={rv}")
 
 
+@pytest.mark.parametrize("T", [1, 3, 5])
+def test_encode_many_tiles_and_chunk_counts(T):
+    """600 tokens per layer (several 256-token workgroups and a ragged last
+    one) at widths T x 64 = 64, 192 and 320: one chunk of W_down rows, a whole
+    number of three-chunk rounds, and a round with two chunks left over."""
+    m = dims(T, 2, 2, 64, 96, 160, PER_HEAD, BF16)
+    B, n_new, pps = 3, 200, 14
+    pt = gen.shuffled_page_table(3501 + T, B, pps)
+    codec = random_codec(m, seed=3502 + T, ortho_down=False)
+    pos0 = np.array([0, 9, 21])
+    got, ref, init = run_both(m, codec, pt, B * pps, pos0, n_new, 0, 2, seed=3503 + T)
+    compare(m, got, ref, init, f"encode T={T} width={64 * T} tokens={B * n_new}")
+
+
 def test_encode_21x_single_token_all_layers():
     """The decode-step append: one token per sequence into every layer (r_k=16, r_v=32)."""
     m = dims(4, 24, 16, 128, 16, 32, PER_HEAD, BF16)
