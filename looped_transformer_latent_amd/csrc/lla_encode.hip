@@ -147,26 +147,12 @@ __global__ __launch_bounds__(256) void encode_append_kernel(EncodeArgs a, int RK
 namespace {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((__vector_size__(2 * sizeof(uint32_t))));
-#define LLA_LDS(p) ((__attribute__((address_space(3))) void *)(p))
 
 // Transposing LDS read: within each 16-lane group, lane i receives element i % 4
 // of the 8-byte rows addressed by lanes i / 4, 4 + i / 4, 8 + i / 4, 12 + i / 4.
 __device__ __forceinline__ u32x2 lds_read_tr(const char *p) {
   const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
   return __builtin_bit_cast(u32x2, v);
-}
-
-// 16 bytes per lane from global memory straight into LDS at lds (+ 16 x lane).
-// Written as assembly on purpose: the compiler does not see that it writes
-// LDS, so it does not hold every later LDS access until all copies in flight
-// have landed (which would undo the prefetch); the copies are instead ordered
-// by the explicit vmcnt waits of barrier_vm.  No register is written; M0 is
-// set inside the block (this kernel keeps nothing else in M0).
-__device__ __forceinline__ void copy16_to_lds(const void *src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src) : "memory", "m0");
-}
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-  return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(__attribute__((address_space(3))) const char *)p);
 }
 
 // Wait until at most VM vector-memory operations of this wave are outstanding,
