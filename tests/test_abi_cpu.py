@@ -159,7 +159,8 @@ def test_full_cache_validation_and_planning():
     assert big > 256 and (big - 256) % (32 * 16 * (128 + 2) * 4) < 256
     assert lla.workspace_bytes(d, lla.OP_FULL_DECODE, 1024, 4096) == 256   # one split at large batch
     assert lla.supported(d, lla.OP_RECONSTRUCT) and lla.supported(d, lla.OP_FULL_DECODE)
-    assert not lla.supported(_dims(r_k=96, r_v=160), lla.OP_RECONSTRUCT)
+    assert lla.supported(_dims(r_k=96, r_v=160), lla.OP_RECONSTRUCT)
+    assert not lla.supported(_dims(r_k=48, r_v=96), lla.OP_RECONSTRUCT)
 
 
 def test_decoupled_validation_and_planning():
