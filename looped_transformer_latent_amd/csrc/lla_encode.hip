@@ -67,6 +67,9 @@ __global__ __launch_bounds__(256) void encode_muw_reduce_kernel(EncodeArgs a) {
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= n) return;
   float s = 0.f;
+  // unrolled so that the loads of 16 ranges are in flight together; the sum
+  // keeps range order
+#pragma unroll 16
   for (int pr = 0; pr < a.muw_parts; ++pr) s += a.muw_part[(long long)pr * n + idx];
   a.muw[idx] = s;
 }
