@@ -32,6 +32,7 @@ DECODE_SOURCES = ("lla_decode_g.hip", "lla_device.h", "lla_internal.h", "lla_api
 PREFILL_SOURCES = ("lla_prefill.hip", "lla_device.h", "lla_internal.h", "lla_api.hip")
 ABSORBED_SOURCES = ("lla_absorbed.hip", "lla_merge.hip", "lla_device.h", "lla_internal.h", "lla_api.hip")
 FULL_SOURCES = ("lla_full.hip", "lla_merge.hip", "lla_device.h", "lla_internal.h", "lla_api.hip")
+D2D_SOURCES = ("lla_decode2d.hip", "lla_device.h", "lla_internal.h", "lla_api.hip")
 HBM_BYTES = 288e9
 
 
@@ -513,7 +514,8 @@ def main():
         achieved = flops / (kern_avg_ms / 1e3) / 1e12
         roof = {"kernel": "decode_2d_kernel", "bound": "mfma", "achieved": achieved,
                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
-                "traffic": None, "algorithmic_flops_per_launch": flops,
+                "traffic": profiled_traffic(w.name, "decode_2d_kernel", D2D_SOURCES),
+                "traffic_unit": "HBM bytes per launch (rocprofv3)", "algorithmic_flops_per_launch": flops,
                 "algorithmic_bytes_per_launch": bytes_per_launch,
                 "hbm_gbs": bytes_per_launch / (kern_avg_ms / 1e3) / 1e9, "avg_launch_ms": kern_avg_ms}
     result = {
