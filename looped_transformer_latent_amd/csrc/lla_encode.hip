@@ -187,43 +187,58 @@ __global__ __launch_bounds__(512) void encode_mfma_kernel(EncodeArgs a, int kv) 
   constexpr int WBUF = NWI * 512 * 16;                     // bytes of one W_down buffer
   constexpr int XW = 16 * TPW * KC * 2;                    // bytes of a wave's x region
   static_assert(R % 16 == 0 && R <= 256 && KC % 32 == 0 && (16 * TPW * XP) % 64 == 0, "r");
-  // The x slots double as the output staging area at the end.
+  // The x slots double as the output staging area at the end of a tile.
   __shared__ __attribute__((aligned(16))) char s_xo[8 * XW > TOK * R * 2 ? 8 * XW : TOK * R * 2];
   __shared__ __attribute__((aligned(16))) char s_w0[WBUF], s_w1[WBUF], s_w2[WBUF];
-  __shared__ long long s_off[TOK];  // element offset of each token's latent row, -1 = dropped
+  __shared__ long long s_off[2][TOK];  // per tile parity: element offset of each token's latent row, -1 = dropped
 
   // wave index as a scalar: branches on it must be uniform scalar branches,
   // never EXEC-masked MFMAs
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, n = lane & 15;
-  const int grp = blockIdx.y, li = blockIdx.z;
   const long long tokens = (long long)a.batch * a.n_new;
-  const long long tok0 = (long long)blockIdx.x * TOK;
-  const long long gl = (long long)li * a.groups + grp;
+  const long long ntt = (tokens + TOK - 1) / TOK;  // token tiles per (layer, group)
+  const long long ntiles = ntt * a.groups * a.n_layers;
   const char *x = kv ? a.x_v : a.x_k;
-  const uint16_t *wd = (const uint16_t *)(kv ? a.wd_v : a.wd_k) + gl * a.width * (long long)R;
-  uint16_t *pool = (uint16_t *)(kv ? a.v_pool : a.k_pool) +
-                   (long long)li * (kv ? a.pool_layer_stride_v : a.pool_layer_stride_k);
+  const uint16_t *wd_all = (const uint16_t *)(kv ? a.wd_v : a.wd_k);
+  uint16_t *pool_all = (uint16_t *)(kv ? a.v_pool : a.k_pool);
+  const long long lstride = kv ? a.pool_layer_stride_v : a.pool_layer_stride_k;
   const long long pstride = kv ? a.pool_page_stride_v : a.pool_page_stride_k;
   const long long hstride = kv ? a.pool_head_stride_v : a.pool_head_stride_k;
 
-  // destination slot of each token (placement is integer work, checked here)
-  if (threadIdx.x < TOK) {
-    const long long tok = tok0 + threadIdx.x;
-    long long off = -1;
-    if (tok < tokens) {
-      const int b = (int)(tok / a.n_new), nn = (int)(tok % a.n_new);
-      const long long pos = (long long)a.pos0[b] + nn;
-      if (pos < 0 || pos >= (long long)a.max_pages * kPage) {
-        atomicOr(a.err, LLA_DEVERR_APPEND);
-      } else {
-        const int page = a.page_table[(long long)b * a.max_pages + pos / kPage];
-        if (page < 0 || page >= a.num_pages) atomicOr(a.err, LLA_DEVERR_PAGE);
-        else off = (long long)page * pstride + grp * hstride + (pos % kPage) * R;
+  // Tiles t = blockIdx.x, + gridDim.x, ...: token tile fastest, then group,
+  // then layer, so that the workgroups running together share W_down in L2.
+  struct Tile {
+    long long tok0;
+    int grp, li;
+  };
+  auto tile_of = [&](long long t) {
+    Tile v;
+    v.tok0 = (t % ntt) * TOK;
+    const long long r = t / ntt;
+    v.grp = (int)(r % a.groups);
+    v.li = (int)(r / a.groups);
+    return v;
+  };
+  // destination slot of each token of tile v (placement is integer work, checked here)
+  auto place = [&](const Tile &v, long long *dst) {
+    if (threadIdx.x < TOK) {
+      const long long tok = v.tok0 + threadIdx.x;
+      long long off = -1;
+      if (tok < tokens) {
+        const int b = (int)(tok / a.n_new), nn = (int)(tok % a.n_new);
+        const long long pos = (long long)a.pos0[b] + nn;
+        if (pos < 0 || pos >= (long long)a.max_pages * kPage) {
+          atomicOr(a.err, LLA_DEVERR_APPEND);
+        } else {
+          const int page = a.page_table[(long long)b * a.max_pages + pos / kPage];
+          if (page < 0 || page >= a.num_pages) atomicOr(a.err, LLA_DEVERR_PAGE);
+          else off = (long long)page * pstride + v.grp * hstride + (pos % kPage) * R;
+        }
       }
+      dst[threadIdx.x] = off;
     }
-    s_off[threadIdx.x] = off;
-  }
+  };
 
   // this wave's x slots: row tl, piece p at tl XP + (p ^ (tl / 2 % XP))
   char *s_x = s_xo + w * XW;
@@ -232,12 +247,20 @@ __global__ __launch_bounds__(512) void encode_mfma_kernel(EncodeArgs a, int kv) 
   // 16 TPW w + that, clamped; dropped at the end), piece l % XP of the chunk
   const char *xsrc[NXI];
   int xslot[NXI];
+  const uint16_t *wd;
+  auto sources = [&](const Tile &v) {
+    wd = wd_all + ((long long)v.li * a.groups + v.grp) * a.width * (long long)R;
+#pragma unroll
+    for (int i = 0; i < NXI; ++i) {
+      const int tl = (64 * i + lane) / XP, p = lane % XP;
+      long long tk = v.tok0 + 16 * TPW * w + tl;
+      if (tk >= tokens) tk = tokens - 1;
+      xsrc[i] = x + ((((long long)v.li * tokens + tk) * a.groups + v.grp) * a.width) * 2 + 16 * p;
+    }
+  };
 #pragma unroll
   for (int i = 0; i < NXI; ++i) {
     const int tl = (64 * i + lane) / XP, p = lane % XP;
-    long long tk = tok0 + 16 * TPW * w + tl;
-    if (tk >= tokens) tk = tokens - 1;
-    xsrc[i] = x + (((li * tokens + tk) * a.groups + grp) * a.width) * 2 + 16 * p;
     xslot[i] = (tl * XP + (p ^ ((tl >> 1) & (XP - 1)))) * 16;
   }
   auto load_x = [&](int c, u32x4 (&d)[NXI]) {
@@ -262,11 +285,6 @@ __global__ __launch_bounds__(512) void encode_mfma_kernel(EncodeArgs a, int kv) 
   };
 
   f32x4 acc[TPW][CT];
-#pragma unroll
-  for (int tt = 0; tt < TPW; ++tt)
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) acc[tt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-
   auto compute = [&](const char *wb) {
 #pragma unroll
     for (int s = 0; s < KC / 32; ++s) {
@@ -294,9 +312,11 @@ __global__ __launch_bounds__(512) void encode_mfma_kernel(EncodeArgs a, int kv) 
   // Chunk c (W_down buffer c % 3): its x rows, in registers since two chunks
   // ago, go to the wave's slots.  The W_down copies of chunk c were issued
   // just before those x loads, so once only the copies and loads of chunk
-  // c + 1 may be outstanding, this wave's part of chunk c is in LDS; all waves
-  // meet, which also frees buffer (c + 2) % 3; then the copies and x loads of
-  // chunk c + 2 are issued and chunk c is multiplied.
+  // c + 1 may be outstanding (older stores of the previous tile's output
+  // complete first: vector-memory operations count down in issue order),
+  // this wave's part of chunk c is in LDS; all waves meet, which also frees
+  // buffer (c + 2) % 3; then the copies and x loads of chunk c + 2 are issued
+  // and chunk c is multiplied.
   const int nch = a.width / KC;
   auto step = [&](int c, const char *buf, char *buf2, u32x4 (&cur)[NXI], u32x4 (&nx2)[NXI]) {
     put_x(cur);
@@ -309,41 +329,74 @@ __global__ __launch_bounds__(512) void encode_mfma_kernel(EncodeArgs a, int kv) 
     compute(buf);
   };
   u32x4 xa[NXI], xb[NXI], xc[NXI];
-  copy_w(0, s_w0);
-  load_x(0, xa);
-  if (nch > 1) {
-    copy_w(1, s_w1);
-    load_x(1, xb);
-  }
-  int c = 0;
-  for (; c + 3 <= nch; c += 3) {
-    step(c, s_w0, s_w2, xa, xc);
-    step(c + 1, s_w1, s_w0, xb, xa);
-    step(c + 2, s_w2, s_w1, xc, xb);
-  }
-  if (c < nch) step(c, s_w0, s_w2, xa, xc);
-  if (c + 1 < nch) step(c + 1, s_w1, s_w0, xb, xa);
+  // the first two chunks of a tile
+  auto start = [&]() {
+    copy_w(0, s_w0);
+    load_x(0, xa);
+    if (nch > 1) {
+      copy_w(1, s_w1);
+      load_x(1, xb);
+    }
+  };
 
-  __syncthreads();  // LDS free for output staging
-  uint16_t *s_out = (uint16_t *)s_xo;  // [TOK][R] bf16
-  const float *muw = a.muw + gl * (a.muw_stride) + (kv ? a.muw_v_off : 0);
-#pragma unroll
-  for (int ct = 0; ct < CT; ++ct) {
-    const int r = 16 * ct + n;
-    const float mw = muw[r];
+  long long t = blockIdx.x;
+  if (t >= ntiles) return;
+  Tile cur = tile_of(t);
+  place(cur, s_off[0]);
+  sources(cur);
+  start();
+  for (int par = 0;; par ^= 1) {
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        s_out[(16 * (TPW * w + tt) + 4 * g + e) * R + r] = (uint16_t)f32_to_bf16(acc[tt][ct][e] - mw);
-  }
-  __syncthreads();
-  for (int q = threadIdx.x; q < TOK * (R / 8); q += blockDim.x) {
-    const int tl = q / (R / 8), c8 = q % (R / 8);
-    const long long off = s_off[tl];
-    if (off >= 0) *(u32x4 *)(pool + off + 8 * c8) = *(const u32x4 *)(s_out + tl * R + 8 * c8);
+      for (int ct = 0; ct < CT; ++ct) acc[tt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    int c = 0;
+    for (; c + 3 <= nch; c += 3) {
+      step(c, s_w0, s_w2, xa, xc);
+      step(c + 1, s_w1, s_w0, xb, xa);
+      step(c + 2, s_w2, s_w1, xc, xb);
+    }
+    if (c < nch) step(c, s_w0, s_w2, xa, xc);
+    if (c + 1 < nch) step(c + 1, s_w1, s_w0, xb, xa);
+
+    // every wave is past its last products: the x slots (output staging) and
+    // the W_down buffers are free
+    barrier_vm<63>();
+    uint16_t *s_out = (uint16_t *)s_xo;  // [TOK][R] bf16
+    const float *muw = a.muw + ((long long)cur.li * a.groups + cur.grp) * a.muw_stride + (kv ? a.muw_v_off : 0);
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const int r = 16 * ct + n;
+      const float mw = muw[r];
+#pragma unroll
+      for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          s_out[(16 * (TPW * w + tt) + 4 * g + e) * R + r] = (uint16_t)f32_to_bf16(acc[tt][ct][e] - mw);
+    }
+    // the next tile's slots, while nothing else is in flight (its loads are waited for)
+    const long long tn = t + gridDim.x;
+    const Tile nxt = tile_of(tn < ntiles ? tn : t);
+    if (tn < ntiles) place(nxt, s_off[par ^ 1]);
+    barrier_vm<63>();
+    uint16_t *pool = pool_all + (long long)cur.li * lstride;
+    for (int q = threadIdx.x; q < TOK * (R / 8); q += blockDim.x) {
+      const int tl = q / (R / 8), c8 = q % (R / 8);
+      const long long off = s_off[par][tl];
+      if (off >= 0) *(u32x4 *)(pool + off + 8 * c8) = *(const u32x4 *)(s_out + tl * R + 8 * c8);
+    }
+    if (tn >= ntiles) break;
+    // the next tile's first chunks load while this tile's output drains
+    t = tn;
+    cur = nxt;
+    sources(cur);
+    start();
+    barrier_vm<63>();  // the staged output has been read before the slots take x rows again
   }
 }
+
+// Persistent grid: one workgroup per CU (LDS and registers allow no more).
+constexpr long long kEncWorkgroups = 256;
 
 #define LLA_ENCODE_R(X) X(16) X(32) X(48) X(64) X(96) X(128) X(160) X(256)
 
@@ -358,8 +411,9 @@ hipError_t launch_encode_mfma(int r, int kv, const EncodeArgs &a, hipStream_t st
   const long long tokens = (long long)a.batch * a.n_new;
 #define X(RR)                                                                                     \
   if (r == RR) {                                                                                  \
-    const dim3 grid((unsigned)((tokens + enc_tok(RR) - 1) / enc_tok(RR)), a.groups, a.n_layers);  \
-    hipLaunchKernelGGL(encode_mfma_kernel<RR>, grid, dim3(512), 0, stream, a, kv);                \
+    const long long tiles = (tokens + enc_tok(RR) - 1) / enc_tok(RR) * a.groups * a.n_layers;      \
+    hipLaunchKernelGGL(encode_mfma_kernel<RR>, dim3((unsigned)(tiles < kEncWorkgroups ? tiles : kEncWorkgroups)), \
+                       dim3(512), 0, stream, a, kv);                                             \
     return hipGetLastError();                                                                     \
   }
   LLA_ENCODE_R(X)

@@ -132,6 +132,19 @@ def test_encode_many_tiles_and_chunk_counts(T):
     compare(m, got, ref, init, f"encode T={T} width={64 * T} tokens={B * n_new}")
 
 
+def test_encode_more_tiles_than_workgroups():
+    """288 (token tile, head, layer) tiles for 256 persistent workgroups: some
+    workgroups run two tiles, so a tile's output drains while the next one's
+    first chunks load (32 heads, 3 layers, 600 tokens, width 64)."""
+    m = dims(1, 3, 32, 64, 96, 160, PER_HEAD, BF16)
+    B, n_new, pps = 3, 200, 14
+    pt = gen.shuffled_page_table(3601, B, pps)
+    codec = random_codec(m, seed=3602, ortho_down=False)
+    pos0 = np.array([3, 0, 17])
+    got, ref, init = run_both(m, codec, pt, B * pps, pos0, n_new, 0, 3, seed=3603)
+    compare(m, got, ref, init, "encode 288 tiles")
+
+
 def test_encode_21x_single_token_all_layers():
     """The decode-step append: one token per sequence into every layer (r_k=16, r_v=32)."""
     m = dims(4, 24, 16, 128, 16, 32, PER_HEAD, BF16)
