@@ -219,3 +219,16 @@ def test_window_validation_and_planning():
     assert lla.workspace_bytes(d, lla.OP_WINDOW_DECODE, 1, 4096, 0) == 0
     assert lla.supported(d, lla.OP_WINDOW_DECODE) and not lla.supported(_dims(dtype=lla.F32, d_head=64),
                                                                          lla.OP_WINDOW_DECODE)
+
+
+def test_m0_check_of_the_build():
+    """The build's scan of device assembly for M0 uses outside the LDS copy
+    blocks (the copies set M0 themselves from inline assembly)."""
+    from looped_transformer_latent_amd import build
+    ok = "\ts_mov_b32 m0, s4\n\tglobal_load_lds_dwordx4 v[2:3], off\n\tv_mov_b32 v1, v2 ; m0 in a comment\n"
+    assert build.m0_misuse(ok) is None
+    assert build.m0_misuse(ok + "\ts_mov_b32 m0, -1\n\tds_read_b32 v1, v2\n") == "s_mov_b32 m0, -1"
+    assert build.m0_misuse("\tv_movrels_b32 v1, v2\n\ts_add_i32 s5, m0, 4\n") == "s_add_i32 s5, m0, 4"
+    built = os.path.join(ROOT, "_build", "lla_encode.hip.s")
+    if os.path.exists(built):  # written by the last build
+        assert build.m0_misuse(open(built).read()) is None
