@@ -397,7 +397,7 @@ def bench_full_cache(w, D, codec, cache, rope, calls, q, q_pos, ctx, out_lat, la
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
+        print(json.dumps({"error": "bench.py measures one GPU only; run with --gpus 1"}))
         sys.exit(2)
     if args.calibrate_copy > 0:
         calibrate_copy(args.calibrate_copy)

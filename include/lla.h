@@ -298,7 +298,7 @@ int32_t lla_decoupled_decode_attn(const lla_dims *dims, const lla_codec *codec, 
  * LLA-2D).  Host only.  ([CR] 方法 item 2; Table 5.) */
 int32_t lla_cache_scalars(const lla_dims *dims, int64_t *teacher, int64_t *latent);
 
-/* 1 if this build has kernels for (dims, op), else 0 (host only). */
+/* 1 if the library has kernels for (dims, op), else 0 (host only). */
 int32_t lla_supported(const lla_dims *dims, int32_t op);
 
 const char *lla_status_string(int32_t status);
