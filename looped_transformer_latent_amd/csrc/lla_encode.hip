@@ -146,7 +146,9 @@ __global__ __launch_bounds__(256) void encode_append_kernel(EncodeArgs a, int RK
 //    32 s + 16 h + 4 g + e, on both operands.
 // mu W_down comes from encode_muw_kernel (once per call).  The result (minus
 // mu W_down, rounded once to bf16) goes through LDS and leaves as 16-byte
-// stores into the paged pool.
+// stores into the paged pool.  Workgroups are persistent (at most one per CU)
+// and walk (token tile, group, layer) tiles; a tile's output stores drain
+// while the next tile's first two chunks load.
 namespace {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((__vector_size__(2 * sizeof(uint32_t))));
