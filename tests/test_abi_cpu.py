@@ -232,3 +232,37 @@ def test_m0_check_of_the_build():
     built = os.path.join(ROOT, "_build", "lla_encode.hip.s")
     if os.path.exists(built):  # written by the last build
         assert build.m0_misuse(open(built).read()) is None
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: asked for more it prints one JSON line saying
+    so and exits non-zero, before touching a device."""
+    import json
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    msg = json.loads(r.stdout.strip().splitlines()[-1])
+    assert "one GPU" in msg["error"]
+
+
+def test_profiled_traffic_needs_matching_sources(tmp_path, monkeypatch):
+    """The bench reports a kernel's profiled HBM traffic only while the digest
+    in its profile matches the current sources."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    (tmp_path / "profiles").mkdir()
+    good = bench.kernel_source_digest(bench.DECODE_SOURCES)
+    (tmp_path / "profiles" / "decode_g_kernel_w1.md").write_text(
+        f"# x\nkernel_source_sha256: {good}\ntraffic_bytes_per_launch: 1234\n")
+    (tmp_path / "profiles" / "decode_g_kernel_w2.md").write_text(
+        "# x\nkernel_source_sha256: 00\ntraffic_bytes_per_launch: 1234\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    # the sources are still those of the repository
+    monkeypatch.setattr(bench, "kernel_source_digest", lambda names=bench.DECODE_SOURCES: good)
+    assert bench.profiled_traffic("w1") == 1234
+    assert bench.profiled_traffic("w2") is None
+    assert bench.profiled_traffic("w3") is None
