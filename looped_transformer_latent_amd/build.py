@@ -29,7 +29,7 @@ HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
              "-Wall", "-Wno-unused-function", "-Wno-unused-variable"]
 
 # Sources whose kernels issue global -> LDS copies from inline assembly that
-# sets M0 itself (copy16_to_lds in lla_device.h): the build checks that the
+# sets M0 itself (copy16_to_lds in lla_encode.hip): the build checks that the
 # compiler keeps nothing else in M0 there.
 M0_CHECKED = ["lla_encode.hip"]
 

@@ -24,21 +24,6 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 }
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// 16 bytes per lane from global memory straight into LDS at byte address
-// lds + 16 x lane (global_load_lds_dwordx4).  Written as assembly on purpose:
-// the compiler does not see that it writes LDS, so it does not hold every
-// later LDS access of the wave until all copies in flight have landed (which
-// undoes any prefetch); callers order the copies with explicit vmcnt waits
-// and barriers instead.  No register is written; M0 is set inside the block
-// (the kernels using it keep nothing else in M0).
-__device__ __forceinline__ void copy16_to_lds(const void *src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src) : "memory", "m0");
-}
-// Wave-uniform LDS byte address of a pointer into __shared__ memory.
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-  return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(__attribute__((address_space(3))) const char *)p);
-}
-
 // 2^x on the hardware exp unit.  Used for softmax weights, whose arguments are
 // <= 0; results below the fp32 normal range may flush to zero, which only drops
 // weights smaller than 2^-126 of the largest one.

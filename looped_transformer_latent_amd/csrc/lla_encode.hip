@@ -160,6 +160,26 @@ __device__ __forceinline__ u32x2 lds_read_tr(const char *p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// 16 bytes per lane from global memory straight into LDS at byte address
+// lds + 16 x lane (global_load_lds_dwordx4).  Written as assembly on purpose:
+// the compiler does not see that it writes LDS, so it does not hold every
+// later LDS access of the wave until all copies in flight have landed (which
+// undoes any prefetch); callers order the copies with explicit vmcnt waits
+// and barriers instead.  No register is written; M0 is set inside the block
+// (the kernels of this file keep nothing else in M0, which the build checks in
+// their assembly; hence the silenced warning about clobbering a reserved
+// register).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void copy16_to_lds(const void *src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+// Wave-uniform LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(__attribute__((address_space(3))) const char *)p);
+}
+
 // Wait until at most VM vector-memory operations of this wave are outstanding,
 // then meet the other waves.
 template <int VM>

@@ -194,7 +194,6 @@ __global__ __launch_bounds__(64 * NW) void reconstruct_kernel(AttnArgs a, char *
     } else {
       uint16_t *kd = (uint16_t *)k_full + ((long long)e * a.H + h) * ls;
       uint16_t *vd = (uint16_t *)v_full + ((long long)e * a.H + h) * ls;
-      const float *rr = a.rope + (long long)(lp * kPage) * DH;  // page's first position (< ctx)
 #pragma unroll
       for (int T = 0; T < NDT / 2; ++T) {
         f32x4 x, y;

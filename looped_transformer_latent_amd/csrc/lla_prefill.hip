@@ -151,9 +151,8 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(AttnArgs a) {
   const int npg = (kend + kPage - 1) / kPage;
 
   const int w0 = r0 + 32 * w;
-  const int wv0 = max(w0, v0), wv1 = min(w0 + 32, v1);
-  const bool wactive = wv1 > wv0;
-  const int qmin = (int)(p0 + wv0), qmax = (int)(p0 + wv1 - 1);
+  const int wv0 = max(w0, v0);
+  const int qmin = (int)(p0 + wv0);  // the wave's first query position
 
   // ---- prologue: Q' = scale log2(e) R(p) q as bf16 B-operands ----
   // qop[f][ks]: lane (n, g) = query w0 + 16 f + n, dims 32 ks + 8 g .. + 7.
