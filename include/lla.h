@@ -298,6 +298,32 @@ int32_t lla_decoupled_decode_attn(const lla_dims *dims, const lla_codec *codec, 
  * LLA-2D).  Host only.  ([CR] 方法 item 2; Table 5.) */
 int32_t lla_cache_scalars(const lla_dims *dims, int64_t *teacher, int64_t *latent);
 
+/* How an attention call is cut into workgroups (host only), for the same
+ * arguments as lla_workspace_bytes with op = LLA_OP_DECODE, LLA_OP_PREFILL,
+ * LLA_OP_WINDOW_DECODE, LLA_OP_DECOUPLED_DECODE or LLA_OP_FULL_DECODE:
+ *   *splits           parts each row's context is cut into; with more than one,
+ *                     each part leaves (max, weight sum, latent value sum)
+ *                     partials in the workspace and a second launch merges them
+ *                     in a fixed order;
+ *   *pages_per_split  pages of a part (for the windowed decode: pages that
+ *                     hold retained tokens, see lla_window_pages).
+ * The chunked prefill kernel reports 1 and 1.  Returns LLA_OK, or
+ * LLA_ERR_INVALID_ARG (null outputs, invalid dims) / LLA_ERR_UNSUPPORTED
+ * where lla_workspace_bytes would return 0. */
+int32_t lla_attn_plan(const lla_dims *dims, int32_t op, int32_t batch, int32_t max_ctx, int32_t n,
+                      int32_t *splits, int32_t *pages_per_split);
+
+/* Token eviction (lla_decode_window_attn): the pages of a sequence of ctx
+ * tokens whose page-table entries the windowed decode reads (host only).  They
+ * are pages [0, *sink_pages), which hold the sink tokens j < n_sink, and pages
+ * [*first_window_page, ceil(ctx / page_size)), which hold the window tokens
+ * j >= ctx - window; *first_window_page is ceil(ctx / page_size) when no token
+ * lies in the window beyond the sink.  Each of these pages holds at least one
+ * retained token; no other entry is read.  Returns LLA_OK or
+ * LLA_ERR_INVALID_ARG (negative sizes, n_sink + window < 1, null outputs). */
+int32_t lla_window_pages(int32_t ctx, int32_t n_sink, int32_t window, int32_t *sink_pages,
+                         int32_t *first_window_page);
+
 /* 1 if the library has kernels for (dims, op), else 0 (host only). */
 int32_t lla_supported(const lla_dims *dims, int32_t op);
 

@@ -314,6 +314,27 @@ void fill_layer(const lla_dims *d, const lla_codec *c, const lla_cache *k, int l
   }
 }
 
+// The plan of an attention call of `op` for the arguments of
+// lla_workspace_bytes; false where that returns 0.
+bool plan_op(const lla_dims *d, int op, int batch, int max_ctx, int n, AttnPlan *p) {
+  if (max_ctx < 1) return false;
+  const long long b1 = batch > 0 ? batch : 1;
+  switch (op) {
+    case LLA_OP_DECOUPLED_DECODE: return plan_decoupled(d, b1, max_ctx, n, p);
+    case LLA_OP_WINDOW_DECODE:
+      return n >= 1 && d->dtype == LLA_BF16 && d->variant == LLA_PER_HEAD &&
+             plan_attn(d, b1, window_plan_ctx(max_ctx, n), p);
+    case LLA_OP_FULL_DECODE: return plan_full(d, b1, max_ctx, p);
+    case LLA_OP_DECODE: return plan_attn(d, b1, max_ctx, p);
+    case LLA_OP_PREFILL: {
+      if (n < 0) return false;
+      const long long rows = (long long)batch * n;
+      return plan_attn(d, rows > 0 ? rows : 1, max_ctx, p, true);
+    }
+    default: return false;
+  }
+}
+
 }  // namespace
 }  // namespace lla
 
@@ -331,29 +352,30 @@ size_t lla_workspace_bytes(const lla_dims *d, int32_t op, int32_t batch, int32_t
   if (!dims_valid(d) || batch < 0) return 0;
   if (op == LLA_OP_ENCODE) return n >= 0 ? encode_ws_bytes(d, n) : 0;
   if (op == LLA_OP_RECONSTRUCT || op == LLA_OP_ROPE_KEY_APPEND) return kHeaderBytes;
-  if (op == LLA_OP_DECOUPLED_DECODE) {
-    AttnPlan p;
-    if (max_ctx < 1 || !plan_decoupled(d, batch > 0 ? batch : 1, max_ctx, n, &p)) return 0;
-    return p.bytes;
-  }
-  if (op == LLA_OP_WINDOW_DECODE) {
-    AttnPlan p;
-    if (max_ctx < 1 || n < 1 || d->dtype != LLA_BF16 || d->variant != LLA_PER_HEAD ||
-        !plan_attn(d, batch > 0 ? batch : 1, window_plan_ctx(max_ctx, n), &p))
-      return 0;
-    return p.bytes;
-  }
-  if (op == LLA_OP_FULL_DECODE) {
-    AttnPlan p;
-    if (max_ctx < 1 || !plan_full(d, batch > 0 ? batch : 1, max_ctx, &p)) return 0;
-    return p.bytes;
-  }
-  if (op != LLA_OP_DECODE && op != LLA_OP_PREFILL) return 0;
-  if (max_ctx < 1 || (op == LLA_OP_PREFILL && n < 0)) return 0;
-  const long long rows = (long long)batch * (op == LLA_OP_PREFILL ? n : 1);
   AttnPlan p;
-  if (!plan_attn(d, rows > 0 ? rows : 1, max_ctx, &p, op == LLA_OP_PREFILL)) return 0;
-  return p.bytes;
+  return plan_op(d, op, batch, max_ctx, n, &p) ? p.bytes : 0;
+}
+
+int32_t lla_attn_plan(const lla_dims *d, int32_t op, int32_t batch, int32_t max_ctx, int32_t n,
+                      int32_t *splits, int32_t *pages_per_split) {
+  if (!dims_valid(d) || batch < 0 || !splits || !pages_per_split)
+    return fail(LLA_ERR_INVALID_ARG, "invalid arguments");
+  AttnPlan p;
+  if (!plan_op(d, op, batch, max_ctx, n, &p)) return fail(LLA_ERR_UNSUPPORTED, "no attention plan for these arguments");
+  *splits = p.splits;
+  *pages_per_split = p.pages_per_split;
+  return LLA_OK;
+}
+
+int32_t lla_window_pages(int32_t ctx, int32_t n_sink, int32_t window, int32_t *sink_pages,
+                         int32_t *first_window_page) {
+  if (ctx < 0 || n_sink < 0 || window < 0 || (long long)n_sink + window < 1 || !sink_pages ||
+      !first_window_page)
+    return fail(LLA_ERR_INVALID_ARG, "need ctx, n_sink, window >= 0 and n_sink + window >= 1");
+  const RetainedPages r = retained_pages(ctx, 1, n_sink, window);
+  *sink_pages = r.n_a;
+  *first_window_page = r.p_b;
+  return LLA_OK;
 }
 
 int32_t lla_encode_append(const lla_dims *d, const lla_codec *c, const lla_cache *k,

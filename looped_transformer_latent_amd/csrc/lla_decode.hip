@@ -359,13 +359,8 @@ __global__ __launch_bounds__(64 * NW) void decode_ph_kernel(AttnArgs a) {
 namespace {
 template <int DH, int RK, int RV, int HPW, int NW>
 hipError_t go(const AttnArgs &a, hipStream_t stream) {
-  static bool lds_raised = false;  // allow more than the default 64 KiB of LDS once per kernel
-  if (!lds_raised) {
-    const hipError_t e = hipFuncSetAttribute((const void *)decode_ph_kernel<DH, RK, RV, HPW, NW>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 1024);
-    if (e != hipSuccess) return e;
-    lds_raised = true;
-  }
+  const hipError_t e = raise_lds_limit<decode_ph_kernel<DH, RK, RV, HPW, NW>>();  // more than the default 64 KiB
+  if (e != hipSuccess) return e;
   const dim3 grid((unsigned)(a.rows * a.head_groups * a.splits));
   const dim3 block((unsigned)(64 * NW));
   constexpr int TS = (LLA_DECODE_LOOK + 2) * kPage * (DH / 4);  // one chunk = ring

@@ -91,19 +91,12 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 1 : 2) void decode_g_kernel(Attn
     ctx = 0;
     qp = 0;
   }
-  const int npages = (ctx + kPage - 1) / kPage;
   // Retained tokens: [0, keep_lo) and [keep_hi, ctx) (token eviction), or the
   // whole context.  Splits run over the pages that hold retained tokens
   // ("virtual" pages v: the sink pages [0, n_a), then the window pages from
   // page p_b on); the other pages' table entries are never read.
-  int keep_lo = ctx, keep_hi = ctx;
-  if (a.evict) {
-    keep_lo = min(a.n_sink, ctx);
-    keep_hi = max(ctx - a.window, keep_lo);
-  }
-  const int n_a = (keep_lo + kPage - 1) / kPage;
-  const int p_b = max(keep_hi / kPage, n_a);
-  const int nvirt = n_a + (npages - p_b);
+  const RetainedPages rp = retained_pages(ctx, a.evict, a.n_sink, a.window);
+  const int keep_lo = rp.keep_lo, keep_hi = rp.keep_hi, n_a = rp.n_a, p_b = rp.p_b, nvirt = rp.nvirt;
   auto logical = [&](int v) -> int { return v < n_a ? v : p_b + (v - n_a); };
   const int lp0 = split * a.pages_per_split;
   const int lp1 = min(lp0 + a.pages_per_split, nvirt);
@@ -116,23 +109,76 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 1 : 2) void decode_g_kernel(Attn
   // region with 16-byte loads: the fold reads it by (pair, column), which as
   // global loads would be one 2-byte load per element and lane.  The RoPE row
   // of q_pos, q and mu_k are read 4 pairs per load.
+  //
+  // Range.  fp16 overflows above 65504 and loses bits below 2^-14, while q, mu
+  // and W_up may be any bf16 values.  Per head, F and (alpha, beta) are packed
+  // scaled by a power of two 2^e chosen so that their largest possible
+  // magnitude lies in [2^14, 2^15): by Cauchy-Schwarz on a pair,
+  // |A_ir|, |B_ir| <= |(q'_a, q'_b)| |(W[a][r], W[b][r])| <= qscale max_i |(q_a, q_b)| sqrt(2) max |W|,
+  // and the same with mu for (alpha_i, beta_i).  The scores are multiplied by
+  // 2^-e after the products; scaling by a power of two commutes with every
+  // rounding in normal range, so nothing else changes.
   extern __shared__ __attribute__((aligned(16))) char smem[];
   u32x4 F[HPW][RT][KS];
   u32x4 Fa[KS];
+  float unscale[HPW];  // 2^-e per head (wave-uniform)
   {
     uint16_t *s_w = (uint16_t *)(smem + w_stage_offset<DH, RK, RV, HPW, NW>(a.pages_per_split)) +
                     wave * (HPW * DH * RK);
+    uint32_t mag[HPW];  // largest |bf16| bit pattern of W_up,k and mu_k (magnitude order = integer order)
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
       const u32x4 *src = (const u32x4 *)((const uint16_t *)a.wup_k + (long long)(h0 + hh) * a.wup_head_stride_k);
       u32x4 *dst = (u32x4 *)(s_w + hh * DH * RK);
+      mag[hh] = 0;
 #pragma unroll
-      for (int c = 0; c < DH * RK / 8 / 64; ++c) dst[c * 64 + lane] = src[c * 64 + lane];
+      for (int c = 0; c < DH * RK / 8 / 64; ++c) {
+        const u32x4 v = src[c * 64 + lane];
+        dst[c * 64 + lane] = v;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) mag[hh] = max(mag[hh], max(v[k] & 0x7FFFu, (v[k] >> 16) & 0x7FFFu));
+      }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const float *rq = a.rope + (long long)qp * DH;
+    float qscale_h[HPW];
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      const int h = h0 + hh;
+      const uint16_t *qrow = (const uint16_t *)a.q + ((long long)row * a.H + h) * DH;
+      const uint16_t *mu = (const uint16_t *)a.mu_k + (long long)h * a.mu_head_stride;
+      float qn2 = 0.f;  // largest |(q_a, q_b)|^2 of the lane's pairs
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const int i0 = 16 * s + 4 * g;
+        const u32x2 qa4 = *(const u32x2 *)(qrow + i0), qb4 = *(const u32x2 *)(qrow + i0 + HALF);
+        const u32x2 ma4 = *(const u32x2 *)(mu + i0), mb4 = *(const u32x2 *)(mu + i0 + HALF);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const float qa = p & 1 ? bf16_hi(qa4[p >> 1]) : bf16_lo(qa4[p >> 1]);
+          const float qb = p & 1 ? bf16_hi(qb4[p >> 1]) : bf16_lo(qb4[p >> 1]);
+          qn2 = fmaxf(qn2, qa * qa + qb * qb);
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+          mag[hh] = max(mag[hh], max(max(ma4[k] & 0x7FFFu, (ma4[k] >> 16) & 0x7FFFu),
+                                     max(mb4[k] & 0x7FFFu, (mb4[k] >> 16) & 0x7FFFu)));
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        qn2 = fmaxf(qn2, __shfl_xor(qn2, o));
+        mag[hh] = max(mag[hh], (uint32_t)__shfl_xor((int)mag[hh], o));
+      }
+      const float bound = a.qscale * sqrtf(qn2) * 1.41421356f * bf16_to_f32(mag[hh]);
+      // bound = f 2^k with f in [1, 2): e = 14 - k, clamped to normal fp32 powers
+      int e = 14 - ((int)((__float_as_uint(bound) >> 23) & 0xFFu) - 127);
+      e = min(max(e, -100), 100);
+      e = __builtin_amdgcn_readfirstlane(e);
+      qscale_h[hh] = a.qscale * __uint_as_float((uint32_t)(127 + e) << 23);
+      unscale[hh] = __uint_as_float((uint32_t)(127 - e) << 23);
+    }
 #pragma unroll
     for (int s = 0; s < KS; ++s) Fa[s] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
@@ -154,8 +200,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 1 : 2) void decode_g_kernel(Attn
           const float c = cq[2 * (p & 1)], sn = cq[2 * (p & 1) + 1];
           const float qa = p & 1 ? bf16_hi(qa4[p >> 1]) : bf16_lo(qa4[p >> 1]);
           const float qb = p & 1 ? bf16_hi(qb4[p >> 1]) : bf16_lo(qb4[p >> 1]);
-          const float pa = a.qscale * (qa * c - qb * sn);
-          const float pb = a.qscale * (qa * sn + qb * c);
+          const float pa = qscale_h[hh] * (qa * c - qb * sn);
+          const float pb = qscale_h[hh] * (qa * sn + qb * c);
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt) {
             const int r = 16 * rt + n;
@@ -348,7 +394,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 1 : 2) void decode_g_kernel(Attn
         sc = fmaf(bf16_hi(cur.k[hh][rt][1]), G[3], sc);
       }
       sc = sum_across_rows(sc);
-      sc = valid ? sc : -INFINITY;
+      sc = valid ? sc * unscale[hh] : -INFINITY;
       const float mt = max_in_row(sc);
       if (mt > m_run[hh]) {  // wave-uniform
         const float corr = fast_exp2(m_run[hh] - mt);
@@ -357,7 +403,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 1 : 2) void decode_g_kernel(Attn
         for (int k = 0; k < CV; ++k) acc[hh][k] *= corr;
         m_run[hh] = mt;
       }
-      const float p = fast_exp2(sc - m_run[hh]);
+      // a masked token weighs 0, also while m_run is still -inf (no valid token yet)
+      const float p = valid ? fast_exp2(sc - m_run[hh]) : 0.f;
       z[hh] += p;
 #pragma unroll
       for (int kv = 0; kv < KV; ++kv) {
@@ -476,13 +523,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 1 : 2) void decode_g_kernel(Attn
 namespace {
 template <int DH, int RK, int RV, int HPW, int NW>
 hipError_t go_g(const AttnArgs &a, hipStream_t stream) {
-  static bool lds_raised = false;  // allow more than the default 64 KiB of LDS once per kernel
-  if (!lds_raised) {
-    const hipError_t e = hipFuncSetAttribute((const void *)decode_g_kernel<DH, RK, RV, HPW, NW>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 1024);
-    if (e != hipSuccess) return e;
-    lds_raised = true;
-  }
+  const hipError_t e = raise_lds_limit<decode_g_kernel<DH, RK, RV, HPW, NW>>();  // more than the default 64 KiB
+  if (e != hipSuccess) return e;
   const dim3 grid((unsigned)(a.rows * a.head_groups * a.splits));
   const dim3 block((unsigned)(64 * NW));
   const size_t shmem = w_stage_offset<DH, RK, RV, HPW, NW>(a.pages_per_split) +

@@ -4,6 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "lla.h"
 
 namespace lla {
@@ -73,6 +76,54 @@ struct EncodeArgs {
   int muw_parts;               // row ranges of W_down summed independently
   int *err;
 };
+
+// Pages of one sequence that a decode reads under token eviction (keep the
+// first n_sink and the last `window` tokens of [0, ctx)).  The split plan runs
+// over "virtual" pages: the sink pages [0, n_a), then the window pages
+// [p_b, npages), so virtual page v is logical page v (v < n_a) or
+// p_b + v - n_a.  Every virtual page holds at least one retained token, and
+// no other page is read.  Without eviction every page is a sink page.
+struct RetainedPages {
+  int keep_lo, keep_hi;  // retained tokens: [0, keep_lo) and [keep_hi, ctx)
+  int n_a, p_b, nvirt;
+};
+__host__ __device__ inline RetainedPages retained_pages(int ctx, int evict, int n_sink, int window) {
+  RetainedPages r;
+  const int npages = (ctx + kPage - 1) / kPage;
+  r.keep_lo = ctx;
+  r.keep_hi = ctx;
+  if (evict) {
+    r.keep_lo = n_sink < ctx ? n_sink : ctx;
+    r.keep_hi = ctx - window > r.keep_lo ? ctx - window : r.keep_lo;
+  }
+  r.n_a = (r.keep_lo + kPage - 1) / kPage;
+  // No window tokens (window 0, or the sink covers the context): no window
+  // pages.  Otherwise the first window page holds token keep_hi.
+  r.p_b = r.keep_hi >= ctx ? npages : (r.keep_hi / kPage > r.n_a ? r.keep_hi / kPage : r.n_a);
+  r.nvirt = r.n_a + (npages - r.p_b);
+  return r;
+}
+
+// Raise a kernel's dynamic-LDS limit to what a CU offers, once per device.
+// Thread-safe: concurrent first calls serialise on a mutex, later calls see
+// the device's bit set.
+// One instantiation (and one set of flags) per kernel.
+constexpr int kLdsLimit = 160 * 1024 - 1024;
+template <auto kernel>
+hipError_t raise_lds_limit() {
+  static std::atomic<uint64_t> done{0};  // one bit per device ordinal < 64
+  static std::mutex mu;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  std::lock_guard<std::mutex> lock(mu);
+  if (bit && (done.load(std::memory_order_relaxed) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsLimit);
+  if (e == hipSuccess) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
 
 // Kernel dispatch: return hipSuccess, or hipErrorInvalidConfiguration when the
 // shape has no instantiated kernel.

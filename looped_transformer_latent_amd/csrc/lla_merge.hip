@@ -60,11 +60,14 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int d_head, int 
     M = fmaxf(fmaxf(s_red[0][32], s_red[1][32]), fmaxf(s_red[2][32], s_red[3][32]));
     __syncthreads();
   }
+  // A split that saw no token (m = -inf: its pages all lie past the row's
+  // context) weighs 0; exp2(-inf - M) would be NaN when M is -inf as well.
+  auto weight = [&](float m) -> float { return m == -INFINITY ? 0.f : exp2f(m - M); };
   float Z = 0.f;
   if (live)
     for (int s = u; s < S; s += G) {
       const float m = pb[(long long)s * stride + r_v];
-      Z += exp2f(m - M) * pb[(long long)s * stride + r_v + 1];  // NaN Z poisons the row
+      Z += weight(m) * pb[(long long)s * stride + r_v + 1];  // NaN Z poisons the row
     }
   Z = group_sum(Z, 32);
 
@@ -76,7 +79,7 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int d_head, int 
     if (live)
       for (int s = u; s < S; s += G) {
         const float *row = pb + (long long)s * stride;
-        const float wgt = exp2f(row[r_v] - M);
+        const float wgt = weight(row[r_v]);
 #pragma unroll
         for (int k = 0; k < 32; k += 2) {
           if (c0 + k < r_v) {  // r_v is a multiple of 8: pairs stay whole

@@ -26,7 +26,7 @@ DEVERR_CTX, DEVERR_PAGE, DEVERR_APPEND = 1, 2, 4
 EXPORTS = ["lla_rope_table", "lla_workspace_bytes", "lla_encode_append", "lla_decode_attn",
            "lla_prefill_attn", "lla_reconstruct_kv", "lla_full_decode_attn", "lla_rope_key_append",
            "lla_decoupled_decode_attn", "lla_decode_window_attn", "lla_cache_scalars", "lla_supported", "lla_status_string",
-           "lla_last_error"]
+           "lla_last_error", "lla_attn_plan", "lla_window_pages"]
 
 
 class LlaError(RuntimeError):
@@ -81,13 +81,16 @@ def load() -> ctypes.CDLL:
     lib.lla_decode_window_attn.argtypes = [pd, pc, pk, P, I, I, I, P, P, P, I, I, I, F, P, P, S, P]
     lib.lla_cache_scalars.argtypes = [pd, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
     lib.lla_supported.argtypes = [pd, I]
+    pi = ctypes.POINTER(I)
+    lib.lla_attn_plan.argtypes = [pd, I, I, I, I, pi, pi]
+    lib.lla_window_pages.argtypes = [I, I, I, pi, pi]
     lib.lla_status_string.argtypes = [I]
     lib.lla_status_string.restype = ctypes.c_char_p
     lib.lla_last_error.argtypes = []
     lib.lla_last_error.restype = ctypes.c_char_p
     for name in ("lla_rope_table", "lla_encode_append", "lla_decode_attn", "lla_prefill_attn",
                  "lla_reconstruct_kv", "lla_full_decode_attn",
-                 "lla_cache_scalars", "lla_supported"):
+                 "lla_cache_scalars", "lla_supported", "lla_attn_plan", "lla_window_pages"):
         getattr(lib, name).restype = I
     _lib = lib
     return lib
@@ -162,6 +165,20 @@ def supported(dims: Dims, op: int) -> bool:
 
 def workspace_bytes(dims: Dims, op: int, batch: int, max_ctx: int, n: int = 0) -> int:
     return int(load().lla_workspace_bytes(ctypes.byref(dims), op, batch, max_ctx, n))
+
+
+def attn_plan(dims: Dims, op: int, batch: int, max_ctx: int, n: int = 0) -> tuple[int, int]:
+    """(splits, pages per split) of an attention call (lla_attn_plan)."""
+    s, p = ctypes.c_int32(), ctypes.c_int32()
+    _check(load().lla_attn_plan(ctypes.byref(dims), op, batch, max_ctx, n, ctypes.byref(s), ctypes.byref(p)))
+    return s.value, p.value
+
+
+def window_pages(ctx: int, n_sink: int, window: int) -> tuple[int, int]:
+    """(sink pages, first window page) that a windowed decode reads (lla_window_pages)."""
+    a, b = ctypes.c_int32(), ctypes.c_int32()
+    _check(load().lla_window_pages(ctx, n_sink, window, ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
 
 
 def workspace(dims: Dims, op: int, batch: int, max_ctx: int, n: int = 0, device="cuda") -> torch.Tensor:

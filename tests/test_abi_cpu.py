@@ -7,6 +7,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from looped_transformer_latent_amd import lla
@@ -266,3 +267,45 @@ def test_profiled_traffic_needs_matching_sources(tmp_path, monkeypatch):
     assert bench.profiled_traffic("w1") == 1234
     assert bench.profiled_traffic("w2") is None
     assert bench.profiled_traffic("w3") is None
+
+
+def _retained_pages_brute(ctx, n_sink, window):
+    """Pages holding at least one retained token, from the definition: token j of
+    [0, ctx) is kept when j < n_sink or j >= ctx - window."""
+    return sorted({j // 16 for j in range(ctx) if j < n_sink or j >= ctx - window})
+
+
+@pytest.mark.parametrize("batch,max_ctx,n_sink,window", [
+    (1, 1000, 225, 0), (1, 1000, 4, 0), (5, 4001, 225, 0), (768, 4096, 4, 256), (1, 4096, 4, 256),
+    (3, 16384, 4, 256), (2, 300, 20, 37), (1, 4000, 0, 16), (1, 4000, 17, 1), (64, 8192, 1024, 1024),
+    (1, 257, 300, 0), (1, 5000, 0, 4999)])
+def test_window_plan_reads_only_retained_pages(batch, max_ctx, n_sink, window):
+    """The windowed decode's splits run over exactly the pages that hold a
+    retained token (lla_window_pages, the rule the kernel itself evaluates),
+    every such page lies in some split, so no split can see only evicted
+    tokens; a split past the last such page is empty and merges with weight 0."""
+    d = _dims()
+    splits, pps = lla.attn_plan(d, lla.OP_WINDOW_DECODE, batch, max_ctx, n_sink + window)
+    rng = np.random.default_rng(max_ctx + n_sink + window)
+    ctxs = sorted(set(range(1, min(max_ctx, 70) + 1)) | set(rng.integers(1, max_ctx + 1, 60).tolist()) |
+                  {max_ctx, max(1, max_ctx - 1)})
+    for ctx in ctxs:
+        n_a, p_b = lla.window_pages(ctx, n_sink, window)
+        npages = (ctx + 15) // 16
+        virtual = list(range(n_a)) + list(range(p_b, npages))
+        assert virtual == _retained_pages_brute(ctx, n_sink, window), (ctx, n_a, p_b)
+        assert len(virtual) <= splits * pps, (ctx, splits, pps)
+
+
+def test_window_plan_sink_only_case_has_an_empty_split():
+    """Batch 1, 16 heads, sink 225, no window, ctx = max_ctx = 1000: 4 splits of 5
+    pages over 15 sink pages; the last split holds no page at all (the page of
+    tokens 992..999, all evicted, is not one of them)."""
+    d = _dims()
+    assert lla.attn_plan(d, lla.OP_WINDOW_DECODE, 1, 1000, 225) == (4, 5)
+    assert lla.window_pages(1000, 225, 0) == (15, 63)
+    assert lla.window_pages(1000, 4, 256) == (1, 46)
+    with pytest.raises(lla.LlaError):
+        lla.window_pages(10, 0, 0)
+    with pytest.raises(lla.LlaError):
+        lla.attn_plan(_dims(d_head=96), lla.OP_DECODE, 1, 100)

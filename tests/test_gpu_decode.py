@@ -84,6 +84,66 @@ def test_tiny_fp32_svd_codec_all_loops():
         check(m, codec, kp, vp, pt, q, [L - 1], [L], 0, t, "tiny-fp32")
 
 
+def test_tiny_fp32_gpu_encode_then_gpu_decode():
+    """The tiny fp32 workload end to end on the GPU: the 256 fresh tokens are
+    appended by lla_encode_append into an empty pool (checked against the
+    oracle's encode at 1e-4 per latent row), then every loop's decode reads the
+    GPU-written cache; the reference is the oracle's decode over the oracle's
+    own cache."""
+    T, H, d, L, rk, rv = 4, 2, 64, 256, 16, 32
+    m = dims(T, 1, H, d, rk, rv, PER_HEAD, F32)
+    sh = param_shapes(m)
+    codec = {k: np.zeros(v) for k, v in sh.items()}
+    xs = {}
+    for h in range(H):
+        for kv, r in (("k", rk), ("v", rv)):
+            stream = 5000 + 10 * h + (0 if kv == "k" else 5)
+            mu, wd, wu = svd_codec_one(rank8_activations(1001, stream, 4096, T * d), r, T, d)
+            codec["mu_" + kv][0, h] = mu.reshape(T, d)
+            codec["w_down_" + kv][0, h] = wd
+            codec["w_up_" + kv][0, h] = wu
+            xs[kv + str(h)] = rank8_activations(1001, stream, L, T * d, draw=1)
+    codec = {k: store(v, F32) for k, v in codec.items()}
+    npages = L // 16
+    pt = gen.identity_page_table(1, npages)
+    xk = store(np.stack([xs["k%d" % h] for h in range(H)], 1).reshape(1, 1, L, H, T, d), F32)
+    xv = store(np.stack([xs["v%d" % h] for h in range(H)], 1).reshape(1, 1, L, H, T, d), F32)
+    kp_ref = np.zeros(pool_shape(m, npages, "k"), np.float32)
+    vp_ref = np.zeros(pool_shape(m, npages, "v"), np.float32)
+    assert oracle.encode(m, codec, kp_ref, vp_ref, pt, xk, xv, np.array([0]), L, 0, 1) == 0
+
+    D = lla.dims_from_dict(m)
+    c, keep = device_codec(codec)
+    kp_d = torch.full(pool_shape(m, npages, "k"), float("nan"), dtype=torch.float32, device="cuda")
+    vp_d = torch.full(pool_shape(m, npages, "v"), float("nan"), dtype=torch.float32, device="cuda")
+    pt_d = to_device(pt)
+    cache = lla.make_cache(kp_d, vp_d, pt_d, npages)
+    ws = lla.workspace(D, lla.OP_ENCODE, 1, 0, 1)
+    lla.encode_append(D, c, cache, to_device(xk), to_device(xv), to_device(np.int32([0])), L, 0, 1, ws)
+    torch.cuda.synchronize()
+    assert lla.device_error_word(ws) == 0
+    for g, r in ((kp_d, kp_ref), (vp_d, vp_ref)):
+        gh = g.cpu().numpy().astype(np.float64).reshape(-1, g.shape[-1])
+        err = row_rel_err(gh, r.astype(np.float64).reshape(-1, r.shape[-1]))
+        assert np.isfinite(gh).all() and err.max() <= 1e-4, err.max()
+
+    rope = lla.rope_table(D, L)
+    q = gen.normal(1001, 301, (1, H, d), dtype="f32")
+    q_d = to_device(q)
+    wsd = lla.workspace(D, lla.OP_DECODE, 1, L)
+    for t in range(T):
+        out = torch.empty_like(q_d)
+        lla.decode_attn(D, c, cache, rope, 0, t, q_d, to_device(np.int32([L - 1])), to_device(np.int32([L])),
+                        L, out, wsd)
+        torch.cuda.synchronize()
+        ref, rc = oracle.decode(m, codec, kp_ref, vp_ref, pt, 0, t, q, np.int32([L - 1]), np.int32([L]))
+        assert rc == 0
+        err = row_rel_err(out_to_f64(out), ref)
+        print(f"tiny fp32 GPU encode -> GPU decode, loop {t}: max row rel err {err.max():.3e}", flush=True)
+        assert err.max() <= 1e-4
+    assert lla.device_error_word(wsd) == 0
+
+
 # ---------------------------------------------------------------- Ouro-shaped, reduced sizes
 
 @pytest.mark.parametrize("dtype", [BF16, F32])
@@ -124,6 +184,30 @@ def test_mild_compression_r96_r160():
     pt = gen.shuffled_page_table(2204, 2, 33)
     q = gen.normal(2205, 1, (2, 16, 128))
     check(m, codec, kp, vp, pt, q, ctx - 1, ctx, 0, 2, "r96")
+
+
+def _scaled(bits: np.ndarray, k: int) -> np.ndarray:
+    """bf16 storage array times 2^k (exact: only the exponent changes)."""
+    return store(gen.storage_to_f64(bits) * 2.0 ** k, BF16)
+
+
+@pytest.mark.parametrize("shape", [(128, 16, 32), (128, 96, 160)])
+@pytest.mark.parametrize("a,b", [(10, 10), (-10, -6), (-14, 0)])
+def test_decoder_fold_range(shape, a, b):
+    """Magnitudes far from N(0,1): q x 2^a, W_up,k x 2^b, mu_k x 2^-a and c_k x
+    2^-(a+b) leave every score unchanged in exact arithmetic, while the folded
+    decoder q' W_up,k grows by 2^(a+b) (2^20: beyond fp16's 65504) or shrinks
+    (2^-16: below fp16's normal range).  The result must still match the oracle
+    on the scaled inputs within the bf16 bar."""
+    d, rk, rv = shape
+    m = dims(4, 1, 16, d, rk, rv, PER_HEAD, BF16)
+    ctx = np.array([300, 1000])
+    codec = random_codec(m, seed=2152, ortho_down=False)
+    kp, vp = random_pools(m, 2 * 64, seed=2153)
+    pt = gen.shuffled_page_table(2154, 2, 64)
+    q = gen.normal(2155, 1, (2, 16, d))
+    codec = dict(codec, w_up_k=_scaled(codec["w_up_k"], b), mu_k=_scaled(codec["mu_k"], -a))
+    check(m, codec, _scaled(kp, -(a + b)), vp, pt, _scaled(q, a), ctx - 1, ctx, 0, 1, f"range a={a} b={b} {shape}")
 
 
 # ---------------------------------------------------------------- bitwise properties

@@ -168,6 +168,64 @@ def test_encode_lla2d(dtype):
     compare(m, got, ref, init, f"encode 2D dt={dtype}")
 
 
+@pytest.mark.timeout(600)
+def test_encode_lla2d_benchmark_shape():
+    """The LLA-2D decode step's append in the benchmark's launch configuration:
+    one token per sequence for 128 sequences into all 4 layers, width
+    T H d = 8 x 32 x 128 = 32768, r_k = r_v = 256, seeded x as the benchmark
+    draws it, pos0 = 16383.  The pool holds one page per sequence (the token's
+    page, shuffled; the launch does not depend on the pool size).  Placement is
+    checked bit-exact over every layer; the latents of 8 sequences in layers 0
+    and 3 against the oracle's encode."""
+    from looped_transformer_latent_amd import workloads as wl
+    w = wl.WORKLOADS["lla2d-t8-h32-b128"]
+    m = w.dims
+    codec_h = wl.codec_host(w)
+    B, pos = w.batch, w.ctx - 1
+    perm = gen.shuffled_page_table(w.seed, 1, B)[0]
+    pt = np.full((B, w.pages_per_seq), -1, np.int32)  # entries never read stay -1
+    pt[:, pos // 16] = perm
+    sent = SENT[BF16]
+    kp = np.full(pool_shape(m, B, "k"), sent)
+    vp = np.full(pool_shape(m, B, "v"), sent)
+    D = lla.dims_from_dict(m)
+    c, keep = device_codec(codec_h)
+    kp_d, vp_d = to_device(kp), to_device(vp)
+    cache = lla.make_cache(kp_d, vp_d, to_device(pt), B)
+    xs = (w.D, B, 1, w.T, w.H, w.d_head)
+    x_k = torch.empty(xs, dtype=torch.bfloat16, device="cuda")
+    x_v = torch.empty(xs, dtype=torch.bfloat16, device="cuda")
+    lla.gen_normal_(x_k, w.seed, wl.STREAMS["x_k"])
+    lla.gen_normal_(x_v, w.seed, wl.STREAMS["x_v"])
+    ws = lla.workspace(D, lla.OP_ENCODE, B, 0, w.D)
+    lla.encode_append(D, c, cache, x_k, x_v, to_device(np.full(B, pos, np.int32)), 1, 0, w.D, ws)
+    torch.cuda.synchronize()
+    assert lla.device_error_word(ws) == 0
+    gk, gv = to_host(kp_d), to_host(vp_d)
+    for g, init in ((gk, kp), (gv, vp)):          # placement: row 15 of each token's page only
+        written = np.zeros(g.shape[:3], bool)
+        written[:, perm, pos % 16] = True
+        assert ((g != init).any(axis=-1) == written).all()
+        assert (g[:, perm, pos % 16] != sent).all()
+    width = w.T * w.H * w.d_head
+    rows = np.array([0, 1, 37, 63, 64, 100, 126, 127])
+    for layer in (0, w.D - 1):
+        m1 = dict(m, D=1)
+        codec1 = {k: np.ascontiguousarray(v[layer:layer + 1]) for k, v in codec_h.items()}
+        xk = np.concatenate([gen.normal(w.seed, wl.STREAMS["x_k"], (1, 1, 1, w.T, w.H, w.d_head),
+                                        offset=(layer * B + b) * width) for b in rows], axis=1)
+        xv = np.concatenate([gen.normal(w.seed, wl.STREAMS["x_v"], (1, 1, 1, w.T, w.H, w.d_head),
+                                        offset=(layer * B + b) * width) for b in rows], axis=1)
+        local = np.arange(len(rows), dtype=np.int32)[:, None]
+        kr = np.full((1, len(rows), 16, w.r_k), sent)
+        vr = np.full((1, len(rows), 16, w.r_v), sent)
+        assert oracle.encode(m1, codec1, kr, vr, local, xk, xv, np.zeros(len(rows), np.int32) + pos % 16,
+                             1, 0, 1) == 0
+        got = (gk[layer:layer + 1, perm[rows]], gv[layer:layer + 1, perm[rows]])
+        init = (np.full_like(kr, sent), np.full_like(vr, sent))
+        compare(m1, got, (kr, vr), init, f"encode 2D benchmark shape, layer {layer}")
+
+
 def test_encode_device_errors():
     """A position past the page-table row, or a page entry out of range, is
     flagged in the workspace error word and the slot is not written."""

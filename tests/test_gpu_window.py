@@ -49,7 +49,8 @@ def problem(shape, B, ctx_max, seed):
 
 CASES = [((128, 16, 32, 16), 4, 256), ((128, 16, 32, 16), 0, 16), ((128, 16, 32, 16), 20, 37),
          ((128, 96, 160, 16), 4, 256), ((64, 16, 32, 16), 4, 256), ((128, 32, 64, 8), 4, 1024),
-         ((128, 16, 32, 16), 4, 8000)]  # a budget above max_ctx keeps every token
+         ((128, 16, 32, 16), 4, 8000),  # a budget above max_ctx keeps every token
+         ((128, 16, 32, 16), 225, 0), ((128, 16, 32, 16), 4, 0), ((128, 96, 160, 16), 20, 0)]  # sink only
 
 
 @pytest.mark.parametrize("shape,n_sink,window", CASES, ids=lambda v: str(v))
@@ -106,3 +107,24 @@ def test_window_decode_with_small_retained_set_at_long_context():
     ref, rc = oracle.decode_window(m, codec, kp, vp, pt, 1, 3, q, ctx - 1, ctx, n_sink, window)
     assert rc == 0 and errw == 0
     assert row_rel_err(got, ref).max() <= TOL
+
+
+@pytest.mark.parametrize("n_sink,ctx", [(225, 1000), (4, 1000), (4, 37)])
+def test_sink_only_ragged_context(n_sink, ctx):
+    """No window (window = 0) at a ragged context: batch 1, 16 heads, context =
+    max_ctx.  With sink 225 and ctx 1000 the plan has 4 splits of 5 pages over
+    the 15 sink pages, so the last split holds no page; the page of tokens
+    992..999 (all evicted) must not become a split of its own.  Entries of every
+    page past the sink are released (-1): none of them is read."""
+    shape = (128, 16, 32, 16)
+    m, codec, kp, vp, pt, q = problem(shape, 1, ctx, seed=6400 + n_sink + ctx)
+    c = np.array([ctx])
+    released = pt.copy()
+    released[0, (n_sink + 15) // 16:] = -1
+    got, errw, _ = run_window(m, codec, kp, vp, released, q, c - 1, c, n_sink, 0, 0, 1, ctx)
+    ref, rc = oracle.decode_window(m, codec, kp, vp, pt, 0, 1, q, c - 1, c, n_sink, 0)
+    assert rc == 0 and errw == 0
+    assert np.isfinite(got).all()
+    err = row_rel_err(got, ref)
+    print(f"sink-only {n_sink} ctx {ctx}: max row rel err {err.max():.3e}", flush=True)
+    assert err.max() <= TOL
