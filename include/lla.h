@@ -173,6 +173,26 @@ int32_t lla_decode_attn(const lla_dims *dims, const lla_codec *codec, const lla_
                         int32_t max_ctx, float scale, void *out, void *workspace,
                         size_t ws_bytes, hipStream_t stream);
 
+/* lla_decode_attn without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same computation, kernels and arguments as
+ * lla_decode_attn, except:
+ *   err   device int32, caller-owned: the error word (LLA_DEVERR_* bits OR-ed
+ *         in, sticky, never cleared by the library), as byte 0 of the
+ *         workspace of lla_decode_attn.
+ * The split partials live in a 16 MiB device array inside the library, one
+ * per GPU, held until the process ends; every call on a GPU shares it, so
+ * calls that may overlap on one GPU (other streams, other threads) race and
+ * must be serialised by the caller.  A call whose partials would exceed
+ * 16 MiB (lla_workspace_bytes(.., LLA_OP_DECODE, ..) - 256 bytes, when above
+ * 256) returns LLA_ERR_WORKSPACE before anything is enqueued.  The call never
+ * allocates or frees memory; the first call on a device looks up the array's
+ * address once. */
+int32_t lla_decode_attn_noalloc(const lla_dims *dims, const lla_codec *codec, const lla_cache *cache,
+                                const float *rope_table, int32_t rope_len, int32_t layer, int32_t loop,
+                                const void *q, const int32_t *q_pos, const int32_t *ctx_len,
+                                int32_t max_ctx, float scale, void *out, int32_t *err, hipStream_t stream);
+
 /* Decode attention with token eviction composed with LLA ([CR] 四:结果 item 10,
  * Table 9: a 4-token attention sink plus a 256-token window; item 9: 1024
  * retained tokens of the 21.3x cache take 36 KiB x 1024).  Of the ctx_len[b]

@@ -200,11 +200,46 @@ int window_plan_ctx(int max_ctx, int n_keep) {
   return t < max_ctx ? (int)t : max_ctx;
 }
 
+// ---- scratch of the allocation-free decode (lla_decode_attn_noalloc) ----
+// The split partials of that entry point live in this array, one copy per
+// device, held until the process ends.  Host code never passes the array's
+// name to a kernel (on the host it only stands in for the symbol): it uses the
+// device address that hipGetSymbolAddress returns, looked up once per device
+// on the first call made with that device current.
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+hipError_t scratch_address(float **out) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void *> addr[kMaxDevices];
+  static std::mutex mu;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void *p = addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(mu);
+    p = addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = (float *)p;
+  return hipSuccess;
+}
+
+// noalloc_err: non-null selects the allocation-free form: the error word is
+// that device int32 and the split partials go to the per-device scratch array
+// (ws and ws_bytes are ignored).
 int32_t attn_call(const lla_dims *d, const lla_codec *c, const lla_cache *k, const float *rope,
                   int32_t rope_len, int32_t layer, int32_t loop, const void *q,
                   const int32_t *q_pos, const int32_t *ctx_len, const int32_t *p0, int32_t n_q,
                   int32_t prefill, int32_t max_ctx, float scale, void *out, void *ws,
-                  size_t ws_bytes, hipStream_t stream, int evict = 0, int n_sink = 0, int window = 0) {
+                  size_t ws_bytes, hipStream_t stream, int evict = 0, int n_sink = 0, int window = 0,
+                  int32_t *noalloc_err = nullptr) {
   if (!dims_valid(d)) return fail(LLA_ERR_INVALID_ARG, "invalid lla_dims");
   if (!c || !k) return fail(LLA_ERR_INVALID_ARG, "null codec or cache");
   if (!c->mu_k || !c->mu_v || !c->w_up_k || !c->w_up_v)
@@ -235,7 +270,18 @@ int32_t attn_call(const lla_dims *d, const lla_codec *c, const lla_cache *k, con
   if (!plan_attn(d, rows > 0 ? rows : 1, evict ? window_plan_ctx(max_ctx, n_sink + window) : max_ctx, &p,
                  prefill != 0))
     return fail(LLA_ERR_UNSUPPORTED, "no attention kernel built for this (dtype, d_head, r_k, r_v)");
-  if (!ws || ws_bytes < p.bytes) return fail(LLA_ERR_WORKSPACE, "workspace missing or too small");
+  if (noalloc_err) {
+    const size_t need = p.splits > 1 ? p.bytes - p.partials_off : 0;
+    if (need > kNoAllocScratchBytes) {
+      char msg[192];
+      snprintf(msg, sizeof msg,
+               "split partials of %zu bytes exceed the %zu-byte scratch of the allocation-free decode", need,
+               kNoAllocScratchBytes);
+      return fail(LLA_ERR_WORKSPACE, msg);
+    }
+  } else if (!ws || ws_bytes < p.bytes) {
+    return fail(LLA_ERR_WORKSPACE, "workspace missing or too small");
+  }
   if (rows == 0) return LLA_OK;
 
   AttnArgs a = {};
@@ -266,8 +312,17 @@ int32_t attn_call(const lla_dims *d, const lla_codec *c, const lla_cache *k, con
   a.window = window;
   const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)d->d_head);
   a.qscale = sc * 1.4426950408889634f;
-  a.err = (int *)ws;
-  a.partials = (float *)((char *)ws + p.partials_off);
+  if (noalloc_err) {
+    const hipError_t e = scratch_address(&a.partials);
+    if (e != hipSuccess) {
+      g_last_error = std::string("no scratch address on this device: ") + hipGetErrorString(e);
+      return LLA_ERR_LAUNCH;
+    }
+    a.err = noalloc_err;
+  } else {
+    a.err = (int *)ws;
+    a.partials = (float *)((char *)ws + p.partials_off);
+  }
   if (p.prefill) return check_launch(launch_prefill(d->d_head, d->r_k, d->r_v, a, stream));
   const int32_t rc = check_launch(p.two_d ? launch_decode2d(d->d_head, d->r_k, d->r_v, a, stream)
                                           : launch_decode(d->dtype, d->d_head, d->r_k, d->r_v, a, stream));
@@ -443,6 +498,15 @@ int32_t lla_decode_attn(const lla_dims *d, const lla_codec *c, const lla_cache *
                         hipStream_t stream) {
   return attn_call(d, c, k, rope, rope_len, layer, loop, q, q_pos, ctx_len, nullptr, 1, 0,
                    max_ctx, scale, out, ws, ws_bytes, stream);
+}
+
+int32_t lla_decode_attn_noalloc(const lla_dims *d, const lla_codec *c, const lla_cache *k,
+                                const float *rope, int32_t rope_len, int32_t layer, int32_t loop,
+                                const void *q, const int32_t *q_pos, const int32_t *ctx_len,
+                                int32_t max_ctx, float scale, void *out, int32_t *err, hipStream_t stream) {
+  if (!err) return fail(LLA_ERR_INVALID_ARG, "null device error word");
+  return attn_call(d, c, k, rope, rope_len, layer, loop, q, q_pos, ctx_len, nullptr, 1, 0, max_ctx, scale,
+                   out, nullptr, 0, stream, 0, 0, 0, err);
 }
 
 int32_t lla_decode_window_attn(const lla_dims *d, const lla_codec *c, const lla_cache *k,

@@ -26,7 +26,7 @@ DEVERR_CTX, DEVERR_PAGE, DEVERR_APPEND = 1, 2, 4
 EXPORTS = ["lla_rope_table", "lla_workspace_bytes", "lla_encode_append", "lla_decode_attn",
            "lla_prefill_attn", "lla_reconstruct_kv", "lla_full_decode_attn", "lla_rope_key_append",
            "lla_decoupled_decode_attn", "lla_decode_window_attn", "lla_cache_scalars", "lla_supported", "lla_status_string",
-           "lla_last_error", "lla_attn_plan", "lla_window_pages"]
+           "lla_last_error", "lla_attn_plan", "lla_window_pages", "lla_decode_attn_noalloc"]
 
 
 class LlaError(RuntimeError):
@@ -78,6 +78,7 @@ def load() -> ctypes.CDLL:
     lib.lla_full_decode_attn.argtypes = [pd, pk, P, P, P, I, P, P, P, I, F, P, P, S, P]
     lib.lla_rope_key_append.argtypes = [pd, pk, I, P, P, I, P, P, I, I, I, P, S, P]
     lib.lla_decoupled_decode_attn.argtypes = [pd, pc, pk, I, P, P, I, I, I, P, P, P, I, F, P, P, S, P]
+    lib.lla_decode_attn_noalloc.argtypes = [pd, pc, pk, P, I, I, I, P, P, P, I, F, P, P, P]
     lib.lla_decode_window_attn.argtypes = [pd, pc, pk, P, I, I, I, P, P, P, I, I, I, F, P, P, S, P]
     lib.lla_cache_scalars.argtypes = [pd, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
     lib.lla_supported.argtypes = [pd, I]
@@ -213,6 +214,18 @@ def decode_attn(dims: Dims, codec: Codec, cache: Cache, rope: torch.Tensor, laye
                                   _ptr(rope), rope.shape[0], layer, loop, _ptr(q), _ptr(q_pos),
                                   _ptr(ctx_len), max_ctx, scale, _ptr(out), _ptr(ws), ws.numel(),
                                   _stream(stream)))
+
+
+def decode_attn_noalloc(dims: Dims, codec: Codec, cache: Cache, rope: torch.Tensor, layer: int, loop: int,
+                        q, q_pos, ctx_len, max_ctx: int, out, err: torch.Tensor, scale: float = 0.0,
+                        stream=None) -> None:
+    """lla_decode_attn_noalloc: no workspace; err is a device int32 error word."""
+    if err.dtype != torch.int32 or err.numel() < 1:
+        raise ValueError("err must be a device int32 tensor")
+    _check(load().lla_decode_attn_noalloc(ctypes.byref(dims), ctypes.byref(codec), ctypes.byref(cache),
+                                          _ptr(rope), rope.shape[0], layer, loop, _ptr(q), _ptr(q_pos),
+                                          _ptr(ctx_len), max_ctx, scale, _ptr(out), _ptr(err),
+                                          _stream(stream)))
 
 
 def decode_window_attn(dims: Dims, codec: Codec, cache: Cache, rope: torch.Tensor, layer: int, loop: int,
