@@ -94,9 +94,17 @@ def calibrate_copy(gib: float) -> None:
                       "bytes_written_per_launch": 4 * n, "launches": 3}), flush=True)
 
 
+def spread(ms) -> dict:
+    """Median, p10 and p90 of per-launch times (ms) and how many there were."""
+    a = np.asarray(ms, dtype=np.float64)
+    return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
+            "p90": float(np.percentile(a, 90)), "n": int(a.size)}
+
+
 def cpu_baseline(w, codec_h, pt_h, layer, loop, target_s):
     """Time the fp64 oracle on a bounded sample of the same call: whole
-    sequences (all heads, full context) of one (layer, loop)."""
+    sequences (all heads, full context) of one (layer, loop), with every host
+    thread it may use (OpenMP over (sequence, head)) and with one thread."""
     import oracle
     from looped_transformer_latent_amd import workloads as wl
 
@@ -113,28 +121,50 @@ def cpu_baseline(w, codec_h, pt_h, layer, loop, target_s):
     kr = wl.pool_pages_host(w, "kr", layer, pages)[None] if w.d_rope else None
     local = np.arange(len(pages), dtype=np.int32).reshape(n_data, -1)
 
-    def run(n_seq):
+    def run(n_seq, threads):
         pt_local = np.ascontiguousarray(local[np.arange(n_seq) % n_data])
         q = wl.q_host(w, n_seq)
         ctx = np.full(n_seq, w.ctx, np.int32)
         t0 = time.perf_counter()
         if w.d_rope:
-            _, rc = oracle.decoupled_decode(one, codec1, kp, vp, kr, pt_local, 0, loop, q, ctx - 1, ctx, w.d_rope)
+            _, rc = oracle.decoupled_decode(one, codec1, kp, vp, kr, pt_local, 0, loop, q, ctx - 1, ctx, w.d_rope,
+                                            threads=threads)
         else:
-            _, rc = oracle.decode(one, codec1, kp, vp, pt_local, 0, loop, q, ctx - 1, ctx)
+            _, rc = oracle.decode(one, codec1, kp, vp, pt_local, 0, loop, q, ctx - 1, ctx, threads=threads)
         dt = time.perf_counter() - t0
         assert rc == 0
         return dt
 
-    threads = oracle.max_threads(0)
-    t1 = run(1)
+    threads = oracle.max_threads(0)       # the OpenMP default of this host (before any override)
+    t1 = run(1, threads)
     n = int(max(1, min(w.batch, round(target_s / max(t1, 1e-3)))))
-    dt = run(n) if n > 1 else t1
-    reads = n * w.ctx
-    return {"value": reads / dt, "unit": "cached-token reads/s", "cores": threads, "kind": "oracle",
+    dt = run(n, threads) if n > 1 else t1
+    # one thread: whole sequences again, about a quarter of the time budget
+    s1 = run(1, 1)
+    n1 = int(max(1, min(w.batch, round(target_s / 4 / max(s1, 1e-3)))))
+    dt1 = run(n1, 1) if n1 > 1 else s1
+    oracle.max_threads(threads)           # restore the default for later oracle calls
+    return {"value": n * w.ctx / dt, "unit": "cached-token reads/s", "cores": threads, "kind": "oracle",
             "sample": f"{n} of {w.batch} sequences x full context {w.ctx} x all {w.H} heads, "
                       f"one (layer, loop) call (latent data of {n_data} sequences, reused); "
-                      f"fp64 C oracle, OpenMP over (sequence, head); {dt:.1f} s"}
+                      f"fp64 C oracle, OpenMP over (sequence, head), {threads} threads; {dt:.1f} s",
+            "single_thread": {"value": n1 * w.ctx / dt1, "cores": 1,
+                              "sample": f"{n1} sequences of the same call, 1 thread; {dt1:.1f} s"},
+            "host_cpu": host_cpu()}
+
+
+def host_cpu() -> str:
+    """CPU model of this host and the logical CPUs it reports."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return f"{model}; {os.cpu_count()} logical CPUs visible"
 
 
 def cpu_prefill_baseline(w, codec_h, pt_h, layer, loop, n_new, target_s):
@@ -206,7 +236,7 @@ def bench_window(w, D, codec, cache, rope, calls, q, q_pos, ctx, codec_h, pt_h, 
     nbytes = w.batch * kept * w.read_bytes()
     gbs = nbytes / (avg / 1e3) / 1e9
     res = {"kernel": "decode_g_kernel (eviction)", "n_sink": n_sink, "window": window, "calls": len(calls),
-           "avg_ms": avg, "value": w.batch * kept / (avg / 1e3), "unit": "retained-token reads/s",
+           "avg_ms": avg, "call_ms": spread(ms), "value": w.batch * kept / (avg / 1e3), "unit": "retained-token reads/s",
            "retained_latent_bytes_per_sequence_all_layers": kept * w.read_bytes() * w.D,
            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": gbs / HBM_PEAK_GBS,
@@ -272,7 +302,8 @@ def cpu_encode_baseline(w, codec_h, layer, target_s):
     n = int(max(16, min(1 << 16, round(16 * target_s / max(t1, 1e-4)))))
     dt = run(n)
     return {"value": n / dt, "unit": "appended token-layers/s (all heads)", "cores": 1, "kind": "oracle",
-            "sample": f"{n} tokens of one layer, all {w.H} heads; fp64 C oracle (single thread); {dt:.1f} s"}
+            "sample": f"{n} tokens of one layer, all {w.H} heads; fp64 C oracle, whose encode is a serial "
+                      f"loop (1 thread is all it uses); {dt:.1f} s"}
 
 
 def bench_prefill(w, D, codec, cache, rope, calls, n_new, dt_t, p0, stream):
@@ -314,7 +345,7 @@ def bench_prefill(w, D, codec, cache, rope, calls, n_new, dt_t, p0, stream):
                              + n_new * 2.0 * w.r_v * w.d_head)
     tflops = flops / (avg / 1e3) / 1e12
     return {"kernel": "prefill_kernel", "calls": len(calls), "queries_per_call": w.batch * n_new,
-            "positions": [w.ctx - n_new, w.ctx - 1], "avg_ms": avg,
+            "positions": [w.ctx - n_new, w.ctx - 1], "avg_ms": avg, "call_ms": spread(ms),
             "value": w.batch * n_new / (avg / 1e3), "unit": "prefill query tokens/s (all heads, one (loop, layer))",
             "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
@@ -506,7 +537,8 @@ def main():
         roof = {"kernel": kname, "bound": "hbm", "achieved": achieved,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                 "traffic": profiled_traffic(w.name, kname, ABSORBED_SOURCES if decoupled else DECODE_SOURCES), "traffic_unit": "HBM bytes per launch (rocprofv3)",
-                "algorithmic_bytes_per_launch": bytes_per_launch, "avg_launch_ms": kern_avg_ms}
+                "algorithmic_bytes_per_launch": bytes_per_launch, "avg_launch_ms": kern_avg_ms,
+                "launch_ms": spread(kern_ms)}
     else:
         # LLA-2D is bound by the matrix cores: per token and head, rebuilding K is
         # 2 d r_k FLOP and the latent-space value sum 2 r_v FLOP
@@ -517,7 +549,8 @@ def main():
                 "traffic": profiled_traffic(w.name, "decode_2d_kernel", D2D_SOURCES),
                 "traffic_unit": "HBM bytes per launch (rocprofv3)", "algorithmic_flops_per_launch": flops,
                 "algorithmic_bytes_per_launch": bytes_per_launch,
-                "hbm_gbs": bytes_per_launch / (kern_avg_ms / 1e3) / 1e9, "avg_launch_ms": kern_avg_ms}
+                "hbm_gbs": bytes_per_launch / (kern_avg_ms / 1e3) / 1e9, "avg_launch_ms": kern_avg_ms,
+                "launch_ms": spread(kern_ms)}
     result = {
         "metric": "latent-cache decode attention: cached-token reads/s and achieved HBM GB/s",
         "value": value,
@@ -548,7 +581,7 @@ def main():
                  + w.D * w.groups * width * (w.r_k + w.r_v) * w.esize)
     enc_flops = 2 * tok * w.groups * width * (w.r_k + w.r_v)
     result["encode"] = {"kernel": "encode_mfma_kernel", "tokens_per_layer": w.batch * n_new,
-                        "layers": w.D, "avg_ms": enc_avg,
+                        "layers": w.D, "avg_ms": enc_avg, "call_ms": spread(enc_ms),
                         "value": tok / (enc_avg / 1e3), "unit": "appended token-layers/s (all heads)",
                         "algorithmic_bytes": enc_bytes,
                         "achieved_gbs": enc_bytes / (enc_avg / 1e3) / 1e9,
