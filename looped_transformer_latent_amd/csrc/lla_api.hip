@@ -62,11 +62,11 @@ bool plan_attn_2d(const lla_dims *d, long long rows, int max_ctx, AttnPlan *p) {
   long long s = (1024 + base - 1) / base;
   const long long smax = (pages + 7) / 8;
   if (s > smax) s = smax;
-  const long long smin = (pages + kMaxPagesPerSplit - 1) / kMaxPagesPerSplit;
+  const long long smin = (pages + kMaxPages2d - 1) / kMaxPages2d;
   if (s < smin) s = smin;
   if (s < 1) s = 1;
   int pps = (int)((pages + s - 1) / s);
-  pps += pps & 1;  // whole 32-token blocks
+  pps += pps & 1;  // whole 32-token blocks (kMaxPages2d is even)
   p->pages_per_split = pps;
   p->splits = (pages + pps - 1) / pps;
   if (p->splits < 1) p->splits = 1;

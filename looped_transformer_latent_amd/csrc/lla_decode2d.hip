@@ -19,8 +19,9 @@
 //    result in registers as the A-operands of v_mfma_f32_32x32x16_bf16
 //    (alpha / beta as hi + lo bf16 in one extra K-step).
 //  * Tokens go in blocks of 32 (two 16-token pages).  The block's c_k, c_v and
-//    RoPE rows are copied global -> LDS with direct-to-LDS loads (no register
-//    staging) into three buffers: the copy of block b+2 is in flight while the
+//    RoPE rows are copied global -> LDS with buffer loads straight into LDS (no
+//    register staging; whole rows per instruction, one shared lane offset as
+//    the only vector operand) into three buffers: the copy of block b+2 is in flight while the
 //    K-side products of block b+1 share a barrier interval with the softmax of
 //    block b, and the value sum of block b with the cos / sin weighting of
 //    block b+1 (two barriers per block).
@@ -45,6 +46,19 @@ typedef uint32_t u32x2 __attribute__((__vector_size__(2 * sizeof(uint32_t))));
 
 #define LLA_LDS(p) ((__attribute__((address_space(3))) void *)(p))
 
+// Word 3 of a raw buffer descriptor on gfx9-family parts: 32-bit data format,
+// no swizzle, no index stride (untyped loads by byte offset).
+constexpr int kBufferWord3 = 0x00020000;
+
+// 16 bytes per active lane from base + soff + voff into LDS at lds + 16 lane,
+// as a buffer load of the `bytes`-long range at base (reads past it give zeros).
+// base, bytes and soff are uniform; only voff is per lane.
+__device__ __forceinline__ void buffer_to_lds16(const char *base, uint32_t bytes, void *lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)bytes, kBufferWord3), LLA_LDS(lds), 16, voff,
+      soff, 0, 0);
+}
+
 // Barrier that first waits for this wave's LDS writes and for all but its VM
 // most recent vector-memory operations (direct-to-LDS copies still in flight).
 template <int VM>
@@ -56,11 +70,16 @@ __device__ __forceinline__ void barrier_vm() {
   asm volatile("" ::: "memory");
 }
 
+// One 32-token block in LDS.  c_k and the RoPE rows keep their memory layout,
+// one token per row, with each row padded by 16 bytes: a copy instruction
+// then reads one whole row (512 contiguous bytes), and the operand reads (16
+// lanes of consecutive tokens at one 16-byte piece) hit 16 distinct bank
+// groups at immediate offsets.
 template <int DH, int RK, int RV>
 struct Tile2d {
-  u32x4 ck[RK / 8 * 32];    // [r chunk of 8][token 32]: 16-byte MFMA B-operand pieces
-  u32x4 cv[32 * RV / 8];    // [token 32][r_v]: row-major latent rows
-  f32x4 trig[DH / 4 * 32];  // [pair chunk of 2][token 32]: (cos, sin) x 2, fp32
+  u32x4 ck[32][RK / 8 + 1];    // [token][r chunk of 8], padded row
+  u32x4 cv[32 * RV / 8];       // [token 32][r_v]: row-major latent rows
+  f32x4 trig[32][DH / 4 + 1];  // [token][pair chunk of 2]: (cos, sin) x 2, fp32, padded row
 };
 
 template <int DH, int RK, int RV>
@@ -71,19 +90,17 @@ __global__ __launch_bounds__(512) void decode_2d_kernel(AttnArgs a) {
   constexpr int PW = HALF / 2;   // pairs per wave
   constexpr int RTW = PW / 16;   // 32-row tiles per wave (X and Y rows of 16 pairs each)
   constexpr int KS = RK / 16;    // K-steps of 16 (8 per lane half)
-  constexpr int CKQ = RK / 16;   // 1 KiB direct loads per tile: c_k
-  constexpr int CVQ = RV / 16;   //                               c_v
-  constexpr int TRQ = DH / 8;    //                               RoPE rows
+  constexpr int CVQ = RV / 16;   // 1 KiB direct loads per tile: c_v
   constexpr int VR = RV / NW;    // V columns per wave (all 4 heads)
   constexpr int VT = VR / 16;    // V MFMA tiles per wave (16x16x32)
   static_assert(PW % 16 == 0 && RK % 128 == 0 && VR == 32 && VT == 2, "shape");
-  static_assert(CKQ % NW == 0 && CVQ % NW == 0 && TRQ % NW == 0, "tile split");
+  static_assert(CVQ % NW == 0 && 32 % NW == 0 && RK / 8 <= 64 && DH / 4 <= 64 && RV == 256, "tile split");
 
   __shared__ Tile2d<DH, RK, RV> tile0, tile1, tile2;
   __shared__ __attribute__((aligned(16))) uint16_t s_p[16][32];  // bf16 weights; rows >= 4 stay 0
   __shared__ float s_alpha[16];                                   // rescale per head; >= 4 stay 1
   __shared__ float s_part[NH][2][32];                             // half-scores per head
-  __shared__ int s_pt[2048 + 2];
+  __shared__ int s_pt[kMaxPages2d + 2];
   __shared__ float s_red[NH][RV + 2];  // epilogue: normalised latent sums per head
   __shared__ float s_z[NH];
 
@@ -186,33 +203,43 @@ __global__ __launch_bounds__(512) void decode_2d_kernel(AttnArgs a) {
 
   // ---- direct-to-LDS loads of one 32-token block ----
   const char *rope_b = (const char *)a.rope;
+  // Every copy instruction reads whole rows as a buffer load into LDS: a
+  // descriptor for the page (or the block's RoPE rows) in scalar registers, the
+  // row offset as a scalar, and 16 bytes per lane as the only vector operand.
+  // Offsets past a descriptor's size read zeros.  Waves 0 .. NW/2 - 1 copy
+  // the block's first page, the others its second.
+  const int lane16 = 16 * lane;
   auto issue = [&](int blk, Tile2d<DH, RK, RV> &T) {
     const int j0 = j_lo + 32 * blk;
-    const int lpa = min(j0 / kPage, lp1 - 1) - lp0, lpb = min(j0 / kPage + 1, lp1 - 1) - lp0;
-    const long long pa = s_pt[lpa], pb = s_pt[lpb];
-    const char *kb = a.k_pool + (t < 16 ? pa : pb) * a.pool_page_stride_k * 2;
+    const int lp = min(j0 / kPage + (w >= NW / 2 ? 1 : 0), lp1 - 1) - lp0;
+    const long long pg = __builtin_amdgcn_readfirstlane(s_pt[lp]);
+    // c_k: one row (token) per half-wave instruction
+    constexpr int CPT = RK / 8;  // 16-byte pieces per c_k row
+    const char *kpg = a.k_pool + pg * a.pool_page_stride_k * 2;
 #pragma unroll
-    for (int i = 0; i < CKQ / NW; ++i) {
-      const int q = w * (CKQ / NW) + i;
-      const int c = 2 * q + kh;  // lane (kh, t) -> chunk c, token t
-      __builtin_amdgcn_global_load_lds((const void *)(kb + ((t & 15) * RK + 8 * c) * 2),
-                                       LLA_LDS(&T.ck[q * 64]), 16, 0, 0);
+    for (int i = 0; i < 32 / NW; ++i) {
+      const int tok = w * (32 / NW) + i;
+      if (lane < CPT)
+        buffer_to_lds16(kpg, kPage * RK * 2, &T.ck[tok][0], lane16, (tok & 15) * RK * 2);
     }
+    // c_v: two rows per instruction
+    const char *vpg = a.v_pool + pg * a.pool_page_stride_v * 2;
 #pragma unroll
     for (int i = 0; i < CVQ / NW; ++i) {
       const int q = w * (CVQ / NW) + i;
-      const int tok = (q * 64 + lane) / (RV / 8), c = (q * 64 + lane) % (RV / 8);
-      const char *vb = a.v_pool + (tok < 16 ? pa : pb) * a.pool_page_stride_v * 2;
-      __builtin_amdgcn_global_load_lds((const void *)(vb + ((tok & 15) * RV + 8 * c) * 2),
-                                       LLA_LDS(&T.cv[q * 64]), 16, 0, 0);
+      buffer_to_lds16(vpg, kPage * RV * 2, &T.cv[q * 64], lane16, ((2 * q) & 15) * RV * 2);
     }
-    const int pos = min(j0 + t, a.rope_len - 1);
+    // RoPE rows of the block's positions: one row per half-wave instruction;
+    // rows past the table read zeros (their tokens lie past the context)
+    constexpr int TPT = DH / 4;  // 16-byte pieces per RoPE row
+    const int jr = min(j0, a.rope_len - 1);
+    const char *rrow = rope_b + (long long)jr * (DH * 4);
+    const uint32_t rbytes = (uint32_t)(a.rope_len - jr) * (DH * 4);
 #pragma unroll
-    for (int i = 0; i < TRQ / NW; ++i) {
-      const int q = w * (TRQ / NW) + i;
-      const int c = 2 * q + kh;
-      __builtin_amdgcn_global_load_lds((const void *)(rope_b + (long long)pos * (DH * 4) + c * 16),
-                                       LLA_LDS(&T.trig[q * 64]), 16, 0, 0);
+    for (int i = 0; i < 32 / NW; ++i) {
+      const int tok = w * (32 / NW) + i;
+      if (lane < TPT)
+        buffer_to_lds16(rrow, rbytes, &T.trig[tok][0], lane16, (j0 - jr + tok) * (DH * 4));
     }
   };
 
@@ -231,15 +258,20 @@ __global__ __launch_bounds__(512) void decode_2d_kernel(AttnArgs a) {
   auto kside = [&](Tile2d<DH, RK, RV> &T, f32x16 (&acc)[RTW]) {
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) acc[rt] = f32x16{};
-    u32x4 bk[3];
-    bk[0] = T.ck[(kh * KS + 0) * 32 + t];
-    bk[1] = T.ck[(kh * KS + 1) * 32 + t];
+    // B-operand pieces PF K-steps ahead; the scheduling fence keeps each read
+    // above the products it feeds (the compiler would otherwise sink it to its use)
+    constexpr int PF = 4;
+    u32x4 bk[PF + 1];
+    auto piece = [&](int c) { return T.ck[t][c]; };  // r chunk c of token t
+#pragma unroll
+    for (int p = 0; p < PF; ++p) bk[p] = piece(kh * KS + p);
 #pragma unroll
     for (int s8 = 0; s8 < KS; ++s8) {
-      if (s8 + 2 < KS) bk[(s8 + 2) % 3] = T.ck[(kh * KS + s8 + 2) * 32 + t];
+      if (s8 + PF < KS) bk[(s8 + PF) % (PF + 1)] = piece(kh * KS + s8 + PF);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int rt = 0; rt < RTW; ++rt)
-        acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[rt][s8], as_bf16x8(bk[s8 % 3]), acc[rt], 0, 0, 0);
+        acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[rt][s8], as_bf16x8(bk[s8 % (PF + 1)]), acc[rt], 0, 0, 0);
     }
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt)
@@ -253,7 +285,7 @@ __global__ __launch_bounds__(512) void decode_2d_kernel(AttnArgs a) {
       const int gt = RTW * rh + rt;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const f32x4 tr = T.trig[(8 * gt + 4 * kh + q) * 32 + t];
+        const f32x4 tr = T.trig[t][8 * gt + 4 * kh + q];
         sp = fmaf(tr[0], acc[rt][4 * q + 0], sp);
         sp = fmaf(tr[1], acc[rt][4 * q + 1], sp);
         sp = fmaf(tr[2], acc[rt][4 * q + 2], sp);
@@ -318,7 +350,7 @@ __global__ __launch_bounds__(512) void decode_2d_kernel(AttnArgs a) {
     }
   };
   // this wave's copy instructions per block (all of them count on vmcnt)
-  constexpr int NCOPY = CKQ / NW + CVQ / NW + TRQ / NW;
+  constexpr int NCOPY = 2 * (32 / NW) + CVQ / NW;
   auto step = [&](int blk, Tile2d<DH, RK, RV> &Tb, Tile2d<DH, RK, RV> &Tn, Tile2d<DH, RK, RV> &Tnn) {
     issue(min(blk + 2, nblk - 1), Tnn);  // past the end: a harmless re-copy of the last block
     __builtin_amdgcn_sched_barrier(0);
@@ -422,7 +454,7 @@ bool decode2d_supported(int dtype, int d_head, int r_k, int r_v) {
 
 hipError_t launch_decode2d(int d_head, int r_k, int r_v, const AttnArgs &a, hipStream_t stream) {
   if (a.waves != 8 || a.heads_per_wave != 1) return hipErrorInvalidConfiguration;
-  if (a.pages_per_split > 2048 || a.pages_per_split % 2) return hipErrorInvalidConfiguration;
+  if (a.pages_per_split > kMaxPages2d || a.pages_per_split % 2) return hipErrorInvalidConfiguration;
   const long long units = (long long)a.rows * a.splits;
   const long long grid = (units + 7) / 8 * 8 * a.head_groups;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;

@@ -17,6 +17,7 @@ constexpr int kPage = 16;          // tokens per cache page
 #endif
 constexpr int kDecodeRing = LLA_DECODE_LOOK + 2;  // decode page-ring slots = pages per trip
 constexpr int kHeaderBytes = 256;  // workspace header: int32 error word at byte 0
+constexpr int kMaxPages2d = 1024;  // LLA-2D decode: page-table entries a workgroup stages in LDS
 
 // Arguments of one attention launch (decode or prefill).  All pointers are
 // device pointers; codec and pool pointers are already offset to (layer, loop).

@@ -309,3 +309,13 @@ def test_window_plan_sink_only_case_has_an_empty_split():
         lla.window_pages(10, 0, 0)
     with pytest.raises(lla.LlaError):
         lla.attn_plan(_dims(d_head=96), lla.OP_DECODE, 1, 100)
+
+
+def test_lla2d_plan_stays_within_the_staged_page_table():
+    """LLA-2D workgroups stage at most 1024 page-table entries: long contexts at
+    large batch get several splits of whole 32-token blocks (even page counts)."""
+    d = _dims(T=8, D=4, H=32, d_head=128, r_k=256, r_v=256, variant=lla.TWO_D)
+    for batch, ctx in ((128, 16384), (128, 40000), (1, 1 << 20), (512, 2049)):
+        splits, pps = lla.attn_plan(d, lla.OP_DECODE, batch, ctx)
+        assert pps <= 1024 and pps % 2 == 0 and splits * pps * 16 >= ctx, (batch, ctx, splits, pps)
+    assert lla.attn_plan(d, lla.OP_DECODE, 128, 40000)[0] >= 3

@@ -68,6 +68,24 @@ def test_lla2d_ragged_contexts_shuffled_pages(shape):
         check(m, codec, kp, vp, pt, q, ctx, layer, loop, f"2D H={H} d={d} r={rk}/{rv}")
 
 
+def test_lla2d_context_beyond_one_split_stage():
+    """One row of 20000 tokens (1250 pages): more pages than a workgroup stages
+    (1024), so the row is cut into several splits of whole 32-token blocks and
+    merged; plus a short second row.  The oracle runs the whole context."""
+    H, d, rk, rv = 8, 64, 128, 256
+    m = dims(2, 1, H, d, rk, rv, TWO_D, BF16)
+    ctx = np.array([20000, 77])
+    B, pps = len(ctx), 1250
+    codec = random_codec(m, seed=5102, ortho_down=False)
+    kp, vp = random_pools(m, B * pps, seed=5103)
+    pt = gen.shuffled_page_table(5104, B, pps)
+    q = gen.normal(5105, 1, (B, H, d))
+    D = lla.dims_from_dict(m)
+    splits, per = lla.attn_plan(D, lla.OP_DECODE, B, int(ctx.max()))
+    assert splits >= 2 and per <= 1024 and per % 2 == 0
+    check(m, codec, kp, vp, pt, q, ctx, 0, 1, "2D 20000 tokens")
+
+
 def test_lla2d_unused_slots_may_hold_nan_and_page_table_invariance():
     m = dims(2, 1, 8, 64, 128, 256, TWO_D, BF16)
     ctx = np.array([45, 70])
