@@ -176,11 +176,15 @@ bool plan_full(const lla_dims *d, long long rows, int max_ctx, AttnPlan *p) {
   return true;
 }
 
+// Encode workspace: header, mu W_down [n_layers][groups][r_k + r_v], its
+// per-range partial sums, and (for launches with few tiles over a wide input)
+// the fp32 partial products of the split over the width.
 size_t encode_ws_bytes(const lla_dims *d, int n_layers) {
   const int groups = d->variant == LLA_PER_HEAD ? d->H : 1;
   const int width = d->variant == LLA_PER_HEAD ? d->T * d->d_head : d->T * d->H * d->d_head;
   const size_t one = sizeof(float) * (size_t)n_layers * groups * (d->r_k + d->r_v);
-  return align256(kHeaderBytes + one) + align256(one * encode_muw_parts(width));
+  return align256(kHeaderBytes + one) + align256(one * encode_muw_parts(width)) +
+         align256(encode_kpart_bytes(width, groups, n_layers, d->r_k, d->r_v));
 }
 
 int32_t check_launch(hipError_t e) {
@@ -488,6 +492,11 @@ int32_t lla_encode_append(const lla_dims *d, const lla_codec *c, const lla_cache
                                                                     (d->r_k + d->r_v)));
   a.muw_stride = d->r_k + d->r_v;
   a.muw_v_off = d->r_k;
+  {
+    const size_t one = sizeof(float) * (size_t)n_layers * groups * (d->r_k + d->r_v);
+    a.kpart = (float *)((char *)ws + align256(kHeaderBytes + one) + align256(one * a.muw_parts));
+    a.kpart_bytes = encode_kpart_bytes(width, groups, n_layers, d->r_k, d->r_v);
+  }
   return check_launch(launch_encode(d->dtype, d->r_k, d->r_v, a, stream));
 }
 

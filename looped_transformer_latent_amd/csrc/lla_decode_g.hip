@@ -44,16 +44,30 @@ __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
          ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
 }
 
-// LDS layout of decode_g_kernel: [RoPE chunk buffers: 2 x TSB x 16 B][page-table
-// entries of the split][epilogue: NW x HPW x (RV + 2) floats][W_up,k stage:
-// NW x HPW x DH x RK bf16].  Offset of the last part (16-byte aligned).
+// LDS layout of decode_g_kernel: the RoPE chunk buffers [2][TSB] x 16 B at 0;
+// the split's page-table entries and the epilogue's [NW][HPW][RV + 2] floats
+// after them; the W_up,k stage [NW][HPW][DH][RK] bf16 that the prologue folds
+// from (and that wide latents reuse for the per-page transposition).  For
+// r_k <= 32 the stage is dead once the fold is done, so it shares its bytes
+// with the RoPE buffers: a workgroup then takes under half of a CU's LDS (the
+// register count decides how many run per CU).
 template <int DH, int RK, int RV, int HPW, int NW>
-__host__ __device__ constexpr size_t w_stage_offset(int pages_per_split) {
-  constexpr int TS = (LLA_DECODE_LOOK + 2) * kPage * (DH / 8);
-  constexpr int TSB = (TS + 64 * NW - 1) / (64 * NW) * (64 * NW);
-  return (2 * (size_t)TSB * 16 + sizeof(int) * (size_t)pages_per_split +
-          sizeof(float) * NW * HPW * (RV + 2) + 15) / 16 * 16;
-}
+struct GLayout {
+  static constexpr int TS = (LLA_DECODE_LOOK + 2) * kPage * (DH / 8);
+  static constexpr int TSB = (TS + 64 * NW - 1) / (64 * NW) * (64 * NW);
+  static constexpr size_t trig_bytes = 2 * (size_t)TSB * 16;
+  static constexpr size_t w_bytes = sizeof(uint16_t) * NW * HPW * DH * RK;
+  static constexpr size_t epi_bytes = sizeof(float) * NW * HPW * (RV + 2);
+  static constexpr bool alias = RK <= 32;
+  static constexpr size_t pt_off = alias && w_bytes > trig_bytes ? w_bytes : trig_bytes;
+  __host__ __device__ static constexpr size_t epi_off(int pps) { return pt_off + sizeof(int) * (size_t)pps; }
+  __host__ __device__ static constexpr size_t w_off(int pps) {
+    return alias ? 0 : (epi_off(pps) + epi_bytes + 15) / 16 * 16;
+  }
+  __host__ __device__ static constexpr size_t total(int pps) {
+    return alias ? epi_off(pps) + epi_bytes : w_off(pps) + w_bytes;
+  }
+};
 
 // NW = 4 runs one wave per SIMD (up to 512 registers): the shape with the
 // widest latents (r_k = 96, r_v = 160) needs them for its decoder and page ring.
@@ -123,7 +137,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 1 : 2) void decode_g_kernel(Attn
   u32x4 Fa[KS];
   float unscale[HPW];  // 2^-e per head (wave-uniform)
   {
-    uint16_t *s_w = (uint16_t *)(smem + w_stage_offset<DH, RK, RV, HPW, NW>(a.pages_per_split)) +
+    uint16_t *s_w = (uint16_t *)(smem + GLayout<DH, RK, RV, HPW, NW>::w_off(a.pages_per_split)) +
                     wave * (HPW * DH * RK);
     uint32_t mag[HPW];  // largest |bf16| bit pattern of W_up,k and mu_k (magnitude order = integer order)
 #pragma unroll
@@ -261,8 +275,9 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 1 : 2) void decode_g_kernel(Attn
   constexpr int TS = CH * kPage * SPR;  // 16-byte slots of one chunk
   constexpr int SLOTS = (TS + NTH - 1) / NTH;
   constexpr int TSB = SLOTS * NTH;
-  char *s_trig = smem;
-  int *s_pt = (int *)(smem + 2 * TSB * 16);
+  char *s_trig = smem;  // (aliases the prologue's W_up,k stage at narrow ranks)
+  int *s_pt = (int *)(smem + GLayout<DH, RK, RV, HPW, NW>::pt_off);
+  static_assert(GLayout<DH, RK, RV, HPW, NW>::TSB == TSB, "layout");
   {
     const int *pt_row = a.page_table + (long long)b * a.max_pages;
     for (int i = threadIdx.x; i < lp1 - lp0; i += blockDim.x) s_pt[i] = pt_row[logical(lp0 + i)];
@@ -343,7 +358,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 1 : 2) void decode_g_kernel(Attn
                        (j < keep_lo || j >= keep_hi);         // evicted rows of edge pages
     const int row_n = min(n, cur.last);
     if constexpr (XP) {  // address order -> compute layout, through the wave's LDS region
-      uint16_t *xb = (uint16_t *)(smem + w_stage_offset<DH, RK, RV, HPW, NW>(a.pages_per_split)) +
+      uint16_t *xb = (uint16_t *)(smem + GLayout<DH, RK, RV, HPW, NW>::w_off(a.pages_per_split)) +
                      wave * (HPW * DH * RK);
       uint16_t *xv = xb + kPage * SKP;
 #pragma unroll
@@ -464,7 +479,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 1 : 2) void decode_g_kernel(Attn
   if (errbits && threadIdx.x == 0) atomicOr(a.err, errbits);
   const bool bad = __syncthreads_or(errbits != 0);
 
-  float *sh = (float *)(s_pt + a.pages_per_split);  // [waves][HPW][RV + 2]
+  float *sh = (float *)(smem + GLayout<DH, RK, RV, HPW, NW>::epi_off(a.pages_per_split));  // [waves][HPW][RV + 2]
   float *mine = sh + (wave * HPW) * (RV + 2);
 
   if (a.splits > 1) {  // partials for the merge launch
@@ -527,8 +542,7 @@ hipError_t go_g(const AttnArgs &a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)(a.rows * a.head_groups * a.splits));
   const dim3 block((unsigned)(64 * NW));
-  const size_t shmem = w_stage_offset<DH, RK, RV, HPW, NW>(a.pages_per_split) +
-                       sizeof(uint16_t) * NW * HPW * DH * RK;
+  const size_t shmem = GLayout<DH, RK, RV, HPW, NW>::total(a.pages_per_split);
   hipLaunchKernelGGL((decode_g_kernel<DH, RK, RV, HPW, NW>), grid, block, shmem, stream, a);
   return hipGetLastError();
 }

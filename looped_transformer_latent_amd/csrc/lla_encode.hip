@@ -19,18 +19,24 @@ __device__ __forceinline__ float ldx(const char *p, long long i) {
 
 // muw[li][grp][kv ? RK + r : r] = sum_i mu[i] W_down[i][r], fp32: a constant of
 // (layer, latent group), computed once per call and shared by every token tile.
-// The rows of W_down are cut into muw_parts ranges of kMuwRows rows, summed by
-// separate workgroups (one per (range, group), layer, K|V) into muw_part; a
-// second launch adds the ranges in fixed order.  Within a range, wave w sums
-// rows w, w + 4, ... (lanes over r, coalesced rows of W_down) and the 4 wave
-// sums are added in fixed order.
+// The rows of W_down are cut into at most 64 ranges of a multiple of 64 rows,
+// summed by separate workgroups (one per (range, group), layer, K|V) into
+// muw_part; a second launch adds the ranges in fixed order.  Within a range,
+// lane l of wave w reads 8 columns (16 bytes) of row w RPI + l / P8 and then
+// every 4 RPI rows (P8 = R / 8 lanes per row, RPI = 64 / P8 rows per load
+// instruction); the lanes' sums of a column are added in fixed order.
 constexpr int kMuwRows = 64;
+constexpr int kMuwMaxParts = 64;
 
-int encode_muw_parts(int width) { return (width + kMuwRows - 1) / kMuwRows; }
+__host__ __device__ int encode_muw_rows(int width) {
+  const int blocks = (width + kMuwRows - 1) / kMuwRows;  // 64-row blocks
+  return kMuwRows * ((blocks + kMuwMaxParts - 1) / kMuwMaxParts);
+}
+int encode_muw_parts(int width) { return (width + encode_muw_rows(width) - 1) / encode_muw_rows(width); }
 
 template <bool BF>
 __global__ __launch_bounds__(256) void encode_muw_kernel(EncodeArgs a, int RK, int RV) {
-  __shared__ float part[4][256];
+  __shared__ float part[4][64][8];  // [wave][lane][8 columns]
   const int grp = blockIdx.x % a.groups, pr = blockIdx.x / a.groups;
   const int li = blockIdx.y, kv = blockIdx.z;
   const int R = kv ? RV : RK;
@@ -39,24 +45,64 @@ __global__ __launch_bounds__(256) void encode_muw_kernel(EncodeArgs a, int RK, i
   const long long gl = (long long)li * a.groups + grp;  // relative to layer0
   const char *mu = (kv ? a.mu_v : a.mu_k) + gl * a.width * esz;
   const char *wd = (kv ? a.wd_v : a.wd_k) + gl * a.width * (long long)R * esz;
-  const int i0 = pr * kMuwRows, i1 = min(i0 + kMuwRows, a.width);
+  const int rows = encode_muw_rows(a.width);
+  const int i0 = pr * rows, i1 = min(i0 + rows, a.width);
   float *dst = a.muw_part + ((long long)pr * a.n_layers * a.groups + gl) * (RK + RV) + (kv ? RK : 0);
-  for (int r0 = 0; r0 < R; r0 += 256) {
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int i = i0 + w; i < i1; i += 4) {
-      const float m = ldx<BF>(mu, i);
+  if (R % 8 || R > 512) {  // other widths: lanes over columns, wave w sums rows w, w + 4, ...
+    __shared__ float part1[4][256];
+    for (int r0 = 0; r0 < R; r0 += 256) {
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int i = i0 + w; i < i1; i += 4) {
+        const float m = ldx<BF>(mu, i);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = r0 + lane + 64 * j;
-        if (r < R) acc[j] = fmaf(m, ldx<BF>(wd, (long long)i * R + r), acc[j]);
+        for (int j = 0; j < 4; ++j) {
+          const int r = r0 + lane + 64 * j;
+          if (r < R) acc[j] = fmaf(m, ldx<BF>(wd, (long long)i * R + r), acc[j]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) part1[w][lane + 64 * j] = acc[j];
+      __syncthreads();
+      const int r = r0 + threadIdx.x;
+      if (r < R) dst[r] = ((part1[0][threadIdx.x] + part1[1][threadIdx.x]) + part1[2][threadIdx.x]) + part1[3][threadIdx.x];
+      __syncthreads();
+    }
+    return;
+  }
+  const int P8 = R / 8, RPI = 64 / P8;
+  const int ro = lane / P8, p = lane % P8;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (ro < RPI) {
+#pragma unroll 8
+    for (int i = i0 + w * RPI + ro; i < i1; i += 4 * RPI) {
+      const float m = ldx<BF>(mu, i);
+      const char *src = wd + ((long long)i * R + 8 * p) * esz;
+      if constexpr (BF) {
+        const u32x4 v = *(const u32x4 *)src;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          acc[2 * k] = fmaf(m, bf16_lo(v[k]), acc[2 * k]);
+          acc[2 * k + 1] = fmaf(m, bf16_hi(v[k]), acc[2 * k + 1]);
+        }
+      } else {
+        const f32x4 lo = *(const f32x4 *)src, hi = *(const f32x4 *)(src + 16);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          acc[k] = fmaf(m, lo[k], acc[k]);
+          acc[4 + k] = fmaf(m, hi[k], acc[4 + k]);
+        }
       }
     }
+  }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) part[w][lane + 64 * j] = acc[j];
-    __syncthreads();
-    const int r = r0 + threadIdx.x;
-    if (r < R) dst[r] = ((part[0][threadIdx.x] + part[1][threadIdx.x]) + part[2][threadIdx.x]) + part[3][threadIdx.x];
-    __syncthreads();
+  for (int k = 0; k < 8; ++k) part[w][lane][k] = acc[k];
+  __syncthreads();
+  // column r: lanes q P8 + r / 8 of every wave, added in (wave, q) order
+  for (int r = threadIdx.x; r < R; r += blockDim.x) {
+    float s = 0.f;
+    for (int ww = 0; ww < 4; ++ww)
+      for (int q = 0; q < RPI; ++q) s += part[ww][q * P8 + r / 8][r % 8];
+    dst[r] = s;
   }
 }
 
@@ -199,7 +245,7 @@ __host__ __device__ constexpr int enc_tok(int r) { return 128 * enc_tpw(r); }
 __host__ __device__ constexpr int enc_kc(int r) { return r <= 160 ? 64 : 32; }
 
 template <int R>
-__global__ __launch_bounds__(512) void encode_mfma_kernel(EncodeArgs a, int kv) {
+__global__ __launch_bounds__(512) void encode_mfma_kernel(EncodeArgs a, int kv, int ksplit) {
   constexpr int TPW = enc_tpw(R), TOK = enc_tok(R), KC = enc_kc(R);
   constexpr int XP = KC / 8;                               // 16-byte pieces of a token's chunk row
   constexpr int NXI = 16 * TPW * XP / 64;                  // x load instructions per wave and chunk
@@ -221,6 +267,10 @@ __global__ __launch_bounds__(512) void encode_mfma_kernel(EncodeArgs a, int kv) 
   const long long tokens = (long long)a.batch * a.n_new;
   const long long ntt = (tokens + TOK - 1) / TOK;  // token tiles per (layer, group)
   const long long ntiles = ntt * a.groups * a.n_layers;
+  // Work item t: tile t % ntiles over chunk range t / ntiles of the width (one
+  // range unless the width is split: then the item's fp32 products go to
+  // a.kpart and encode_splitk_reduce_kernel finishes the tile).
+  const long long nwork = ntiles * ksplit;
   const char *x = kv ? a.x_v : a.x_k;
   const uint16_t *wd_all = (const uint16_t *)(kv ? a.wd_v : a.wd_k);
   uint16_t *pool_all = (uint16_t *)(kv ? a.v_pool : a.k_pool);
@@ -236,6 +286,7 @@ __global__ __launch_bounds__(512) void encode_mfma_kernel(EncodeArgs a, int kv) 
   };
   auto tile_of = [&](long long t) {
     Tile v;
+    t %= ntiles;
     v.tok0 = (t % ntt) * TOK;
     const long long r = t / ntt;
     v.grp = (int)(r % a.groups);
@@ -339,32 +390,39 @@ __global__ __launch_bounds__(512) void encode_mfma_kernel(EncodeArgs a, int kv) 
   // this wave's part of chunk c is in LDS; all waves meet, which also frees
   // buffer (c + 2) % 3; then the copies and x loads of chunk c + 2 are issued
   // and chunk c is multiplied.
-  const int nch = a.width / KC;
+  const int nch_all = a.width / KC;
+  const int per = (nch_all + ksplit - 1) / ksplit;  // chunks of one range
+  int c_lo = 0, nch = nch_all;                     // the current item's range
+  auto range_of = [&](long long t) {
+    c_lo = (int)(t / ntiles) * per;
+    nch = min(per, nch_all - c_lo);
+  };
   auto step = [&](int c, const char *buf, char *buf2, u32x4 (&cur)[NXI], u32x4 (&nx2)[NXI]) {
     put_x(cur);
     if (c + 1 < nch) barrier_vm<NWI + NXI>();
     else barrier_vm<0>();
     if (c + 2 < nch) {
-      copy_w(c + 2, buf2);
-      load_x(c + 2, nx2);
+      copy_w(c_lo + c + 2, buf2);
+      load_x(c_lo + c + 2, nx2);
     }
     compute(buf);
   };
   u32x4 xa[NXI], xb[NXI], xc[NXI];
-  // the first two chunks of a tile
+  // the first two chunks of an item
   auto start = [&]() {
-    copy_w(0, s_w0);
-    load_x(0, xa);
+    copy_w(c_lo, s_w0);
+    load_x(c_lo, xa);
     if (nch > 1) {
-      copy_w(1, s_w1);
-      load_x(1, xb);
+      copy_w(c_lo + 1, s_w1);
+      load_x(c_lo + 1, xb);
     }
   };
 
   long long t = blockIdx.x;
-  if (t >= ntiles) return;
+  if (t >= nwork) return;
   Tile cur = tile_of(t);
-  place(cur, s_off[0]);
+  range_of(t);
+  if (ksplit == 1) place(cur, s_off[0]);
   sources(cur);
   start();
   for (int par = 0;; par ^= 1) {
@@ -384,6 +442,23 @@ __global__ __launch_bounds__(512) void encode_mfma_kernel(EncodeArgs a, int kv) 
     // every wave is past its last products: the x slots (output staging) and
     // the W_down buffers are free
     barrier_vm<63>();
+    if (ksplit > 1) {  // fp32 products of this range, [item][token of the tile][r]
+      float *dst = a.kpart + t * TOK * R;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dst[(16 * (TPW * w + tt) + 4 * g + e) * R + 16 * ct + n] = acc[tt][ct][e];
+      const long long tn = t + gridDim.x;
+      if (tn >= nwork) break;
+      t = tn;
+      cur = tile_of(t);
+      range_of(t);
+      sources(cur);
+      start();
+      continue;
+    }
     uint16_t *s_out = (uint16_t *)s_xo;  // [TOK][R] bf16
     const float *muw = a.muw + ((long long)cur.li * a.groups + cur.grp) * a.muw_stride + (kv ? a.muw_v_off : 0);
 #pragma unroll
@@ -417,8 +492,65 @@ __global__ __launch_bounds__(512) void encode_mfma_kernel(EncodeArgs a, int kv) 
   }
 }
 
+// Finishes the tiles of a split width: adds the ranges' fp32 products in
+// range order, subtracts mu W_down, rounds once to bf16 and stores each
+// token's latent row in its slot.  One thread per (tile, token, 8 columns).
+template <int R>
+__global__ __launch_bounds__(256) void encode_splitk_reduce_kernel(EncodeArgs a, int kv, int ksplit) {
+  constexpr int TOK = enc_tok(R), C8 = R / 8;
+  const long long tokens = (long long)a.batch * a.n_new;
+  const long long ntt = (tokens + TOK - 1) / TOK;
+  const long long ntiles = ntt * a.groups * a.n_layers;
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= ntiles * TOK * C8) return;
+  const long long ti = idx / (TOK * C8);
+  const int tl = (int)(idx / C8 % TOK), c8 = (int)(idx % C8);
+  const long long tok = ti % ntt * TOK + tl;
+  if (tok >= tokens) return;
+  const long long rest = ti / ntt;
+  const int grp = (int)(rest % a.groups), li = (int)(rest / a.groups);
+  float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  // unrolled so that the loads of 16 ranges are in flight together; the sum
+  // keeps range order
+#pragma unroll 16
+  for (int sp = 0; sp < ksplit; ++sp) {
+    const float *src = a.kpart + ((sp * ntiles + ti) * TOK + tl) * R + 8 * c8;
+    const f32x4 lo = *(const f32x4 *)src, hi = *(const f32x4 *)(src + 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sum[j] += lo[j];
+      sum[4 + j] += hi[j];
+    }
+  }
+  const int b = (int)(tok / a.n_new), nn = (int)(tok % a.n_new);
+  const long long pos = (long long)a.pos0[b] + nn;
+  if (pos < 0 || pos >= (long long)a.max_pages * kPage) {
+    if (c8 == 0) atomicOr(a.err, LLA_DEVERR_APPEND);
+    return;
+  }
+  const int page = a.page_table[(long long)b * a.max_pages + pos / kPage];
+  if (page < 0 || page >= a.num_pages) {
+    if (c8 == 0) atomicOr(a.err, LLA_DEVERR_PAGE);
+    return;
+  }
+  const float *muw = a.muw + ((long long)li * a.groups + grp) * a.muw_stride + (kv ? a.muw_v_off : 0) + 8 * c8;
+  u32x4 o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) o[j] = pack_bf16(sum[2 * j] - muw[2 * j], sum[2 * j + 1] - muw[2 * j + 1]);
+  const long long lstride = kv ? a.pool_layer_stride_v : a.pool_layer_stride_k;
+  const long long off = (long long)page * (kv ? a.pool_page_stride_v : a.pool_page_stride_k) +
+                        grp * (kv ? a.pool_head_stride_v : a.pool_head_stride_k) + (pos % kPage) * R + 8 * c8;
+  uint16_t *pool = (uint16_t *)(kv ? a.v_pool : a.k_pool) + (long long)li * lstride;
+  *(u32x4 *)(pool + off) = o;
+}
+
 // Persistent grid: one workgroup per CU (LDS and registers allow no more).
 constexpr long long kEncWorkgroups = 256;
+// Split of the width: only for launches with fewer tiles than half the
+// workgroups and at least kSplitMinChunks chunks of W_down; at most
+// kSplitMaxItems (tile, range) items, which bounds the fp32 products region.
+constexpr int kSplitMinChunks = 16;
+constexpr long long kSplitMaxItems = kEncWorkgroups + kEncWorkgroups / 2;
 
 #define LLA_ENCODE_R(X) X(16) X(32) X(48) X(64) X(96) X(128) X(160) X(256)
 
@@ -429,14 +561,45 @@ bool encode_mfma_r(int r) {
   return false;
 }
 
+size_t encode_kpart_bytes(int width, int groups, int n_layers, int r_k, int r_v) {
+  if (width % 64 || !encode_mfma_r(r_k) || !encode_mfma_r(r_v) || (long long)groups * n_layers >= kEncWorkgroups / 2)
+    return 0;
+  size_t bytes = 0;
+  for (const int r : {r_k, r_v})
+    if (width / enc_kc(r) >= kSplitMinChunks) {
+      const size_t b = sizeof(float) * kSplitMaxItems * enc_tok(r) * r;
+      if (b > bytes) bytes = b;
+    }
+  return bytes;
+}
+
+// Ranges the width is split into for a launch of ntiles tiles (1: no split).
+int encode_ksplit(long long ntiles, int nch, size_t region, size_t tile_bytes) {
+  if (ntiles >= kEncWorkgroups / 2 || nch < kSplitMinChunks || region == 0) return 1;
+  int ks = (int)((kEncWorkgroups + ntiles - 1) / ntiles);
+  if (ks > nch / 4) ks = nch / 4;  // at least 4 chunks per range
+  const int per = (nch + ks - 1) / ks;
+  ks = (nch + per - 1) / per;      // no empty range
+  if (ks < 2 || (size_t)(ntiles * ks) * tile_bytes > region) return 1;
+  return ks;
+}
+
 hipError_t launch_encode_mfma(int r, int kv, const EncodeArgs &a, hipStream_t stream) {
   const long long tokens = (long long)a.batch * a.n_new;
-#define X(RR)                                                                                     \
-  if (r == RR) {                                                                                  \
-    const long long tiles = (tokens + enc_tok(RR) - 1) / enc_tok(RR) * a.groups * a.n_layers;      \
-    hipLaunchKernelGGL(encode_mfma_kernel<RR>, dim3((unsigned)(tiles < kEncWorkgroups ? tiles : kEncWorkgroups)), \
-                       dim3(512), 0, stream, a, kv);                                             \
-    return hipGetLastError();                                                                     \
+#define X(RR)                                                                                          \
+  if (r == RR) {                                                                                       \
+    const long long tiles = (tokens + enc_tok(RR) - 1) / enc_tok(RR) * a.groups * a.n_layers;           \
+    const int ks = encode_ksplit(tiles, a.width / enc_kc(RR), a.kpart_bytes,                           \
+                                 sizeof(float) * enc_tok(RR) * RR);                                    \
+    const long long items = tiles * ks;                                                                \
+    hipLaunchKernelGGL(encode_mfma_kernel<RR>, dim3((unsigned)(items < kEncWorkgroups ? items : kEncWorkgroups)), \
+                       dim3(512), 0, stream, a, kv, ks);                                              \
+    if (ks > 1) {                                                                                      \
+      const long long threads = tiles * enc_tok(RR) * (RR / 8);                                        \
+      hipLaunchKernelGGL(encode_splitk_reduce_kernel<RR>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, \
+                         stream, a, kv, ks);                                                          \
+    }                                                                                                  \
+    return hipGetLastError();                                                                          \
   }
   LLA_ENCODE_R(X)
 #undef X

@@ -76,6 +76,8 @@ struct EncodeArgs {
   float *muw_part;             // workspace [muw_parts][n_layers][groups][r_k + r_v]: partial sums
   int muw_parts;               // row ranges of W_down summed independently
   int *err;
+  float *kpart;                // split over the width: fp32 partial products [splits x tiles][tokens of a tile][r]
+  size_t kpart_bytes;          // size of that region (0: no split)
 };
 
 // Pages of one sequence that a decode reads under token eviction (keep the
@@ -150,6 +152,7 @@ bool absorbed_supported(int d_head, int r_k, int r_v, int d_rope, int heads_per_
 hipError_t launch_absorbed(int d_head, int r_k, int r_v, int d_rope, const AttnArgs &a, hipStream_t stream);
 hipError_t launch_rope_key_append(const RopeAppendArgs &a, hipStream_t stream);
 int encode_muw_parts(int width);
+size_t encode_kpart_bytes(int width, int groups, int n_layers, int r_k, int r_v);
 hipError_t launch_rope_table(int n_pos, int d_head, double base, float *table, hipStream_t s);
 
 }  // namespace lla

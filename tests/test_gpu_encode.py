@@ -168,6 +168,28 @@ def test_encode_lla2d(dtype):
     compare(m, got, ref, init, f"encode 2D dt={dtype}")
 
 
+@pytest.mark.parametrize("case", ["per-head", "2D"])
+def test_encode_split_over_the_width(case):
+    """Few tiles over a wide input: the width is cut into ranges whose fp32
+    products are added in a second launch (per-head: 4 heads, width 1024, 3
+    sequences x 37 tokens -> 4 tiles, 4 ranges; LLA-2D: width 4096, 2 layers,
+    16 ranges), ragged positions, shuffled pages."""
+    if case == "per-head":
+        m = dims(8, 1, 4, 128, 96, 160, PER_HEAD, BF16)
+        B, pps, n_new, n_layers = 3, 6, 37, 1
+    else:
+        m = dims(8, 2, 8, 64, 32, 48, TWO_D, BF16)
+        B, pps, n_new, n_layers = 4, 3, 21, 2
+    pt = gen.shuffled_page_table(3701, B, pps)
+    codec = random_codec(m, seed=3702, ortho_down=False)
+    pos0 = np.arange(B) * 7 % 16
+    D = lla.dims_from_dict(m)
+    assert lla.workspace_bytes(D, lla.OP_ENCODE, B, 0, n_layers) > lla.workspace_bytes(
+        lla.dims_from_dict(dict(m, T=1)), lla.OP_ENCODE, B, 0, n_layers)  # the products region
+    got, ref, init = run_both(m, codec, pt, B * pps, pos0, n_new, 0, n_layers, seed=3703)
+    compare(m, got, ref, init, f"encode split width {case}")
+
+
 @pytest.mark.timeout(600)
 def test_encode_lla2d_benchmark_shape():
     """The LLA-2D decode step's append in the benchmark's launch configuration:
