@@ -244,8 +244,11 @@ __host__ __device__ constexpr int enc_tpw(int r) { return r <= 160 ? 2 : 1; }
 __host__ __device__ constexpr int enc_tok(int r) { return 128 * enc_tpw(r); }
 __host__ __device__ constexpr int enc_kc(int r) { return r <= 160 ? 64 : 32; }
 
-template <int R>
-__global__ __launch_bounds__(512) void encode_mfma_kernel(EncodeArgs a, int kv, int ksplit) {
+// SPLIT: the width is cut into ksplit ranges (a separate instantiation, so
+// that the unsplit kernel carries none of its state).
+template <int R, bool SPLIT>
+__global__ __launch_bounds__(512) void encode_mfma_kernel(EncodeArgs a, int kv, int ksplit_arg) {
+  const int ksplit = SPLIT ? ksplit_arg : 1;
   constexpr int TPW = enc_tpw(R), TOK = enc_tok(R), KC = enc_kc(R);
   constexpr int XP = KC / 8;                               // 16-byte pieces of a token's chunk row
   constexpr int NXI = 16 * TPW * XP / 64;                  // x load instructions per wave and chunk
@@ -394,8 +397,10 @@ __global__ __launch_bounds__(512) void encode_mfma_kernel(EncodeArgs a, int kv, 
   const int per = (nch_all + ksplit - 1) / ksplit;  // chunks of one range
   int c_lo = 0, nch = nch_all;                     // the current item's range
   auto range_of = [&](long long t) {
-    c_lo = (int)(t / ntiles) * per;
-    nch = min(per, nch_all - c_lo);
+    if constexpr (SPLIT) {
+      c_lo = (int)(t / ntiles) * per;
+      nch = min(per, nch_all - c_lo);
+    }
   };
   auto step = [&](int c, const char *buf, char *buf2, u32x4 (&cur)[NXI], u32x4 (&nx2)[NXI]) {
     put_x(cur);
@@ -422,7 +427,7 @@ __global__ __launch_bounds__(512) void encode_mfma_kernel(EncodeArgs a, int kv, 
   if (t >= nwork) return;
   Tile cur = tile_of(t);
   range_of(t);
-  if (ksplit == 1) place(cur, s_off[0]);
+  if (!SPLIT) place(cur, s_off[0]);
   sources(cur);
   start();
   for (int par = 0;; par ^= 1) {
@@ -442,7 +447,7 @@ __global__ __launch_bounds__(512) void encode_mfma_kernel(EncodeArgs a, int kv, 
     // every wave is past its last products: the x slots (output staging) and
     // the W_down buffers are free
     barrier_vm<63>();
-    if (ksplit > 1) {  // fp32 products of this range, [item][token of the tile][r]
+    if constexpr (SPLIT) {  // fp32 products of this range, [item][token of the tile][r]
       float *dst = a.kpart + t * TOK * R;
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
@@ -561,12 +566,15 @@ bool encode_mfma_r(int r) {
   return false;
 }
 
+// Ranks whose split instantiation fits in registers (128 and 160 would spill).
+__host__ __device__ constexpr bool enc_can_split(int r) { return r != 128 && r != 160; }
+
 size_t encode_kpart_bytes(int width, int groups, int n_layers, int r_k, int r_v) {
   if (width % 64 || !encode_mfma_r(r_k) || !encode_mfma_r(r_v) || (long long)groups * n_layers >= kEncWorkgroups / 2)
     return 0;
   size_t bytes = 0;
   for (const int r : {r_k, r_v})
-    if (width / enc_kc(r) >= kSplitMinChunks) {
+    if (enc_can_split(r) && width / enc_kc(r) >= kSplitMinChunks) {
       const size_t b = sizeof(float) * kSplitMaxItems * enc_tok(r) * r;
       if (b > bytes) bytes = b;
     }
@@ -589,11 +597,15 @@ hipError_t launch_encode_mfma(int r, int kv, const EncodeArgs &a, hipStream_t st
 #define X(RR)                                                                                          \
   if (r == RR) {                                                                                       \
     const long long tiles = (tokens + enc_tok(RR) - 1) / enc_tok(RR) * a.groups * a.n_layers;           \
-    const int ks = encode_ksplit(tiles, a.width / enc_kc(RR), a.kpart_bytes,                           \
-                                 sizeof(float) * enc_tok(RR) * RR);                                    \
+    const int ks = enc_can_split(RR) ? encode_ksplit(tiles, a.width / enc_kc(RR), a.kpart_bytes,       \
+                                                     sizeof(float) * enc_tok(RR) * RR)                 \
+                                     : 1;                                                              \
     const long long items = tiles * ks;                                                                \
-    hipLaunchKernelGGL(encode_mfma_kernel<RR>, dim3((unsigned)(items < kEncWorkgroups ? items : kEncWorkgroups)), \
-                       dim3(512), 0, stream, a, kv, ks);                                              \
+    const dim3 grid((unsigned)(items < kEncWorkgroups ? items : kEncWorkgroups));                       \
+    if (ks > 1)                                                                                        \
+      hipLaunchKernelGGL((encode_mfma_kernel<RR, true>), grid, dim3(512), 0, stream, a, kv, ks);       \
+    else                                                                                               \
+      hipLaunchKernelGGL((encode_mfma_kernel<RR, false>), grid, dim3(512), 0, stream, a, kv, 1);       \
     if (ks > 1) {                                                                                      \
       const long long threads = tiles * enc_tok(RR) * (RR / 8);                                        \
       hipLaunchKernelGGL(encode_splitk_reduce_kernel<RR>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, \
