@@ -49,8 +49,27 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((__vector_size__(2 * sizeof(uint32_t))));
 typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
 typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
 
 #define LLA_LDS(p) ((__attribute__((address_space(3))) void *)(p))
+
+// Byte address in LDS of byte off of the LDS object at base (wave-uniform).
+__device__ __forceinline__ uint32_t lds_addr(const char *base, int off) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)base + off);
+}
+
+// Direct global -> LDS copies: lane l's 16 (4) bytes at g land at LDS byte
+// lds + 16 l (4 l).  They are issued here rather than through the compiler's
+// builtin so that the compiler adds no waits of its own for them: the tile
+// pipeline waits for its copies itself (vmcnt at each step's barrier), and the
+// compiler's tracking of such copies made every access to another LDS buffer
+// wait for all copies in flight.  No register is written by them.
+__device__ __forceinline__ void dma_lds16(const void *g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void dma_lds4(const void *g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
 
 // Two fp32 values to packed bf16 (hardware round to nearest even).
 __device__ __forceinline__ uint32_t cvt2(float lo, float hi) {
@@ -74,6 +93,23 @@ __device__ __forceinline__ u32x2 lds_read_tr(const char *p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// Max and sum of a value over lanes l and l ^ 32 (v_permlane32_swap hands each
+// lane both its own value and its partner's).
+__device__ __forceinline__ float max_across_halves(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float sum_across_halves(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
@@ -94,34 +130,52 @@ __device__ __forceinline__ void barrier_vm() {
 
 }  // namespace
 
-template <int DH, int RK, int RV>
-__global__ __launch_bounds__(512, 1) void prefill_kernel(AttnArgs a) {
-  constexpr int NW = 8, NTH = NW * 64, QB = NW * 32, KT = 32;  // queries per workgroup, tokens per tile
-  constexpr int HALF = DH / 2, NDT = DH / 16, KSD = DH / 32;
-  constexpr int NU = NDT;                          // rebuild units: 2 token halves x NDT / 2 tile pairs
+template <int DH, int RK, int RV, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(AttnArgs a) {
+  constexpr int NTH = NW * 64, QB = 256, QW = QB / NW, QF = QW / 32, KT = 32;  // queries per workgroup / wave, tokens per tile
+  constexpr int HALF = DH / 2, KSQ = DH / 16;      // score K-steps of 16 dims
+  constexpr int NDB = DH / 32;                     // 16-dim blocks in each RoPE half
+  constexpr int NTW = 2 * NDB / NW;               // 16-token halves of a tile each wave rebuilds
   constexpr int KS32 = RK / 32;
-  constexpr bool TAIL = (RK % 32) != 0;            // one extra 16-wide K-step
-  constexpr int NRT = RV / 16, KSV = RV / 32;
-  // LDS rows of a slot, in 16-byte chunks: RK / 8 (+1 pad) for c_k, RV / 8 (+2 pad) for c_v
-  constexpr int CPK = RK / 8 + 1, CPV = RV / 8 + 2;
+  constexpr bool TAIL = (RK % 32) != 0;            // one extra 16-wide rebuild K-step
+  constexpr int KSW = KS32 > 0 ? KS32 : 1;
+  constexpr int NRB = RV / 32, KSV = RV / 16;      // 32-row blocks of O^T, up-projection K-steps
+  // LDS rows of a slot, in 16-byte chunks: RK / 8 (+1 pad) for c_k; for c_v the
+  // first count >= RV / 8 that is 4 or 12 mod 16, so that the four rows a
+  // 16-lane group of a transposing read touches fall in four disjoint 16-bank
+  // quarters (64 banks of 4 bytes)
+  constexpr int CPK = RK / 8 + 1;
+  constexpr int CPV = (RV / 8) % 16 <= 4 ? RV / 8 + (4 - (RV / 8) % 16) : (RV / 8) % 16 <= 12 ? RV / 8 + (12 - (RV / 8) % 16) : RV / 8 + (20 - (RV / 8) % 16);
   constexpr int SK = 16 * CPK, SV = 16 * CPV, SKH = 2 * DH + 16;  // row strides, bytes
   constexpr int VOFF = KT * SK;
   constexpr int NPOS = (KT * (CPK + CPV) + 63) / 64 * 64;  // copied chunks per tile (pad included)
   constexpr int NCP = NPOS / 64;                            // wave-wide copies per tile
-  constexpr int IPW = (NCP + NW - 1) / NW;                  // copies per wave (the last ones partial)
-  constexpr int IPW_MIN = NCP / NW;                         // copies every wave issues
-  constexpr int SLOT = NPOS * 16;
+  constexpr int NROPE = DH / 64;                            // 256-byte copies of the RoPE row
+  constexpr int NJOB = NCP + NROPE;
+  // Copies per wave and tile, the same for every wave (the last jobs repeat
+  // latent copies), so that the compiler's count of outstanding copies is exact.
+  constexpr int CPW = (NJOB + NW - 1) / NW;
+  constexpr int ROPE_OFF = NPOS * 16;                       // (cos, sin) row of the tile's first position
+  constexpr int SLOT = ROPE_OFF + 4 * DH;
+  // Tile y is copied in step y - 5 into slot y % 6, rebuilt in step y - 1 and
+  // attended in step y.  At the end of step x a wave may still have in flight
+  // the copies of steps x - 2 .. x.
+  constexpr int NSLOT = 6, DIST = NSLOT - 1;
+  constexpr int VM_KEEP = 3 * CPW;
+  constexpr int PTC = 512;  // page-table entries staged per chunk
   static_assert(RK % 16 == 0 && RV % 32 == 0 && (DH == 64 || DH == 128), "shape");
-  static_assert(NU <= NW && IPW <= 4, "tile split");
+  static_assert(QF * 32 * NW == QB && NTW >= 1 && NTW * NW == 2 * NDB, "wave split");
+  static_assert(CPW <= 8 && VM_KEEP < 64 && NW * CPW - NJOB <= NCP && (CPW - 1) * NW <= NCP, "copy split");
 
-  __shared__ __attribute__((aligned(16))) char s_c0[SLOT], s_c1[SLOT], s_c2[SLOT], s_c3[SLOT];
-  __shared__ __attribute__((aligned(16))) char s_kh0[KT * SKH], s_kh1[KT * SKH];  // rotated K, bf16
-  __shared__ __attribute__((aligned(16))) char s_wk[DH * SK];                      // W_up,k,t rows
-  __shared__ int s_pt[2][1024];  // page-table entries: chunk c (1024 logical pages) in s_pt[c % 2]
+  __shared__ __attribute__((aligned(16))) char s_c0[SLOT], s_c1[SLOT], s_c2[SLOT], s_c3[SLOT], s_c4[SLOT], s_c5[SLOT];
+  __shared__ __attribute__((aligned(16))) char s_k0[KT * SKH], s_k1[KT * SKH];  // rotated K, bf16
+  __shared__ __attribute__((aligned(16))) char s_wk[NDB * 32 * SK];               // W_up,k,t rows of each dim block and its partner
+  __shared__ int s_pt[2][PTC];  // page-table entries: chunk c (PTC logical pages) in s_pt[c % 2]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n = lane & 15, g = lane >> 4;
+  const int n16 = lane & 15, g16 = lane >> 4;  // lane coordinates of the 16x16 products
+  const int n32 = lane & 31, g32 = lane >> 5;  // lane coordinates of the 32x32 products
 
   // ---- work item: (sequence, head, query block); the query blocks of one
   // (sequence, head) are dispatched to one XCD so that they share its L2 ----
@@ -150,25 +204,24 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(AttnArgs a) {
   const int nt = (kend + KT - 1) / KT;
   const int npg = (kend + kPage - 1) / kPage;
 
-  const int w0 = r0 + 32 * w;
-  const int wv0 = max(w0, v0);
-  const int qmin = (int)(p0 + wv0);  // the wave's first query position
+  const int w0 = r0 + QW * w;
+  const int qmin = (int)(p0 + max(w0, v0));  // the wave's first query position
 
   // ---- prologue: Q' = scale log2(e) R(p) q as bf16 B-operands ----
-  // qop[f][ks]: lane (n, g) = query w0 + 16 f + n, dims 32 ks + 8 g .. + 7.
-  u32x4 qop[2][KSD];
-  int qpos[2];
-  bool qok[2];
+  // qop[f][ks]: lane (n32, g32) = query w0 + 32 f + n32, dims 16 ks + 8 g32 .. + 7.
+  u32x4 qop[QF][KSQ];
+  int qpos[QF];
+  bool qok[QF];
 #pragma unroll
-  for (int f = 0; f < 2; ++f) {
-    const int iq = w0 + 16 * f + n;
+  for (int f = 0; f < QF; ++f) {
+    const int iq = w0 + 32 * f + n32;
     qok[f] = iq >= v0 && iq < v1;
     qpos[f] = qok[f] ? (int)(p0 + iq) : 0;
     const uint16_t *qrow = (const uint16_t *)a.q + (((long long)b * nq + (qok[f] ? iq : v0)) * a.H + h) * DH;
     const float *rq = a.rope + (long long)qpos[f] * DH;
 #pragma unroll
-    for (int ks = 0; ks < KSD / 2; ++ks) {
-      const int d0 = 32 * ks + 8 * g;
+    for (int ks = 0; ks < KSQ / 2; ++ks) {
+      const int d0 = 16 * ks + 8 * g32;
       u32x4 x = u32x4{0u, 0u, 0u, 0u}, y = x;
       if (qok[f]) {
         x = *(const u32x4 *)(qrow + d0);
@@ -184,31 +237,29 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(AttnArgs a) {
         pb[e2] = cvt2(a.qscale * (qa0 * cs[1] + qb0 * cs[0]), a.qscale * (qa1 * cs[3] + qb1 * cs[2]));
       }
       qop[f][ks] = pa;
-      qop[f][ks + KSD / 2] = pb;
+      qop[f][ks + KSQ / 2] = pb;
     }
   }
 
-  // ---- W_up,k,t of the head in LDS (rows padded like the c_k rows), mu_k ----
-  // Rebuild unit (tau, T) of wave w: tokens 16 tau .. + 15 of each tile, dims
-  // 16 T + n and 16 T + n + d/2 (tile T and its RoPE partner tile).
-  const int tau = w & 1, T = w >> 1;
-  float muk[2][4];
+  // ---- this wave's share of the K rebuild: W_up,k,t rows in LDS, mu_k in registers ----
+  // Wave w rebuilds dims dlo .. + 15 and their RoPE partners dlo + d/2 .. + 15
+  // (block 1) at tokens 16 tau .. + 15 of each tile, tau = tau0 .. tau0 + NTW - 1.
+  const int dlo = 16 * (w % (HALF / 16));
+  const int tau0 = NTW * (w / (HALF / 16));
+  f32x4 muk[2];
+  char *const wk_lds = s_wk + 32 * (dlo / 16) * SK;  // this wave's rows: block j at 16 j
   {
     const char *wkh = a.wup_k + (long long)h * a.wup_head_stride_k * 2;
-    for (int c = tid; c < DH * RK / 8; c += NTH) {
-      const int d = c / (RK / 8), k8 = c - d * (RK / 8);
-      *(u32x4 *)(s_wk + d * SK + k8 * 16) = *(const u32x4 *)(wkh + ((long long)d * RK + 8 * k8) * 2);
-    }
     const uint16_t *mkh = (const uint16_t *)a.mu_k + (long long)h * a.mu_head_stride;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 2; ++j) {
+      const int dblk = dlo + j * HALF;
+      const char *wrow = wkh + (long long)(dblk + n16) * RK * 2;
+      if (w < NDB)  // the first wave of each dim block stores its rows (read after the next barrier)
+        for (int c = g16; c < RK / 8; c += 4)
+          *(u32x4 *)(wk_lds + (16 * j + n16) * SK + 16 * c) = *(const u32x4 *)(wrow + 16 * c);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) muk[j][i] = 0.f;
-    if (w < NU) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) muk[j][i] = bf16_to_f32(mkh[16 * T + 4 * g + i + j * HALF]);
+      for (int i = 0; i < 4; ++i) muk[j][i] = bf16_to_f32(mkh[dblk + 4 * g16 + i]);
     }
   }
 
@@ -220,21 +271,27 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(AttnArgs a) {
   int bad_lp = 0x7FFFFFFF;  // first logical page with an out-of-range table entry
 
   auto fill_pt = [&](int c) {
-    for (int i = tid; i < 1024; i += NTH) {
-      const int lp = 1024 * c + i;
+    for (int i = tid; i < PTC; i += NTH) {
+      const int lp = PTC * c + i;
       s_pt[c & 1][i] = lp < npg ? pt_row[lp] : 0;
     }
   };
 
-  // Copy it of this wave covers chunk positions 64 (it NW + w) .. + 63 of the
-  // slot; lane position pos -> (c_v?, row, chunk) is the same for every tile.
-  // Pad positions copy the row's first chunk (never read).
-  int cp_off[IPW];   // byte offset within the page (from the K or V page base)
-  int cp_row[IPW];   // tile row 0..31, or 32 for positions past the rows
-  bool cp_v[IPW];
+  // Job J = it NW + w of a tile: J < NCP copies chunk positions 64 J .. + 63 of
+  // the slot (lane position pos -> (c_v?, row, chunk) is the same for every
+  // tile; pad positions copy the row's first chunk, never read); NCP <= J < NJOB
+  // copies part J - NCP of the RoPE row; J >= NJOB repeats latent job J - NJOB.
+  // cp[it] packs the byte offset within the page (from the K or V page base,
+  // bits 0..15), the tile row (0..31, or 32 past the rows; bits 16..21) and
+  // whether the chunk is c_v (bit 22).
+  auto job_pos = [&](int it) {
+    const int J = it * NW + w;
+    return J < NCP ? J : (J >= NJOB ? J - NJOB : -1);
+  };
+  int cp[CPW];
 #pragma unroll
-  for (int it = 0; it < IPW; ++it) {
-    const int pos = 64 * (it * NW + w) + lane;
+  for (int it = 0; it < CPW; ++it) {
+    const int pos = 64 * max(job_pos(it), 0) + lane;
     int row = 32, off = 0;
     bool isv = false;
     if (pos < KT * CPK) {
@@ -248,29 +305,38 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(AttnArgs a) {
       const int c = p2 - row * CPV;
       off = ((row & 15) * RV + 8 * (c < RV / 8 ? c : 0)) * 2;
     }
-    cp_off[it] = off;
-    cp_row[it] = row;
-    cp_v[it] = isv;
+    cp[it] = off | (row << 16) | (isv ? 1 << 22 : 0);
   }
+  auto cp_row = [&](int it) { return (cp[it] >> 16) & 63; };
   // Direct-to-LDS copy of tile x (clamped to the last tile) into slot sb;
   // returns the page-validity bits (bit 0: first page, bit 1: second).
   auto copy_tile = [&](int x, char *sb) -> int {
     x = min(x, nt - 1);
     const int l0 = min(2 * x, npg - 1), l1 = min(2 * x + 1, npg - 1);
-    const int e0 = __builtin_amdgcn_readfirstlane(s_pt[(l0 >> 10) & 1][l0 & 1023]);
-    const int e1 = __builtin_amdgcn_readfirstlane(s_pt[(l1 >> 10) & 1][l1 & 1023]);
+    const int e0 = __builtin_amdgcn_readfirstlane(s_pt[(l0 / PTC) & 1][l0 % PTC]);
+    const int e1 = __builtin_amdgcn_readfirstlane(s_pt[(l1 / PTC) & 1][l1 % PTC]);
     const bool ok0 = e0 >= 0 && e0 < a.num_pages, ok1 = e1 >= 0 && e1 < a.num_pages;
     if (!ok0) bad_lp = min(bad_lp, l0);
     if (!ok1) bad_lp = min(bad_lp, l1);
     const long long pg0 = ok0 ? e0 : 0, pg1 = ok1 ? e1 : 0;
-    const char *k0 = kpool + pg0 * pstride_k, *k1 = kpool + pg1 * pstride_k;
-    const char *v0p = vpool + pg0 * pstride_v, *v1p = vpool + pg1 * pstride_v;
+    uint64_t k0 = (uint64_t)(kpool + pg0 * pstride_k), k1 = (uint64_t)(kpool + pg1 * pstride_k);
+    uint64_t v0 = (uint64_t)(vpool + pg0 * pstride_v), v1 = (uint64_t)(vpool + pg1 * pstride_v);
+    // (opaque, so that each lane selects one of the four page addresses and adds
+    // its offset, rather than the compiler multiplying a selected page number)
+    asm volatile("" : "+s"(k0), "+s"(k1), "+s"(v0), "+s"(v1));
 #pragma unroll
-    for (int it = 0; it < IPW; ++it) {
-      if (it < IPW_MIN || it * NW + w < NCP) {
-        const bool p1 = cp_row[it] >= 16 && cp_row[it] < 32;
-        const char *base = cp_v[it] ? (p1 ? v1p : v0p) : (p1 ? k1 : k0);
-        __builtin_amdgcn_global_load_lds((const void *)(base + cp_off[it]), LLA_LDS(sb + 64 * 16 * (it * NW + w)), 16, 0, 0);
+    for (int it = 0; it < CPW; ++it) {
+      const int J = it * NW + w;
+      const bool rope_job = it + 1 == CPW && J >= NCP && J < NJOB;
+      if (!rope_job) {
+        const int jp = J < NCP ? J : J - NJOB;
+        const bool p1 = ((cp[it] >> 20) & 3) == 1;  // rows 16..31
+        const bool isv = (cp[it] >> 22) != 0;
+        const uint64_t pa = isv ? v0 : k0, pb = isv ? v1 : k1;
+        dma_lds16((const char *)((p1 ? pb : pa) + (uint32_t)(cp[it] & 0xFFFF)), lds_addr(sb, 1024 * jp));
+      } else {
+        const int k = J - NCP;
+        dma_lds4(a.rope + (long long)KT * x * DH + 64 * k + lane, lds_addr(sb, ROPE_OFF + 256 * k));
       }
     }
     return (ok0 ? 1 : 0) | (ok1 ? 2 : 0);
@@ -279,211 +345,316 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(AttnArgs a) {
   // come from a bad page.
   auto clear_tile = [&](int x, char *sb, int okm) {
 #pragma unroll
-    for (int it = 0; it < IPW; ++it) {
-      if (it < IPW_MIN || it * NW + w < NCP) {
-        const int r = cp_row[it];
+    for (int it = 0; it < CPW; ++it) {
+      if (it * NW + w < NCP) {
+        const int r = cp_row(it);
         if (r < 32 && (KT * x + r >= kend || !((okm >> (r >> 4)) & 1)))
           *(u32x4 *)(sb + 16 * (64 * (it * NW + w) + lane)) = u32x4{0u, 0u, 0u, 0u};
       }
     }
   };
+  auto needs_clear = [&](int y, int okm) { return y < nt && (okm != 3 || (y == nt - 1 && kend % KT != 0)); };
 
-  // RoPE rows of this wave's rebuild unit: pairs 16 T + 4 g .. + 3 at its token.
-  f32x4 rp[2];
-  auto load_rope = [&](int x) {
-    const int pos = min(KT * min(x, nt - 1) + 16 * tau + n, kend - 1);
-    const float *rr = a.rope + (long long)pos * DH + 2 * (16 * (w < NU ? T : 0) + 4 * g);
-    rp[0] = *(const f32x4 *)rr;
-    rp[1] = *(const f32x4 *)(rr + 4);
-  };
-  // Rotated K of the tile in slot sb into K buffer kb.
-  auto rebuild = [&](const char *sb, char *kb) {
-    if (w < NU) {
-      const char *ck = sb + (16 * tau + n) * SK;
-      const char *wa = s_wk + (16 * T + n) * SK, *wb = wa + HALF * SK;
-      f32x4 k0 = f32x4{0.f, 0.f, 0.f, 0.f}, k1 = k0;
+  // RoPE of this wave's rebuild share: the angle of position 32 y + r is the
+  // sum of the angle of 32 y (a row copied with the tile) and that of r, the
+  // lane's row in the tile (held here: (cos, sin) of pairs dlo + 4 g16 + i at
+  // r = 16 tau + n16, tau = tau0 + t; rows past the table only serve tokens
+  // past the context, which are masked).  No global loads in the main loop
+  // besides the tile copies, so that the compiler's waits stay on them.
+  float ro_c[NTW][4], ro_s[NTW][4];
 #pragma unroll
-      for (int ks = 0; ks < KS32; ++ks) {
-        const int off = (32 * ks + 8 * g) * 2;
-        const u32x4 bop = *(const u32x4 *)(ck + off);
-        k0 = mfma16(*(const u32x4 *)(wa + off), bop, k0);
-        k1 = mfma16(*(const u32x4 *)(wb + off), bop, k1);
-      }
+  for (int t = 0; t < NTW; ++t) {
+    const int r = min(16 * (tau0 + t) + n16, a.rope_len - 1);
+    const float *rr = a.rope + (long long)r * DH + 2 * (dlo + 4 * g16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ro_c[t][i] = rr[2 * i];
+      ro_s[t][i] = rr[2 * i + 1];
+    }
+  }
+  // K^T blocks (16 dims x 16 tokens) of the tile in slot sb, plus mu: kacc[2 t + j]
+  // gives lane (n16, g16) dims dlo + j d/2 + 4 g16 .. + 3 at token 16 (tau0 + t) + n16.
+  const int ck_lane = (16 * tau0 + n16) * SK + 16 * g16;
+  const int wa_lane = 32 * (dlo / 16) * SK + n16 * SK + 16 * g16;
+  auto rebuild_mfma = [&](const char *sb, f32x4 (&kacc)[2 * NTW]) {
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) {
+      u32x4 bop[KSW];
+#pragma unroll
+      for (int ks = 0; ks < KS32; ++ks) bop[ks] = *(const u32x4 *)(sb + (ck_lane + 16 * t * SK + 64 * ks));
+#pragma unroll
+      for (int j = 0; j < 2; ++j) kacc[2 * t + j] = muk[j];
+#pragma unroll
+      for (int ks = 0; ks < KS32; ++ks)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          kacc[2 * t + j] = mfma16(*(const u32x4 *)(s_wk + (wa_lane + 16 * j * SK + 64 * ks)), bop[ks], kacc[2 * t + j]);
       if constexpr (TAIL) {
-        const int off = (32 * KS32 + 4 * g) * 2;
-        const bf16x4 bt = __builtin_bit_cast(bf16x4, *(const u32x2 *)(ck + off));
-        k0 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, *(const u32x2 *)(wa + off)), bt, k0, 0, 0, 0);
-        k1 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, *(const u32x2 *)(wb + off)), bt, k1, 0, 0, 0);
+        const bf16x4 bt = __builtin_bit_cast(bf16x4, *(const u32x2 *)(sb + (ck_lane + 16 * t * SK + 64 * KS32 - 8 * g16)));
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          kacc[2 * t + j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+              __builtin_bit_cast(bf16x4, *(const u32x2 *)(s_wk + (wa_lane + 16 * j * SK + 64 * KS32 - 8 * g16))), bt,
+              kacc[2 * t + j], 0, 0, 0);
       }
+    }
+  };
+  // RoPE on the rebuilt blocks, bf16 rows of K buffer kb.
+  const int kw_lane = (16 * tau0 + n16) * SKH + (dlo + 4 * g16) * 2;
+  const int rb_lane = ROPE_OFF + 8 * (dlo + 4 * g16);
+  auto rebuild_store = [&](const f32x4 (&kacc)[2 * NTW], const char *sb, char *kb) {
+    const f32x4 b01 = *(const f32x4 *)(sb + rb_lane), b23 = *(const f32x4 *)(sb + (rb_lane + 16));
+    const float bc[4] = {b01[0], b01[2], b23[0], b23[2]}, bs[4] = {b01[1], b01[3], b23[1], b23[3]};
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) {
       float ra[4], rb[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float ka = k0[i] + muk[0][i], kb2 = k1[i] + muk[1][i];
-        const float c = rp[i >> 1][2 * (i & 1)], s = rp[i >> 1][2 * (i & 1) + 1];
+        const float c = bc[i] * ro_c[t][i] - bs[i] * ro_s[t][i];
+        const float s = bs[i] * ro_c[t][i] + bc[i] * ro_s[t][i];
+        const float ka = kacc[2 * t][i], kb2 = kacc[2 * t + 1][i];
         ra[i] = ka * c - kb2 * s;
         rb[i] = ka * s + kb2 * c;
       }
-      char *row = kb + (16 * tau + n) * SKH;
-      *(u32x2 *)(row + (16 * T + 4 * g) * 2) = u32x2{cvt2(ra[0], ra[1]), cvt2(ra[2], ra[3])};
-      *(u32x2 *)(row + (HALF + 16 * T + 4 * g) * 2) = u32x2{cvt2(rb[0], rb[1]), cvt2(rb[2], rb[3])};
+      *(u32x2 *)(kb + (kw_lane + 16 * t * SKH)) = u32x2{cvt2(ra[0], ra[1]), cvt2(ra[2], ra[3])};
+      *(u32x2 *)(kb + (kw_lane + 16 * t * SKH + HALF * 2)) = u32x2{cvt2(rb[0], rb[1]), cvt2(rb[2], rb[3])};
     }
   };
+  // S^T = K Q'^T of the tile in K buffer kb: lane (n32, g32) gets query 32 f + n32
+  // at tokens 8 (e / 4) + 4 g32 + e % 4 (element e).
+  const int kr_lane = n32 * SKH + 16 * g32;
 
-  // ---- online softmax state and latent-space value sums ----
-  f32x4 o[2][NRT];
-  float m_ref[2], l_run[2];
+  // ---- softmax state and latent-space value sums ----
+  // The weights of a query use one fixed reference m_ref: the max of its scores
+  // in the first tile (first pass), so the accumulators are never rescaled.  A
+  // weight is 2^(s - m_ref); should any score exceed m_ref by more than 64 or
+  // the sum of weights not be finite, the block runs again with m_ref = the
+  // exact max of each query's scores (second pass), where every weight is <= 1.
+  // The shift cancels in the normalised result.
+  f32x16 o[QF][NRB];
+  float m_ref[QF] = {}, l_run[QF], m_run[QF];
+  // Causal mask of tile x's scores and the running max of this lane's scores.
+  auto softmax_max = [&](int x, f32x16 (&s)[QF]) {
+    if (KT * x + KT - 1 > qmin) {
 #pragma unroll
-  for (int f = 0; f < 2; ++f) {
-    m_ref[f] = -INFINITY;
-    l_run[f] = 0.f;
+      for (int f = 0; f < QF; ++f)
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) o[f][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  auto attend = [&](int x, const char *sb, const char *kb) {
-    f32x4 s[2][2];
-#pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-      for (int f = 0; f < 2; ++f) s[t2][f] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KSD; ++ks) {
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        const u32x4 ak = *(const u32x4 *)(kb + (16 * t2 + n) * SKH + (32 * ks + 8 * g) * 2);
-#pragma unroll
-        for (int f = 0; f < 2; ++f) s[t2][f] = mfma16(ak, qop[f][ks], s[t2][f]);
-      }
+        for (int e = 0; e < 16; ++e)
+          if (KT * x + 8 * (e >> 2) + 4 * g32 + (e & 3) > qpos[f]) s[f][e] = -INFINITY;
     }
-    const bool masked = KT * x + KT - 1 > qmin;
-    u32x4 pop[2];
 #pragma unroll
-    for (int f = 0; f < 2; ++f) {
-      if (masked) {
+    for (int f = 0; f < QF; ++f) {
+      float m = fmaxf(fmaxf(s[f][0], s[f][1]), s[f][2]);
 #pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (KT * x + 16 * t2 + 4 * g + i > qpos[f]) s[t2][f][i] = -INFINITY;
-      }
-      float mx = fmaxf(fmaxf(fmaxf(s[0][f][0], s[0][f][1]), fmaxf(s[0][f][2], s[0][f][3])),
-                       fmaxf(fmaxf(s[1][f][0], s[1][f][1]), fmaxf(s[1][f][2], s[1][f][3])));
-      mx = max_across_rows(mx);
-      if (__builtin_amdgcn_ballot_w64(mx > m_ref[f] + 8.f)) {
-        const float mn = fmaxf(m_ref[f], mx);
-        const float al = mn == -INFINITY ? 1.f : fast_exp2(m_ref[f] - mn);
-#pragma unroll
-        for (int rt = 0; rt < NRT; ++rt) o[f][rt] *= al;
-        l_run[f] *= al;
-        m_ref[f] = mn;
-      }
-      const float mu = m_ref[f] == -INFINITY ? 0.f : m_ref[f];
-      float e[8];
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) e[4 * t2 + i] = fast_exp2(s[t2][f][i] - mu);
-      l_run[f] += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
-      pop[f] = u32x4{cvt2(e[0], e[1]), cvt2(e[2], e[3]), cvt2(e[4], e[5]), cvt2(e[6], e[7])};
+      for (int e = 3; e < 15; e += 2) m = fmaxf(fmaxf(m, s[f][e]), s[f][e + 1]);
+      m_run[f] = fmaxf(fmaxf(m, s[f][15]), m_run[f]);
     }
-    // O^T += C_v^T P^T; K index 8 g + e <-> token 16 (e / 4) + 4 g + e % 4
-    const char *vb = sb + VOFF + (4 * g + (n >> 2)) * SV + 8 * (n & 3);
+  };
+  // Weights of tile x and the latent-space value sums, one 16-token K-step at a
+  // time.  The weights of K-step k are bf16 B-operands holding accumulator
+  // elements 8 k .. + 7, i.e. K index 8 g32 + e <-> token 16 k + 8 (e / 4) +
+  // 4 g32 + e % 4; the sums of weights are taken of the bf16 values.
+  // O^T[r][q] += C_v^T[r][t] P^T[t][q] reads the c_v rows of the tile (slot sb)
+  // transposed: lane (m, g32) of K-step k gets rows 16 k + 8 h + 4 g32 + 0..3.
+  // (Each LDS address is one integer offset from its slot: the compiler loses
+  // the LDS alias scopes on long address chains.)
+  const int vb_lane = VOFF + (4 * g32 + ((lane & 15) >> 2)) * SV + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
+  auto weights = [&](const f32x16 (&s)[QF], int k, u32x4 (&pop)[QF]) {
+    const uint32_t one2 = 0x3F803F80u;  // (1, 1) in bf16
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
-      const u32x2 lo2 = lds_read_tr(vb + 32 * rt);
-      const u32x2 hi2 = lds_read_tr(vb + 16 * SV + 32 * rt);
-      const u32x4 av = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+    for (int f = 0; f < QF; ++f) {
+      const float mu = m_ref[f];
+      float lsum = l_run[f];
 #pragma unroll
-      for (int f = 0; f < 2; ++f) o[f][rt] = mfma16(av, pop[f], o[f][rt]);
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t pe = cvt2(fast_exp2(s[f][8 * k + 2 * e] - mu), fast_exp2(s[f][8 * k + 2 * e + 1] - mu));
+        pop[f][e] = pe;
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pe), __builtin_bit_cast(bf16x2, one2), lsum, false);
+      }
+      l_run[f] = lsum;
     }
+  };
+  auto cv_operands = [&](const char *sb, int k, u32x4 (&av)[NRB]) {
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const u32x2 lo2 = lds_read_tr(sb + (vb_lane + 16 * k * SV + 64 * rb));
+      const u32x2 hi2 = lds_read_tr(sb + (vb_lane + (16 * k + 8) * SV + 64 * rb));
+      av[rb] = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+    }
+  };
+  auto value_sums = [&](const u32x4 (&av)[NRB], const u32x4 (&pop)[QF]) {
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+      for (int f = 0; f < QF; ++f) o[f][rb] = mfma32(av[rb], pop[f], o[f][rb]);
   };
 
   // ---- main loop ----
-  // Step x: clear tile x + 1 if it needs it, load the RoPE rows for its
-  // rebuild, copy tile x + 3 into its slot, attend tile x, rebuild tile x + 1,
-  // barrier.  Tile y lives in slot y % 4 and K buffer y % 2; the copy of tile
-  // y (issued in step y - 3) is complete in every wave after the barrier of
-  // step y - 2 (each wave leaves only the copies of step y - 2 in flight).
-  int okm0 = 3, okm1 = 3, okm2 = 3, okm3 = 3;
+  // Step x: clear tile x + 1 if it needs it, copy tile x + 5, scores of tile x,
+  // mask and max, weights and latent-space value sums of tile x, rebuild of
+  // tile x + 1, barrier.  Tile y lives in slot y % 6 and K buffer y % 2.  The
+  // LDS operands of each matrix phase are loaded in a batch ahead of it
+  // (scheduling fences keep the compiler from pairing each load with its
+  // product, which would expose the LDS latency at every product).
+  // Every load the compiler sees lands before the first tile copy: its own waits
+  // count only those loads, so none of them may be left for the main loop.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt (7) and lgkmcnt (15) not waited
+  int okm0 = 3, okm1 = 3, okm2 = 3, okm3 = 3, okm4 = 3, okm5 = 3;
+#pragma unroll 1
+  for (int pass = 0; pass < 2; ++pass) {
+  for (int f = 0; f < QF; ++f) {
+    l_run[f] = 0.f;
+    m_run[f] = -INFINITY;
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) o[f][rb] = f32x16{};
+  }
   if (nt > 0) {
     fill_pt(0);
-    if (npg > 1024) fill_pt(1);
-    __syncthreads();  // s_pt, s_wk
+    if (npg > PTC) fill_pt(1);
+    __syncthreads();  // s_pt
     okm0 = copy_tile(0, s_c0);
-    if (nt > 1) okm1 = copy_tile(1, s_c1);
-    if (nt > 2) okm2 = copy_tile(2, s_c2);
-    load_rope(0);
-    barrier_vm<0>();
-    clear_tile(0, s_c0, okm0);
-    if (nt > 1) clear_tile(1, s_c1, okm1);
-    barrier_vm<0>();
-    rebuild(s_c0, s_kh0);
-    barrier_vm<0>();
+    okm1 = copy_tile(1, s_c1);
+    okm2 = copy_tile(2, s_c2);
+    okm3 = copy_tile(3, s_c3);
+    okm4 = copy_tile(4, s_c4);
+    barrier_vm<4 * CPW>();  // tile 0
+    if (needs_clear(0, okm0)) clear_tile(0, s_c0, okm0);
+    barrier_vm<4 * CPW>();
+    f32x4 kacc[2 * NTW];
+    rebuild_mfma(s_c0, kacc);
+    rebuild_store(kacc, s_c0, s_k0);
+    barrier_vm<3 * CPW>();  // tile 1, K of tile 0
   }
-  auto step = [&](int x, char *sx, char *sx1, char *sx3, int okx1, int &okx3, char *kbx, char *kbx1) {
-    if (x + 1 < nt && x >= 1 && (x + 1 == nt - 1 || okx1 != 3)) {  // tiles 0 and 1 were cleared above
+  auto step = [&](int x, const char *sx, char *sx1, char *sxd, int okx1, int &okxd, const char *kb0, char *kb1) {
+    if (needs_clear(x + 1, okx1)) {
       clear_tile(x + 1, sx1, okx1);
       barrier_vm<63>();
     }
-    if (((2 * (x + 3)) & 1023) == 0 && 2 * (x + 3) + 1024 < npg) fill_pt(((2 * (x + 3)) >> 10) + 1);
-    load_rope(x + 1);
-    okx3 = copy_tile(x + 3, sx3);
-    attend(x, sx, kbx);
-    if (x + 1 < nt) rebuild(sx1, kbx1);
-    barrier_vm<IPW_MIN>();
+    if ((2 * (x + DIST)) % PTC == 0 && 2 * (x + DIST) + PTC < npg) fill_pt(2 * (x + DIST) / PTC + 1);
+    okxd = copy_tile(x + DIST, sxd);
+    if (x < nt) {
+      u32x4 ak[KSQ];
+#pragma unroll
+      for (int ks = 0; ks < KSQ; ++ks) ak[ks] = *(const u32x4 *)(kb0 + (kr_lane + 32 * ks));
+      __builtin_amdgcn_sched_barrier(0);
+      f32x16 sc[QF];
+#pragma unroll
+      for (int ks = 0; ks < KSQ; ++ks)
+#pragma unroll
+        for (int f = 0; f < QF; ++f) sc[f] = mfma32(ak[ks], qop[f][ks], ks == 0 ? f32x16{} : sc[f]);
+      u32x4 av0[NRB];
+      cv_operands(sx, 0, av0);
+      __builtin_amdgcn_sched_barrier(0);
+      softmax_max(x, sc);
+      if (pass == 0 && x == 0) {
+#pragma unroll
+        for (int f = 0; f < QF; ++f) m_ref[f] = max_across_halves(m_run[f]);
+      }
+      u32x4 pop0[QF], pop1[QF], av1[NRB];
+      weights(sc, 0, pop0);
+      cv_operands(sx, 1, av1);
+      __builtin_amdgcn_sched_barrier(0);
+      value_sums(av0, pop0);
+      weights(sc, 1, pop1);
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 kacc[2 * NTW];
+      value_sums(av1, pop1);
+      rebuild_mfma(sx1, kacc);
+      __builtin_amdgcn_sched_barrier(0);
+      rebuild_store(kacc, sx1, kb1);
+    }
+    barrier_vm<VM_KEEP>();
   };
-  for (int x = 0; x < nt; x += 4) {
-    step(x, s_c0, s_c1, s_c3, okm1, okm3, s_kh0, s_kh1);
-    if (x + 1 < nt) step(x + 1, s_c1, s_c2, s_c0, okm2, okm0, s_kh1, s_kh0);
-    if (x + 2 < nt) step(x + 2, s_c2, s_c3, s_c1, okm3, okm1, s_kh0, s_kh1);
-    if (x + 3 < nt) step(x + 3, s_c3, s_c0, s_c2, okm0, okm2, s_kh1, s_kh0);
+  // Whole groups of six steps; the steps past the last tile only copy (clamped
+  // tiles) and meet.  Every path through a group issues the same copies, so
+  // that the compiler's count of outstanding copies stays exact and its waits
+  // stay on them.
+  for (int x = 0; x < nt; x += 6) {
+    step(x, s_c0, s_c1, s_c5, okm1, okm5, s_k0, s_k1);
+    step(x + 1, s_c1, s_c2, s_c0, okm2, okm0, s_k1, s_k0);
+    step(x + 2, s_c2, s_c3, s_c1, okm3, okm1, s_k0, s_k1);
+    step(x + 3, s_c3, s_c4, s_c2, okm4, okm2, s_k1, s_k0);
+    step(x + 4, s_c4, s_c5, s_c3, okm5, okm3, s_k0, s_k1);
+    step(x + 5, s_c5, s_c0, s_c4, okm0, okm4, s_k1, s_k0);
   }
-  __syncthreads();  // no copy in flight past the loop
+  barrier_vm<0>();  // no copy in flight past the loop
+  // Second pass if a weight could have left the safe range (a workgroup-wide decision).
+  if (pass == 1) break;
+  bool redo = false;
+#pragma unroll
+  for (int f = 0; f < QF; ++f) {
+    const float z = sum_across_halves(l_run[f]);
+    redo |= m_run[f] > m_ref[f] + 64.f || !(fabsf(z) <= 3.0e38f);
+  }
+  if (tid == 0) s_pt[0][0] = 0;
+  __syncthreads();
+  if (__builtin_amdgcn_ballot_w64(redo) && lane == 0) s_pt[0][0] = 1;
+  __syncthreads();
+  if (!__builtin_amdgcn_readfirstlane(s_pt[0][0])) break;
+  __syncthreads();
+#pragma unroll
+  for (int f = 0; f < QF; ++f) m_ref[f] = max_across_halves(m_run[f]);
+  }
 
   // ---- epilogue: normalise, up-project with W_up,v, add mu_v ----
   if (bad_lp != 0x7FFFFFFF) errbits |= LLA_DEVERR_PAGE;
   if (errbits && tid == 0) atomicOr(a.err, errbits);
 
-  u32x4 bup[2][KSV];  // B-operands: a[q][r] with K index 8 g + e <-> r = 32 ks + 16 (e / 4) + 4 g + e % 4
+  // B-operands: K-step k holds r = 16 k + 8 (e / 4) + 4 g32 + e % 4 (elements 8 (k % 2) .. + 7 of block k / 2)
+  u32x4 bup[QF][KSV];
 #pragma unroll
-  for (int f = 0; f < 2; ++f) {
-    const float z = sum_across_rows(l_run[f]);
+  for (int f = 0; f < QF; ++f) {
+    const float z = sum_across_halves(l_run[f]);
     const bool bad = !qok[f] || (long long)qpos[f] >= (long long)kPage * bad_lp;
     const float inv = bad ? __builtin_nanf("") : 1.f / z;
 #pragma unroll
-    for (int ks = 0; ks < KSV; ++ks) {
-      const f32x4 u0 = o[f][2 * ks] * inv, u1 = o[f][2 * ks + 1] * inv;
-      bup[f][ks] = u32x4{cvt2(u0[0], u0[1]), cvt2(u0[2], u0[3]), cvt2(u1[0], u1[1]), cvt2(u1[2], u1[3])};
+    for (int k = 0; k < KSV; ++k) {
+      const f32x16 &u = o[f][k >> 1];
+      const int e0 = 8 * (k & 1);
+      bup[f][k] = u32x4{cvt2(u[e0] * inv, u[e0 + 1] * inv), cvt2(u[e0 + 2] * inv, u[e0 + 3] * inv),
+                        cvt2(u[e0 + 4] * inv, u[e0 + 5] * inv), cvt2(u[e0 + 6] * inv, u[e0 + 7] * inv)};
     }
   }
   const char *wvh = a.wup_v + (long long)h * a.wup_head_stride_v * 2;
   const uint16_t *mvh = (const uint16_t *)a.mu_v + (long long)h * a.mu_head_stride;
-#pragma unroll 2
-  for (int et = 0; et < NDT; ++et) {
-    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    const char *wr = wvh + ((long long)(16 * et + n) * RV + 4 * g) * 2;
+#pragma unroll 1
+  for (int db = 0; db < DH / 32; ++db) {
+    f32x16 acc[QF];
 #pragma unroll
-    for (int ks = 0; ks < KSV; ++ks) {
-      const u32x2 w0v = *(const u32x2 *)(wr + 64 * ks);
-      const u32x2 w1v = *(const u32x2 *)(wr + 64 * ks + 32);
-      const u32x4 av = u32x4{w0v[0], w0v[1], w1v[0], w1v[1]};
+    for (int f = 0; f < QF; ++f) acc[f] = f32x16{};
+    const char *wr = wvh + ((long long)(32 * db + n32) * RV + 4 * g32) * 2;
 #pragma unroll
-      for (int f = 0; f < 2; ++f) acc[f] = mfma16(av, bup[f][ks], acc[f]);
+    for (int k = 0; k < KSV; ++k) {
+      const u32x2 wlo = *(const u32x2 *)(wr + 32 * k);
+      const u32x2 whi = *(const u32x2 *)(wr + 32 * k + 16);
+      const u32x4 av = u32x4{wlo[0], wlo[1], whi[0], whi[1]};
+#pragma unroll
+      for (int f = 0; f < QF; ++f) acc[f] = mfma32(av, bup[f][k], acc[f]);
     }
-    const u32x2 mu2 = *(const u32x2 *)(mvh + 16 * et + 4 * g);
 #pragma unroll
-    for (int f = 0; f < 2; ++f) {
-      const int iq = w0 + 16 * f + n;
-      if (iq < r1) {
-        uint16_t *orow = (uint16_t *)a.out + (((long long)b * nq + iq) * a.H + h) * DH + 16 * et + 4 * g;
-        *(u32x2 *)orow = u32x2{cvt2(acc[f][0] + bf16_lo(mu2[0]), acc[f][1] + bf16_hi(mu2[0])),
-                               cvt2(acc[f][2] + bf16_lo(mu2[1]), acc[f][3] + bf16_hi(mu2[1]))};
+    for (int j = 0; j < 4; ++j) {
+      const int d = 32 * db + 8 * j + 4 * g32;
+      const u32x2 mu2 = *(const u32x2 *)(mvh + d);
+#pragma unroll
+      for (int f = 0; f < QF; ++f) {
+        const int iq = w0 + 32 * f + n32;
+        if (iq < r1) {
+          uint16_t *orow = (uint16_t *)a.out + (((long long)b * nq + iq) * a.H + h) * DH + d;
+          *(u32x2 *)orow = u32x2{cvt2(acc[f][4 * j] + bf16_lo(mu2[0]), acc[f][4 * j + 1] + bf16_hi(mu2[0])),
+                                 cvt2(acc[f][4 * j + 2] + bf16_lo(mu2[1]), acc[f][4 * j + 3] + bf16_hi(mu2[1]))};
+        }
       }
     }
   }
 }
 
 // ---------------------------------------------------------------- dispatch
+
+// Waves per workgroup (256 queries): two per SIMD at d = 128, one at d = 64.
+#ifndef PREFILL_WAVES128
+#define PREFILL_WAVES128 8
+#endif
+#define PREFILL_WAVES(DH) ((DH) == 128 ? PREFILL_WAVES128 : 4)
 
 // (d_head, r_k, r_v)
 #define LLA_PREFILL_SHAPES(X) \
@@ -508,7 +679,8 @@ hipError_t launch_prefill(int d_head, int r_k, int r_v, const AttnArgs &a, hipSt
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
 #define X(DH, RK, RV)                                                                                \
   if (d_head == DH && r_k == RK && r_v == RV) {                                                      \
-    hipLaunchKernelGGL((prefill_kernel<DH, RK, RV>), dim3((unsigned)grid), dim3(512), 0, stream, a); \
+    hipLaunchKernelGGL((prefill_kernel<DH, RK, RV, PREFILL_WAVES(DH)>), dim3((unsigned)grid),              \
+                       dim3(64 * PREFILL_WAVES(DH)), 0, stream, a);                                            \
     return hipGetLastError();                                                                        \
   }
   LLA_PREFILL_SHAPES(X)
