@@ -13,30 +13,34 @@
 // multiply-adds per token and query.  With a chunk of queries it is cheaper to
 // rebuild each K tile once per workgroup (the close reading's long-prefill
 // remark: rebuild per layer, keep nothing) and run a dense attention:
-//  * A workgroup = 8 waves = 256 consecutive queries of one (sequence, head);
-//    wave w owns 32 of them as two 16-query MFMA columns (two waves per SIMD).
-//  * Keys go in 32-token tiles (two pages).  A tile's c_k and c_v rows are
-//    copied global -> LDS with direct-to-LDS loads three tiles ahead, into one
-//    of four slots (separate LDS objects, so that the compiler's waits stay
-//    per slot; rows padded against bank conflicts).  Rows past the last needed
-//    position, and rows of a page whose table entry is out of range, are
-//    cleared to zero before use.  The page-table entries of the sequence are
-//    staged in LDS, 1024 at a time.
-//  * Rebuild, one tile ahead: every wave turns one 16-token x (16 + 16)-dim
-//    block of the tile into rotated K (v_mfma_f32_16x16x32_bf16 with W_up,k rows
-//    from LDS as the A-operand; mu and RoPE in fp32 on the accumulator, which
-//    holds both halves of each RoPE pair in one lane) and stores it in bf16 to
-//    a double-buffered LDS tile.
-//  * S^T = K Q'^T per 16x16 block with Q' = scale log2(e) R(p) q in bf16
-//    registers; each lane holds one query's column, so the online softmax
-//    needs only two cross-row swaps for the max.  The running max is moved
-//    only when a tile exceeds it by more than 8 (weights stay <= 2^8; the
-//    result is the same), which skips most rescales of the accumulator.
+//  * A workgroup = 256 consecutive queries of one (sequence, head): 8 waves of
+//    32 queries at d = 128 (two waves per SIMD), 4 waves of 64 at d = 64.
+//  * Keys go in 32-token tiles (two pages).  A tile's c_k and c_v rows and the
+//    RoPE row of its first position are copied global -> LDS with direct-to-LDS
+//    loads five tiles ahead, into one of six slots.  The copies are issued in
+//    inline asm and waited for explicitly (each step's barrier leaves the
+//    newest copies in flight), so that the compiler adds no waits of its own
+//    on them.  c_k rows are padded and c_v rows sized so that the transposing
+//    reads avoid bank conflicts.  Rows past the last needed position, and rows
+//    of a page whose table entry is out of range, are cleared to zero before
+//    use.  The page-table entries of the sequence are staged in LDS.
+//  * Rebuild, one tile ahead: each wave turns a 16-dim block and its RoPE
+//    partner block of the tile into rotated K (v_mfma_f32_16x16x32_bf16 with
+//    the W_up,k rows staged once in LDS as the A-operand; mu as the initial
+//    accumulator; RoPE in fp32 by angle addition from the copied row of the
+//    tile's first position and per-lane constants of the row offset) and stores
+//    it in bf16 to a double-buffered LDS tile.
+//  * S^T = K Q'^T with v_mfma_f32_32x32x16_bf16 and Q' = scale log2(e) R(p) q
+//    in bf16 registers: each lane holds one query's column for 16 tokens.
+//  * Softmax with one fixed reference per query (the max of its first tile):
+//    no rescaling of the accumulators.  If a score exceeds the reference by
+//    more than 64 or the sum of weights is not finite, the block runs again
+//    with the exact max as the reference.  The sums of weights are taken of the
+//    bf16 weights the value sums use.
 //  * O^T[r][q] += C_v^T[r][t] P^T[t][q]: the bf16 weights come straight from
 //    the score accumulator as the B-operand; the c_v tile is read transposed
 //    with ds_read_b64_tr_b16 as the A-operand.
-//  * One barrier per tile: each wave first waits for its own copies of the
-//    tile the next step rebuilds, then all waves meet.
+//  * The LDS operands of each matrix phase are loaded in a batch ahead of it.
 //  * Epilogue: O / Z in bf16 times W_up,v on the matrix cores, plus mu_v.
 #include "lla_device.h"
 #include "lla_internal.h"
