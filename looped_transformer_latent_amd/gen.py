@@ -2,7 +2,7 @@
 
 This module holds random-number generation only -- none of the attention,
 encoder or decoder arithmetic.  It is the one piece shared by the oracle tests
-and the GPU tests: both draw their inputs from it.  ``csrc/gen.hip`` implements
+and the GPU tests: both draw their inputs from it.  ``csrc/gen/lla_gen.hip`` implements
 the same generator on the device (for inputs too large to upload, such as a
 100 GB latent pool), and tests check that both give identical bits.
 
