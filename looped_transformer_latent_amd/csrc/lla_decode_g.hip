@@ -130,8 +130,9 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 1 : 2) void decode_g_kernel(Attn
   // magnitude lies in [2^14, 2^15): by Cauchy-Schwarz on a pair,
   // |A_ir|, |B_ir| <= |(q'_a, q'_b)| |(W[a][r], W[b][r])| <= qscale max_i |(q_a, q_b)| sqrt(2) max |W|,
   // and the same with mu for (alpha_i, beta_i).  The scores are multiplied by
-  // 2^-e after the products; scaling by a power of two commutes with every
-  // rounding in normal range, so nothing else changes.
+  // 2^-e after the products (inside the exponent's argument); scaling by a
+  // power of two commutes with every rounding in normal range, so nothing
+  // else changes.
   extern __shared__ __attribute__((aligned(16))) char smem[];
   u32x4 F[HPW][RT][KS];
   u32x4 Fa[KS];
@@ -232,10 +233,13 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 1 : 2) void decode_g_kernel(Attn
     }
   }
 
-  float m_run[HPW], z[HPW], acc[HPW][CV];
+  // m_run: running maximum of the raw (2^e-scaled) scores; nmu = -m_run 2^-e,
+  // so that a token's weight is exp2(fma(score, 2^-e, nmu)).
+  float m_run[HPW], nmu[HPW], z[HPW], acc[HPW][CV];
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
     m_run[hh] = -INFINITY;
+    nmu[hh] = 0.f;
     z[hh] = 0.f;
 #pragma unroll
     for (int k = 0; k < CV; ++k) acc[hh][k] = 0.f;
@@ -316,17 +320,21 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 1 : 2) void decode_g_kernel(Attn
     }
   };
 
+  // Per-head pools: [page][H][kPage][r] with the heads kPage r elements apart.
+  const uint32_t kpb = (uint32_t)a.pool_page_stride_k * 2u, vpb = (uint32_t)a.pool_page_stride_v * 2u;
+  constexpr int KHB = kPage * RK * 2, VHB = kPage * RV * 2;  // bytes per (page, head)
+  const uint32_t kwave = (uint32_t)(h0 * KHB), vwave = (uint32_t)(h0 * VHB);
   auto load_page = [&](int lp, int pp_raw, Page &pg) {
-    pg.ok = (pp_raw >= 0 && pp_raw < a.num_pages);
-    const long long pp = pg.ok ? pp_raw : 0;
+    pg.ok = (uint32_t)pp_raw < (uint32_t)a.num_pages;
+    const uint32_t pp = pg.ok ? (uint32_t)pp_raw : 0u;
     pg.last = min(kPage - 1, ctx - 1 - logical(lp) * kPage);
     const int row_n = min(n, pg.last);
     // uniform page bases + 32-bit lane offsets; latents are read exactly once
-    const char *kpage = a.k_pool + pp * a.pool_page_stride_k * 2;
-    const char *vpage = a.v_pool + pp * a.pool_page_stride_v * 2;
+    const char *kpage = a.k_pool + (uint64_t)pp * kpb;
+    const char *vpage = a.v_pool + (uint64_t)pp * vpb;
     if constexpr (XP) {  // whole (page, head) block in address order
-      const uint32_t koff = (uint32_t)(h0 * a.pool_head_stride_k * 2 + 8 * lane);
-      const uint32_t voff = (uint32_t)(h0 * a.pool_head_stride_v * 2 + 16 * lane);
+      const uint32_t koff = kwave + 8 * lane;
+      const uint32_t voff = vwave + 16 * lane;
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
         pg.k[0][rt] = __builtin_nontemporal_load((const u32x2 *)(kpage + koff + 512 * rt));
@@ -335,27 +343,35 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 1 : 2) void decode_g_kernel(Attn
         pg.v[0][kv] = __builtin_nontemporal_load((const u32x4 *)(vpage + voff + 1024 * kv));
       return;
     }
+    const uint32_t koff = kwave + (uint32_t)((row_n * RK + 4 * g) * 2);
+    const uint32_t voff = vwave + (uint32_t)((row_n * RV + CV * g) * 2);
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
-      const int h = h0 + hh;
-      const uint32_t koff = (uint32_t)((h * a.pool_head_stride_k + row_n * RK + 4 * g) * 2);
-      const uint32_t voff = (uint32_t)((h * a.pool_head_stride_v + row_n * RV + CV * g) * 2);
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
-        pg.k[hh][rt] = __builtin_nontemporal_load((const u32x2 *)(kpage + koff + 32 * rt));
+        pg.k[hh][rt] = __builtin_nontemporal_load((const u32x2 *)(kpage + koff + hh * KHB + 32 * rt));
 #pragma unroll
       for (int kv = 0; kv < KV; ++kv)
-        pg.v[hh][kv] = __builtin_nontemporal_load((const u32x4 *)(vpage + voff + kv * 16));
+        pg.v[hh][kv] = __builtin_nontemporal_load((const u32x4 *)(vpage + voff + hh * VHB + kv * 16));
     }
   };
 
   // An invalid page-table entry was replaced by page 0 at load time; its
   // tokens are masked out here and the row is poisoned through the error bits.
-  auto compute_page = [&](Page &cur, int lp) {
+  // th_off[s]: the lane's 16-byte slot (pairs 16 s + 4 g .. + 3, token row n)
+  // within a page's rows of a RoPE chunk buffer.
+  uint32_t th_off[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) th_off[s] = (uint32_t)((n * SPR + ((4 * s + g) ^ (n & SWZ))) * 16);
+  auto compute_page = [&](Page &cur, int lp, const char *trip_rope, int u) {
     errbits |= cur.ok ? 0 : LLA_DEVERR_PAGE;
-    const int j = logical(lp) * kPage + n;  // this lane's token
-    const bool valid = cur.ok && n <= cur.last && lp < lp1 &&  // lp >= lp1: ring padding
-                       (j < keep_lo || j >= keep_hi);         // evicted rows of edge pages
+    // Lane token lo + n takes part iff it is retained and below ctx; a bad
+    // page or ring padding (lp >= lp1) takes no token.  Written with bitwise
+    // operators so that it stays a lane mask (no branches).
+    const int lo = logical(lp) * kPage;
+    const bool pg_in = cur.ok && lp < lp1;
+    const int la = pg_in ? keep_lo - lo : 0, lb = keep_hi - lo, lc = pg_in ? ctx - lo : 0;
+    const bool valid = (n < la) | ((n >= lb) & (n < lc));
     const int row_n = min(n, cur.last);
     if constexpr (XP) {  // address order -> compute layout, through the wave's LDS region
       uint16_t *xb = (uint16_t *)(smem + GLayout<DH, RK, RV, HPW, NW>::w_off(a.pages_per_split)) +
@@ -382,12 +398,12 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 1 : 2) void decode_g_kernel(Attn
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-    const char *tb = s_trig + (((lp - lp0) / CH) & 1) * TSB * 16 +
-                     (((lp - lp0) % CH) * kPage + row_n) * SPR * 16;
-    // B-operands: RoPE pairs 16 s + 4 g .. + 3 of token n, (cos, sin) fp16
+    // B-operands: RoPE pairs 16 s + 4 g .. + 3 of token n, (cos, sin) fp16.
+    // Rows past ctx hold the RoPE row of ctx - 1 (the staging clamps), so
+    // they stay finite; their scores are masked.
     u32x4 th[KS];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) th[s] = *(const u32x4 *)(tb + (((4 * s + g) ^ (row_n & SWZ)) * 16));
+    for (int s = 0; s < KS; ++s) th[s] = *(const u32x4 *)(trip_rope + th_off[s] + u * (kPage * SPR * 16));
     // G0 of the wave's heads: rows 0 .. HPW-1 (lane (0, n) element hh)
     f32x4 Ga = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -409,17 +425,20 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 1 : 2) void decode_g_kernel(Attn
         sc = fmaf(bf16_hi(cur.k[hh][rt][1]), G[3], sc);
       }
       sc = sum_across_rows(sc);
-      sc = valid ? sc * unscale[hh] : -INFINITY;
-      const float mt = max_in_row(sc);
-      if (mt > m_run[hh]) {  // wave-uniform
-        const float corr = fast_exp2(m_run[hh] - mt);
+      sc = valid ? sc : -INFINITY;
+      // Raise the running maximum only when a token of the page exceeds it
+      // (after the first pages, rarely): same maxima as a max per page.
+      if (__builtin_amdgcn_ballot_w64(sc > m_run[hh]) != 0) {  // wave-uniform
+        const float mt = max_in_row(sc);  // all four rows hold the same 16 scores
+        const float corr = fast_exp2((m_run[hh] - mt) * unscale[hh]);
         z[hh] *= corr;
 #pragma unroll
         for (int k = 0; k < CV; ++k) acc[hh][k] *= corr;
         m_run[hh] = mt;
+        nmu[hh] = -mt * unscale[hh];
       }
-      // a masked token weighs 0, also while m_run is still -inf (no valid token yet)
-      const float p = valid ? fast_exp2(sc - m_run[hh]) : 0.f;
+      // a masked token (-inf) weighs 0, also before the first valid token
+      const float p = fast_exp2(fmaf(sc, unscale[hh], nmu[hh]));
       z[hh] += p;
 #pragma unroll
       for (int kv = 0; kv < KV; ++kv) {
@@ -454,11 +473,17 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 1 : 2) void decode_g_kernel(Attn
     __syncthreads();
     stage_load(1);
     for (int lp = lp0; lp < lp_end; lp += NBUF) {
+      int pid[NBUF];  // the trip's page-table entries, read together (one LDS wait per trip)
+#pragma unroll
+      for (int u = 0; u < NBUF; ++u) pid[u] = s_pt[min(lp + u + LOOK, lp1 - 1) - lp0];
+#pragma unroll
+      for (int u = 0; u < NBUF; ++u) pid[u] = __builtin_amdgcn_readfirstlane(pid[u]);
+      const char *trip_rope = s_trig + (((lp - lp0) / CH) & 1) * TSB * 16;
 #pragma unroll
       for (int u = 0; u < NBUF; ++u) {
         const int l = min(lp + u + LOOK, lp1 - 1);
-        load_page(l, page_at(l), ring[(u + LOOK) % NBUF]);
-        compute_page(ring[u], lp + u);
+        load_page(l, pid[u], ring[(u + LOOK) % NBUF]);
+        compute_page(ring[u], lp + u, trip_rope, u);
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -492,7 +517,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 1 : 2) void decode_g_kernel(Attn
         for (int k = 0; k < CV; ++k) part[CV * g + k] = acc[hh][k];
       }
       if (lane == 0) {
-        part[RV] = m_run[hh];
+        part[RV] = m_run[hh] * unscale[hh];
         part[RV + 1] = bad ? __builtin_nanf("") : z[hh];
       }
     }
