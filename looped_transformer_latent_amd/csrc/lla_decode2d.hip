@@ -11,13 +11,14 @@
 // Per token this is d*r_k multiply-adds per head for the K side (2 MFLOP per
 // token at H=32, d=128, r_k=256), so unlike per-head LLA the path is bound by
 // the matrix cores, not by HBM.  Layout of the work:
-//  * A workgroup = 4 waves = 4 heads of one query row and one split of the
-//    context.  Wave w folds the rotated query of its head into the K decoder
-//    (the same exact algebra as the per-head kernel: for RoPE pair i,
-//    X_i = alpha_i + A_i . c, Y_i = beta_i + B_i . c and
-//    s * log2(e) = sum_i cos_i(j) X_i + sin_i(j) Y_i) and keeps the d x (r_k+1)
-//    result in registers as the A-operands of v_mfma_f32_32x32x16_bf16
-//    (alpha / beta as hi + lo bf16 in one extra K-step).
+//  * A workgroup = 8 waves = 4 heads of one query row and one split of the
+//    context, two waves per head.  The waves of a head fold its rotated query
+//    into the K decoder (the same exact algebra as the per-head kernel: for
+//    RoPE pair i, X_i = alpha_i + A_i . c, Y_i = beta_i + B_i . c and
+//    s * log2(e) = sum_i cos_i(j) X_i + sin_i(j) Y_i), each for half of the
+//    RoPE pairs, and keep that half of the d x (r_k+1) result in registers as
+//    the A-operands of v_mfma_f32_32x32x16_bf16 (alpha / beta as hi + lo bf16
+//    in one extra K-step).
 //  * Tokens go in blocks of 32 (two 16-token pages).  The block's c_k, c_v and
 //    RoPE rows are copied global -> LDS with buffer loads straight into LDS (no
 //    register staging; whole rows per instruction, one shared lane offset as
@@ -28,12 +29,13 @@
 //    The tile is shared by the 4 waves, so each latent is fetched from L2 once
 //    per workgroup.  Workgroups of the same (row, split) but different head
 //    groups are dispatched to the same XCD so that they share its L2.
-//  * K side: 4 x 17 MFMAs per wave per block give X / Y for the 64 pairs x 32
-//    tokens; each lane weights its 32 values by cos / sin (fp32) and one
-//    permlane32 swap completes the score.  Online softmax in base 2.
+//  * K side: 2 x 17 MFMAs per wave per block give X / Y for its 32 pairs x 32
+//    tokens; each lane weights its values by cos / sin (fp32), one permlane32
+//    swap completes the wave's half-score, and the two halves of a head meet
+//    in LDS (added in the same order by both).  Online softmax in base 2.
 //  * V side, exact by linearity: sum_j p_j,h c_v,j for the 4 heads is one more
 //    MFMA product, P[tokens x 4 heads] (bf16 weights via LDS) times the c_v
-//    tile; wave w owns r_v/4 of the columns for all 4 heads.
+//    tile; wave w owns r_v/8 of the columns for all 4 heads.
 //  * With one split the workgroup up-projects once per head; with several it
 //    writes (m, Z, acc) partials for the merge launch (lla_merge.hip).
 #include "lla_device.h"
