@@ -140,46 +140,69 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 1 : 2) void decode_g_kernel(Attn
   {
     uint16_t *s_w = (uint16_t *)(smem + GLayout<DH, RK, RV, HPW, NW>::w_off(a.pages_per_split)) +
                     wave * (HPW * DH * RK);
+    // Every global load of the prologue goes out first (one round trip instead
+    // of one per stage): the wave's W_up,k rows, its q and mu_k pairs, and the
+    // RoPE row of q_pos.
+    constexpr int WC = DH * RK / 8 / 64;  // 16-byte pieces of a head's W_up,k per lane
+    u32x4 wv[HPW][WC];
+    u32x2 qa4[HPW][KS], qb4[HPW][KS], ma4[HPW][KS], mb4[HPW][KS];
+    f32x4 cs01[KS], cs23[KS];
+    const float *rq = a.rope + (long long)qp * DH;
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      const int h = h0 + hh;
+      const u32x4 *src = (const u32x4 *)((const uint16_t *)a.wup_k + (long long)h * a.wup_head_stride_k);
+#pragma unroll
+      for (int c = 0; c < WC; ++c) wv[hh][c] = src[c * 64 + lane];
+      const uint16_t *qrow = (const uint16_t *)a.q + ((long long)row * a.H + h) * DH;
+      const uint16_t *mu = (const uint16_t *)a.mu_k + (long long)h * a.mu_head_stride;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const int i0 = 16 * s + 4 * g;  // pairs i0 .. i0 + 3 of this lane
+        qa4[hh][s] = *(const u32x2 *)(qrow + i0);
+        qb4[hh][s] = *(const u32x2 *)(qrow + i0 + HALF);
+        ma4[hh][s] = *(const u32x2 *)(mu + i0);
+        mb4[hh][s] = *(const u32x2 *)(mu + i0 + HALF);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int i0 = 16 * s + 4 * g;
+      cs01[s] = *(const f32x4 *)(rq + 2 * i0);
+      cs23[s] = *(const f32x4 *)(rq + 2 * i0 + 4);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads above together
     uint32_t mag[HPW];  // largest |bf16| bit pattern of W_up,k and mu_k (magnitude order = integer order)
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
-      const u32x4 *src = (const u32x4 *)((const uint16_t *)a.wup_k + (long long)(h0 + hh) * a.wup_head_stride_k);
       u32x4 *dst = (u32x4 *)(s_w + hh * DH * RK);
       mag[hh] = 0;
 #pragma unroll
-      for (int c = 0; c < DH * RK / 8 / 64; ++c) {
-        const u32x4 v = src[c * 64 + lane];
-        dst[c * 64 + lane] = v;
+      for (int c = 0; c < WC; ++c) {
+        dst[c * 64 + lane] = wv[hh][c];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) mag[hh] = max(mag[hh], max(v[k] & 0x7FFFu, (v[k] >> 16) & 0x7FFFu));
+        for (int k = 0; k < 4; ++k) mag[hh] = max(mag[hh], max(wv[hh][c][k] & 0x7FFFu, (wv[hh][c][k] >> 16) & 0x7FFFu));
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const float *rq = a.rope + (long long)qp * DH;
     float qscale_h[HPW];
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
-      const int h = h0 + hh;
-      const uint16_t *qrow = (const uint16_t *)a.q + ((long long)row * a.H + h) * DH;
-      const uint16_t *mu = (const uint16_t *)a.mu_k + (long long)h * a.mu_head_stride;
       float qn2 = 0.f;  // largest |(q_a, q_b)|^2 of the lane's pairs
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const int i0 = 16 * s + 4 * g;
-        const u32x2 qa4 = *(const u32x2 *)(qrow + i0), qb4 = *(const u32x2 *)(qrow + i0 + HALF);
-        const u32x2 ma4 = *(const u32x2 *)(mu + i0), mb4 = *(const u32x2 *)(mu + i0 + HALF);
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          const float qa = p & 1 ? bf16_hi(qa4[p >> 1]) : bf16_lo(qa4[p >> 1]);
-          const float qb = p & 1 ? bf16_hi(qb4[p >> 1]) : bf16_lo(qb4[p >> 1]);
+          const float qa = p & 1 ? bf16_hi(qa4[hh][s][p >> 1]) : bf16_lo(qa4[hh][s][p >> 1]);
+          const float qb = p & 1 ? bf16_hi(qb4[hh][s][p >> 1]) : bf16_lo(qb4[hh][s][p >> 1]);
           qn2 = fmaxf(qn2, qa * qa + qb * qb);
         }
 #pragma unroll
         for (int k = 0; k < 2; ++k)
-          mag[hh] = max(mag[hh], max(max(ma4[k] & 0x7FFFu, (ma4[k] >> 16) & 0x7FFFu),
-                                     max(mb4[k] & 0x7FFFu, (mb4[k] >> 16) & 0x7FFFu)));
+          mag[hh] = max(mag[hh], max(max(ma4[hh][s][k] & 0x7FFFu, (ma4[hh][s][k] >> 16) & 0x7FFFu),
+                                     max(mb4[hh][s][k] & 0x7FFFu, (mb4[hh][s][k] >> 16) & 0x7FFFu)));
       }
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) {
@@ -199,22 +222,16 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 1 : 2) void decode_g_kernel(Attn
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const int i0 = 16 * s + 4 * g;  // pairs i0 .. i0 + 3 of this lane
-      const f32x4 cs01 = *(const f32x4 *)(rq + 2 * i0), cs23 = *(const f32x4 *)(rq + 2 * i0 + 4);
 #pragma unroll
       for (int hh = 0; hh < HPW; ++hh) {
-        const int h = h0 + hh;
-        const uint16_t *qrow = (const uint16_t *)a.q + ((long long)row * a.H + h) * DH;
-        const uint16_t *mu = (const uint16_t *)a.mu_k + (long long)h * a.mu_head_stride;
-        const u32x2 qa4 = *(const u32x2 *)(qrow + i0), qb4 = *(const u32x2 *)(qrow + i0 + HALF);
-        const u32x2 ma4 = *(const u32x2 *)(mu + i0), mb4 = *(const u32x2 *)(mu + i0 + HALF);
         const uint16_t *w = s_w + hh * DH * RK;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           const int i = i0 + p;
-          const f32x4 &cq = p < 2 ? cs01 : cs23;
+          const f32x4 &cq = p < 2 ? cs01[s] : cs23[s];
           const float c = cq[2 * (p & 1)], sn = cq[2 * (p & 1) + 1];
-          const float qa = p & 1 ? bf16_hi(qa4[p >> 1]) : bf16_lo(qa4[p >> 1]);
-          const float qb = p & 1 ? bf16_hi(qb4[p >> 1]) : bf16_lo(qb4[p >> 1]);
+          const float qa = p & 1 ? bf16_hi(qa4[hh][s][p >> 1]) : bf16_lo(qa4[hh][s][p >> 1]);
+          const float qb = p & 1 ? bf16_hi(qb4[hh][s][p >> 1]) : bf16_lo(qb4[hh][s][p >> 1]);
           const float pa = qscale_h[hh] * (qa * c - qb * sn);
           const float pb = qscale_h[hh] * (qa * sn + qb * c);
 #pragma unroll
@@ -224,8 +241,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 1 : 2) void decode_g_kernel(Attn
             const float wb = bf16_to_f32(w[(i + HALF) * RK + r]);
             F[hh][rt][s][p] = pack_f16(pa * wa + pb * wb, pb * wa - pa * wb);
           }
-          const float ma = p & 1 ? bf16_hi(ma4[p >> 1]) : bf16_lo(ma4[p >> 1]);
-          const float mb = p & 1 ? bf16_hi(mb4[p >> 1]) : bf16_lo(mb4[p >> 1]);
+          const float ma = p & 1 ? bf16_hi(ma4[hh][s][p >> 1]) : bf16_lo(ma4[hh][s][p >> 1]);
+          const float mb = p & 1 ? bf16_hi(mb4[hh][s][p >> 1]) : bf16_lo(mb4[hh][s][p >> 1]);
           const uint32_t ab = pack_f16(pa * ma + pb * mb, pb * ma - pa * mb);
           if (n == hh) Fa[s][p] = ab;
         }
