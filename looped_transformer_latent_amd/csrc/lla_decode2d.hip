@@ -95,7 +95,7 @@ __global__ __launch_bounds__(512) void decode_2d_kernel(AttnArgs a) {
   constexpr int CVQ = RV / 16;   // 1 KiB direct loads per tile: c_v
   constexpr int VR = RV / NW;    // V columns per wave (all 4 heads)
   constexpr int VT = VR / 16;    // V MFMA tiles per wave (16x16x32)
-  static_assert(PW % 16 == 0 && RK % 128 == 0 && VR == 32 && VT == 2, "shape");
+  static_assert(PW % 16 == 0 && RK % 128 == 0 && VR == 32 && VT == 2 && KS >= 5, "shape");
   static_assert(CVQ % NW == 0 && 32 % NW == 0 && RK / 8 <= 64 && DH / 4 <= 64 && RV == 256, "tile split");
 
   __shared__ Tile2d<DH, RK, RV> tile0, tile1, tile2;
@@ -211,38 +211,50 @@ __global__ __launch_bounds__(512) void decode_2d_kernel(AttnArgs a) {
   // Offsets past a descriptor's size read zeros.  Waves 0 .. NW/2 - 1 copy
   // the block's first page, the others its second.
   const int lane16 = 16 * lane;
-  auto issue = [&](int blk, Tile2d<DH, RK, RV> &T) {
+  // s_pt index of the page this wave copies for block blk
+  auto page_idx = [&](int blk) -> int {
+    return min((j_lo + 32 * blk) / kPage + (w >= NW / 2 ? 1 : 0), lp1 - 1) - lp0;
+  };
+  // pg: that page (read from s_pt a step earlier, so no LDS wait sits here)
+  // The copies of one block in five parts of two instructions each (c_k rows,
+  // c_v, RoPE rows), so that they can be issued between K-side products: a
+  // wave that issued them all at once waited on the copy queue.
+  auto issue_part = [&](int blk, long long pg, Tile2d<DH, RK, RV> &T, int part) {
     const int j0 = j_lo + 32 * blk;
-    const int lp = min(j0 / kPage + (w >= NW / 2 ? 1 : 0), lp1 - 1) - lp0;
-    const long long pg = __builtin_amdgcn_readfirstlane(s_pt[lp]);
-    // c_k: one row (token) per half-wave instruction
-    constexpr int CPT = RK / 8;  // 16-byte pieces per c_k row
-    const char *kpg = a.k_pool + pg * a.pool_page_stride_k * 2;
+    if (part < 2) {  // c_k: one row (token) per half-wave instruction
+      constexpr int CPT = RK / 8;  // 16-byte pieces per c_k row
+      const char *kpg = a.k_pool + pg * a.pool_page_stride_k * 2;
 #pragma unroll
-    for (int i = 0; i < 32 / NW; ++i) {
-      const int tok = w * (32 / NW) + i;
-      if (lane < CPT)
-        buffer_to_lds16(kpg, kPage * RK * 2, &T.ck[tok][0], lane16, (tok & 15) * RK * 2);
-    }
-    // c_v: two rows per instruction
-    const char *vpg = a.v_pool + pg * a.pool_page_stride_v * 2;
+      for (int i = 2 * part; i < 2 * part + 2; ++i) {
+        const int tok = w * (32 / NW) + i;
+        if (lane < CPT)
+          buffer_to_lds16(kpg, kPage * RK * 2, &T.ck[tok][0], lane16, (tok & 15) * RK * 2);
+      }
+    } else if (part == 2) {  // c_v: two rows per instruction
+      const char *vpg = a.v_pool + pg * a.pool_page_stride_v * 2;
 #pragma unroll
-    for (int i = 0; i < CVQ / NW; ++i) {
-      const int q = w * (CVQ / NW) + i;
-      buffer_to_lds16(vpg, kPage * RV * 2, &T.cv[q * 64], lane16, ((2 * q) & 15) * RV * 2);
-    }
-    // RoPE rows of the block's positions: one row per half-wave instruction;
-    // rows past the table read zeros (their tokens lie past the context)
-    constexpr int TPT = DH / 4;  // 16-byte pieces per RoPE row
-    const int jr = min(j0, a.rope_len - 1);
-    const char *rrow = rope_b + (long long)jr * (DH * 4);
-    const uint32_t rbytes = (uint32_t)(a.rope_len - jr) * (DH * 4);
+      for (int i = 0; i < CVQ / NW; ++i) {
+        const int q = w * (CVQ / NW) + i;
+        buffer_to_lds16(vpg, kPage * RV * 2, &T.cv[q * 64], lane16, ((2 * q) & 15) * RV * 2);
+      }
+    } else {  // RoPE rows of the block's positions: one row per half-wave
+              // instruction; rows past the table read zeros (their tokens lie
+              // past the context)
+      constexpr int TPT = DH / 4;  // 16-byte pieces per RoPE row
+      const int jr = min(j0, a.rope_len - 1);
+      const char *rrow = rope_b + (long long)jr * (DH * 4);
+      const uint32_t rbytes = (uint32_t)(a.rope_len - jr) * (DH * 4);
 #pragma unroll
-    for (int i = 0; i < 32 / NW; ++i) {
-      const int tok = w * (32 / NW) + i;
-      if (lane < TPT)
-        buffer_to_lds16(rrow, rbytes, &T.trig[tok][0], lane16, (j0 - jr + tok) * (DH * 4));
+      for (int i = 2 * (part - 3); i < 2 * (part - 3) + 2; ++i) {
+        const int tok = w * (32 / NW) + i;
+        if (lane < TPT)
+          buffer_to_lds16(rrow, rbytes, &T.trig[tok][0], lane16, (j0 - jr + tok) * (DH * 4));
+      }
     }
+  };
+  auto issue = [&](int blk, long long pg, Tile2d<DH, RK, RV> &T) {
+#pragma unroll
+    for (int part = 0; part < 5; ++part) issue_part(blk, pg, T, part);
   };
 
   float m_run = -INFINITY, z_run = 0.f;
@@ -257,7 +269,8 @@ __global__ __launch_bounds__(512) void decode_2d_kernel(AttnArgs a) {
   //   interval B(b): value sum(b); cos / sin weighting(b + 1) -> s_part
   // A(b) ends with a barrier that leaves this wave's copies of block b + 2 in
   // flight; B(b) ends with a barrier after all copies have landed.
-  auto kside = [&](Tile2d<DH, RK, RV> &T, f32x16 (&acc)[RTW]) {
+  // between(s8) runs after the products of K-step s8
+  auto kside = [&](Tile2d<DH, RK, RV> &T, f32x16 (&acc)[RTW], auto &&between) {
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) acc[rt] = f32x16{};
     // B-operand pieces PF K-steps ahead; the scheduling fence keeps each read
@@ -274,6 +287,7 @@ __global__ __launch_bounds__(512) void decode_2d_kernel(AttnArgs a) {
 #pragma unroll
       for (int rt = 0; rt < RTW; ++rt)
         acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[rt][s8], as_bf16x8(bk[s8 % (PF + 1)]), acc[rt], 0, 0, 0);
+      between(s8);
     }
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt)
@@ -353,11 +367,17 @@ __global__ __launch_bounds__(512) void decode_2d_kernel(AttnArgs a) {
   };
   // this wave's copy instructions per block (all of them count on vmcnt)
   constexpr int NCOPY = 2 * (32 / NW) + CVQ / NW;
+  int pgv = 0;  // s_pt entry of the next copy, loaded one step ahead
   auto step = [&](int blk, Tile2d<DH, RK, RV> &Tb, Tile2d<DH, RK, RV> &Tn, Tile2d<DH, RK, RV> &Tnn) {
-    issue(min(blk + 2, nblk - 1), Tnn);  // past the end: a harmless re-copy of the last block
-    __builtin_amdgcn_sched_barrier(0);
+    const long long pg = __builtin_amdgcn_readfirstlane(pgv);
+    pgv = s_pt[page_idx(min(blk + 3, nblk - 1))];
+    const int cb = min(blk + 2, nblk - 1);  // past the end: a harmless re-copy of the last block
     f32x16 acc[RTW];
-    kside(Tn, acc);  // block b + 1 (past the end: ignored)
+    kside(Tn, acc, [&](int s8) {  // block b + 1 (past the end: ignored)
+#pragma unroll
+      for (int part = 0; part < 5; ++part)  // every part once: K-steps 0, KS/5, .. (distinct for KS >= 5)
+        if (s8 == part * KS / 5) issue_part(cb, pg, Tnn, part);
+    });
     softmax(blk);
     barrier_vm<NCOPY>();
     weigh(Tn, acc);
@@ -366,11 +386,12 @@ __global__ __launch_bounds__(512) void decode_2d_kernel(AttnArgs a) {
   };
 
   if (nblk > 0) {
-    issue(0, tile0);
-    issue(min(1, nblk - 1), tile1);
+    issue(0, __builtin_amdgcn_readfirstlane(s_pt[page_idx(0)]), tile0);
+    issue(min(1, nblk - 1), __builtin_amdgcn_readfirstlane(s_pt[page_idx(min(1, nblk - 1))]), tile1);
+    pgv = s_pt[page_idx(min(2, nblk - 1))];
     barrier_vm<0>();
     f32x16 acc0[RTW];
-    kside(tile0, acc0);
+    kside(tile0, acc0, [](int) {});
     weigh(tile0, acc0);
     barrier_vm<0>();
     int blk = 0;
