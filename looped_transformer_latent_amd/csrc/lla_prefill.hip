@@ -312,13 +312,25 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(AttnArgs a) {
     cp[it] = off | (row << 16) | (isv ? 1 << 22 : 0);
   }
   auto cp_row = [&](int it) { return (cp[it] >> 16) & 63; };
-  // Direct-to-LDS copy of tile x (clamped to the last tile) into slot sb;
-  // returns the page-validity bits (bit 0: first page, bit 1: second).
-  auto copy_tile = [&](int x, char *sb) -> int {
+  // Direct-to-LDS copy of tile x (clamped to the last tile) into slot sb, in
+  // three parts: the tile's two page-table entries (an LDS read, issued a step
+  // before they are needed), the page bases, and the CPW copy instructions,
+  // which the main loop spreads over its step (a wave that issued them back to
+  // back waited on the copy queue).
+  auto tile_pages = [&](int x, int &e0, int &e1) {
     x = min(x, nt - 1);
     const int l0 = min(2 * x, npg - 1), l1 = min(2 * x + 1, npg - 1);
-    const int e0 = __builtin_amdgcn_readfirstlane(s_pt[(l0 / PTC) & 1][l0 % PTC]);
-    const int e1 = __builtin_amdgcn_readfirstlane(s_pt[(l1 / PTC) & 1][l1 % PTC]);
+    e0 = s_pt[(l0 / PTC) & 1][l0 % PTC];
+    e1 = s_pt[(l1 / PTC) & 1][l1 % PTC];
+  };
+  struct CopyBase {
+    uint64_t k0, k1, v0, v1;
+    int okm;  // page-validity bits (bit 0: first page, bit 1: second)
+  };
+  auto copy_base = [&](int x, int e0v, int e1v) -> CopyBase {
+    x = min(x, nt - 1);
+    const int l0 = min(2 * x, npg - 1), l1 = min(2 * x + 1, npg - 1);
+    const int e0 = __builtin_amdgcn_readfirstlane(e0v), e1 = __builtin_amdgcn_readfirstlane(e1v);
     const bool ok0 = e0 >= 0 && e0 < a.num_pages, ok1 = e1 >= 0 && e1 < a.num_pages;
     if (!ok0) bad_lp = min(bad_lp, l0);
     if (!ok1) bad_lp = min(bad_lp, l1);
@@ -328,22 +340,36 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(AttnArgs a) {
     // (opaque, so that each lane selects one of the four page addresses and adds
     // its offset, rather than the compiler multiplying a selected page number)
     asm volatile("" : "+s"(k0), "+s"(k1), "+s"(v0), "+s"(v1));
-#pragma unroll
-    for (int it = 0; it < CPW; ++it) {
-      const int J = it * NW + w;
-      const bool rope_job = it + 1 == CPW && J >= NCP && J < NJOB;
-      if (!rope_job) {
-        const int jp = J < NCP ? J : J - NJOB;
-        const bool p1 = ((cp[it] >> 20) & 3) == 1;  // rows 16..31
-        const bool isv = (cp[it] >> 22) != 0;
-        const uint64_t pa = isv ? v0 : k0, pb = isv ? v1 : k1;
-        dma_lds16((const char *)((p1 ? pb : pa) + (uint32_t)(cp[it] & 0xFFFF)), lds_addr(sb, 1024 * jp));
-      } else {
-        const int k = J - NCP;
-        dma_lds4(a.rope + (long long)KT * x * DH + 64 * k + lane, lds_addr(sb, ROPE_OFF + 256 * k));
-      }
+    return CopyBase{k0, k1, v0, v1, (ok0 ? 1 : 0) | (ok1 ? 2 : 0)};
+  };
+  auto copy_job = [&](int x, char *sb, const CopyBase &cb, int it) {
+    x = min(x, nt - 1);
+    const int J = it * NW + w;
+    const bool rope_job = it + 1 == CPW && J >= NCP && J < NJOB;
+    if (!rope_job) {
+      const int jp = J < NCP ? J : J - NJOB;
+      const bool p1 = ((cp[it] >> 20) & 3) == 1;  // rows 16..31
+      const bool isv = (cp[it] >> 22) != 0;
+      const uint64_t pa = isv ? cb.v0 : cb.k0, pb = isv ? cb.v1 : cb.k1;
+      dma_lds16((const char *)((p1 ? pb : pa) + (uint32_t)(cp[it] & 0xFFFF)), lds_addr(sb, 1024 * jp));
+    } else {
+      const int k = J - NCP;
+      dma_lds4(a.rope + (long long)KT * x * DH + 64 * k + lane, lds_addr(sb, ROPE_OFF + 256 * k));
     }
-    return (ok0 ? 1 : 0) | (ok1 ? 2 : 0);
+  };
+  // copy jobs it with it * 3 / CPW == point: three insertion points per step
+  auto copy_jobs_at = [&](int x, char *sb, const CopyBase &cb, int point) {
+#pragma unroll
+    for (int it = 0; it < CPW; ++it)
+      if (it * 3 / CPW == point) copy_job(x, sb, cb, it);
+  };
+  auto copy_tile = [&](int x, char *sb) -> int {
+    int e0, e1;
+    tile_pages(x, e0, e1);
+    const CopyBase cb = copy_base(x, e0, e1);
+#pragma unroll
+    for (int it = 0; it < CPW; ++it) copy_job(x, sb, cb, it);
+    return cb.okm;
   };
   // Clear the rows of tile x (in slot sb, copies landed) that are past kend or
   // come from a bad page.
@@ -529,13 +555,21 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(AttnArgs a) {
     rebuild_store(kacc, s_c0, s_k0);
     barrier_vm<3 * CPW>();  // tile 1, K of tile 0
   }
+  int pe0 = 0, pe1 = 0;  // page-table entries of the next step's copy (read a step ahead)
+  tile_pages(DIST, pe0, pe1);
   auto step = [&](int x, const char *sx, char *sx1, char *sxd, int okx1, int &okxd, const char *kb0, char *kb1) {
     if (needs_clear(x + 1, okx1)) {
       clear_tile(x + 1, sx1, okx1);
       barrier_vm<63>();
     }
     if ((2 * (x + DIST)) % PTC == 0 && 2 * (x + DIST) + PTC < npg) fill_pt(2 * (x + DIST) / PTC + 1);
-    okxd = copy_tile(x + DIST, sxd);
+    const CopyBase cbx = copy_base(x + DIST, pe0, pe1);
+    okxd = cbx.okm;
+    tile_pages(x + DIST + 1, pe0, pe1);
+    if (x >= nt) {  // past the last tile: the copies only
+#pragma unroll
+      for (int point = 0; point < 3; ++point) copy_jobs_at(x + DIST, sxd, cbx, point);
+    }
     if (x < nt) {
       u32x4 ak[KSQ];
 #pragma unroll
@@ -546,6 +580,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(AttnArgs a) {
       for (int ks = 0; ks < KSQ; ++ks)
 #pragma unroll
         for (int f = 0; f < QF; ++f) sc[f] = mfma32(ak[ks], qop[f][ks], ks == 0 ? f32x16{} : sc[f]);
+      copy_jobs_at(x + DIST, sxd, cbx, 0);
       u32x4 av0[NRB];
       cv_operands(sx, 0, av0);
       __builtin_amdgcn_sched_barrier(0);
@@ -558,11 +593,13 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(AttnArgs a) {
       weights(sc, 0, pop0);
       cv_operands(sx, 1, av1);
       __builtin_amdgcn_sched_barrier(0);
+      copy_jobs_at(x + DIST, sxd, cbx, 1);
       value_sums(av0, pop0);
       weights(sc, 1, pop1);
       __builtin_amdgcn_sched_barrier(0);
       f32x4 kacc[2 * NTW];
       value_sums(av1, pop1);
+      copy_jobs_at(x + DIST, sxd, cbx, 2);
       rebuild_mfma(sx1, kacc);
       __builtin_amdgcn_sched_barrier(0);
       rebuild_store(kacc, sx1, kb1);
