@@ -176,25 +176,28 @@ __global__ __launch_bounds__(256) void encode_append_kernel(EncodeArgs a, int RK
 //
 // Per (layer, latent group, K|V) the encoder is a plain GEMM,
 //   C[tokens x r] = X[tokens x width] W_down[width x r] - 1 (mu W_down),
-// on v_mfma_f32_16x16x32_bf16.  A workgroup (8 waves) takes 256 tokens (128
-// for r > 160); wave w owns two 16-row tiles (one) and all r columns.  The
+// on v_mfma_f32_16x16x32_bf16, computed transposed (W_down^T as the A
+// operand, x^T as the B operand) so that each lane ends with four consecutive
+// latent columns of one token.  A workgroup (8 waves) takes 256 tokens (128
+// for r > 160); wave w owns two 16-token tiles (one) and all r columns.  The
 // contraction runs over chunks of 64 rows of W_down (32 for r > 160):
 //  * x: each wave loads its rows x chunk bytes in address order (for 64-row
-//    chunks one load instruction covers 8 whole 128-byte row pieces), two
-//    chunks ahead in registers, and passes them through its own LDS region
-//    (16-byte slots XOR-swizzled by row) into the A-operand layout;
+//    chunks one load instruction covers 8 whole 128-byte row pieces) with
+//    buffer loads, two chunks ahead in registers, and passes them through its
+//    own LDS region (16-byte slots XOR-swizzled by row) into operand layout;
 //  * W_down: the chunk's rows are copied as stored (r contiguous; rows padded
 //    so that the transposing reads below hit distinct banks) straight into
 //    LDS by the 8 waves together (global_load_lds_dwordx4), two chunks ahead
 //    in three buffers, one barrier per chunk;
-//  * B-operands come from ds_read_b64_tr_b16, which hands lane (g, n) column n
-//    of four consecutive rows: K-slot 8 g + 4 h + e of K-step s is chunk row
-//    32 s + 16 h + 4 g + e, on both operands.
-// mu W_down comes from encode_muw_kernel (once per call).  The result (minus
-// mu W_down, rounded once to bf16) goes through LDS and leaves as 16-byte
-// stores into the paged pool.  Workgroups are persistent (at most one per CU)
-// and walk (token tile, group, layer) tiles; a tile's output stores drain
-// while the next tile's first two chunks load.
+//  * W_down operands come from ds_read_b64_tr_b16, which hands lane (g, n)
+//    column n of four consecutive rows: K-slot 8 g + 4 h + e of K-step s is
+//    chunk row 32 s + 16 h + 4 g + e, on both operands.
+// mu W_down comes from encode_muw_kernel (once per call) and is copied into
+// LDS with the tile's first chunk.  The result (minus mu W_down, rounded once
+// to bf16) is staged in LDS with 8-byte stores and leaves as 16-byte stores
+// into the paged pool.  Workgroups are persistent (at most one per CU) and
+// walk (group, token tile, layer) tiles, group fastest; the next tile's first
+// two chunks load while a tile's output is staged and drains.
 namespace {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((__vector_size__(2 * sizeof(uint32_t))));
@@ -219,6 +222,17 @@ __device__ __forceinline__ u32x2 lds_read_tr(const char *p) {
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void copy16_to_lds(const void *src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src) : "memory", "m0");
+}
+// Raw buffer descriptor word 3 on gfx9-family parts (32-bit data format, no
+// swizzle, no index stride: untyped loads by byte offset), and the buffer
+// load's cache-policy bit for data read once (nt).
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kNonTemporal = 2;
+
+// The same from the wave-uniform address base + off (off: this lane's 32-bit
+// byte offset), in the instruction's scalar-base form.
+__device__ __forceinline__ void copy16_to_lds_at(const void *base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"(base) : "memory", "m0");
 }
 #pragma clang diagnostic pop
 // Wave-uniform LDS byte address of a pointer into __shared__ memory.
@@ -262,6 +276,7 @@ __global__ __launch_bounds__(512) void encode_mfma_kernel(EncodeArgs a, int kv, 
   __shared__ __attribute__((aligned(16))) char s_xo[8 * XW > TOK * R * 2 ? 8 * XW : TOK * R * 2];
   __shared__ __attribute__((aligned(16))) char s_w0[WBUF], s_w1[WBUF], s_w2[WBUF];
   __shared__ long long s_off[2][TOK];  // per tile parity: element offset of each token's latent row, -1 = dropped
+  __shared__ __attribute__((aligned(16))) float s_muw[2][SPLIT ? 4 : R];  // mu W_down per tile parity
 
   // wave index as a scalar: branches on it must be uniform scalar branches,
   // never EXEC-masked MFMAs
@@ -281,8 +296,12 @@ __global__ __launch_bounds__(512) void encode_mfma_kernel(EncodeArgs a, int kv, 
   const long long pstride = kv ? a.pool_page_stride_v : a.pool_page_stride_k;
   const long long hstride = kv ? a.pool_head_stride_v : a.pool_head_stride_k;
 
-  // Tiles t = blockIdx.x, + gridDim.x, ...: token tile fastest, then group,
-  // then layer, so that the workgroups running together share W_down in L2.
+  // Tiles t = blockIdx.x, + gridDim.x, ...: group fastest, then token tile,
+  // then layer.  x is [layer][token][group][width], so the workgroups running
+  // together read neighbouring pieces of the same token rows (DRAM pages stay
+  // open: in a read-only test of this access pattern, reads at 6.0 TB/s with
+  // token tile fastest and 6.8 TB/s with group fastest); the workgroups of one
+  // XCD (blockIdx.x mod 8) still share a few groups' W_down in L2.
   struct Tile {
     long long tok0;
     int grp, li;
@@ -290,10 +309,10 @@ __global__ __launch_bounds__(512) void encode_mfma_kernel(EncodeArgs a, int kv, 
   auto tile_of = [&](long long t) {
     Tile v;
     t %= ntiles;
-    v.tok0 = (t % ntt) * TOK;
-    const long long r = t / ntt;
-    v.grp = (int)(r % a.groups);
-    v.li = (int)(r / a.groups);
+    v.grp = (int)(t % a.groups);
+    const long long r = t / a.groups;
+    v.tok0 = (r % ntt) * TOK;
+    v.li = (int)(r / ntt);
     return v;
   };
   // destination slot of each token of tile v (placement is integer work, checked here)
@@ -320,20 +339,36 @@ __global__ __launch_bounds__(512) void encode_mfma_kernel(EncodeArgs a, int kv, 
   char *s_x = s_xo + w * XW;
 
   // x loads: instruction i, lane l -> local row (64 i + l) / XP (token
-  // 16 TPW w + that, clamped; dropped at the end), piece l % XP of the chunk
-  const char *xsrc[NXI];
+  // 16 TPW w + that, clamped; dropped at the end), piece l % XP of the chunk.
+  // They are buffer loads over the wave's rows (a uniform descriptor from its
+  // first row, clamped) with a 32-bit byte offset per lane and the chunk's
+  // offset in a scalar; W_down copies take the tile's W_down as a uniform base
+  // plus a fixed per-lane offset.  So few registers stay live for addresses.
+  __amdgpu_buffer_rsrc_t xrs;
+  uint32_t xoff[NXI];
   int xslot[NXI];
-  const uint16_t *wd;
+  const char *wbase;
   auto sources = [&](const Tile &v) {
-    wd = wd_all + ((long long)v.li * a.groups + v.grp) * a.width * (long long)R;
+    wbase = (const char *)(wd_all + ((long long)v.li * a.groups + v.grp) * a.width * (long long)R);
+    const long long row0 = min(v.tok0 + 16 * TPW * w, tokens - 1);
+    const char *xbase = x + ((((long long)v.li * tokens + row0) * a.groups + v.grp) * a.width) * 2;
+    const long long xbytes = (long long)16 * TPW * a.groups * a.width * 2;  // covers every row the wave reads
+    xrs = __builtin_amdgcn_make_buffer_rsrc((void *)xbase, (short)0, (int)min(xbytes, 0x7FFFFFFFll), kBufferWord3);
 #pragma unroll
     for (int i = 0; i < NXI; ++i) {
       const int tl = (64 * i + lane) / XP, p = lane % XP;
-      long long tk = v.tok0 + 16 * TPW * w + tl;
-      if (tk >= tokens) tk = tokens - 1;
-      xsrc[i] = x + ((((long long)v.li * tokens + tk) * a.groups + v.grp) * a.width) * 2 + 16 * p;
+      const long long tk = min(v.tok0 + 16 * TPW * w + tl, tokens - 1);
+      xoff[i] = (uint32_t)((tk - row0) * a.groups * a.width * 2 + 16 * p);
     }
   };
+  uint32_t woff[NWI];
+#pragma unroll
+  for (int i = 0; i < NWI; ++i) {
+    const int slot = (i * 8 + w) * 64 + lane;
+    const int k = slot / PW, pc = slot - k * PW;
+    const bool ok = k < KC && pc < R / 8;
+    woff[i] = (uint32_t)(((ok ? k : 0) * R + (ok ? 8 * pc : 0)) * 2);
+  }
 #pragma unroll
   for (int i = 0; i < NXI; ++i) {
     const int tl = (64 * i + lane) / XP, p = lane % XP;
@@ -341,7 +376,8 @@ __global__ __launch_bounds__(512) void encode_mfma_kernel(EncodeArgs a, int kv, 
   }
   auto load_x = [&](int c, u32x4 (&d)[NXI]) {
 #pragma unroll
-    for (int i = 0; i < NXI; ++i) d[i] = __builtin_nontemporal_load((const u32x4 *)(xsrc[i] + c * (KC * 2)));
+    for (int i = 0; i < NXI; ++i)
+      d[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, xoff[i], c * (KC * 2), kNonTemporal));
   };
   auto put_x = [&](const u32x4 (&d)[NXI]) {
 #pragma unroll
@@ -351,13 +387,8 @@ __global__ __launch_bounds__(512) void encode_mfma_kernel(EncodeArgs a, int kv, 
   // copy the chunk's first piece (never read)
   auto copy_w = [&](int c, char *dst) {
 #pragma unroll
-    for (int i = 0; i < NWI; ++i) {
-      const int slot = (i * 8 + w) * 64 + lane;
-      const int k = slot / PW, pc = slot - k * PW;
-      const bool ok = k < KC && pc < R / 8;
-      const uint16_t *src = wd + (long long)(c * KC + (ok ? k : 0)) * R + (ok ? 8 * pc : 0);
-      copy16_to_lds(src, lds_addr(dst + (i * 8 + w) * 1024));
-    }
+    for (int i = 0; i < NWI; ++i)
+      copy16_to_lds_at(wbase + (long long)c * (KC * R * 2), woff[i], lds_addr(dst + (i * 8 + w) * 1024));
   };
 
   f32x4 acc[TPW][CT];
@@ -380,19 +411,20 @@ __global__ __launch_bounds__(512) void encode_mfma_kernel(EncodeArgs a, int kv, 
         const u32x4 bw = u32x4{lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt)
-          acc[tt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[tt]), as_bf16x8(bw), acc[tt][ct], 0, 0, 0);
+          acc[tt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(bw), as_bf16x8(av[tt]), acc[tt][ct], 0, 0, 0);
       }
     }
   };
 
   // Chunk c (W_down buffer c % 3): its x rows, in registers since two chunks
   // ago, go to the wave's slots.  The W_down copies of chunk c were issued
-  // just before those x loads, so once only the copies and loads of chunk
-  // c + 1 may be outstanding (older stores of the previous tile's output
-  // complete first: vector-memory operations count down in issue order),
-  // this wave's part of chunk c is in LDS; all waves meet, which also frees
-  // buffer (c + 2) % 3; then the copies and x loads of chunk c + 2 are issued
-  // and chunk c is multiplied.
+  // just before those x loads, so once at most NWI + NXI vector-memory
+  // operations are outstanding (they count down in issue order), this wave's
+  // part of chunk c is in LDS; all waves meet, which also frees buffer
+  // (c + 2) % 3; then the copies and x loads of chunk c + 2 are issued and
+  // chunk c is multiplied.  At a tile's first chunk the previous tile's
+  // output stores are the most recent operations, so that wait also covers
+  // chunk 1 and some of the stores: conservative, never short.
   const int nch_all = a.width / KC;
   const int per = (nch_all + ksplit - 1) / ksplit;  // chunks of one range
   int c_lo = 0, nch = nch_all;                     // the current item's range
@@ -414,7 +446,15 @@ __global__ __launch_bounds__(512) void encode_mfma_kernel(EncodeArgs a, int kv, 
   };
   u32x4 xa[NXI], xb[NXI], xc[NXI];
   // the first two chunks of an item
-  auto start = [&]() {
+  auto start = [&](const Tile &v, int par) {
+    if constexpr (!SPLIT) {
+      // mu W_down of the item's (layer, group): R/4 lanes of wave 0, older than
+      // the first chunk's copies, so the first chunk's wait covers it
+      if (w == 0) {
+        const float *muw = a.muw + ((long long)v.li * a.groups + v.grp) * a.muw_stride + (kv ? a.muw_v_off : 0);
+        if (lane < R / 4) copy16_to_lds(muw + 4 * lane, lds_addr(s_muw[par]));
+      }
+    }
     copy_w(c_lo, s_w0);
     load_x(c_lo, xa);
     if (nch > 1) {
@@ -429,7 +469,7 @@ __global__ __launch_bounds__(512) void encode_mfma_kernel(EncodeArgs a, int kv, 
   range_of(t);
   if (!SPLIT) place(cur, s_off[0]);
   sources(cur);
-  start();
+  start(cur, 0);
   for (int par = 0;; par ^= 1) {
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt)
@@ -452,47 +492,51 @@ __global__ __launch_bounds__(512) void encode_mfma_kernel(EncodeArgs a, int kv, 
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int tt = 0; tt < TPW; ++tt)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) dst[(16 * (TPW * w + tt) + 4 * g + e) * R + 16 * ct + n] = acc[tt][ct][e];
+        for (int tt = 0; tt < TPW; ++tt) *(f32x4 *)(dst + (16 * (TPW * w + tt) + n) * R + 16 * ct + 4 * g) = acc[tt][ct];
       const long long tn = t + gridDim.x;
       if (tn >= nwork) break;
       t = tn;
       cur = tile_of(t);
       range_of(t);
       sources(cur);
-      start();
+      start(cur, 0);
       continue;
     }
-    uint16_t *s_out = (uint16_t *)s_xo;  // [TOK][R] bf16
-    const float *muw = a.muw + ((long long)cur.li * a.groups + cur.grp) * a.muw_stride + (kv ? a.muw_v_off : 0);
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      const int r = 16 * ct + n;
-      const float mw = muw[r];
-#pragma unroll
-      for (int tt = 0; tt < TPW; ++tt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          s_out[(16 * (TPW * w + tt) + 4 * g + e) * R + r] = (uint16_t)f32_to_bf16(acc[tt][ct][e] - mw);
-    }
-    // the next tile's slots, while nothing else is in flight (its loads are waited for)
+    // The next tile's first two chunks load from here on, while this tile's
+    // output is staged and drains (W_down buffers and x registers are free).
     const long long tn = t + gridDim.x;
     const Tile nxt = tile_of(tn < ntiles ? tn : t);
+    if (tn < ntiles) {
+      sources(nxt);
+      start(nxt, par ^ 1);
+    }
+    // lane (g, n) holds columns 16 ct + 4 g .. + 3 of token 16 (TPW w + tt) + n
+    uint16_t *s_out = (uint16_t *)s_xo;  // [TOK][R] bf16
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const f32x4 mw = *(const f32x4 *)(s_muw[par] + 16 * ct + 4 * g);
+#pragma unroll
+      for (int tt = 0; tt < TPW; ++tt)
+        *(u32x2 *)(s_out + (16 * (TPW * w + tt) + n) * R + 16 * ct + 4 * g) =
+            u32x2{pack_bf16(acc[tt][ct][0] - mw[0], acc[tt][ct][1] - mw[1]),
+                  pack_bf16(acc[tt][ct][2] - mw[2], acc[tt][ct][3] - mw[3])};
+    }
     if (tn < ntiles) place(nxt, s_off[par ^ 1]);
     barrier_vm<63>();
     uint16_t *pool = pool_all + (long long)cur.li * lstride;
-    for (int q = threadIdx.x; q < TOK * (R / 8); q += blockDim.x) {
-      const int tl = q / (R / 8), c8 = q % (R / 8);
-      const long long off = s_off[par][tl];
-      if (off >= 0) *(u32x4 *)(pool + off + 8 * c8) = *(const u32x4 *)(s_out + tl * R + 8 * c8);
+    constexpr int NQ = TOK * (R / 8);  // 16-byte pieces of the tile's output
+#pragma unroll 5  // five pieces per thread in flight fit the register budget of every instance
+    for (int q0 = 0; q0 < NQ; q0 += 512) {
+      const int q = q0 + (int)threadIdx.x;
+      if (NQ % 512 == 0 || q < NQ) {
+        const int tl = q / (R / 8), c8 = q % (R / 8);
+        const long long off = s_off[par][tl];
+        if (off >= 0) *(u32x4 *)(pool + off + 8 * c8) = *(const u32x4 *)(s_out + tl * R + 8 * c8);
+      }
     }
     if (tn >= ntiles) break;
-    // the next tile's first chunks load while this tile's output drains
     t = tn;
     cur = nxt;
-    sources(cur);
-    start();
     barrier_vm<63>();  // the staged output has been read before the slots take x rows again
   }
 }
@@ -566,15 +610,12 @@ bool encode_mfma_r(int r) {
   return false;
 }
 
-// Ranks whose split instantiation fits in registers (128 and 160 would spill).
-__host__ __device__ constexpr bool enc_can_split(int r) { return r != 128 && r != 160; }
-
 size_t encode_kpart_bytes(int width, int groups, int n_layers, int r_k, int r_v) {
   if (width % 64 || !encode_mfma_r(r_k) || !encode_mfma_r(r_v) || (long long)groups * n_layers >= kEncWorkgroups / 2)
     return 0;
   size_t bytes = 0;
   for (const int r : {r_k, r_v})
-    if (enc_can_split(r) && width / enc_kc(r) >= kSplitMinChunks) {
+    if (width / enc_kc(r) >= kSplitMinChunks) {
       const size_t b = sizeof(float) * kSplitMaxItems * enc_tok(r) * r;
       if (b > bytes) bytes = b;
     }
@@ -597,9 +638,7 @@ hipError_t launch_encode_mfma(int r, int kv, const EncodeArgs &a, hipStream_t st
 #define X(RR)                                                                                          \
   if (r == RR) {                                                                                       \
     const long long tiles = (tokens + enc_tok(RR) - 1) / enc_tok(RR) * a.groups * a.n_layers;           \
-    const int ks = enc_can_split(RR) ? encode_ksplit(tiles, a.width / enc_kc(RR), a.kpart_bytes,       \
-                                                     sizeof(float) * enc_tok(RR) * RR)                 \
-                                     : 1;                                                              \
+    const int ks = encode_ksplit(tiles, a.width / enc_kc(RR), a.kpart_bytes, sizeof(float) * enc_tok(RR) * RR); \
     const long long items = tiles * ks;                                                                \
     const dim3 grid((unsigned)(items < kEncWorkgroups ? items : kEncWorkgroups));                       \
     if (ks > 1)                                                                                        \
