@@ -248,6 +248,76 @@ def test_encode_lla2d_benchmark_shape():
         compare(m1, got, (kr, vr), init, f"encode 2D benchmark shape, layer {layer}")
 
 
+@pytest.mark.timeout(600)
+def test_encode_4x_benchmark_shape():
+    """The 4x append in the benchmark's launch configuration: 512 tokens for
+    each of 64 sequences into all 24 layers (r_k = 96, r_v = 160, width
+    T d = 512 per head), seeded x as the benchmark draws it, pos0 = 7680, so
+    every workgroup runs many tiles (both tile parities, several groups and
+    layers).  The pool holds the 32 pages each sequence's new tokens land in,
+    shuffled among 512 pages that no sequence owns.  Placement is checked
+    bit-exact over the whole pool (owned pages fully written, the others
+    untouched); the latents of 16 tokens in layers 0, 11 and 23 against the
+    oracle's encode."""
+    from looped_transformer_latent_amd import workloads as wl
+    w = wl.WORKLOADS["ouro1.4b-4x-b64-encode"]
+    m = w.dims
+    B, n_new = w.batch, w.n_new
+    pos0 = w.ctx - n_new
+    first, owned = pos0 // 16, n_new // 16
+    spare = 512
+    perm = np.random.default_rng(w.seed + 7).permutation(B * owned + spare).astype(np.int32)
+    pt = np.full((B, w.pages_per_seq), -1, np.int32)  # entries never read stay -1
+    pt[:, first:first + owned] = perm[:B * owned].reshape(B, owned)
+    num_pages = B * owned + spare
+    sent = int(SENT[BF16])
+    pools = {kv: torch.full(pool_shape(m, num_pages, kv), sent, dtype=torch.int16, device="cuda")
+             for kv in ("k", "v")}
+    codec_h = wl.codec_host(w)
+    D = lla.dims_from_dict(m)
+    c, keep = device_codec(codec_h)
+    cache = lla.make_cache(pools["k"].view(torch.bfloat16), pools["v"].view(torch.bfloat16),
+                           to_device(pt), num_pages)
+    xs = (w.D, B, n_new, w.H, w.T, w.d_head)
+    x_k = torch.empty(xs, dtype=torch.bfloat16, device="cuda")
+    x_v = torch.empty(xs, dtype=torch.bfloat16, device="cuda")
+    lla.gen_normal_(x_k, w.seed, wl.STREAMS["x_k"])
+    lla.gen_normal_(x_v, w.seed, wl.STREAMS["x_v"])
+    ws = lla.workspace(D, lla.OP_ENCODE, B, 0, w.D)
+    lla.encode_append(D, c, cache, x_k, x_v, to_device(np.full(B, pos0, np.int32)), n_new, 0, w.D, ws)
+    torch.cuda.synchronize()
+    assert lla.device_error_word(ws) == 0
+    del x_k, x_v
+    used = torch.from_numpy(perm[:B * owned].astype(np.int64)).cuda()
+    unused = torch.from_numpy(perm[B * owned:].astype(np.int64)).cuda()
+    for kv, t in pools.items():
+        for layer in range(w.D):
+            assert not (t[layer].index_select(0, used) == sent).any(), f"{kv} layer {layer}: slot left unwritten"
+            assert (t[layer].index_select(0, unused) == sent).all(), f"{kv} layer {layer}: page not owned was written"
+    width = w.H * w.T * w.d_head
+    toks = [(0, 0), (0, 511), (1, 17), (5, 255), (9, 256), (13, 100), (20, 301), (31, 15),
+            (32, 16), (40, 479), (47, 480), (50, 7), (55, 333), (60, 128), (62, 500), (63, 511)]
+    for layer in (0, 11, w.D - 1):
+        m1 = dict(m, D=1)
+        codec1 = {k: np.ascontiguousarray(v[layer:layer + 1]) for k, v in codec_h.items()}
+        xk = np.concatenate([gen.normal(w.seed, wl.STREAMS["x_k"], (1, 1, 1, w.H, w.T, w.d_head),
+                                        offset=((layer * B + b) * n_new + n) * width) for b, n in toks], axis=1)
+        xv = np.concatenate([gen.normal(w.seed, wl.STREAMS["x_v"], (1, 1, 1, w.H, w.T, w.d_head),
+                                        offset=((layer * B + b) * n_new + n) * width) for b, n in toks], axis=1)
+        local = np.arange(len(toks), dtype=np.int32)[:, None]
+        slots = np.int32([(pos0 + n) % 16 for _, n in toks])
+        kr = np.full((1, len(toks), w.H, 16, w.r_k), SENT[BF16])
+        vr = np.full((1, len(toks), w.H, 16, w.r_v), SENT[BF16])
+        assert oracle.encode(m1, codec1, kr, vr, local, xk, xv, slots, 1, 0, 1) == 0
+        got = (np.full_like(kr, SENT[BF16]), np.full_like(vr, SENT[BF16]))
+        for i, (b, n) in enumerate(toks):
+            page = int(pt[b, (pos0 + n) // 16])
+            for g, t in zip(got, (pools["k"], pools["v"])):
+                g[0, i, :, slots[i]] = t[layer, page, :, slots[i]].cpu().numpy().view(np.uint16)
+        init = (np.full_like(kr, SENT[BF16]), np.full_like(vr, SENT[BF16]))
+        compare(m1, got, (kr, vr), init, f"encode 4x benchmark shape, layer {layer}")
+
+
 def test_encode_device_errors():
     """A position past the page-table row, or a page entry out of range, is
     flagged in the workspace error word and the slot is not written."""
