@@ -231,6 +231,32 @@ def test_deterministic_and_page_table_invariant_bitwise():
     assert np.array_equal(a, c)
 
 
+def test_split_merges_share_one_workspace_across_shapes():
+    """Several context splits per row, merged by the merge launch: one
+    workspace serves calls of 4, 48, 49 and again 4 rows (different split
+    layouts over the same scratch); every result matches the oracle and the
+    header beyond the error word stays zero."""
+    m = dims(4, 1, 16, 128, 16, 32, PER_HEAD, BF16)
+    D = lla.dims_from_dict(m)
+    codec = random_codec(m, seed=2402, ortho_down=False)
+    pps = 16
+    ws = lla.workspace(D, lla.OP_DECODE, 64, pps * 16)
+    for B, seed in ((4, 2410), (48, 2420), (49, 2430), (4, 2440)):
+        ctx = 256 - (np.arange(B) * 37) % 200
+        kp, vp = random_pools(m, B * pps, seed=seed)
+        pt = gen.shuffled_page_table(seed + 1, B, pps)
+        q = gen.normal(seed + 2, 1, (B, 16, 128))
+        splits, _ = lla.attn_plan(D, lla.OP_DECODE, B, int(ctx.max()))
+        assert splits > 1
+        got, _ = gpu_decode(m, codec, kp, vp, pt, q, ctx - 1, ctx, 0, 2, max_ctx=int(ctx.max()), ws=ws)
+        ref, rc = oracle.decode(m, codec, kp, vp, pt, 0, 2, q, np.int32(ctx - 1), np.int32(ctx))
+        assert rc == 0
+        err = row_rel_err(got, ref)
+        print(f"B={B} splits={splits}: max row rel err {err.max():.3e}", flush=True)
+        assert np.isfinite(got).all() and err.max() <= TOL[BF16]
+        assert (ws[:256].cpu().numpy() == 0).all()
+
+
 def test_unused_slots_may_hold_nan():
     """Slots past ctx_len inside the last page (and whole unused pages) are never
     read into the result, even when they hold NaN."""
