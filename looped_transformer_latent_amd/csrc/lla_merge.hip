@@ -143,8 +143,90 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int d_head, int 
   }
 }
 
+// The same merge for few splits and narrow latents (S <= 64, r_v = RV in
+// {32, 64}, d_head in {64, 128}), shaped for latency: one wave per (row,
+// head); its decoder rows and mu are loaded first (they do not depend on the
+// partials), lane s loads split s's whole partial row in one batch, and every
+// lane ends with the merged latent vector in registers after one wave
+// reduction per value.  Same reduction trees and fma order as merge_kernel,
+// so the results are bitwise the same; the memory round trips per (row,
+// head) drop from four dependent ones to one.
+template <bool BF, int RV, int EPL>
+__global__ __launch_bounds__(256) void merge_few_kernel(AttnArgs a) {
+  constexpr int DH = 64 * EPL;
+  constexpr int ES = BF ? 2 : 4;
+  constexpr int WV = RV * ES / 16;  // 16-byte loads per decoder row
+  const int lane = threadIdx.x & 63;
+  const long long rh = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);  // row * H + head
+  if (rh >= (long long)a.rows * a.H) return;  // a whole wave; no barrier follows
+  const int h = (int)(rh % a.H), S = a.splits;
+  const char *wv = a.wup_v + (long long)h * a.wup_head_stride_v * ES;
+  const char *mu = a.mu_v + (long long)h * a.mu_head_stride * ES;
+  u32x4 wr[EPL][WV];
+  float mue[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int e = lane + 64 * j;
+#pragma unroll
+    for (int i = 0; i < WV; ++i) wr[j][i] = *(const u32x4 *)(wv + ((long long)e * RV * ES + 16 * i));
+    mue[j] = BF ? bf16_to_f32(((const uint16_t *)mu)[e]) : ((const float *)mu)[e];
+  }
+  constexpr int STRIDE = RV + 2;
+  const float *ps = a.partials + (rh * S + lane) * STRIDE;
+  float v[STRIDE];
+  const bool mine = lane < S;
+#pragma unroll
+  for (int k = 0; k < STRIDE; k += 2) {
+    const float2 t = mine ? *(const float2 *)(ps + k) : float2{-INFINITY, 0.f};
+    v[k] = t.x;
+    v[k + 1] = t.y;
+  }
+  const float m = mine ? v[RV] : -INFINITY;
+  const float M = max_in_wave(m);
+  // a split that saw no token (m = -inf) weighs 0; a NaN Z poisons the row
+  const float wgt = m == -INFINITY ? 0.f : exp2f(m - M);
+  const float Z = sum_across_rows(sum_in_row(mine ? wgt * v[RV + 1] : 0.f));
+  float an[RV];
+#pragma unroll
+  for (int k = 0; k < RV; ++k) an[k] = sum_across_rows(sum_in_row(fmaf(wgt, mine ? v[k] : 0.f, 0.f))) / Z;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int e = lane + 64 * j;
+    float o = mue[j];
+    if constexpr (BF) {
+#pragma unroll
+      for (int i = 0; i < WV; ++i)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          o = fmaf(bf16_lo(wr[j][i][k]), an[8 * i + 2 * k], o);
+          o = fmaf(bf16_hi(wr[j][i][k]), an[8 * i + 2 * k + 1], o);
+        }
+      ((uint16_t *)a.out)[rh * DH + e] = (uint16_t)f32_to_bf16(o);
+    } else {
+#pragma unroll
+      for (int i = 0; i < WV; ++i)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o = fmaf(__uint_as_float(wr[j][i][k]), an[4 * i + k], o);
+      ((float *)a.out)[rh * DH + e] = o;
+    }
+  }
+}
+
 namespace {
 constexpr int kWholeGroupSplits = 64;  // more splits than this: 4 waves per (row, head)
+
+template <bool BF>
+bool go_merge_few(const AttnArgs &a, int d_head, int r_v, long long blocks, hipStream_t stream) {
+  if (a.splits > 64) return false;
+#define LLA_MERGE_FEW(RV, EPL)                                                                      \
+  if (r_v == RV && d_head == 64 * EPL) {                                                            \
+    hipLaunchKernelGGL((merge_few_kernel<BF, RV, EPL>), dim3((unsigned)blocks), dim3(256), 0, stream, a); \
+    return true;                                                                                    \
+  }
+  LLA_MERGE_FEW(32, 1) LLA_MERGE_FEW(32, 2) LLA_MERGE_FEW(64, 1) LLA_MERGE_FEW(64, 2)
+#undef LLA_MERGE_FEW
+  return false;
+}
 
 template <bool BF, bool IDENT>
 hipError_t go_merge(const AttnArgs &a, int d_head, int r_v, hipStream_t stream) {
@@ -153,6 +235,9 @@ hipError_t go_merge(const AttnArgs &a, int d_head, int r_v, hipStream_t stream) 
   const bool whole = a.splits > kWholeGroupSplits;
   const long long blocks = whole ? pairs : (pairs + 3) / 4;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  if constexpr (!IDENT) {
+    if (go_merge_few<BF>(a, d_head, r_v, blocks, stream)) return hipGetLastError();
+  }
   const size_t shmem = sizeof(float) * (whole ? 1 : 4) * r_v;
   if (whole)
     hipLaunchKernelGGL((merge_kernel<BF, IDENT, 4>), dim3((unsigned)blocks), dim3(256), shmem, stream, a, d_head, r_v);
