@@ -391,6 +391,15 @@ __global__ __launch_bounds__(512) void encode_mfma_kernel(EncodeArgs a, int kv, 
       copy16_to_lds_at(wbase + (long long)c * (KC * R * 2), woff[i], lds_addr(dst + (i * 8 + w) * 1024));
   };
 
+  // Staged output rows: 16-byte piece c of row tl sits at c ^ out_swz(tl).
+  // Rows P apart start on the same LDS bank (P = 64 / gcd(64, R / 2) for 64
+  // banks of 4 bytes), so the swizzle takes row / P; it flips at most the low
+  // bits that keep a piece inside its row (SWM + 1 divides R / 8).
+  constexpr int RD = R / 2, GCD = RD % 64 == 0 ? 64 : RD % 32 == 0 ? 32 : RD % 16 == 0 ? 16 : RD % 8 == 0 ? 8 : 4;
+  constexpr int SWP = 64 / GCD;
+  constexpr int P8 = R / 8, SWM = P8 % 16 == 0 ? 15 : P8 % 8 == 0 ? 7 : P8 % 4 == 0 ? 3 : P8 % 2 == 0 ? 1 : 0;
+  auto out_swz = [](int tl) { return (tl / SWP) & SWM; };
+
   f32x4 acc[TPW][CT];
   auto compute = [&](const char *wb) {
 #pragma unroll
@@ -511,15 +520,18 @@ __global__ __launch_bounds__(512) void encode_mfma_kernel(EncodeArgs a, int kv, 
       start(nxt, par ^ 1);
     }
     // lane (g, n) holds columns 16 ct + 4 g .. + 3 of token 16 (TPW w + tt) + n
-    uint16_t *s_out = (uint16_t *)s_xo;  // [TOK][R] bf16
+    uint16_t *s_out = (uint16_t *)s_xo;  // [TOK][R] bf16, 16-byte pieces swizzled per row
+    const int tl0 = 16 * TPW * w + n;
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
       const f32x4 mw = *(const f32x4 *)(s_muw[par] + 16 * ct + 4 * g);
 #pragma unroll
-      for (int tt = 0; tt < TPW; ++tt)
-        *(u32x2 *)(s_out + (16 * (TPW * w + tt) + n) * R + 16 * ct + 4 * g) =
+      for (int tt = 0; tt < TPW; ++tt) {
+        const int tl = tl0 + 16 * tt;
+        *(u32x2 *)(s_out + tl * R + 8 * ((2 * ct + (g >> 1)) ^ out_swz(tl)) + 4 * (g & 1)) =
             u32x2{pack_bf16(acc[tt][ct][0] - mw[0], acc[tt][ct][1] - mw[1]),
                   pack_bf16(acc[tt][ct][2] - mw[2], acc[tt][ct][3] - mw[3])};
+      }
     }
     if (tn < ntiles) place(nxt, s_off[par ^ 1]);
     barrier_vm<63>();
@@ -531,7 +543,7 @@ __global__ __launch_bounds__(512) void encode_mfma_kernel(EncodeArgs a, int kv, 
       if (NQ % 512 == 0 || q < NQ) {
         const int tl = q / (R / 8), c8 = q % (R / 8);
         const long long off = s_off[par][tl];
-        if (off >= 0) *(u32x4 *)(pool + off + 8 * c8) = *(const u32x4 *)(s_out + tl * R + 8 * c8);
+        if (off >= 0) *(u32x4 *)(pool + off + 8 * c8) = *(const u32x4 *)(s_out + tl * R + 8 * (c8 ^ out_swz(tl)));
       }
     }
     if (tn >= ntiles) break;
