@@ -212,15 +212,89 @@ __global__ __launch_bounds__(256) void merge_few_kernel(AttnArgs a) {
   }
 }
 
+// The same for 64 < S <= 256: one workgroup per (row, head), thread s loads
+// split s's partial row; wave reductions, then the four waves' results added
+// in wave order through LDS (as merge_kernel with WPR = 4), with two barriers.
+template <bool BF, int RV, int EPL>
+__global__ __launch_bounds__(256) void merge_many_kernel(AttnArgs a) {
+  constexpr int DH = 64 * EPL;
+  constexpr int ES = BF ? 2 : 4;
+  constexpr int WV = RV * ES / 16;
+  constexpr int STRIDE = RV + 2;
+  __shared__ float s_red[4][STRIDE];
+  const int u = threadIdx.x, lane = u & 63, wg = u >> 6;
+  const long long rh = blockIdx.x;  // row * H + head
+  const int h = (int)(rh % a.H), S = a.splits;
+  const char *wv = a.wup_v + (long long)h * a.wup_head_stride_v * ES;
+  const char *mu = a.mu_v + (long long)h * a.mu_head_stride * ES;
+  const bool has_e = u < DH;  // thread u writes output element u
+  u32x4 wr[WV];
+  float mue = 0.f;
+  if (has_e) {
+#pragma unroll
+    for (int i = 0; i < WV; ++i) wr[i] = *(const u32x4 *)(wv + ((long long)u * RV * ES + 16 * i));
+    mue = BF ? bf16_to_f32(((const uint16_t *)mu)[u]) : ((const float *)mu)[u];
+  }
+  const float *ps = a.partials + (rh * S + u) * STRIDE;
+  float v[STRIDE];
+  const bool mine = u < S;
+#pragma unroll
+  for (int k = 0; k < STRIDE; k += 2) {
+    const float2 t = mine ? *(const float2 *)(ps + k) : float2{-INFINITY, 0.f};
+    v[k] = t.x;
+    v[k + 1] = t.y;
+  }
+  const float m = mine ? v[RV] : -INFINITY;
+  const float mw = max_in_wave(m);
+  if (lane == 0) s_red[wg][RV] = mw;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(s_red[0][RV], s_red[1][RV]), fmaxf(s_red[2][RV], s_red[3][RV]));
+  const float wgt = m == -INFINITY ? 0.f : exp2f(m - M);
+  const float zw = sum_across_rows(sum_in_row(mine ? wgt * v[RV + 1] : 0.f));
+  if (lane == 0) s_red[wg][RV + 1] = zw;
+#pragma unroll
+  for (int k = 0; k < RV; ++k) {
+    const float t = sum_across_rows(sum_in_row(fmaf(wgt, mine ? v[k] : 0.f, 0.f)));
+    if (lane == 0) s_red[wg][k] = t;
+  }
+  __syncthreads();
+  if (!has_e) return;  // after the last barrier
+  const float Z = s_red[0][RV + 1] + s_red[1][RV + 1] + s_red[2][RV + 1] + s_red[3][RV + 1];
+  float o = mue;
+#pragma unroll
+  for (int i = 0; i < WV; ++i) {
+    if constexpr (BF) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int c = 8 * i + 2 * k;
+        o = fmaf(bf16_lo(wr[i][k]), (s_red[0][c] + s_red[1][c] + s_red[2][c] + s_red[3][c]) / Z, o);
+        o = fmaf(bf16_hi(wr[i][k]), (s_red[0][c + 1] + s_red[1][c + 1] + s_red[2][c + 1] + s_red[3][c + 1]) / Z, o);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int c = 4 * i + k;
+        o = fmaf(__uint_as_float(wr[i][k]), (s_red[0][c] + s_red[1][c] + s_red[2][c] + s_red[3][c]) / Z, o);
+      }
+    }
+  }
+  if constexpr (BF) ((uint16_t *)a.out)[rh * DH + u] = (uint16_t)f32_to_bf16(o);
+  else ((float *)a.out)[rh * DH + u] = o;
+}
+
 namespace {
 constexpr int kWholeGroupSplits = 64;  // more splits than this: 4 waves per (row, head)
 
 template <bool BF>
 bool go_merge_few(const AttnArgs &a, int d_head, int r_v, long long blocks, hipStream_t stream) {
-  if (a.splits > 64) return false;
+  if (a.splits > 256) return false;
+  const bool many = a.splits > 64;  // then blocks is the (row, head) count
 #define LLA_MERGE_FEW(RV, EPL)                                                                      \
   if (r_v == RV && d_head == 64 * EPL) {                                                            \
-    hipLaunchKernelGGL((merge_few_kernel<BF, RV, EPL>), dim3((unsigned)blocks), dim3(256), 0, stream, a); \
+    if (many)                                                                                       \
+      hipLaunchKernelGGL((merge_many_kernel<BF, RV, EPL>), dim3((unsigned)blocks), dim3(256), 0, stream, a); \
+    else                                                                                            \
+      hipLaunchKernelGGL((merge_few_kernel<BF, RV, EPL>), dim3((unsigned)blocks), dim3(256), 0, stream, a); \
     return true;                                                                                    \
   }
   LLA_MERGE_FEW(32, 1) LLA_MERGE_FEW(32, 2) LLA_MERGE_FEW(64, 1) LLA_MERGE_FEW(64, 2)
