@@ -485,10 +485,13 @@ def main():
     pos0 = ctx - n_new
     ws_enc = lla.workspace(D, lla.OP_ENCODE, w.batch, 0, w.D)
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in calls]
-
-    ev_enc = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    # one set of events per timed step: the steps run back to back (as in a
+    # serving loop) and are synchronised only at the ends of the timed region
+    def mk_events():
+        return ([(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls],
+                (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
+    step_events = [mk_events() for _ in range(args.steps)]
+    ev, ev_enc = step_events[0]
 
     def step(record):
         if record:
@@ -514,12 +517,14 @@ def main():
     torch.cuda.synchronize()
     kern_ms, enc_ms = [], []
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for k in range(args.steps):
+        ev, ev_enc = step_events[k]
         step(True)
-        torch.cuda.synchronize()
-        kern_ms += [a.elapsed_time(b) for a, b in ev]
-        enc_ms.append(ev_enc[0].elapsed_time(ev_enc[1]))
+    torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    for evs, enc in step_events:
+        kern_ms += [a.elapsed_time(b) for a, b in evs]
+        enc_ms.append(enc[0].elapsed_time(enc[1]))
     assert lla.device_error_word(ws_dec) == 0 and lla.device_error_word(ws_enc) == 0
     assert not decoupled or lla.device_error_word(ws_app) == 0
     assert torch.isfinite(out.float()).all().item()
