@@ -257,6 +257,24 @@ def test_split_merges_share_one_workspace_across_shapes():
         assert (ws[:256].cpu().numpy() == 0).all()
 
 
+@pytest.mark.parametrize("dtype", [BF16, F32])
+def test_one_long_row_many_splits(dtype):
+    """One sequence of 8000 tokens (500 pages): the context is cut into more
+    than 64 splits, which a workgroup per (row, head) merges (one split per
+    thread), for both storage types."""
+    m = dims(4, 1, 16, 128, 16, 32, PER_HEAD, dtype)
+    D = lla.dims_from_dict(m)
+    ctx = np.array([8000])
+    pps = 500
+    codec = random_codec(m, seed=2502, ortho_down=False)
+    kp, vp = random_pools(m, pps, seed=2503)
+    pt = gen.shuffled_page_table(2504, 1, pps)
+    q = gen.normal(2505, 1, (1, 16, 128), dtype="bf16" if dtype == BF16 else "f32")
+    splits, _ = lla.attn_plan(D, lla.OP_DECODE, 1, int(ctx[0]))
+    assert 64 < splits <= 256, splits
+    check(m, codec, kp, vp, pt, q, ctx - 1, ctx, 0, 3, f"one long row, {splits} splits, dt={dtype}")
+
+
 def test_unused_slots_may_hold_nan():
     """Slots past ctx_len inside the last page (and whole unused pages) are never
     read into the result, even when they hold NaN."""
