@@ -194,8 +194,8 @@ __global__ __launch_bounds__(256) void encode_append_kernel(EncodeArgs a, int RK
 //    chunk row 32 s + 16 h + 4 g + e, on both operands.
 // mu W_down comes from encode_muw_kernel (once per call) and is copied into
 // LDS with the tile's first chunk.  The result (minus mu W_down, rounded once
-// to bf16) is staged in LDS with 8-byte stores and leaves as 16-byte stores
-// into the paged pool.  Workgroups are persistent (at most one per CU) and
+// to bf16) is staged in LDS with 8-byte stores (16-byte pieces swizzled per
+// row across the banks) and leaves as 16-byte stores into the paged pool.  Workgroups are persistent (at most one per CU) and
 // walk (group, token tile, layer) tiles, group fastest; the next tile's first
 // two chunks load while a tile's output is staged and drains.
 namespace {
